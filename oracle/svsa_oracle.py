@@ -1,0 +1,284 @@
+"""Plain, slow, fp64 CPU oracle of the block-sparse video attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no
+code with the HIP library (no kernels, headers, helpers or tables); the only
+thing both sides use is the seeded input generator ``svsa_synth``.
+
+Every stage reads the *same* bf16 (or fp32) values as the GPU, widened
+exactly to float64, and computes in float64 with NumPy.  Sources (web pages;
+cited by title and section):
+
+* [PSA]   "Parameterized Stripe Attention for Efficient Video Generation".
+* [iCATS] "iCATS: Fast Video Generation via Interaction-Aware Sparse Attention
+          and Timestep-Adaptive Sparsity" (paper summary page).
+* [SPADE] "SPADE: An Input-Adaptive Sparse Attention Engine for Fast Video
+          Diffusion Models Inference" (abstract page).
+* [SVOO]  "Attention Sparsity is Input-Stable: Training-Free Sparse Attention
+          for Video Generation via Offline Sparsity Profiling and Online QK
+          Co-Clustering" (metadata page with harvested function names).
+
+Readings taken where the pages are silent (each is pinned by a test):
+
+* Blocks are consecutive Bk-token chunks of the tile-ordered sequence, Bk =
+  tile volume, nb = ceil(N / Bk); only the tail of the sequence is padded.
+  Partial edge tiles stay in place (tile grid walked row-major).
+* A block summary is the mean over the block's valid tokens only.
+* Block scores are a row softmax of pooled logits scaled by 1/sqrt(D) over
+  all nb key blocks; no size weighting.
+* Top-p keeps the shortest prefix of the score-descending order (ties: lower
+  key index first) whose cumulative mass reaches p (>=); p >= 1 keeps all.
+  The diagonal band |i - j| <= w - 1 is added afterwards and is not counted
+  toward the mass.  Fixed mode keeps ceil(f_h * nb) blocks instead.
+* Attention excludes padded keys (their logits are -inf) and leaves padded
+  query rows unspecified (they are not compared).
+
+parity pins: see tests/test_oracle_*.py; every public function is pinned.
+"""
+from math import ceil, sqrt
+
+import numpy as np
+
+__all__ = [
+    "num_blocks", "tile_order", "permute_fwd", "permute_inv", "block_valid_counts",
+    "pool", "block_logits", "block_scores", "select_row", "block_mask",
+    "attention", "attention_rows", "dense_attention", "kept_flops", "widen",
+]
+
+
+def widen(x):
+    """bf16 bit patterns (uint16) or float32 values -> float64, exactly."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def num_blocks(N, Bk):
+    """nb = ceil(N / Bk): the tail block holds the remainder."""
+    return -(-N // Bk)
+
+
+# --------------------------------------------------------------------------
+# Stage 1: tile order.  [PSA] Sec. 3.2 "Efficient and Flexible Kernel": Q, K, V
+# are reorganised from the (T, H, W) layout into a block-centric arrangement
+# (T', H', W', b_t, b_h, b_w) so that every block is contiguous in memory.
+# The natural index is i = t*H*W + h*W + w ([PSA] App. D, Prop. 1).  [SVOO]
+# names the forward / inverse pair "token_reorder_to_frame_major" /
+# "to_token_major".
+# --------------------------------------------------------------------------
+def tile_order(grid, tile):
+    """pi: int64 [N]; pi[j] = natural index of the j-th token in tile order.
+
+    Tiles are visited row-major over the tile grid (ceil(T/tt), ceil(H/th),
+    ceil(W/tw)); tokens inside a tile row-major in (t, h, w).  Edge tiles are
+    partial and keep their place.  Built as a lexicographic sort of the
+    (tile coordinates, in-tile coordinates) key of every token.
+    """
+    T, H, W = grid
+    tt, th, tw = tile
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    t, h, w = t.ravel(), h.ravel(), w.ravel()
+    natural = (t * H + h) * W + w
+    # np.lexsort sorts by the last key first.
+    order = np.lexsort((w % tw, h % th, t % tt, w // tw, h // th, t // tt))
+    return natural[order].astype(np.int64)
+
+
+def permute_fwd(x, grid, tile):
+    """X'[..., j, :] = X[..., pi(j), :] for j < N; rows N..nb*Bk-1 are zero.
+
+    x: [B, Hh, N, D] in natural order (any float dtype or bf16 bits).
+    Returns float64 [B, Hh, nb*Bk, D].
+    """
+    xf = widen(x)
+    B, Hh, N, D = xf.shape
+    Bk = int(np.prod(tile))
+    nb = num_blocks(N, Bk)
+    pi = tile_order(grid, tile)
+    assert pi.shape[0] == N
+    out = np.zeros((B, Hh, nb * Bk, D))
+    out[:, :, :N, :] = xf[:, :, pi, :]
+    return out
+
+
+def permute_inv(xp, grid, tile):
+    """O[..., pi(j), :] = O'[..., j, :] for j < N (the padded tail is dropped)."""
+    xf = widen(xp)
+    N = int(np.prod(grid))
+    pi = tile_order(grid, tile)
+    out = np.empty(xf.shape[:2] + (N, xf.shape[3]))
+    out[:, :, pi, :] = xf[:, :, :N, :]
+    return out
+
+
+def block_valid_counts(N, Bk):
+    """n_i: number of real (non-padding) tokens in each block."""
+    nb = num_blocks(N, Bk)
+    n = np.full(nb, Bk, dtype=np.int64)
+    n[-1] = N - (nb - 1) * Bk
+    return n
+
+
+# --------------------------------------------------------------------------
+# Stage 2: block summaries.  [SPADE] abstract: dynamic masks are expressed as
+# a "Summarizer" followed by an "Estimator"; [iCATS] Sec. 4: region
+# importance is scored at the level of token groups.  Reading: the summary of
+# a block is the arithmetic mean of its valid tokens.
+# --------------------------------------------------------------------------
+def pool(xp, N, Bk):
+    """Xbar_i = (1/n_i) * sum of the valid rows of block i.  -> [B, Hh, nb, D]."""
+    xf = widen(xp)
+    B, Hh, Np, D = xf.shape
+    nb = num_blocks(N, Bk)
+    assert Np == nb * Bk
+    counts = block_valid_counts(N, Bk)
+    out = np.empty((B, Hh, nb, D))
+    for i in range(nb):
+        rows = xf[:, :, i * Bk: i * Bk + counts[i], :]
+        out[:, :, i, :] = rows.sum(axis=2) / counts[i]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Stage 3a: block-to-block importance, softmax(Qbar Kbar^T / sqrt(d)), one row
+# per query block ([SPADE] "Estimator"; [iCATS] Sec. 4 cluster-level scores).
+# --------------------------------------------------------------------------
+def block_logits(qbar, kbar, scale):
+    """L[b, h, i, j] = scale * <Qbar_i, Kbar_j>  (float64)."""
+    return np.matmul(qbar, np.swapaxes(kbar, -1, -2)) * scale
+
+
+def block_scores(qbar, kbar, scale):
+    """S[b, h, i, :] = exp(L - max L) / sum exp(L - max L) over all nb blocks."""
+    L = block_logits(qbar, kbar, scale)
+    e = np.exp(L - L.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Stage 3b: selection.  [iCATS] abstract and Sec. 3.2: a fixed top-p rule keeps
+# the most important key regions until their cumulative importance reaches p.
+# The band width follows the width convention of [PSA] Alg. 1 (a distance d
+# is inside a band of width w when d <= w - 1).  The fixed-fraction mode is
+# the per-layer intrinsic pruning level of [SVOO] (abstract).
+# --------------------------------------------------------------------------
+def select_row(s_row, i, band, top_p=None, keep_frac=None):
+    """Kept key blocks of query block i, ascending.
+
+    s_row: float64 [nb] block scores of the row.  Exactly one of top_p /
+    keep_frac is given (both float32 values, widened exactly).
+    """
+    nb = s_row.shape[0]
+    # score-descending, ties by ascending key index (stable sort of -s)
+    order = np.argsort(-s_row, kind="stable")
+    if keep_frac is not None:
+        k = int(ceil(float(np.float32(keep_frac)) * nb))
+        k = min(max(k, 1), nb)
+    else:
+        p = float(np.float32(top_p))
+        if p >= 1.0:
+            k = nb
+        else:
+            csum = np.cumsum(s_row[order])       # csum[r] = mass of the top r+1
+            # smallest k >= 1 whose top-k mass reaches p
+            reached = np.nonzero(csum >= p)[0]
+            k = int(reached[0]) + 1 if reached.size else nb
+    kept = np.zeros(nb, dtype=bool)
+    kept[order[:k]] = True
+    j = np.arange(nb)
+    kept |= np.abs(j - i) <= band - 1
+    return np.nonzero(kept)[0].astype(np.int32)
+
+
+def block_mask(S, band, top_p=None, keep_frac=None):
+    """CSR of kept blocks over rows r = (b*Hh + h)*nb + i.
+
+    S: [B, Hh, nb, nb] block scores; top_p / keep_frac: per-head arrays (one is
+    None).  Returns (row_ptr int64 [B*Hh*nb+1], col_idx int32 [nnz]).
+    """
+    B, Hh, nb, _ = S.shape
+    counts, cols = [], []
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nb):
+                if keep_frac is not None:
+                    c = select_row(S[b, h, i], i, band, keep_frac=keep_frac[h])
+                else:
+                    c = select_row(S[b, h, i], i, band, top_p=top_p[h])
+                cols.append(c)
+                counts.append(c.size)
+    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
+    return row_ptr, col_idx
+
+
+# --------------------------------------------------------------------------
+# Stage 4: block-sparse attention over the kept blocks.  [PSA] App. B, Alg. 2:
+# per query block, S = Q K^T over each listed KV block, invalid (padded)
+# positions set to -inf, safe softmax, P V accumulated into the output.
+# The oracle evaluates the same quantity directly: one softmax over the union
+# of the kept blocks' valid keys (what the blockwise accumulation equals).
+# --------------------------------------------------------------------------
+def attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale):
+    """Output rows of query block i of (b, h) as float64 [n_i, D].
+
+    qp, kp, vp: tiled [B, Hh, nb*Bk, D] arrays (bf16 bits or float).
+    cols: kept key blocks of this row.
+    """
+    nb = num_blocks(N, Bk)
+    n_i = min(Bk, N - i * Bk)
+    q = widen(qp[b, h, i * Bk: i * Bk + n_i])
+    keys = np.concatenate([np.arange(j * Bk, min((j + 1) * Bk, N)) for j in cols])
+    assert all(0 <= j < nb for j in cols)
+    k = widen(kp[b, h, keys])
+    v = widen(vp[b, h, keys])
+    logits = (q @ k.T) * scale
+    wgt = np.exp(logits - logits.max(axis=1, keepdims=True))
+    wgt /= wgt.sum(axis=1, keepdims=True)
+    return wgt @ v
+
+
+def attention(qp, kp, vp, row_ptr, col_idx, N, Bk, scale, rows=None):
+    """O' (tiled, float64 [B, Hh, nb*Bk, D]) for the listed query blocks.
+
+    rows: optional iterable of (b, h, i); default all.  Rows not computed and
+    padded query rows are NaN.
+    """
+    B, Hh, Np, D = qp.shape
+    nb = num_blocks(N, Bk)
+    out = np.full((B, Hh, Np, D), np.nan)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(Hh) for i in range(nb)]
+    for (b, h, i) in rows:
+        r = (b * Hh + h) * nb + i
+        cols = col_idx[row_ptr[r]: row_ptr[r + 1]]
+        n_i = min(Bk, N - i * Bk)
+        out[b, h, i * Bk: i * Bk + n_i] = attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale)
+    return out
+
+
+def dense_attention(q, k, v, scale):
+    """softmax(Q K^T * scale) V over all N keys, natural order, float64."""
+    qf, kf, vf = widen(q), widen(k), widen(v)
+    logits = np.matmul(qf, np.swapaxes(kf, -1, -2)) * scale
+    wgt = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    wgt /= wgt.sum(axis=-1, keepdims=True)
+    return np.matmul(wgt, vf)
+
+
+def kept_flops(row_ptr, col_idx, N, Bk, D, nrows_per_head=None):
+    """Algorithmic FLOPs of block-sparse attention: 4*D*sum_(i,j kept) n_i*n_j.
+
+    This is the accounting of [PSA] Table 2, whose dense rows equal 4*N^2*D*heads.
+    """
+    nb = num_blocks(N, Bk)
+    n = block_valid_counts(N, Bk)
+    total = 0
+    nrows = len(row_ptr) - 1
+    for r in range(nrows):
+        i = r % nb
+        cols = col_idx[row_ptr[r]: row_ptr[r + 1]]
+        total += int(n[i]) * int(n[cols].sum())
+    return 4 * D * total

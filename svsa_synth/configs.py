@@ -1,0 +1,66 @@
+"""The five workload shapes of the block-sparse video attention path.
+
+Grids and head shapes follow the pages: the Wan2.1 / HunyuanVideo latent
+grids 21x45x80 and 33x45x80 are the DiT shapes given in the PSA paper
+(Parameterized Stripe Attention for Efficient Video Generation), App. C.2
+"Initialization of Mask Candidates", and heads x head_dim (40x128 for Wan2.1-14B, 24x128
+for HunyuanVideo) are the ones that reproduce the dense TFLOP column of PSA
+Table 2 (4*N^2*D*heads).  The tiny and small cases are CPU-checkable shapes.
+"""
+from dataclasses import dataclass, field
+from math import ceil
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    cfg_id: int          # enters every seed, so configs never share draws
+    batch: int
+    heads: int
+    head_dim: int
+    grid: tuple          # (T, H, W) latent grid
+    tile: tuple          # (tt, th, tw) tile shape; block = one tile volume
+    src_dtype: str       # "fp32" (tiny case) or "bf16"
+    top_p: tuple         # top-p values run on this config (first = default)
+    band: int = 1        # diagonal band width w: keep |i-j| <= w-1
+    pe_scale: str = "fixed"      # "fixed" (1.5) or "uniform" (U[0.5, 3.0] per head)
+    pe_freq: str = "unit"        # "unit" or "per_head" (2^U[-2,0] per head)
+    fixed_mode: bool = False     # also run the per-head keep-fraction mode
+
+    @property
+    def N(self):
+        T, H, W = self.grid
+        return T * H * W
+
+    @property
+    def Bk(self):
+        tt, th, tw = self.tile
+        return tt * th * tw
+
+    @property
+    def nb(self):
+        return ceil(self.N / self.Bk)
+
+    @property
+    def N_pad(self):
+        return self.nb * self.Bk
+
+
+CONFIGS = {
+    "tiny": Config("tiny", 1, 1, 1, 64, (4, 8, 8), (2, 4, 4), "fp32", (0.9,)),
+    "small": Config("small", 2, 1, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
+                    pe_freq="per_head"),
+    "wan480": Config("wan480", 3, 1, 40, 128, (21, 30, 52), (4, 4, 4), "bf16", (0.9,),
+                     pe_scale="uniform"),
+    "wan720": Config("wan720", 4, 1, 40, 128, (21, 45, 80), (4, 4, 4), "bf16",
+                     (0.9, 0.8, 0.95), pe_scale="uniform"),
+    "hv720": Config("hv720", 5, 1, 24, 128, (33, 45, 80), (4, 4, 4), "bf16", (0.9,),
+                    pe_scale="uniform", fixed_mode=True),
+}
+
+
+def get_config(name):
+    try:
+        return CONFIGS[name]
+    except KeyError:
+        raise KeyError(f"unknown config {name!r}; known: {sorted(CONFIGS)}") from None

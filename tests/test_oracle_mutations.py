@@ -1,0 +1,98 @@
+"""Each pin must catch a plausible mistake: plant one in the oracle (on the CPU,
+via monkeypatch) and check that the corresponding pin test fails."""
+import numpy as np
+import pytest
+
+from oracle import svsa_oracle as orc
+import tests.test_oracle_attention as ta
+import tests.test_oracle_permute as tp
+import tests.test_oracle_select as ts
+
+
+def _scores_no_scale(qbar, kbar, scale):
+    L = np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+    e = np.exp(L - L.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _scores_transposed(qbar, kbar, scale):
+    L = np.matmul(kbar, np.swapaxes(qbar, -1, -2)) * scale
+    e = np.exp(L - L.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def _pool_divide_by_bk(xp, N, Bk):
+    xf = orc.widen(xp)
+    B, Hh, Np, D = xf.shape
+    return xf.reshape(B, Hh, Np // Bk, Bk, D).sum(axis=3) / Bk
+
+
+def _tile_order_swapped(grid, tile):
+    T, H, W = grid
+    tt, th, tw = tile
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    t, h, w = t.ravel(), h.ravel(), w.ravel()
+    order = np.lexsort((h % th, w % tw, t % tt, w // tw, h // th, t // tt))
+    return ((t * H + h) * W + w)[order]
+
+
+_orig_select = orc.select_row
+
+
+def _select_band_off_by_one(s_row, i, band, top_p=None, keep_frac=None):
+    return _orig_select(s_row, i, band + 1, top_p=top_p, keep_frac=keep_frac)
+
+
+def _select_strict(s_row, i, band, top_p=None, keep_frac=None):
+    if top_p is None:
+        return _orig_select(s_row, i, band, keep_frac=keep_frac)
+    order = np.argsort(-s_row, kind="stable")
+    csum = np.cumsum(s_row[order])
+    k = int(np.nonzero(csum > float(np.float32(top_p)))[0][0]) + 1 if np.any(
+        csum > float(np.float32(top_p))) else s_row.size
+    kept = np.zeros(s_row.size, bool)
+    kept[order[:k]] = True
+    kept |= np.abs(np.arange(s_row.size) - i) <= band - 1
+    return np.nonzero(kept)[0]
+
+
+def _attention_rows_with_pads(qp, kp, vp, b, h, i, cols, N, Bk, scale):
+    n_i = min(Bk, N - i * Bk)
+    q = orc.widen(qp[b, h, i * Bk: i * Bk + n_i])
+    keys = np.concatenate([np.arange(j * Bk, (j + 1) * Bk) for j in cols])
+    k, v = orc.widen(kp[b, h, keys]), orc.widen(vp[b, h, keys])
+    lg = q @ k.T * scale
+    w = np.exp(lg - lg.max(1, keepdims=True))
+    return (w / w.sum(1, keepdims=True)) @ v
+
+
+def _attention_rows_v_is_k(qp, kp, vp, b, h, i, cols, N, Bk, scale):
+    return _orig_rows(qp, kp, kp, b, h, i, cols, N, Bk, scale)
+
+
+_orig_rows = orc.attention_rows
+
+MUTATIONS = [
+    ("block_scores", _scores_no_scale, ts.test_scores_closed_form_one_channel, ()),
+    ("block_scores", _scores_transposed, ts.test_scores_closed_form_one_channel, ()),
+    ("pool", _pool_divide_by_bk, tp.test_pool_tail_uses_valid_count_and_constant_stays_constant, ()),
+    ("tile_order", _tile_order_swapped, tp.test_tile_order_worked_example, ("golden",)),
+    ("select_row", _select_band_off_by_one, ts.test_band_width, ()),
+    ("select_row", _select_strict, ts.test_topp_reaching_p_exactly_is_inclusive, ()),
+    ("attention_rows", _attention_rows_with_pads, ta.test_padded_keys_are_excluded, ()),
+    ("attention_rows", _attention_rows_v_is_k, ta.test_all_blocks_kept_equals_dense_sdpa,
+     ("grid_tile",)),
+]
+
+
+@pytest.mark.parametrize("name,fn,pin,args", MUTATIONS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_pin_catches_planted_mistake(monkeypatch, golden_dir, name, fn, pin, args):
+    monkeypatch.setattr(orc, name, fn)
+    call = []
+    for a in args:
+        call.append(golden_dir if a == "golden" else None)
+    if args == ("grid_tile",):
+        call = [(4, 8, 8), (2, 4, 4)]
+    with pytest.raises(AssertionError):
+        pin(*call)
