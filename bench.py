@@ -1,0 +1,261 @@
+"""Benchmark of the block-sparse video attention path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: tile reorder of Q, K, V -> block means of Q, K ->
+top-p block mask -> block-sparse attention -> inverse reorder of the output.
+
+Prints ONE JSON line.  ``value`` = kept-block attention FLOPs per step divided
+by the whole step time (TFLOP/s); the attention kernel alone, the dense run
+(every block kept, same kernel, same inputs), per-stage times, the roofline of
+the attention kernel and the CPU oracle baseline are reported beside it.
+
+FLOP accounting: 4 * D * sum over kept (i, j) of n_i * n_j (valid tokens only);
+with every block kept this is 4 * N^2 * D * heads, the dense column of the PSA
+paper's Table 2 (117.05 TFLOP for the Wan2.1-720p shape).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+from math import sqrt
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan720",
+                    choices=["tiny", "small", "wan480", "wan720", "hv720"])
+    ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--fixed", action="store_true", help="per-head keep-fraction mode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def kept_flops_from_csr(rp, ci, N, Bk, nb, D):
+    """4*D*sum n_i*n_j from host copies of the CSR (vectorised bookkeeping)."""
+    n = np.full(nb, Bk, np.int64)
+    n[-1] = N - (nb - 1) * Bk
+    rows = len(rp) - 1
+    counts = np.diff(rp)
+    row_i = np.repeat(np.arange(rows) % nb, counts)
+    return 4 * D * int(np.sum(n[row_i] * n[ci[: rp[-1]]]))
+
+
+def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
+    """The oracle on a bounded sample: the full mask stages of one head plus the
+    attention of seeded query blocks of that head, extrapolated to a whole step."""
+    from oracle import svsa_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    N, Bk, nb, D = cfg.N, cfg.Bk, cfg.nb, cfg.head_dim
+    scale = 1 / sqrt(D)
+    t0 = time.perf_counter()
+    qp = orc.permute_fwd(inp_head.q, cfg.grid, cfg.tile)
+    kp = orc.permute_fwd(inp_head.k, cfg.grid, cfg.tile)
+    vp = orc.permute_fwd(inp_head.v, cfg.grid, cfg.tile)
+    S = orc.block_scores(orc.pool(qp, N, Bk), orc.pool(kp, N, Bk), scale)
+    rp, ci = orc.block_mask(S, cfg.band, top_p=np.array([top_p], np.float32))
+    t_mask = time.perf_counter() - t0
+    rng = np.random.default_rng(11)
+    order = rng.permutation(nb)
+    t1 = time.perf_counter()
+    done, flops = 0, 0
+    n = orc.block_valid_counts(N, Bk)
+    for i in order:
+        cols = ci[rp[i]: rp[i + 1]]
+        orc.attention_rows(qp, kp, vp, 0, 0, int(i), cols, N, Bk, scale)
+        flops += 4 * D * int(n[i]) * int(n[cols].sum())
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_attn = time.perf_counter() - t1
+    # extrapolate: mask stages per head x heads, attention at the measured FLOP rate
+    step_s = t_mask * heads_total + total_flops / (flops / t_attn)
+    return {
+        "value": total_flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: permute+pool+scores+top-p mask of 1 head "
+                   f"({t_mask:.2f} s) and attention of {done}/{nb} seeded query blocks of that "
+                   f"head ({t_attn:.2f} s, {flops / t_attn / 1e9:.2f} GFLOP/s); whole-step time "
+                   f"extrapolated to {heads_total} heads = {step_s:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by head "
+              "across GPUs with no exchange inside the op, so a single-GPU figure is the unit.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_17_amd as m
+    from svsa_synth import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    geom = m.Geometry(*cfg.grid, *cfg.tile)
+    top_p = args.top_p if args.top_p is not None else cfg.top_p[0]
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg, seed=args.seed)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] inputs {cfg.name} generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    bsa = m.BlockSparseAttention(cfg.batch, cfg.heads, cfg.head_dim, geom)
+    tp = None if args.fixed else np.full(cfg.heads, top_p, np.float32)
+    kf = inp.keep_frac if args.fixed else None
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stage_names = ["permute_qkv", "pool", "mask", "attention", "permute_out"]
+
+    def step(record=None):
+        marks = [ev() for _ in range(6)] if record is not None else None
+        if marks: marks[0].record(stream)
+        bsa.permute_in(q, k, v)
+        if marks: marks[1].record(stream)
+        m.svsa_pool(bsa.qt, bsa.qbar, geom)
+        m.svsa_pool(bsa.kt, bsa.kbar, geom)
+        if marks: marks[2].record(stream)
+        m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
+                          bsa.mask_ws, top_p=tp, keep_frac=kf, band_width=cfg.band)
+        if marks: marks[3].record(stream)
+        bsa.attend()
+        if marks: marks[4].record(stream)
+        bsa.permute_out()
+        if marks:
+            marks[5].record(stream)
+            record.append(marks)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region: exactly K whole steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    recs = []
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    stage_ms = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]))
+                for i, n in enumerate(stage_names)}
+    step_ms = float(np.mean([r[0].elapsed_time(r[5]) for r in recs]))
+    print(f"[bench] timed {args.steps} steps: {wall_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    rp = bsa.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bsa.col_idx[: int(rp[-1])].cpu().numpy()
+    flops = kept_flops_from_csr(rp, ci, cfg.N, cfg.Bk, cfg.nb, cfg.head_dim)
+    dense_flops = 4 * cfg.N * cfg.N * cfg.head_dim * cfg.heads * cfg.batch
+    kept_frac = flops / dense_flops
+    counts = np.diff(rp).reshape(cfg.batch * cfg.heads, cfg.nb)
+    sparsity_per_head = 1 - counts.sum(1) / cfg.nb ** 2
+
+    attn_ms = stage_ms["attention"]
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+
+    dense = None
+    if not args.no_dense:
+        # same kernel with every block kept, same inputs
+        m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
+                          bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
+        bsa.attend()
+        torch.cuda.synchronize()
+        reps = max(2, min(5, args.steps))
+        d_ev = [(ev(), ev()) for _ in range(reps)]
+        for a, b in d_ev:
+            a.record(stream)
+            bsa.attend()
+            b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in d_ev]))
+        dense = {"attention_ms": dense_ms,
+                 "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                 "frac_peak": dense_flops / (dense_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "speedup_attention": dense_ms / attn_ms,
+                 "speedup_step": (step_ms - attn_ms + dense_ms) / step_ms}
+        print(f"[bench] dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        head = 0
+        inp1 = make_inputs(cfg, seed=args.seed, heads=[head])
+        cpu = cpu_baseline(cfg, inp1, top_p if not args.fixed else 0.9, args.cpu_budget_s,
+                           cfg.heads * cfg.batch, flops)
+        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "kept-block attention TFLOP/s and % bf16 MFMA peak; speedup vs dense, 1 GPU",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + shared 3D sinusoidal positional term, bf16)",
+        "config": {
+            "workload": (f"{cfg.name}: grid {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]} "
+                         f"({cfg.N} tokens), tiles {cfg.tile[0]}x{cfg.tile[1]}x{cfg.tile[2]}, "
+                         f"{cfg.nb} blocks, {cfg.heads} heads, head_dim {cfg.head_dim}, batch "
+                         f"{cfg.batch}, " + ("fixed keep-fraction mode" if args.fixed
+                                             else f"top-p {top_p}") + f", band {cfg.band}"),
+            "global_batch": cfg.batch,
+            "seq_len": cfg.N,
+            "parallelism": "single GPU",
+        },
+        "kept_tflop_per_step": flops / 1e12,
+        "dense_tflop": dense_flops / 1e12,
+        "kept_fraction": kept_frac,
+        "sparsity_per_head": {"min": float(sparsity_per_head.min()),
+                              "mean": float(sparsity_per_head.mean()),
+                              "max": float(sparsity_per_head.max())},
+        "stage_ms": stage_ms,
+        "attention_tflops": attn_tflops,
+        "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
+        "dense": dense,
+        "roofline": {
+            "kernel": "svsa_block_sparse_attn (union + order + attn_kernel)",
+            "bound": "mfma",
+            "achieved": attn_tflops,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": attn_tflops / BF16_PEAK_TFLOPS,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

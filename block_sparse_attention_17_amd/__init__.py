@@ -1,0 +1,15 @@
+"""MI355X (gfx950) block-sparse video attention: top-p block masks over 3D tiles.
+
+Python face of ``libsvsa.so`` (HIP kernels behind a C ABI, ``include/svsa.h``).
+Importing fails loudly when the library has not been built.
+"""
+from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, library, library_path,
+                      status_string, svsa_attn_workspace_bytes, svsa_block_mask,
+                      svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
+                      svsa_status_string, svsa_tile_permute, svsa_version)
+from .pipeline import BlockSparseAttention
+
+__all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
+           "library_path", "status_string", "svsa_attn_workspace_bytes", "svsa_block_mask",
+           "svsa_block_mask_workspace_bytes", "svsa_block_sparse_attn", "svsa_pool",
+           "svsa_status_string", "svsa_tile_permute", "svsa_version", "BlockSparseAttention"]

@@ -1,0 +1,221 @@
+"""ctypes binding of libsvsa.so: argument marshalling only.
+
+Every function here has the name of the C entry point it wraps and does no
+arithmetic of the method: it checks tensor properties, turns torch tensors
+into device pointers and the current torch stream into a hipStream_t, calls
+the library, and raises ``SvsaError`` on a non-zero status.  torch provides
+device memory and streams; all computation runs in the HIP kernels.
+
+The library must be built (``python -m block_sparse_attention_17_amd._build``);
+importing this module without it raises immediately: there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvsa.so")
+
+SVSA_BF16, SVSA_F32 = 0, 1
+SVSA_OK = 0
+
+
+class SvsaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "W", "tt", "th", "tw")]
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """Latent grid (T, H, W) and tile shape (tt, th, tw)."""
+    T: int
+    H: int
+    W: int
+    tt: int
+    th: int
+    tw: int
+
+    @property
+    def N(self):
+        return self.T * self.H * self.W
+
+    @property
+    def Bk(self):
+        return self.tt * self.th * self.tw
+
+    @property
+    def nb(self):
+        return -(-self.N // self.Bk)
+
+    @property
+    def N_pad(self):
+        return self.nb * self.Bk
+
+    def c(self):
+        return _Geom(self.T, self.H, self.W, self.tt, self.th, self.tw)
+
+    @staticmethod
+    def from_config(cfg):
+        return Geometry(*cfg.grid, *cfg.tile)
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m block_sparse_attention_17_amd._build` "
+            "(the block-sparse attention path has no non-HIP fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz, dbl, flt = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_size_t, ctypes.c_double, ctypes.c_float)
+    gp = ctypes.POINTER(_Geom)
+    fp = ctypes.POINTER(ctypes.c_float)
+    sig = {
+        "svsa_tile_permute": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, gp, i32, vp]),
+        "svsa_pool": (ctypes.c_int, [vp, i32, vp, i32, i32, i32, gp, vp]),
+        "svsa_block_mask_workspace_bytes": (sz, [i32, i32, i32]),
+        "svsa_block_mask": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, dbl, fp, fp, i32, vp, vp,
+                                           i64, vp, sz, vp]),
+        "svsa_attn_workspace_bytes": (sz, [i32, i32, gp]),
+        "svsa_block_sparse_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp, vp,
+                                                  vp, sz, vp]),
+        "svsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "svsa_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
+            "svsa_block_mask", "svsa_attn_workspace_bytes", "svsa_block_sparse_attn",
+            "svsa_status_string", "svsa_version")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def library():
+    return _lib
+
+
+def status_string(status):
+    return _lib.svsa_status_string(int(status)).decode()
+
+
+svsa_status_string = status_string
+
+
+def svsa_version():
+    return _lib.svsa_version()
+
+
+def _check(fn, status):
+    if status != SVSA_OK:
+        raise SvsaError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t, name, dtypes=None, device=True):
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SVSA_BF16
+    if t.dtype == torch.float32:
+        return SVSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def svsa_tile_permute(src, dst, geom, inverse=False, stream=None):
+    """dst <- tile-ordered src (inverse=False) or natural-ordered src (inverse=True)."""
+    import torch
+    B, Hh, _, D = src.shape
+    _check("svsa_tile_permute", _lib.svsa_tile_permute(
+        _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
+        _dtype_code(src), B, Hh, D, ctypes.byref(geom.c()), int(bool(inverse)), _stream(stream)))
+    return dst
+
+
+def svsa_pool(x_tiled, out, geom, stream=None):
+    """out (float64 [B, Hh, nb, D]) <- per-block means of the valid rows of x_tiled."""
+    import torch
+    B, Hh, _, D = x_tiled.shape
+    _check("svsa_pool", _lib.svsa_pool(
+        _ptr(x_tiled, "x_tiled", (torch.bfloat16, torch.float32)), _dtype_code(x_tiled),
+        _ptr(out, "out", (torch.float64,)), B, Hh, D, ctypes.byref(geom.c()), _stream(stream)))
+    return out
+
+
+def svsa_block_mask_workspace_bytes(batch, heads, nb):
+    return int(_lib.svsa_block_mask_workspace_bytes(batch, heads, nb))
+
+
+def _host_f32(a, heads, name):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.broadcast_to(np.asarray(a, dtype=np.float32), (heads,)))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def svsa_block_mask(qbar, kbar, softmax_scale, row_ptr, col_idx, workspace, top_p=None,
+                    keep_frac=None, band_width=1, stream=None):
+    """CSR (row_ptr, col_idx) of kept key blocks from float64 block summaries."""
+    import torch
+    B, Hh, nb, D = qbar.shape
+    tp_arr, tp = _host_f32(top_p, Hh, "top_p")
+    kf_arr, kf = _host_f32(keep_frac, Hh, "keep_frac")
+    _check("svsa_block_mask", _lib.svsa_block_mask(
+        _ptr(qbar, "qbar", (torch.float64,)), _ptr(kbar, "kbar", (torch.float64,)), B, Hh, nb, D,
+        float(softmax_scale), tp, kf, int(band_width), _ptr(row_ptr, "row_ptr", (torch.int32,)),
+        _ptr(col_idx, "col_idx", (torch.int32,)), col_idx.numel(),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+    del tp_arr, kf_arr
+    return row_ptr, col_idx
+
+
+def svsa_attn_workspace_bytes(batch, heads, geom):
+    return int(_lib.svsa_attn_workspace_bytes(batch, heads, ctypes.byref(geom.c())))
+
+
+def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, workspace,
+                           stream=None):
+    """out (bf16, tile order) <- block-sparse attention of q, k, v over the CSR lists."""
+    import torch
+    B, Hh, _, D = q.shape
+    bf = (torch.bfloat16,)
+    _check("svsa_block_sparse_attn", _lib.svsa_block_sparse_attn(
+        _ptr(q, "q", bf), _ptr(k, "k", bf), _ptr(v, "v", bf), _ptr(out, "out", bf), B, Hh, D,
+        ctypes.byref(geom.c()), float(softmax_scale), _ptr(row_ptr, "row_ptr", (torch.int32,)),
+        _ptr(col_idx, "col_idx", (torch.int32,)), _ptr(workspace, "workspace", (torch.uint8,)),
+        workspace.numel(), _stream(stream)))
+    return out

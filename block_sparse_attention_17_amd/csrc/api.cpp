@@ -1,0 +1,162 @@
+// C ABI of the block-sparse video attention library: argument checks, geometry,
+// workspace sizing and launches on the caller's stream.  Every check runs on
+// the host before any work is enqueued; no C++ exception leaves this file.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/svsa.h"
+#include "svsa_internal.h"
+
+using svsa::Geom;
+
+namespace {
+
+constexpr int32_t kMaxHeadsMask = 256;
+constexpr int32_t kMaxNb = 4096;
+
+bool make_geom(const svsa_geom* in, Geom* g) {
+  if (!in) return false;
+  if (in->T < 1 || in->H < 1 || in->W < 1 || in->tt < 1 || in->th < 1 || in->tw < 1) return false;
+  const int64_t N = (int64_t)in->T * in->H * in->W;
+  const int64_t Bk = (int64_t)in->tt * in->th * in->tw;
+  if (N >= (1ll << 30) || Bk >= 65536) return false;
+  g->T = in->T; g->H = in->H; g->W = in->W;
+  g->tt = in->tt; g->th = in->th; g->tw = in->tw;
+  g->nT = (in->T + in->tt - 1) / in->tt;
+  g->nH = (in->H + in->th - 1) / in->th;
+  g->nW = (in->W + in->tw - 1) / in->tw;
+  g->N = (int32_t)N;
+  g->Bk = (int32_t)Bk;
+  g->nb = (int32_t)((N + Bk - 1) / Bk);
+  const int64_t Npad = (int64_t)g->nb * Bk;
+  if (Npad >= (1ll << 30)) return false;
+  g->Npad = (int32_t)Npad;
+  return true;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int elt_bytes(int32_t dtype) {
+  return dtype == SVSA_BF16 ? 2 : dtype == SVSA_F32 ? 4 : 0;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? SVSA_OK : SVSA_E_HIP; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int svsa_version(void) { return 100; }
+
+const char* svsa_status_string(int status) {
+  switch (status) {
+    case SVSA_OK: return "ok";
+    case SVSA_E_INVALID: return "invalid argument";
+    case SVSA_E_UNSUPPORTED: return "unsupported argument (dtype, head_dim or size limit)";
+    case SVSA_E_WORKSPACE: return "workspace too small";
+    case SVSA_E_CAPACITY: return "col_idx capacity below the worst case";
+    case SVSA_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int svsa_tile_permute(const void* src, void* dst, int32_t dtype, int32_t batch, int32_t heads,
+                      int32_t head_dim, const svsa_geom* gin, int32_t inverse, void* stream) {
+  Geom g;
+  if (!src || !dst || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
+    return SVSA_E_INVALID;
+  const int eb = elt_bytes(dtype);
+  if (!eb) return SVSA_E_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)head_dim * eb;
+  if (row_bytes % 16 != 0 || !is_pow2(row_bytes / 16) || row_bytes > 4096)
+    return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * g.nT * g.nH * g.nW > 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  const size_t src_bytes = (size_t)bh * (inverse ? g.Npad : g.N) * row_bytes;
+  const size_t dst_bytes = (size_t)bh * (inverse ? g.N : g.Npad) * row_bytes;
+  if (overlaps(src, src_bytes, dst, dst_bytes)) return SVSA_E_INVALID;
+  return from_hip(svsa::launch_tile_permute(src, dst, eb, (int32_t)bh, head_dim, g, inverse != 0,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int svsa_pool(const void* x_tiled, int32_t dtype, double* out, int32_t batch, int32_t heads,
+              int32_t head_dim, const svsa_geom* gin, void* stream) {
+  Geom g;
+  if (!x_tiled || !out || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
+    return SVSA_E_INVALID;
+  const int eb = elt_bytes(dtype);
+  if (!eb) return SVSA_E_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)head_dim * eb;
+  if (row_bytes % 16 != 0 || row_bytes / 16 > 256 || 256 % (row_bytes / 16) != 0 ||
+      (256 / (row_bytes / 16)) * head_dim * 8 > 64 * 1024)
+    return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * g.nb > 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  return from_hip(svsa::launch_pool(x_tiled, dtype == SVSA_BF16, out, (int32_t)bh, head_dim, g,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t svsa_block_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nb) {
+  if (batch < 1 || heads < 1 || nb < 1) return 0;
+  return svsa::mask_ws_layout((int64_t)batch * heads * nb, nb).total;
+}
+
+int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32_t heads,
+                    int32_t nb, int32_t head_dim, double softmax_scale, const float* top_p,
+                    const float* keep_frac, int32_t band_width, int32_t* row_ptr,
+                    int32_t* col_idx, int64_t col_capacity, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  if (!qbar || !kbar || !row_ptr || !col_idx || batch < 1 || heads < 1 || nb < 1 ||
+      head_dim < 1 || band_width < 1 || !isfinite(softmax_scale))
+    return SVSA_E_INVALID;
+  if ((top_p == nullptr) == (keep_frac == nullptr)) return SVSA_E_INVALID;
+  const float* par = top_p ? top_p : keep_frac;
+  for (int32_t h = 0; h < heads && h < kMaxHeadsMask; ++h)
+    if (!(par[h] > 0.f && par[h] <= 1.f)) return SVSA_E_INVALID;
+  if (heads > kMaxHeadsMask || nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int64_t worst = (int64_t)batch * heads * nb * nb;
+  if (worst >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (col_capacity < worst) return SVSA_E_CAPACITY;
+  if (!workspace || ws_bytes < svsa_block_mask_workspace_bytes(batch, heads, nb))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_block_mask(qbar, kbar, batch * heads, heads, nb, head_dim,
+                                          softmax_scale, top_p, keep_frac, band_width, row_ptr,
+                                          col_idx, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
+  Geom g;
+  if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;
+  return svsa::attn_ws_layout(batch * heads, g.nb).total;
+}
+
+int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                           int32_t heads, int32_t head_dim, const svsa_geom* gin,
+                           float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  if (!q || !k || !v || !out || !row_ptr || !col_idx || batch < 1 || heads < 1 ||
+      head_dim < 1 || !make_geom(gin, &g) || !isfinite(softmax_scale))
+    return SVSA_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
+  if (g.Bk != 64 || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * g.nb * (int64_t)g.nb >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;
+  if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
+      overlaps(out, tbytes, v, tbytes))
+    return SVSA_E_INVALID;
+  if (!workspace || ws_bytes < svsa_attn_workspace_bytes(batch, heads, gin))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_block_sparse_attn(q, k, v, out, (int32_t)bh, head_dim, g,
+                                                 softmax_scale, row_ptr, col_idx, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

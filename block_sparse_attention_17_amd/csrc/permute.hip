@@ -1,0 +1,100 @@
+// Stage 1: tile reorder of (T,H,W) tokens (and its inverse).
+//
+// [PSA] "Parameterized Stripe Attention for Efficient Video Generation",
+// Sec. 3.2: Q, K, V are reorganised from (T,H,W) into a block-centric layout
+// so that each block's tokens are contiguous and loads coalesce.
+//
+// One workgroup moves one tile.  Tiles are walked row-major over the tile
+// grid; inside a tile tokens are row-major in (t,h,w); edge tiles are partial.
+// The tiled offset of tile (a,b,c) with extents (sa,sb,sc) is
+//   a*tt*H*W + sa*(b*th)*W + sa*sb*(c*tw)
+// because every tile before it in the walk is full along the axes that are
+// already complete.  Rows are copied 16 bytes per lane, so both the gather
+// side and the scatter side move whole contiguous rows.
+#include "svsa_internal.h"
+
+namespace svsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// floor(n / d) for n, d < 2^16 via a 32-bit reciprocal: m = ceil(2^32 / d)
+// gives the exact quotient because n * (m*d - 2^32) < 2^16 * d <= 2^32.
+__device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t m) {
+  return __umulhi(n, m);
+}
+__device__ __forceinline__ uint32_t recip_small(uint32_t d) {
+  return (uint32_t)((0x100000000ull + d - 1) / d);
+}
+
+// chunks_per_row = head_dim * element_bytes / 16 is a power of two (2^chunk_shift).
+template <int kInverse>
+__global__ void __launch_bounds__(kThreads)
+tile_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int32_t chunk_shift,
+                    Geom g) {
+  const int32_t chunks_per_row = 1 << chunk_shift;
+  const int32_t ntiles = g.nT * g.nH * g.nW;
+  const int32_t tile = blockIdx.x % ntiles;
+  const int64_t bh = blockIdx.x / ntiles;
+  const int32_t a = tile / (g.nH * g.nW);
+  const int32_t b = (tile / g.nW) % g.nH;
+  const int32_t c = tile % g.nW;
+  const int32_t sa = min(g.tt, g.T - a * g.tt);
+  const int32_t sb = min(g.th, g.H - b * g.th);
+  const int32_t sc = min(g.tw, g.W - c * g.tw);
+  const int32_t vol = sa * sb * sc;
+  const int64_t tiled0 = (int64_t)a * g.tt * g.H * g.W + (int64_t)sa * (b * g.th) * g.W +
+                         (int64_t)sa * sb * (c * g.tw);
+  const int64_t nat0 = ((int64_t)(a * g.tt) * g.H + b * g.th) * g.W + c * g.tw;
+  const uint32_t m_sc = recip_small(sc), m_plane = recip_small(sb * sc);
+
+  const int64_t nat_rows = (int64_t)g.N, tiled_rows = (int64_t)g.Npad;
+  const uint4* sbase = src + bh * (kInverse ? tiled_rows : nat_rows) * chunks_per_row;
+  uint4* dbase = dst + bh * (kInverse ? nat_rows : tiled_rows) * chunks_per_row;
+
+  const int32_t total = vol * chunks_per_row;
+  for (int32_t e = threadIdx.x; e < total; e += kThreads) {
+    const uint32_t tok = (uint32_t)e >> chunk_shift;
+    const int32_t ch = e & (chunks_per_row - 1);
+    const uint32_t lt = div_small(tok, m_plane);
+    const uint32_t rem = tok - lt * (uint32_t)(sb * sc);
+    const uint32_t lh = div_small(rem, m_sc);
+    const uint32_t lw = rem - lh * (uint32_t)sc;
+    const int64_t nat = nat0 + ((int64_t)lt * g.H + lh) * g.W + lw;
+    const int64_t til = tiled0 + tok;
+    if (kInverse) {
+      dbase[nat * chunks_per_row + ch] = sbase[til * chunks_per_row + ch];
+    } else {
+      dbase[til * chunks_per_row + ch] = sbase[nat * chunks_per_row + ch];
+    }
+  }
+  // The workgroup of the last tile also clears the padded tail (forward only).
+  if (!kInverse && tile == ntiles - 1) {
+    const int32_t pad_chunks = (g.Npad - g.N) * chunks_per_row;
+    uint4* tail = dbase + (int64_t)g.N * chunks_per_row;
+    for (int32_t e = threadIdx.x; e < pad_chunks; e += kThreads) tail[e] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
+                               int32_t head_dim, const Geom& g, bool inverse,
+                               hipStream_t stream) {
+  const int32_t chunks = head_dim * elt_bytes / 16;
+  int32_t shift = 0;
+  while ((1 << shift) < chunks) ++shift;
+  if ((1 << shift) != chunks) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)bh * g.nT * g.nH * g.nW;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (inverse) {
+    hipLaunchKernelGGL(tile_permute_kernel<1>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       (const uint4*)src, (uint4*)dst, shift, g);
+  } else {
+    hipLaunchKernelGGL(tile_permute_kernel<0>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       (const uint4*)src, (uint4*)dst, shift, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace svsa

@@ -1,0 +1,48 @@
+// Internal declarations shared by the library's translation units (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svsa {
+
+// Derived geometry of one call.
+struct Geom {
+  int32_t T, H, W, tt, th, tw;
+  int32_t nT, nH, nW;   // tile grid
+  int32_t N, Bk, nb, Npad;
+};
+
+// Launchers: enqueue on `stream`, return the launch status.
+hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
+                               int32_t head_dim, const Geom& g, bool inverse,
+                               hipStream_t stream);
+hipError_t launch_pool(const void* x, bool is_bf16, double* out, int32_t bh,
+                       int32_t head_dim, const Geom& g, hipStream_t stream);
+
+// Block-mask workspace layout (all offsets 256-byte aligned).
+struct MaskWs {
+  size_t logits_off, bits_off, counts_off, total;
+  int32_t words;  // bitmap words per row
+};
+MaskWs mask_ws_layout(int64_t rows, int32_t nb);
+hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh, int32_t heads,
+                             int32_t nb, int32_t head_dim, double scale, const float* top_p,
+                             const float* keep_frac, int32_t band, int32_t* row_ptr,
+                             int32_t* col_idx, void* ws, hipStream_t stream);
+
+// Attention workspace layout.
+struct AttnWs {
+  size_t list_off, count_off, order_off, total;
+  int64_t items;
+  int32_t groups;  // query-block groups per (b, h)
+};
+constexpr int kQBlocksPerGroup = 4;  // query blocks sharing one K/V stream
+AttnWs attn_ws_layout(int32_t bh, int32_t nb);
+hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
+                                    int32_t bh, int32_t head_dim, const Geom& g, float scale,
+                                    const int32_t* row_ptr, const int32_t* col_idx, void* ws,
+                                    hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace svsa

@@ -1,0 +1,189 @@
+/*
+ * svsa.h - C ABI of the MI355X (gfx950) block-sparse video attention library.
+ *
+ * The library computes training-free, input-adaptive block-sparse
+ * self-attention over 3D video tokens in four stages, each a separate call:
+ *
+ *   1. svsa_tile_permute  reorder (T,H,W) tokens into contiguous tiles
+ *   2. svsa_pool          mean-pool Q and K per block (block summaries)
+ *   3. svsa_block_mask    softmax(Qbar Kbar^T * scale) per query block, keep the
+ *                         top-p (or a fixed fraction of) key blocks plus a
+ *                         diagonal band, emitted as CSR index lists
+ *   4. svsa_block_sparse_attn
+ *                         flash attention with online softmax over the kept
+ *                         blocks only
+ *
+ * Sources (web pages, cited by title and section):
+ *   [PSA]   "Parameterized Stripe Attention for Efficient Video Generation"
+ *   [iCATS] "iCATS: Fast Video Generation via Interaction-Aware Sparse
+ *           Attention and Timestep-Adaptive Sparsity"
+ *   [SPADE] "SPADE: An Input-Adaptive Sparse Attention Engine for Fast Video
+ *           Diffusion Models Inference"
+ *   [SVOO]  "Attention Sparsity is Input-Stable: Training-Free Sparse
+ *           Attention for Video Generation via Offline Sparsity Profiling and
+ *           Online QK Co-Clustering"
+ *
+ * Conventions shared by every call
+ *   - Tensor pointers are DEVICE pointers allocated and owned by the caller.
+ *     The calls never allocate or free memory and keep no state between calls.
+ *   - Per-head parameter arrays (top_p, keep_frac) are HOST pointers, read
+ *     during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on it and returns without waiting.
+ *   - Geometry: N = T*H*W tokens, Bk = tt*th*tw tokens per block,
+ *     nb = ceil(N / Bk) blocks, N_pad = nb * Bk.  Tensors are
+ *     [batch, heads, tokens, head_dim] row-major; natural token order is
+ *     i = t*H*W + h*W + w ([PSA] App. D, Prop. 1).
+ *   - Errors: argument errors are detected on the host before any work is
+ *     enqueued and return a negative status; a failed launch returns
+ *     SVSA_E_HIP.  No C++ exception crosses this interface.
+ *   - Results are bitwise reproducible run to run (no floating-point atomics).
+ */
+#ifndef SVSA_H
+#define SVSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define SVSA_API __attribute__((visibility("default")))
+#else
+#define SVSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Latent grid (T,H,W) and tile shape (tt,th,tw); all must be >= 1. */
+typedef struct svsa_geom {
+  int32_t T, H, W;
+  int32_t tt, th, tw;
+} svsa_geom;
+
+enum svsa_dtype { SVSA_BF16 = 0, SVSA_F32 = 1 };
+
+enum svsa_status {
+  SVSA_OK = 0,
+  SVSA_E_INVALID = -1,     /* null pointer, non-positive size, bad value     */
+  SVSA_E_UNSUPPORTED = -2, /* valid but not implemented (dtype, head_dim...) */
+  SVSA_E_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes   */
+  SVSA_E_CAPACITY = -4,    /* col_idx capacity below the worst case          */
+  SVSA_E_HIP = -5          /* a HIP launch failed                            */
+};
+
+/*
+ * Stage 1 - tile reorder.  [PSA] Sec. 3.2 "Efficient and Flexible Kernel":
+ * Q, K, V move from the (T,H,W) layout to a block-centric arrangement so that
+ * every block is contiguous in memory.  [SVOO] lists a forward / inverse pair
+ * of token reorders ("..._to_frame_major" / "..._to_token_major").
+ *
+ * Tile order: tiles are walked row-major over the tile grid
+ * (ceil(T/tt), ceil(H/th), ceil(W/tw)), tokens inside a tile row-major in
+ * (t,h,w); tiles at the grid edge are partial and keep their place.
+ *
+ *   inverse == 0: src [batch,heads,N,D] natural  -> dst [batch,heads,N_pad,D]
+ *                 tiled; rows N..N_pad-1 of dst are written with zeros.
+ *   inverse != 0: src [batch,heads,N_pad,D] tiled -> dst [batch,heads,N,D]
+ *                 natural; the padded rows of src are not read.
+ * dtype: SVSA_BF16 or SVSA_F32 (bit-exact copy either way).  head_dim * element
+ * size must be a multiple of 16 bytes.  src and dst must not overlap.
+ * Tile volume must be < 65536.
+ */
+SVSA_API int svsa_tile_permute(const void* src, void* dst, int32_t dtype, int32_t batch,
+                      int32_t heads, int32_t head_dim, const svsa_geom* g,
+                      int32_t inverse, void* stream);
+
+/*
+ * Stage 2 - block summaries.  [SPADE] abstract: dynamic masks are expressed
+ * through a Summarizer and an Estimator; the summary used here is the mean of
+ * a block's valid tokens (the tail block has n = N - (nb-1)*Bk of them).
+ *
+ * x_tiled: [batch,heads,N_pad,D] tiled (output of svsa_tile_permute), dtype
+ * SVSA_BF16 or SVSA_F32.  out: float64 [batch,heads,nb,D];
+ * out[i] = (sum of the valid rows of block i, accumulated in float64) / n_i.
+ */
+SVSA_API int svsa_pool(const void* x_tiled, int32_t dtype, double* out, int32_t batch,
+              int32_t heads, int32_t head_dim, const svsa_geom* g, void* stream);
+
+/*
+ * Workspace (device bytes) needed by svsa_block_mask for these sizes.
+ * Returns 0 if the sizes are invalid.
+ */
+SVSA_API size_t svsa_block_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nb);
+
+/*
+ * Stage 3 - block mask.  Block-to-block importance is the row softmax of
+ * L_ij = softmax_scale * <qbar_i, kbar_j> over all nb key blocks ([SPADE]
+ * Estimator; [iCATS] Sec. 4, cluster-level scores).  Per (batch, head, query
+ * block i) the kept set is
+ *   top-p mode  (top_p != NULL): the shortest prefix of the key blocks sorted
+ *               by score descending (ties: lower index first) whose summed
+ *               score reaches top_p[h] (>=); top_p[h] == 1 keeps every block
+ *               ([iCATS] abstract and Sec. 3.2, the fixed top-p rule);
+ *   fixed mode  (keep_frac != NULL): the ceil(keep_frac[h] * nb) best blocks in
+ *               the same order ([SVOO] abstract, per-layer pruning levels);
+ * united with the diagonal band |i - j| <= band_width - 1 (the width convention
+ * of [PSA] Alg. 1).  The band is added after selection and does not count
+ * toward the mass.  All arithmetic of this stage is float64.
+ *
+ * qbar, kbar: float64 [batch,heads,nb,D] (svsa_pool outputs).
+ * top_p, keep_frac: HOST float arrays [heads]; exactly one is non-NULL; every
+ *   value must lie in (0, 1].
+ * band_width >= 1.
+ * row_ptr: int32 [batch*heads*nb + 1] (rows ordered (b, h, i)); col_idx: int32
+ *   with col_capacity >= batch*heads*nb*nb entries (the worst case; the actual
+ *   count is row_ptr[last]).  Each row's columns are ascending and unique.
+ * workspace: device buffer of at least
+ *   svsa_block_mask_workspace_bytes(batch, heads, nb) bytes.
+ * Limits: nb <= 4096, heads <= 256, batch*heads*nb*nb < 2^31.
+ */
+SVSA_API int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch,
+                    int32_t heads, int32_t nb, int32_t head_dim,
+                    double softmax_scale, const float* top_p,
+                    const float* keep_frac, int32_t band_width,
+                    int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace (device bytes) needed by svsa_block_sparse_attn.  Returns 0 if the
+ * sizes are invalid.
+ */
+SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* g);
+
+/*
+ * Stage 4 - block-sparse attention.  [PSA] App. B, Alg. 2: for each query
+ * block, walk its KV-block list, S = Q K^T, invalid (padded) key positions set
+ * to -inf, safe softmax, P V accumulated into the block's output; [SPADE]
+ * "flash block-sparse attention".  Here the softmax is the online (running
+ * max / running sum) form, so the result equals one softmax over all valid
+ * keys of the kept blocks:
+ *   out[q] = sum_t softmax_t(softmax_scale * <q, k_t>) v_t,
+ *   t over the valid keys (index < N) of the blocks listed for q's block.
+ *
+ * q, k, v, out: bf16 [batch,heads,N_pad,D] in tile order.  Output rows of
+ *   padded query positions (>= N) are written but unspecified.  out must not
+ *   overlap q, k or v.  A query block with an empty list gets zeros.
+ * row_ptr / col_idx: CSR as produced by svsa_block_mask (rows (b,h,i); each
+ *   column in [0, nb)).  Columns outside [0, nb) are ignored.
+ * head_dim: 64 or 128.  Products are bf16 x bf16 on the matrix cores with
+ *   float32 accumulation; the softmax runs in float32.
+ * workspace: at least svsa_attn_workspace_bytes(batch, heads, g) bytes.
+ */
+SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
+                           int32_t batch, int32_t heads, int32_t head_dim,
+                           const svsa_geom* g, float softmax_scale,
+                           const int32_t* row_ptr, const int32_t* col_idx,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+SVSA_API const char* svsa_status_string(int status);
+
+/* Library ABI version (major*100 + minor). */
+SVSA_API int svsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVSA_H */

@@ -1,0 +1,211 @@
+"""Shared machinery of the GPU parity tests: run the HIP path through the C ABI
+and the fp64 oracle on the same seeded inputs, and compare them.
+
+Tolerances (stated by the method's acceptance bar):
+  * permutation and index lists: bit-exact; the only mask difference allowed is
+    a block whose score lies within 1e-4 (relative) of the row's top-p
+    threshold (see ``mask_mismatch``);
+  * block means: bit-exact float64;
+  * attention, run with the oracle's mask: max |err| <= 2e-2 and relative L2
+    error <= 5e-3 over the valid output rows.
+"""
+import sys
+from functools import lru_cache
+from math import sqrt
+
+import numpy as np
+import torch
+
+from oracle import svsa_oracle as orc
+from svsa_synth import get_config, make_inputs
+
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+MASK_REL = 1e-4
+
+
+def log(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_to_bits(t):
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def geometry(cfg):
+    import block_sparse_attention_17_amd as m
+    return m.Geometry(*cfg.grid, *cfg.tile)
+
+
+@lru_cache(maxsize=8)
+def inputs(name, seed=0):
+    log(f"generating inputs {name} seed={seed}")
+    return make_inputs(name, seed=seed)
+
+
+class GpuRun:
+    """Stage-by-stage outputs of the HIP path for one config (host copies)."""
+
+    def __init__(self, name, seed=0):
+        import block_sparse_attention_17_amd as m
+        self.cfg = cfg = get_config(name)
+        self.inp = inp = inputs(name, seed)
+        self.geom = geometry(cfg)
+        self.m = m
+        self.bsa = m.BlockSparseAttention(cfg.batch, cfg.heads, cfg.head_dim, self.geom)
+        log(f"{name}: permute Q,K,V on the GPU")
+        self.q_dev, self.k_dev, self.v_dev = (bits_to_dev(x) for x in (inp.q, inp.k, inp.v))
+        self.bsa.permute_in(self.q_dev, self.k_dev, self.v_dev)
+        log(f"{name}: pool Q,K on the GPU")
+        m.svsa_pool(self.bsa.qt, self.bsa.qbar, self.geom)
+        m.svsa_pool(self.bsa.kt, self.bsa.kbar, self.geom)
+        torch.cuda.synchronize()
+        self.qt_bits = dev_to_bits(self.bsa.qt)
+        self.kt_bits = dev_to_bits(self.bsa.kt)
+        self.vt_bits = dev_to_bits(self.bsa.vt)
+        self.qbar = self.bsa.qbar.cpu().numpy()
+        self.kbar = self.bsa.kbar.cpu().numpy()
+
+    def mask(self, top_p=None, keep_frac=None, band=1):
+        log(f"{self.cfg.name}: block mask top_p={top_p} keep_frac={keep_frac is not None}")
+        self.bsa.build_mask(top_p=top_p, keep_frac=keep_frac, band_width=band)
+        torch.cuda.synchronize()
+        rp = self.bsa.row_ptr.cpu().numpy().astype(np.int64)
+        ci = self.bsa.col_idx[: int(rp[-1])].cpu().numpy()
+        return rp, ci
+
+    def attention(self, rp, ci):
+        """Tiled bf16 output bits of the attention stage run on the given CSR."""
+        log(f"{self.cfg.name}: attention on {int(rp[-1])} kept blocks")
+        rpd = torch.from_numpy(rp.astype(np.int32)).cuda()
+        cid = torch.from_numpy(ci.astype(np.int32)).cuda()
+        self.bsa.attend(row_ptr=rpd, col_idx=cid)
+        torch.cuda.synchronize()
+        return dev_to_bits(self.bsa.ot)
+
+
+@lru_cache(maxsize=8)
+def gpu_run(name, seed=0):
+    return GpuRun(name, seed)
+
+
+class OracleRun:
+    """Oracle stages on the same inputs (independent of every GPU result)."""
+
+    def __init__(self, name, seed=0):
+        self.cfg = cfg = get_config(name)
+        self.inp = inp = inputs(name, seed)
+        log(f"{name}: oracle tile order / pool / scores")
+        self.pi = orc.tile_order(cfg.grid, cfg.tile)
+        self.qt_bits = self._permute_bits(inp.q)
+        self.kt_bits = self._permute_bits(inp.k)
+        self.vt_bits = self._permute_bits(inp.v)
+        self.qbar = np.concatenate([orc.pool(self.qt_bits[:, h:h + 1], cfg.N, cfg.Bk)
+                                    for h in range(cfg.heads)], axis=1)
+        self.kbar = np.concatenate([orc.pool(self.kt_bits[:, h:h + 1], cfg.N, cfg.Bk)
+                                    for h in range(cfg.heads)], axis=1)
+        self.S = orc.block_scores(self.qbar, self.kbar, 1 / sqrt(cfg.head_dim))
+
+    def _permute_bits(self, x):
+        cfg = self.cfg
+        out = np.zeros(x.shape[:2] + (cfg.N_pad, x.shape[3]), np.uint16)
+        out[:, :, : cfg.N] = x[:, :, self.pi]
+        return out
+
+    def mask(self, top_p=None, keep_frac=None, band=1):
+        log(f"{self.cfg.name}: oracle mask")
+        return orc.block_mask(self.S, band, top_p=top_p, keep_frac=keep_frac)
+
+    def attention_blocks(self, rp, ci, rows):
+        cfg = self.cfg
+        scale = 1 / sqrt(cfg.head_dim)
+        res = {}
+        for (b, h, i) in rows:
+            r = (b * cfg.heads + h) * cfg.nb + i
+            cols = ci[rp[r]: rp[r + 1]]
+            res[(b, h, i)] = orc.attention_rows(self.qt_bits, self.kt_bits, self.vt_bits, b, h, i,
+                                                cols, cfg.N, cfg.Bk, scale)
+        return res
+
+
+@lru_cache(maxsize=8)
+def oracle_run(name, seed=0):
+    return OracleRun(name, seed)
+
+
+def mask_mismatch(cfg, S, g_rp, g_ci, o_rp, o_ci, top_p=None, keep_frac=None, band=1):
+    """Rows where GPU and oracle lists differ, split into (tolerated, failing).
+
+    A row is tolerated when either
+      (a) every differing block j is outside the band and its score is within
+          1e-4 relative of tau, the smallest score the oracle selected by
+          top-p / top-k in that row, or
+      (b) the GPU set lies between the oracle's sets at p(1-1e-4) and p(1+1e-4)
+          (top-p mode; the cumulative mass sits within 1e-4 of p).
+    """
+    nb = cfg.nb
+    tolerated, failing = [], []
+    rows = len(o_rp) - 1
+    for r in range(rows):
+        G = g_ci[g_rp[r]: g_rp[r + 1]]
+        R = o_ci[o_rp[r]: o_rp[r + 1]]
+        if G.size == R.size and np.array_equal(G, R):
+            continue
+        b_h, i = divmod(r, nb)
+        b, h = divmod(b_h, cfg.heads)
+        s = S[b, h, i]
+        Gs, Rs = set(G.tolist()), set(R.tolist())
+        band_set = {j for j in range(max(0, i - band + 1), min(nb, i + band))}
+        # selected-by-rule set of the oracle (band-only additions excluded)
+        order = np.argsort(-s, kind="stable")
+        if keep_frac is not None:
+            k = min(max(int(np.ceil(float(np.float32(keep_frac[h])) * nb)), 1), nb)
+        else:
+            p = float(np.float32(top_p[h]))
+            cs = np.cumsum(s[order])
+            hit = np.nonzero(cs >= p)[0]
+            k = nb if p >= 1 else (int(hit[0]) + 1 if hit.size else nb)
+        tau = s[order[k - 1]]
+        ok_a = all((j not in band_set) and abs(s[j] - tau) <= MASK_REL * tau for j in Gs ^ Rs)
+        ok_b = False
+        if top_p is not None:
+            lo = set(orc.select_row(s, i, band, top_p=np.float32(top_p[h] * (1 - MASK_REL))).tolist())
+            hi = set(orc.select_row(s, i, band, top_p=np.float32(min(1.0, top_p[h] * (1 + MASK_REL)))).tolist())
+            ok_b = lo <= Gs <= hi
+        (tolerated if (ok_a or ok_b) else failing).append(r)
+    return tolerated, failing
+
+
+def attn_errors(gpu_tiled_bits, ref_blocks, cfg):
+    """max-abs and rel-L2 of GPU rows against oracle float64 rows (valid rows only)."""
+    g_all, r_all = [], []
+    for (b, h, i), ref in ref_blocks.items():
+        n_i = ref.shape[0]
+        g = orc.widen(gpu_tiled_bits[b, h, i * cfg.Bk: i * cfg.Bk + n_i])
+        g_all.append(g.ravel())
+        r_all.append(ref.ravel())
+    g = np.concatenate(g_all)
+    r = np.concatenate(r_all)
+    max_abs = float(np.max(np.abs(g - r)))
+    rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    return max_abs, rel
+
+
+def sample_rows(cfg, rp, n_per_head, seed=1, heads=None):
+    """Seeded q-block sample: per head the tail block, block 0, the heaviest and
+    lightest rows, plus random ones."""
+    rng = np.random.default_rng(seed)
+    nb = cfg.nb
+    counts = np.diff(rp).reshape(cfg.batch, cfg.heads, nb)
+    rows = []
+    for b in range(cfg.batch):
+        for h in (range(cfg.heads) if heads is None else heads):
+            pick = {0, nb - 1, int(np.argmax(counts[b, h])), int(np.argmin(counts[b, h]))}
+            pick |= set(rng.choice(nb, size=min(nb, n_per_head), replace=False).tolist())
+            rows += [(b, h, i) for i in sorted(pick)]
+    return rows

@@ -1,0 +1,119 @@
+"""The C ABI: the library loads, exports every declared entry point, and rejects
+invalid arguments on the host before touching a GPU (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "svsa.h")).read()
+    return sorted(set(re.findall(r"SVSA_API\s+[\w\s\*]*?\b(svsa_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def mod():
+    import block_sparse_attention_17_amd as m
+    return m
+
+
+def test_every_declared_symbol_is_exported(mod):
+    names = _declared()
+    assert len(names) == 8, names
+    lib = ctypes.CDLL(mod.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mod.EXPORTED)
+
+
+def test_status_strings(mod):
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(mod.status_string(s), str) and mod.status_string(s)
+    assert mod.svsa_version() >= 100
+
+
+def _g(mod, *v):
+    return ctypes.byref(mod.Geometry(*v).c())
+
+
+FAKE = ctypes.c_void_p(0x1000)    # never dereferenced: every call below fails validation
+FAKE2 = ctypes.c_void_p(0x800000)
+
+
+def test_permute_argument_errors(mod):
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)
+    E_INV, E_UNS = -1, -2
+    assert lib.svsa_tile_permute(None, FAKE2, 0, 1, 1, 64, g, 0, None) == E_INV
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 0, 1, 64, g, 0, None) == E_INV
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 7, 1, 1, 64, g, 0, None) == E_UNS   # dtype
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 12, g, 0, None) == E_UNS   # 24-byte rows
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 64, None, 0, None) == E_INV
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 64, _g(mod, 0, 8, 8, 2, 4, 4), 0,
+                                 None) == E_INV
+    assert lib.svsa_tile_permute(FAKE, FAKE, 0, 1, 1, 64, g, 0, None) == E_INV    # in place
+
+
+def test_pool_argument_errors(mod):
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)
+    assert lib.svsa_pool(None, 0, FAKE, 1, 1, 64, g, None) == -1
+    assert lib.svsa_pool(FAKE, 0, None, 1, 1, 64, g, None) == -1
+    assert lib.svsa_pool(FAKE, 3, FAKE2, 1, 1, 64, g, None) == -2
+
+
+def _fa(vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def test_block_mask_argument_errors(mod):
+    lib = mod.library()
+    nb = 8
+    ws = mod.svsa_block_mask_workspace_bytes(1, 2, nb)
+    assert ws > 0 and mod.svsa_block_mask_workspace_bytes(0, 1, 8) == 0
+    cap = 2 * nb * nb
+    ok_p = _fa([0.9, 0.5])
+    args = lambda **kw: [kw.get("qbar", FAKE), FAKE2, 1, 2, nb, 64, 0.125,
+                         kw.get("top_p", ok_p), kw.get("keep", None), kw.get("band", 1), FAKE,
+                         FAKE2, kw.get("cap", cap), kw.get("ws", FAKE), kw.get("wsb", ws), None]
+    assert lib.svsa_block_mask(*args(qbar=None)) == -1
+    assert lib.svsa_block_mask(*args(top_p=None)) == -1                      # neither mode
+    assert lib.svsa_block_mask(*args(keep=_fa([0.2, 0.3]))) == -1            # both modes
+    assert lib.svsa_block_mask(*args(top_p=_fa([0.9, 0.0]))) == -1           # p not in (0,1]
+    assert lib.svsa_block_mask(*args(top_p=_fa([1.5, 0.9]))) == -1
+    assert lib.svsa_block_mask(*args(band=0)) == -1
+    assert lib.svsa_block_mask(*args(cap=cap - 1)) == -4
+    assert lib.svsa_block_mask(*args(wsb=ws - 1)) == -3
+    assert lib.svsa_block_mask(*args(ws=None)) == -3
+    big = [FAKE, FAKE2, 1, 1, 5000, 64, 0.1, _fa([0.9]), None, 1, FAKE, FAKE2, 10 ** 9, FAKE,
+           10 ** 12, None]
+    assert lib.svsa_block_mask(*big) == -2                                   # nb > 4096
+
+
+def test_attention_argument_errors(mod):
+    lib = mod.library()
+    G = mod.Geometry(8, 16, 16, 4, 4, 4)
+    g = ctypes.byref(G.c())
+    ws = mod.svsa_attn_workspace_bytes(1, 2, G)
+    assert ws > 0
+    P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(4)]
+    base = lambda D=64, gg=g, wsb=ws, out=P[3]: [P[0], P[1], P[2], out, 1, 2, D, gg, 0.125, FAKE,
+                                                 FAKE2, FAKE, wsb, None]
+    assert lib.svsa_block_sparse_attn(*base(D=96)) == -2
+    assert lib.svsa_block_sparse_attn(*base(gg=_g(mod, 4, 8, 8, 2, 4, 4))) == -2  # Bk = 32
+    assert lib.svsa_block_sparse_attn(*base(wsb=ws - 1)) == -3
+    assert lib.svsa_block_sparse_attn(*base(out=P[0])) == -1                  # out aliases q
+    b = base(); b[0] = None
+    assert lib.svsa_block_sparse_attn(*b) == -1
+
+
+def test_binding_refuses_host_tensors(mod):
+    import torch
+    G = mod.Geometry(4, 8, 8, 2, 4, 4)
+    x = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16)
+    y = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mod.svsa_tile_permute(x, y, G)

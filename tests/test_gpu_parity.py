@@ -1,0 +1,241 @@
+"""GPU parity of every stage against the fp64 oracle, through the C ABI.
+
+Run on an MI355X:  python -u -m pytest tests -m gpu -x -v --timeout 120 --timeout-method thread
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import svsa_oracle as orc  # noqa: E402
+from svsa_synth import get_config  # noqa: E402
+
+from tests import gpu_cases as gc  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny", "small", "wan480", "wan720", "hv720"]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ---------------------------------------------------------------- stage 1
+@pytest.mark.parametrize("name", ALL)
+def test_permute_bit_exact(name):
+    run, orun = gc.gpu_run(name), gc.oracle_run(name)
+    for tag, g, o in (("q", run.qt_bits, orun.qt_bits), ("k", run.kt_bits, orun.kt_bits),
+                      ("v", run.vt_bits, orun.vt_bits)):
+        assert np.array_equal(g, o), f"{name}: permuted {tag} differs"
+
+
+@pytest.mark.parametrize("name", ["small", "wan720"])
+def test_inverse_permute_round_trip(name):
+    import block_sparse_attention_17_amd as m
+    run = gc.gpu_run(name)
+    back = torch.empty_like(run.q_dev)
+    m.svsa_tile_permute(run.bsa.qt, back, run.geom, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), run.q_dev.view(torch.int16))
+
+
+@pytest.mark.parametrize("grid,tile,D", [((3, 5, 6), (2, 2, 4), 64), ((5, 7, 3), (4, 4, 4), 128),
+                                         ((21, 30, 52), (4, 4, 4), 64), ((1, 1, 1), (2, 2, 2), 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_permute_partial_tiles_and_f32(grid, tile, D, dtype):
+    import block_sparse_attention_17_amd as m
+    G = m.Geometry(*grid, *tile)
+    rng = np.random.default_rng(7)
+    N = G.N
+    if dtype == "f32":
+        x = rng.standard_normal((2, 3, N, D)).astype(np.float32)
+        xd = torch.from_numpy(x).cuda()
+    else:
+        x = rng.integers(0, 0x7F7F, size=(2, 3, N, D), dtype=np.uint16)
+        xd = gc.bits_to_dev(x)
+    out = torch.full((2, 3, G.N_pad, D), 7, dtype=xd.dtype, device="cuda")
+    m.svsa_tile_permute(xd, out, G)
+    ref = orc.permute_fwd(x, grid, tile)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, ref)
+    back = torch.empty_like(xd)
+    m.svsa_tile_permute(out, back, G, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back.cpu(), xd.cpu())
+
+
+# ---------------------------------------------------------------- stage 2
+@pytest.mark.parametrize("name", ALL)
+def test_pool_bit_exact(name):
+    run, orun = gc.gpu_run(name), gc.oracle_run(name)
+    assert np.array_equal(run.qbar, orun.qbar), f"{name}: Qbar differs"
+    assert np.array_equal(run.kbar, orun.kbar), f"{name}: Kbar differs"
+
+
+def test_pool_f32_partial_tail():
+    import block_sparse_attention_17_amd as m
+    G = m.Geometry(3, 5, 6, 2, 2, 4)   # N = 90, Bk = 16, tail block of 10
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, 2, G.N, 64)).astype(np.float32)
+    xt = torch.empty((1, 2, G.N_pad, 64), dtype=torch.float32, device="cuda")
+    m.svsa_tile_permute(torch.from_numpy(x).cuda(), xt, G)
+    out = torch.empty((1, 2, G.nb, 64), dtype=torch.float64, device="cuda")
+    m.svsa_pool(xt, out, G)
+    ref = orc.pool(orc.permute_fwd(x, (3, 5, 6), (2, 2, 4)), G.N, G.Bk)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------- stage 3
+MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
+              ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
+              ("hv720", 0.9, None), ("hv720", None, "keep")]
+
+
+@pytest.mark.parametrize("name,p,mode", MASK_CASES)
+def test_block_mask_matches_oracle(name, p, mode):
+    cfg = get_config(name)
+    run, orun = gc.gpu_run(name), gc.oracle_run(name)
+    heads = cfg.heads
+    top_p = None if mode else np.full(heads, p, np.float32)
+    keep = run.inp.keep_frac if mode else None
+    g_rp, g_ci = run.mask(top_p=top_p, keep_frac=keep, band=cfg.band)
+    o_rp, o_ci = orun.mask(top_p=top_p, keep_frac=keep, band=cfg.band)
+    assert g_rp.shape == o_rp.shape
+    tol, bad = gc.mask_mismatch(cfg, orun.S, g_rp, g_ci, o_rp, o_ci, top_p=top_p,
+                                keep_frac=keep, band=cfg.band)
+    gc.log(f"{name} p={p} mode={mode}: {len(tol)} tolerated rows, {len(bad)} failing, "
+           f"kept fraction {o_rp[-1] / (heads * cfg.nb ** 2):.4f}")
+    assert not bad, f"rows {bad[:10]} differ beyond the threshold tolerance"
+    # every GPU row ascending and unique
+    for r in range(0, len(g_rp) - 1, max(1, (len(g_rp) - 1) // 997)):
+        row = g_ci[g_rp[r]: g_rp[r + 1]]
+        assert np.all(np.diff(row) > 0)
+
+
+def test_block_mask_band_and_limits():
+    cfg = get_config("small")
+    run, orun = gc.gpu_run("small"), gc.oracle_run("small")
+    for kw in (dict(top_p=np.full(cfg.heads, 1.0, np.float32)),
+               dict(top_p=np.full(cfg.heads, 1e-6, np.float32)),
+               dict(keep_frac=np.full(cfg.heads, 1.0, np.float32)),
+               dict(top_p=np.linspace(0.3, 0.99, cfg.heads).astype(np.float32))):
+        for band in (1, 3):
+            g_rp, g_ci = run.mask(band=band, **kw)
+            o_rp, o_ci = orun.mask(band=band, **kw)
+            tol, bad = gc.mask_mismatch(cfg, orun.S, g_rp, g_ci, o_rp, o_ci, band=band, **kw)
+            assert not bad
+
+
+# ---------------------------------------------------------------- stage 4
+ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2)]
+
+
+@pytest.mark.parametrize("name,per_head", ATTN_CASES)
+def test_attention_matches_oracle(name, per_head):
+    cfg = get_config(name)
+    run, orun = gc.gpu_run(name), gc.oracle_run(name)
+    p = cfg.top_p[0]
+    o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, p, np.float32), band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    if per_head is None:
+        rows = [(b, h, i) for b in range(cfg.batch) for h in range(cfg.heads) for i in range(cfg.nb)]
+    else:
+        rows = gc.sample_rows(cfg, o_rp, per_head)
+    ref = orun.attention_blocks(o_rp, o_ci, rows)
+    max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
+    gc.log(f"{name}: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_attention_fixed_mode_hv720():
+    cfg = get_config("hv720")
+    run, orun = gc.gpu_run("hv720"), gc.oracle_run("hv720")
+    keep = run.inp.keep_frac
+    o_rp, o_ci = orun.mask(keep_frac=keep, band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    rows = gc.sample_rows(cfg, o_rp, 2, seed=5)
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+    gc.log(f"hv720 fixed: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_dense_path_equals_dense_attention():
+    """Every block kept (p = 1) through the whole path = dense softmax attention."""
+    import block_sparse_attention_17_amd as m
+    cfg = get_config("small")
+    run = gc.gpu_run("small")
+    out = run.bsa(run.q_dev, run.k_dev, run.v_dev, top_p=np.ones(cfg.heads, np.float32))
+    torch.cuda.synchronize()
+    got = orc.widen(gc.dev_to_bits(out))
+    inp = run.inp
+    ref = orc.dense_attention(inp.q, inp.k, inp.v, 1 / np.sqrt(cfg.head_dim))
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err.max() <= gc.MAX_ABS and rel <= gc.REL_L2
+    assert run.bsa.row_ptr[-1].item() == cfg.heads * cfg.nb * cfg.nb
+
+
+def test_whole_path_bitwise_deterministic():
+    cfg = get_config("wan480")
+    run = gc.gpu_run("wan480")
+    outs = []
+    for _ in range(2):
+        o = run.bsa(run.q_dev, run.k_dev, run.v_dev, top_p=np.full(cfg.heads, 0.9, np.float32))
+        torch.cuda.synchronize()
+        outs.append(o.clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_attention_edge_cases_custom_csr():
+    """Empty row -> zeros; out-of-range columns ignored; one block per row is
+    local attention; the tail block's padded keys never contribute."""
+    import block_sparse_attention_17_amd as m
+    cfg = get_config("small")
+    run, orun = gc.gpu_run("small"), gc.oracle_run("small")
+    nb, H = cfg.nb, cfg.heads
+    rows_cols = []
+    for h in range(H):
+        for i in range(nb):
+            if (h, i) == (0, 5):
+                rows_cols.append([])                      # empty
+            elif (h, i) == (1, 7):
+                rows_cols.append([-3, 2, 7, nb + 4])      # out-of-range ignored
+            else:
+                rows_cols.append([i])                     # diagonal only
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in rows_cols])
+    ci = np.array([c for cs in rows_cols for c in cs], np.int32)
+    out_bits = run.attention(rp, ci)
+    zero_blk = orc.widen(out_bits[0, 0, 5 * 64: 6 * 64])
+    assert np.all(zero_blk == 0)
+    clean = [[c for c in cs if 0 <= c < nb] for cs in rows_cols]
+    rp2 = np.zeros_like(rp)
+    rp2[1:] = np.cumsum([len(c) for c in clean])
+    ci2 = np.array([c for cs in clean for c in cs], np.int32)
+    rows = [(0, h, i) for h in range(H) for i in range(nb) if (h, i) != (0, 5)]
+    ref = orun.attention_blocks(rp2, ci2, rows)
+    max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_tail_keys_masked_wan720():
+    """The 16-token tail block of the Wan-720p shape: padded keys are excluded."""
+    cfg = get_config("wan720")
+    run, orun = gc.gpu_run("wan720"), gc.oracle_run("wan720")
+    nb, H = cfg.nb, cfg.heads
+    # every row of heads 0..1 keeps {0, nb-1}: the tail block is always involved
+    rp_l, ci_l = [0], []
+    for h in range(H):
+        for i in range(nb):
+            cols = sorted({0, i, nb - 1}) if h < 2 else [i]
+            ci_l += cols
+            rp_l.append(len(ci_l))
+    rp = np.array(rp_l, np.int64)
+    ci = np.array(ci_l, np.int32)
+    out_bits = run.attention(rp, ci)
+    rows = [(0, h, i) for h in (0, 1) for i in (0, 1, 500, nb - 2, nb - 1)]
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
