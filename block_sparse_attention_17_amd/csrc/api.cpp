@@ -133,7 +133,7 @@ int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32
 size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
   Geom g;
   if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;
-  return svsa::attn_ws_layout(batch * heads, g.nb).total;
+  return svsa::attn_ws_layout(batch * heads, g.nb, g.Bk).total;
 }
 
 int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
@@ -145,7 +145,7 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
       head_dim < 1 || !make_geom(gin, &g) || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
   if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
-  if (g.Bk != 64 || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  if ((g.Bk != 64 && g.Bk != 32) || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
   const int64_t bh = (int64_t)batch * heads;
   if (bh * g.nb * (int64_t)g.nb >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
   const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;

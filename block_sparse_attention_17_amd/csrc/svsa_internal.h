@@ -34,10 +34,10 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
 struct AttnWs {
   size_t list_off, count_off, order_off, total;
   int64_t items;
-  int32_t groups;  // query-block groups per (b, h)
+  int32_t groups;      // query-block groups per (b, h)
+  int32_t group_size;  // query blocks per group (256 query rows per group)
 };
-constexpr int kQBlocksPerGroup = 4;  // query blocks sharing one K/V stream
-AttnWs attn_ws_layout(int32_t bh, int32_t nb);
+AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk);
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,

@@ -103,7 +103,7 @@ def test_attention_argument_errors(mod):
     base = lambda D=64, gg=g, wsb=ws, out=P[3]: [P[0], P[1], P[2], out, 1, 2, D, gg, 0.125, FAKE,
                                                  FAKE2, FAKE, wsb, None]
     assert lib.svsa_block_sparse_attn(*base(D=96)) == -2
-    assert lib.svsa_block_sparse_attn(*base(gg=_g(mod, 4, 8, 8, 2, 4, 4))) == -2  # Bk = 32
+    assert lib.svsa_block_sparse_attn(*base(gg=_g(mod, 3, 5, 6, 2, 2, 4))) == -2  # Bk = 16
     assert lib.svsa_block_sparse_attn(*base(wsb=ws - 1)) == -3
     assert lib.svsa_block_sparse_attn(*base(out=P[0])) == -1                  # out aliases q
     b = base(); b[0] = None
