@@ -11,9 +11,9 @@
 //
 // Kernels (all float64 arithmetic, all deterministic):
 //   logits_kernel   L = scale * Qbar Kbar^T, 64x64 output tile per workgroup
-//   select_kernel   one workgroup per row: softmax, bitonic sort of
-//                   (score desc, index asc) in LDS, ordered prefix sum, kept
-//                   bitmap, row count
+//   select_kernel   one workgroup per row: softmax, radix select of the
+//                   boundary block over the score bits with fixed-point mass
+//                   histograms, kept bitmap, row count
 //   scan_kernel     exclusive scan of row counts -> row_ptr
 //   compact_kernel  one wavefront per row: bitmap -> ascending col_idx
 #include "svsa_internal.h"
@@ -85,13 +85,20 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 }
 
 // ---------------------------------------------------------------------------
-// Per-row selection.
+// Per-row selection by radix select (no sort).
+//
+// The kept set is a prefix of the (score desc, index asc) order, so it is
+// fixed by its last element tau: every block scoring above tau is kept, and
+// of the blocks scoring exactly tau the lowest-index ones up to the boundary.
+// tau is found by an MSB-first radix select over the score bits (non-negative
+// doubles order like their bit patterns), 8 bits per pass, with a per-bin
+// histogram of counts and of probability mass.  Mass is accumulated in 2^-63
+// fixed point with integer atomics, so the result is independent of the
+// order of the atomics (bitwise deterministic); it differs from a float64
+// running sum by at most nb * 2^-63.  Most rows resolve in 2-3 passes (the
+// boundary bin holds a single block).
 // ---------------------------------------------------------------------------
 constexpr int kSThreads = 256;
-
-__device__ __forceinline__ bool comes_before(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
 
 template <typename T, typename Op>
 __device__ T block_reduce(T v, T* scratch, Op op) {
@@ -107,118 +114,218 @@ __device__ T block_reduce(T v, T* scratch, Op op) {
   return r;
 }
 
-// mode: 0 = top-p, 1 = fixed fraction
+__device__ __forceinline__ uint64_t to_fixed(double s) {
+  return (uint64_t)(s * 9223372036854775808.0);  // floor(s * 2^63)
+}
+
+struct RadixStep {
+  int32_t bin;          // crossing bin, -1 when the target is never reached
+  uint32_t bin_cnt;     // elements in that bin
+  uint32_t above_cnt;   // elements ranked before the bin
+  uint64_t above_mass;  // their fixed-point mass
+};
+
+// mode: 0 = top-p, 1 = fixed fraction.  PER = elements per thread (nb <= 256 * PER).
+template <int PER>
 __global__ void __launch_bounds__(kSThreads)
 select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
-              int32_t* __restrict__ counts, int32_t nb, int32_t heads, int32_t p2, int32_t words,
+              int32_t* __restrict__ counts, int32_t nb, int32_t heads, int32_t words,
               int32_t band, int32_t mode, HeadParams hp) {
-  extern __shared__ uint64_t smem[];
-  uint64_t* key = smem;                                  // [p2]
-  double* red = reinterpret_cast<double*>(key + p2);     // [kSThreads]
-  uint32_t* flag = reinterpret_cast<uint32_t*>(red + kSThreads);  // [words]
-  uint16_t* idx = reinterpret_cast<uint16_t*>(flag + words);      // [p2]
+  __shared__ uint32_t hcnt[256];
+  __shared__ unsigned long long hmass[256];
+  __shared__ double red[kSThreads];
+  __shared__ uint32_t flag[kMaxNb / 32];
+  __shared__ uint32_t tie[kMaxNb / 32];
+  __shared__ RadixStep res;
 
   const int64_t r = blockIdx.x;
   const int32_t i = (int32_t)(r % nb);
   const int32_t h = (int32_t)((r / nb) % heads);
   const double* Lr = L + r * nb;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
 
-  // 1. row max
+  // 1. softmax of the row, elements j = t + 256 k held in registers
+  double x[PER];
   double mx = -INFINITY;
-  for (int32_t j = t; j < nb; j += kSThreads) mx = fmax(mx, Lr[j]);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = t + k * kSThreads;
+    x[k] = j < nb ? Lr[j] : -INFINITY;
+    mx = fmax(mx, x[k]);
+  }
   mx = block_reduce(mx, red, [](double a, double b) { return fmax(a, b); });
-
-  // 2. e_j = exp(L_j - max), thread-sequential partial sums, fixed tree
   double part = 0.0;
-  for (int32_t j = t; j < nb; j += kSThreads) {
-    const double e = exp(Lr[j] - mx);
-    key[j] = __double_as_longlong(e);
-    part += e;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = t + k * kSThreads;
+    x[k] = j < nb ? exp(x[k] - mx) : 0.0;
+    part += x[k];
   }
   const double Z = block_reduce(part, red, [](double a, double b) { return a + b; });
-
-  // 3. scores and sort keys (scores are >= 0, so their bits order like them)
-  for (int32_t j = t; j < p2; j += kSThreads) {
-    if (j < nb) {
-      const double s = __longlong_as_double(key[j]) / Z;
-      key[j] = (uint64_t)__double_as_longlong(s);
-    } else {
-      key[j] = 0;
-    }
-    idx[j] = (uint16_t)j;
+  uint64_t key[PER], mass[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const double sc = x[k] / Z;
+    key[k] = (uint64_t)__double_as_longlong(sc);
+    mass[k] = to_fixed(sc);
   }
-  for (int32_t w = t; w < words; w += kSThreads) flag[w] = 0u;
-  __syncthreads();
 
-  // 4. bitonic sort: descending score, ascending index on ties
-  for (int32_t k = 2; k <= p2; k <<= 1) {
-    for (int32_t j = k >> 1; j > 0; j >>= 1) {
-      for (int32_t q = t; q < (p2 >> 1); q += kSThreads) {
-        const int32_t a = (q / j) * 2 * j + (q % j);
-        const int32_t b = a + j;
-        const uint64_t ka = key[a], kb = key[b];
-        const uint32_t ia = idx[a], ib = idx[b];
-        const bool up = (a & k) == 0;
-        const bool swap = up ? comes_before(kb, ib, ka, ia) : comes_before(ka, ia, kb, ib);
-        if (swap) {
-          key[a] = kb; key[b] = ka;
-          idx[a] = (uint16_t)ib; idx[b] = (uint16_t)ia;
+  // 2. targets
+  const double pval = (double)hp.v[h];
+  uint64_t P = 0;
+  int32_t K = nb;
+  bool keep_all;
+  if (mode == 1) {
+    K = max(1, min((int32_t)ceil(pval * (double)nb), nb));
+    keep_all = K >= nb;
+  } else {
+    keep_all = pval >= 1.0;
+    P = (uint64_t)ceil(pval * 9223372036854775808.0);
+  }
+
+  // 3. radix select of the boundary element
+  uint64_t prefix = 0, A = 0;
+  uint32_t C = 0;
+  int shift = 64;
+  bool resolved = false;
+  uint32_t last_cnt = 0;
+  while (!keep_all && shift > 0) {
+    shift -= 8;
+    hcnt[t] = 0u;
+    hmass[t] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int32_t j = t + k * kSThreads;
+      if (j < nb && (shift == 56 || (key[k] >> (shift + 8)) == prefix)) {
+        const uint32_t b = (uint32_t)(key[k] >> shift) & 255u;
+        atomicAdd(&hcnt[b], 1u);
+        atomicAdd(&hmass[b], (unsigned long long)mass[k]);
+      }
+    }
+    __syncthreads();
+    if (t < 64) {
+      // lane holds positions 4 lane .. 4 lane + 3 of the descending bin order
+      uint64_t ms[4], im[4];
+      uint32_t cs[4], ic[4];
+      uint64_t lm = 0;
+      uint32_t lc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int b = 255 - (4 * lane + q);
+        ms[q] = hmass[b];
+        cs[q] = hcnt[b];
+        lm += ms[q];
+        lc += cs[q];
+        im[q] = lm;
+        ic[q] = lc;
+      }
+      uint64_t pm = lm;
+      uint32_t pc = lc;
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const uint64_t om = __shfl_up(pm, s, 64);
+        const uint32_t oc = __shfl_up(pc, s, 64);
+        if (lane >= s) {
+          pm += om;
+          pc += oc;
         }
       }
-      __syncthreads();
+      pm -= lm;  // exclusive over lanes
+      pc -= lc;
+      int first = -1;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        const bool cross = mode == 1 ? (C + pc + ic[q] >= (uint32_t)K) : (A + pm + im[q] >= P);
+        if (cross) first = q;
+      }
+      const unsigned long long bal = __ballot(first >= 0);
+      if (bal == 0ull) {
+        if (lane == 0) res.bin = -1;
+      } else if (lane == __ffsll((long long)bal) - 1) {
+        res.bin = 255 - (4 * lane + first);
+        res.bin_cnt = cs[first];
+        res.above_cnt = C + pc + ic[first] - cs[first];
+        res.above_mass = A + pm + im[first] - ms[first];
+      }
     }
+    __syncthreads();
+    const RadixStep st = res;
+    if (st.bin < 0) {  // total mass below p (rounding): every block is kept
+      keep_all = true;
+      break;
+    }
+    prefix = (prefix << 8) | (uint64_t)st.bin;
+    A = st.above_mass;
+    C = st.above_cnt;
+    last_cnt = st.bin_cnt;
+    if (st.bin_cnt == 1u) resolved = true;
+    __syncthreads();
+    if (resolved) break;
   }
 
-  // 5. ordered exclusive prefix sums: each thread owns a contiguous run of ranks
-  const int32_t per = p2 / kSThreads > 0 ? p2 / kSThreads : 1;
-  const int32_t lo = t * per;
-  double run = 0.0;
-  for (int32_t q = lo; q < lo + per && q < p2; ++q) run += __longlong_as_double(key[q]);
-  red[t] = run;
+  // 4. kept flags
+  for (int32_t w = t; w < words; w += kSThreads) {
+    flag[w] = 0u;
+    tie[w] = 0u;
+  }
   __syncthreads();
-  if (t == 0) {  // sequential scan of the run totals (fixed order)
-    double acc = 0.0;
-    for (int s = 0; s < kSThreads; ++s) {
-      const double v = red[s];
-      red[s] = acc;
-      acc += v;
+  uint32_t k_tie = 0;
+  if (!keep_all && !resolved) {  // exact ties at tau: lowest indices first
+    if (mode == 1) {
+      k_tie = (uint32_t)K - C;
+    } else {
+      const uint64_t m_tau = to_fixed(__longlong_as_double((long long)prefix));
+      const uint64_t need = P - A;
+      k_tie = (uint32_t)((need + m_tau - 1) / m_tau);
     }
+    k_tie = max(1u, min(k_tie, last_cnt));
   }
-  __syncthreads();
-  const double pval = (double)hp.v[h];
-  int32_t keep_k = nb;
-  if (mode == 1) {
-    keep_k = (int32_t)ceil(pval * (double)nb);
-    keep_k = max(1, min(keep_k, nb));
-  }
-  double excl = red[t];
-  for (int32_t q = lo; q < lo + per && q < p2; ++q) {
-    const uint32_t j = idx[q];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = t + k * kSThreads;
+    if (j >= nb) continue;
     bool kept;
-    if (mode == 1) kept = q < keep_k;
-    else kept = (pval >= 1.0) || q == 0 || excl < pval;
-    if (kept && (int32_t)j < nb) atomicOr(&flag[j >> 5], 1u << (j & 31));
-    excl += __longlong_as_double(key[q]);
+    if (keep_all) {
+      kept = true;
+    } else {
+      const uint64_t hi = key[k] >> shift;
+      kept = hi > prefix || (hi == prefix && resolved);
+      if (hi == prefix && !resolved) atomicOr(&tie[j >> 5], 1u << (j & 31));
+    }
+    if (kept) atomicOr(&flag[j >> 5], 1u << (j & 31));
   }
-  // 6. diagonal band |i - j| <= band - 1
+  // diagonal band |i - j| <= band - 1
   for (int32_t d = t - (band - 1); d <= band - 1; d += kSThreads) {
     const int32_t j = i + d;
     if (j >= 0 && j < nb) atomicOr(&flag[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
+  if (k_tie > 0 && t == 0) {
+    uint32_t taken = 0;
+    for (int32_t w = 0; w < words && taken < k_tie; ++w) {
+      uint32_t f = tie[w];
+      while (f && taken < k_tie) {
+        const uint32_t lowbit = f & (~f + 1u);
+        flag[w] |= lowbit;
+        f ^= lowbit;
+        ++taken;
+      }
+    }
+  }
+  __syncthreads();
 
-  // 7. bitmap out + count
+  // 5. bitmap out + count
   int32_t c = 0;
   for (int32_t w = t; w < words; w += kSThreads) {
     const uint32_t f = flag[w];
     bits[r * words + w] = f;
     c += __popc(f);
   }
-  __syncthreads();
   int32_t* ired = reinterpret_cast<int32_t*>(red);
   const int32_t total = block_reduce(c, ired, [](int32_t a, int32_t b) { return a + b; });
   if (t == 0) counts[r] = total;
+  (void)lane;
 }
 
 // ---------------------------------------------------------------------------
@@ -228,25 +335,45 @@ constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, int64_t rows) {
-  __shared__ int32_t buf[kScanThreads];
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  constexpr int kPer = 4;
+  constexpr int kChunk = kScanThreads * kPer;
   int32_t carry = 0;
-  for (int64_t base = 0; base < rows; base += kScanThreads) {
-    const int64_t r = base + threadIdx.x;
-    const int32_t v = r < rows ? counts[r] : 0;
-    buf[threadIdx.x] = v;
-    __syncthreads();
-    for (int s = 1; s < kScanThreads; s <<= 1) {
-      const int32_t add = threadIdx.x >= s ? buf[threadIdx.x - s] : 0;
-      __syncthreads();
-      buf[threadIdx.x] += add;
-      __syncthreads();
+  for (int64_t base = 0; base < rows; base += kChunk) {
+    int32_t v[kPer];
+    int32_t local = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int64_t r = base + (int64_t)t * kPer + q;
+      v[q] = r < rows ? counts[r] : 0;
+      local += v[q];
     }
-    if (r < rows) row_ptr[r] = carry + buf[threadIdx.x] - v;
-    const int32_t chunk_total = buf[kScanThreads - 1];
+    int32_t inc = local;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const int32_t o = __shfl_up(inc, s, 64);
+      if (lane >= s) inc += o;
+    }
+    if (lane == 63) wsum[wv] = inc;
     __syncthreads();
-    carry += chunk_total;
+    int32_t wbase = 0, total = 0;
+    for (int k = 0; k < kScanThreads / 64; ++k) {
+      const int32_t x = wsum[k];
+      if (k < wv) wbase += x;
+      total += x;
+    }
+    int32_t run = carry + wbase + inc - local;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int64_t r = base + (int64_t)t * kPer + q;
+      if (r < rows) row_ptr[r] = run;
+      run += v[q];
+    }
+    carry += total;
+    __syncthreads();
   }
-  if (threadIdx.x == 0) row_ptr[rows] = carry;
+  if (t == 0) row_ptr[rows] = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -322,13 +449,23 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
   HeadParams hp{};
   const float* src = top_p ? top_p : keep_frac;
   for (int32_t h = 0; h < heads; ++h) hp.v[h] = src[h];
-  int32_t p2 = 1;
-  while (p2 < nb) p2 <<= 1;
-  if (p2 < 2) p2 = 2;
-  const size_t lds = (size_t)p2 * sizeof(uint64_t) + kSThreads * sizeof(double) +
-                     (size_t)m.words * sizeof(uint32_t) + (size_t)p2 * sizeof(uint16_t);
-  hipLaunchKernelGGL(select_kernel, dim3((uint32_t)rows), dim3(kSThreads), lds, stream, L, bits,
-                     counts, nb, heads, p2, m.words, band, top_p ? 0 : 1, hp);
+  const int mode = top_p ? 0 : 1;
+  const dim3 grid((uint32_t)rows), blk(kSThreads);
+  if (nb <= kSThreads)
+    hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+                       m.words, band, mode, hp);
+  else if (nb <= 2 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<2>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+                       m.words, band, mode, hp);
+  else if (nb <= 4 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<4>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+                       m.words, band, mode, hp);
+  else if (nb <= 8 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<8>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+                       m.words, band, mode, hp);
+  else
+    hipLaunchKernelGGL(select_kernel<16>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+                       m.words, band, mode, hp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr, rows);
