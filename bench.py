@@ -42,7 +42,37 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed region, copy 1 GiB device to device once (the "
+                         "reference launch for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan720_hbm_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_17_amd", "csrc", "attn.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or None
+    when the summary is missing, covers another workload, or was taken on an
+    attention source other than the one in the tree."""
+    import hashlib
+    if workload != "wan720" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "\t")):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    with open(ATTN_SOURCE, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    if fields.get("attn_source_sha256") != sha:
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def kept_flops_from_csr(rp, ci, N, Bk, nb, D):
@@ -201,6 +231,13 @@ def main():
                  "speedup_step": (step_ms - attn_ms + dense_ms) / step_ms}
         print(f"[bench] dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     cpu = None
     if not args.no_cpu_baseline:
         head = 0
@@ -244,13 +281,15 @@ def main():
         "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
         "dense": dense,
         "roofline": {
-            "kernel": "svsa_block_sparse_attn (union + order + attn_kernel)",
+            "kernel": "svsa_block_sparse_attn (union_kernel + order_kernel + vt_kernel + "
+                      "attn_kernel; attn_kernel is >99% of it)",
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": None if args.fixed or args.top_p not in (None, 0.9)
+            else measured_traffic(args.workload),
         },
         "cpu_baseline": cpu,
     }

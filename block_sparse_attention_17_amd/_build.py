@@ -1,6 +1,7 @@
 """Compile the HIP sources into the in-tree shared library ``libsvsa.so`` (gfx950).
 
-Run as ``python -m block_sparse_attention_17_amd._build``.  Objects go to
+Run as ``python block_sparse_attention_17_amd/_build.py`` (as a script: the
+package itself refuses to import until the library exists).  Objects go to
 ``_build/`` next to the sources; the library lands inside the package.
 """
 import os
@@ -11,6 +12,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 OUT = os.path.join(PKG, "libsvsa.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("SVSA_OFFLOAD_ARCH", "gfx950")
@@ -26,7 +28,7 @@ def hipcc():
 
 
 def common_flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
             # keep the compiler from forming packed fp32 math (see DESIGN notes)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fvisibility=hidden", "-Wall", "-Wno-unused-result", "-Wno-unused-variable"]
@@ -35,7 +37,7 @@ def common_flags():
 # Per-file flags.  The attention kernel never produces NaN (padded keys are
 # -inf, every row has a finite maximum), so IEEE NaN quieting before each
 # v_max_f32 is dropped there.
-EXTRA = {"attn.hip": ["-fno-honor-nans"]}
+EXTRA = {"attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _compile(src):

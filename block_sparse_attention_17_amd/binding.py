@@ -6,7 +6,7 @@ into device pointers and the current torch stream into a hipStream_t, calls
 the library, and raises ``SvsaError`` on a non-zero status.  torch provides
 device memory and streams; all computation runs in the HIP kernels.
 
-The library must be built (``python -m block_sparse_attention_17_amd._build``);
+The library must be built (``python block_sparse_attention_17_amd/_build.py``);
 importing this module without it raises immediately: there is no fallback.
 """
 import ctypes
@@ -68,7 +68,7 @@ class Geometry:
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(
-            f"{_LIB_PATH} is missing: build it with `python -m block_sparse_attention_17_amd._build` "
+            f"{_LIB_PATH} is missing: build it with `python block_sparse_attention_17_amd/_build.py` "
             "(the block-sparse attention path has no non-HIP fallback)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, sz, dbl, flt = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,

@@ -4,7 +4,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/svsa.h"
+#include "svsa.h"
 #include "svsa_internal.h"
 
 using svsa::Geom;
@@ -146,6 +146,7 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
     return SVSA_E_INVALID;
   if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
   if ((g.Bk != 64 && g.Bk != 32) || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  if ((int64_t)g.Npad * head_dim * 2 >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
   const int64_t bh = (int64_t)batch * heads;
   if (bh * g.nb * (int64_t)g.nb >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
   const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;

@@ -13,23 +13,28 @@
 //    query rows of one (b, h): 4 blocks of 64 tokens, or 8 blocks of 32.
 //    Neighbouring query blocks keep largely the same key blocks, so the
 //    workgroup streams the UNION of their lists through LDS once and every
-//    wavefront whose block keeps the current key block computes on it (up to
-//    8x LDS / L2 reuse of K and V).
+//    wavefront whose block keeps the current key block computes on it.
 //  * The schedule kernel merges the group's CSR rows into that union list,
 //    with a "who keeps it" bit mask per entry, and orders the work items
 //    longest first.
-//  * K and V tiles are double-buffered in LDS: the next key block's global
-//    loads are issued into registers before the current block is computed and
-//    written to the other buffer after it.  Both tiles are row-major with a
-//    16-byte XOR swizzle chosen for their read pattern.
+//  * V is transposed once per call (vt_kernel), so both MFMA A operands (K
+//    rows for S^T, V^T rows for O^T) are plain 16-byte LDS reads.
+//  * Key blocks reach LDS through a 4-slot ring filled by MUBUF buffer loads
+//    with the LDS destination (no VGPR staging), issued two blocks ahead and
+//    waited for with explicit vmcnt counts.  Tiles are XOR-swizzled by row so
+//    that the operand reads are free of bank conflicts.
+//  * Ping-pong: waves 0-3 and 4-7 form two groups (one wave of each per SIMD).
+//    Each key block is two phases per wave: M (O += P V of the previous block
+//    and S^T = K Q^T of this one, on the matrix cores) and V (online softmax
+//    on the vector ALU).  Group 1 runs one phase behind group 0 and phases
+//    are separated by workgroup barriers, so in every interval one wave per
+//    SIMD feeds the matrix cores while the other runs the softmax.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: each lane then owns one query column, so the
 //    row max / row sum are lane-local plus one exchange between the two
 //    32-lane halves.  The float32 probabilities convert in registers into the
-//    bf16 B operand of O^T += V^T P^T; the V^T A operand comes straight from
-//    the row-major V tile through ds_read_b64_tr_b16 (LDS transpose reads).
-//    The key order inside each 16-key MFMA step is permuted identically on
-//    both operands.
+//    bf16 B operand of O^T += V^T P^T; the key order inside each 16-key MFMA
+//    step is permuted identically on both operands.
 //  * Online softmax in base 2 with lazy rescaling: the running max only moves
 //    (and O, l are only rescaled) when a tile raises it by more than 2^8, so
 //    probabilities stay <= 256 and the O rescale is skipped on most tiles.
@@ -49,6 +54,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerItem = 32 * kWaves;  // query rows owned by one workgroup
 constexpr float kLazy = 8.0f;              // log2 of the largest unnormalised probability
+constexpr int kMaxHeadDim = 128;
+constexpr int kEnt = 7;                    // list entries used by one round of 8 intervals
+constexpr int kWin = 8;   // LDS operand reads in flight ahead of the MFMA stream
+constexpr int kPre = 4;   // P V operands read before the barrier that opens an M phase
 
 // ---------------------------------------------------------------------------
 // Schedule: per item (b, h, group of query blocks) the ascending union of the
@@ -143,253 +152,499 @@ order_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ order, int
 }
 
 // ---------------------------------------------------------------------------
+// V^T per key block: vt[bh][j][d][pos(kv)] = v[bh][j * BK + kv][d], with the
+// key order inside each 16-key MFMA step permuted (pos, below) so that the
+// 8 keys one lane-half feeds to an MFMA step are 16 contiguous bytes.  One
+// workgroup per key block; the block goes through LDS so that both the reads
+// and the writes are whole coalesced rows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vt_pos(int kv) {
+  // kv = 16 s + 8 a + 4 h + e  ->  16 s + 8 h + 4 a + e
+  return (kv & ~15) | ((kv & 4) << 1) | ((kv & 8) >> 1) | (kv & 3);
+}
+
+constexpr int kVtThreads = 256;
+
+template <int D, int BK>
+__global__ void __launch_bounds__(kVtThreads)
+vt_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt, int32_t nb, int32_t Npad) {
+  __shared__ uint16_t tile[BK][D + 2];  // +2: odd word stride, conflict-free column reads
+  const int64_t bh = blockIdx.x / nb;
+  const int32_t j = blockIdx.x % nb;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(v) + (bh * Npad + (int64_t)j * BK) * D;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(vt) + (bh * Npad + (int64_t)j * BK) * D;
+  for (int i = threadIdx.x; i < BK * D / 2; i += kVtThreads) {
+    const int kv = (2 * i) / D, d = (2 * i) % D;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(src)[i];
+    tile[kv][d] = (uint16_t)(w & 0xffffu);
+    tile[kv][d + 1] = (uint16_t)(w >> 16);
+  }
+  __syncthreads();
+  // output word i holds positions 2p, 2p+1 of row d
+  for (int i = threadIdx.x; i < BK * D / 2; i += kVtThreads) {
+    const int d = (2 * i) / BK, p = (2 * i) % BK;
+    // positions p, p+1 hold keys vt_pos^-1(p), vt_pos^-1(p+1) (vt_pos is an involution)
+    const uint32_t lo = tile[vt_pos(p)][d], hi = tile[vt_pos(p + 1)][d];
+    reinterpret_cast<uint32_t*>(dst)[i] = lo | (hi << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Attention kernel.
 // ---------------------------------------------------------------------------
 template <int D, int BK>
 struct Cfg {
-  static constexpr int kTileBytes = BK * D * 2;          // one K (or V) tile
-  static constexpr int kStageBytes = 2 * kTileBytes;     // K + V
-  static constexpr int kLdsBytes = 2 * kStageBytes;      // double buffer
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kSTiles = BK / 32;   // 32-key tiles of S^T
-  static constexpr int kPSteps = BK / 16;   // 16-key MFMA steps of P V
+  static constexpr int kTileBytes = BK * D * 2;  // one K (or V) tile
+  static constexpr int kRowBytes = 2 * D;    // K row
+  static constexpr int kVtRowBytes = 2 * BK;  // V^T row
+  static constexpr int kDmaPerTile = kTileBytes / 1024;          // 1 KB per wavefront copy
+  static constexpr int kDmaPerWave = 2 * kDmaPerTile / kWaves;   // K + V, split over the waves
+  static constexpr int kSTiles = BK / 32;    // 32-key tiles of S^T
+  static constexpr int kPSteps = BK / 16;    // 16-key MFMA steps of P V
   static constexpr int kWavesPerBlock = BK / 32;
   static constexpr int kGroup = kWaves / kWavesPerBlock;  // query blocks per item
+  static_assert(kDmaPerWave >= 1 && kDmaPerWave <= 4 && (2 * kDmaPerTile) % kWaves == 0,
+                "copies must split");
 };
 
-// K tile: read as the A operand of S^T (32 consecutive rows, one 16-byte
-// chunk each): the chunk index is XORed with the row so 16 rows hit 16
-// different bank groups.
+// K tile: row-major, 16-byte chunks XOR-swizzled by row so that the S^T
+// A-operand reads (32 consecutive rows at one column) hit distinct banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-// V tile: read by ds_read_b64_tr_b16; a half-wavefront touches 4 rows x 4
-// chunks, spread over all banks by XORing bits 2..3 of the chunk index.
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+// V^T tile: one row per head-dimension index (2 BK bytes), 16-byte chunks
+// XOR-swizzled by row so that 16 consecutive rows read at one column (the
+// V^T A-operand pattern) hit distinct banks.
+template <int BK>
+__device__ __forceinline__ int vt_swz(int row) {
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
-// Staging of one key block (K tile then V tile) through registers: every
-// thread loads kPer 16-byte chunks (coalesced along rows) early in an
-// iteration and writes them, swizzled, into the other LDS buffer at its end.
-template <int D, int BK>
-struct Stage {
-  static constexpr int kChunksPerTile = BK * D / 8;
-  static constexpr int kPer = 2 * kChunksPerTile / kThreads;
-  static_assert((2 * kChunksPerTile) % kThreads == 0, "tile chunks must split over the threads");
-  u32x4 r[kPer];
+// Cross-half exchange: the value held by lane (lane ^ 32).
+__device__ __forceinline__ float swap_halves(float x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
 
-  __device__ __forceinline__ void load(const __bf16* kh, const __bf16* vh, int32_t j, int tid) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + u * kThreads;
-      const bool is_v = c >= kChunksPerTile;
-      const int cc = is_v ? c - kChunksPerTile : c;
-      const int row = cc / (D / 8), lc = cc % (D / 8);
-      r[u] = *reinterpret_cast<const u32x4*>((is_v ? vh : kh) + ((int64_t)j * BK + row) * D +
-                                             lc * 8);
-    }
-  }
-  __device__ __forceinline__ void store(char* stage, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + u * kThreads;
-      const bool is_v = c >= kChunksPerTile;
-      const int cc = is_v ? c - kChunksPerTile : c;
-      const int row = cc / (D / 8), lc = cc % (D / 8);
-      const int pc = lc ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-      *reinterpret_cast<u32x4*>(stage + (is_v ? Cfg<D, BK>::kTileBytes : 0) +
-                                row * Cfg<D, BK>::kRowBytes + (pc << 4)) = r[u];
-    }
-  }
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Workgroup barrier without an implied memory fence: LDS reads are drained
+// (lgkmcnt) and HBM->LDS copies are waited for explicitly, so copies of later
+// key blocks stay in flight across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-wave state of the online softmax.
+template <int D, int BK>
+struct WaveState {
+  static constexpr int kDT = D / 32;
+  f32x16 oacc[kDT];
+  f32x16 sacc[BK / 32];
+  bf16x8 pk[BK / 16];
+  bf16x8 qreg[D / 16];
+  bf16x8 pre[kPre];
+  float m_run, l_run, o_alpha;
+  bool o_rescale;
 };
 
+struct Ctx {
+  __amdgpu_buffer_rsrc_t k_rsrc;   // K of this (b, h)
+  __amdgpu_buffer_rsrc_t vt_rsrc;  // V^T blocks of this (b, h)
+  const int32_t* lst;
+  int32_t n_u, T, nb, last_valid;
+  float c_log2;
+  int wave, lane, qb, l32, hh;
+  uint32_t dma_off[4];  // per-lane source offsets of this wave's copies
+  bool has_rows;
+};
+
+// Per-lane source byte offset, inside one key block, of this wavefront's u-th
+// HBM -> LDS copy (each copy is 64 lanes x 16 contiguous LDS bytes; the LDS
+// swizzle is applied on the source side).  Copies 0 .. kDmaPerTile-1 fill the
+// K tile, the rest the V^T tile.
+template <int D, int BK>
+__device__ __forceinline__ uint32_t copy_src_off(int wave, int lane, int u) {
+  using C = Cfg<D, BK>;
+  const int ld = wave + u * kWaves;
+  const bool is_v = ld >= C::kDmaPerTile;
+  const int byte = (is_v ? ld - C::kDmaPerTile : ld) * 1024 + lane * 16;
+  const int rb = is_v ? C::kVtRowBytes : C::kRowBytes;
+  const int row = byte / rb;
+  const int lc = ((byte % rb) >> 4) ^ (is_v ? vt_swz<BK>(row) : k_swz<D>(row));
+  return (uint32_t)(row * rb + lc * 16);
+}
+
+// Issue this wavefront's copies of key block j into (kdst, vdst): buffer
+// loads with the LDS destination (MUBUF "lds"), addressed by the head's buffer
+// resource, a wave-uniform block offset and a loop-invariant per-lane offset.
+// (A MUBUF copy, unlike the FLAT global_load_lds form, leaves the compiler's
+// counting of LDS reads exact: with a FLAT copy in flight it would wait for
+// every outstanding LDS read before each use.)
+template <int D, int BK>
+__device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kdst, char* vdst) {
+  using C = Cfg<D, BK>;
+  const int32_t boff = j * C::kTileBytes;
+#pragma unroll
+  for (int u = 0; u < C::kDmaPerWave; ++u) {
+    const int ld = cx.wave + u * kWaves;
+    if constexpr (C::kDmaPerTile % kWaves == 0) {
+      // K or V is known per copy at compile time, so every copy targets one
+      // LDS object and the compiler can tell copies and reads of different
+      // ring slots apart
+      constexpr int kPerWaveK = C::kDmaPerTile / kWaves;
+      if (u < kPerWaveK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + ld * 1024), 16,
+            (int)cx.dma_off[u], boff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.vt_rsrc,
+            (__attribute__((address_space(3))) void*)(vdst + (ld - C::kDmaPerTile) * 1024), 16,
+            (int)cx.dma_off[u], boff, 0, 0);
+    } else {
+      if (ld < C::kDmaPerTile)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + ld * 1024), 16,
+            (int)cx.dma_off[u], boff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.vt_rsrc,
+            (__attribute__((address_space(3))) void*)(vdst + (ld - C::kDmaPerTile) * 1024), 16,
+            (int)cx.dma_off[u], boff, 0, 0);
+    }
+  }
+}
+
+// Does this wavefront's query block keep the key block of list entry `ent`?
+__device__ __forceinline__ bool active(const Ctx& cx, int32_t ent) {
+  return ((((uint32_t)ent) >> 24) >> cx.qb) & 1u;
+}
+
+// V^T A operand of P V job i (step s = i / (D / 32), d tile dt = i % (D / 32);
+// consecutive jobs accumulate into different tiles) for lane (d = 32 dt + l32,
+// hh): positions 16 s + 8 hh .. + 7 of V^T row d, i.e. keys
+// 16 s + 4 hh + {0..3, 8..11}.
+template <int D, int BK>
+__device__ __forceinline__ bf16x8 v_operand(const Ctx& cx, const char* vt, int i) {
+  using C = Cfg<D, BK>;
+  const int s = i / (D / 32), dt = i % (D / 32);
+  const int row = 32 * dt + cx.l32;
+  return *reinterpret_cast<const bf16x8*>(vt + row * C::kVtRowBytes +
+                                          (((2 * s + cx.hh) ^ vt_swz<BK>(row)) << 4));
+}
+
+// K A operand of S^T job j (step s = j / kSTiles over D, key tile c = j % kSTiles).
+template <int D, int BK>
+__device__ __forceinline__ bf16x8 k_operand(const Ctx& cx, const char* kt, int j) {
+  using C = Cfg<D, BK>;
+  const int s = j / C::kSTiles, c = j % C::kSTiles;
+  const int row = 32 * c + cx.l32;
+  return *reinterpret_cast<const bf16x8*>(kt + row * C::kRowBytes +
+                                          (((2 * s + cx.hh) ^ k_swz<D>(row)) << 4));
+}
+
+// One stream of MFMA jobs: the P V jobs (if PV) followed by the S^T jobs (if
+// QK), with LDS operand reads kWin jobs ahead of their MFMA.  The operands of
+// the first kPre P V jobs were read at the end of the previous phase.
+template <int D, int BK, bool PV, bool QK>
+__device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx, const char* vprev,
+                                            const char* kcur) {
+  using C = Cfg<D, BK>;
+  constexpr int kNpv = PV ? (D / 32) * C::kPSteps : 0;
+  constexpr int kNqk = QK ? (D / 16) * C::kSTiles : 0;
+  constexpr int kN = kNpv + kNqk;
+  auto rd = [&](int i) {
+    return i < kNpv ? v_operand<D, BK>(cx, vprev, i) : k_operand<D, BK>(cx, kcur, i - kNpv);
+  };
+  // sched_barrier(0) fences keep this source order: the compiler's schedulers
+  // would otherwise either issue every read up front (spilling) or move each
+  // read next to its MFMA (exposing the LDS latency).
+  bf16x8 win[kWin];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i)
+    if (i < kN) win[i] = (PV && i < kPre) ? st.pre[i] : rd(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const bf16x8 a = win[i % kWin];
+    if (i + kWin < kN) win[i % kWin] = rd(i + kWin);
+    if (i < kNpv) {
+      const int s = i / (D / 32), dt = i % (D / 32);
+      st.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pk[s], st.oacc[dt], 0, 0, 0);
+    } else {
+      const int j = i - kNpv;
+      const int s = j / C::kSTiles, c = j % C::kSTiles;
+      const f32x16 acc = s == 0 ? f32x16{} : st.sacc[c];  // S^T starts at 0
+      st.sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[s], acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// M phase for key block e: O += P(e-1) V(e-1); S(e) = K(e) Q^T.
+template <int D, int BK>
+__device__ __forceinline__ void m_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
+                                        int32_t ent_prev, int32_t ent, const char* vprev,
+                                        const char* kcur) {
+  using C = Cfg<D, BK>;
+  constexpr int kDT = D / 32;
+  const bool pv = e >= 1 && e <= cx.n_u && active(cx, ent_prev);
+  const bool qk = e < cx.n_u && active(cx, ent);
+  __builtin_amdgcn_s_setprio(1);
+  if (pv && st.o_rescale) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) st.oacc[dt] = st.oacc[dt] * st.o_alpha;
+  }
+  if (pv) mfma_stream<D, BK, true, false>(st, cx, vprev, kcur);
+  if (qk) mfma_stream<D, BK, false, true>(st, cx, vprev, kcur);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// V phase for key block e: online softmax of S(e) -> P(e).
+template <int D, int BK>
+__device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
+                                        int32_t ent, const char* vcur) {
+  using C = Cfg<D, BK>;
+  if (!(e < cx.n_u && active(cx, ent))) return;
+  // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
+  if ((ent & 0xffffff) == cx.nb - 1 && cx.last_valid < BK) {
+#pragma unroll
+    for (int c = 0; c < C::kSTiles; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kv = 32 * c + 8 * (r >> 2) + 4 * cx.hh + (r & 3);
+        if (kv >= cx.last_valid) st.sacc[c][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < C::kSTiles; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.sacc[c][r], st.sacc[c][r + 1]));
+  mx = fmaxf(mx, swap_halves(mx, cx.lane));
+  const float mxs = mx * cx.c_log2;
+  // lazy rescale: the running max moves only when it grows by > kLazy; O itself
+  // is rescaled by o_alpha at the start of the next P V
+  const bool need = mxs > st.m_run + kLazy;
+  st.o_rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+  if (st.o_rescale) {
+    const float m_new = need ? mxs : st.m_run;
+    st.o_alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= st.o_alpha;
+  }
+  float rs = 0.f;
+#pragma unroll
+  for (int c = 0; c < C::kSTiles; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(st.sacc[c][r], cx.c_log2, -st.m_run));
+      st.sacc[c][r] = p;
+      rs += p;
+    }
+  st.l_run += rs;
+  // P^T as the bf16 B operand of step s: keys 16 s + 4 hh + {0..3, 8..11}
+#pragma unroll
+  for (int s = 0; s < C::kPSteps; ++s)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) st.pk[s][x] = (__bf16)st.sacc[s >> 1][8 * (s & 1) + x];
+  // The next phase of this wave is M(e + 1), whose P V reads V^T(e): block e
+  // is complete in LDS and its slot is not rewritten before interval 2 e + 4,
+  // so its first operands are read now, ahead of the barrier.
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) st.pre[i] = v_operand<D, BK>(cx, vcur, i);
+}
+
+// LDS ring: key block e lives in slot e % 4 (separate LDS objects, so the
+// compiler can tell the copies into one slot from the reads of another).
+template <int D, int BK>
+struct Ring {
+  char* k[4];
+  char* v[4];
+};
+
+// One interval t = t0 + I of group G (t0 is a multiple of 8, so every ring
+// slot and every index into ent[] below is a compile-time constant).
+//  * even t: every wave issues its copies of key block t / 2 + 2;
+//  * phase ph = t - G: even -> M phase of block ph / 2, odd -> V phase;
+//  * odd t: wait for this wave's copies of block (t + 1) / 2 before the
+//    barrier, so the block is complete when group 0 reads it at t + 1.
+// ent[x] is list entry t0 / 2 - 1 + x.
+template <int D, int BK, int G, int I>
+__device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, const Ring<D, BK>& rg,
+                                         int32_t t0, const int32_t (&ent)[kEnt]) {
+  using C = Cfg<D, BK>;
+  const int32_t t = t0 + I;
+  if ((I & 1) == 0) {
+    // Past the end of the list this copies the last block again (ent[] is
+    // clamped) into a slot that is no longer read: unconditional copies keep
+    // the per-wave count of copies in flight fixed.
+    constexpr int slot = (I / 2 + 2) & 3;
+    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xffffff, rg.k[slot], rg.v[slot]);
+  }
+  const int32_t ph = t - G;
+  if (ph >= 0 && cx.has_rows) {
+    const int32_t e = ph >> 1;
+    constexpr int x = ((I - G) >> 1) + 1;  // ent[] index of entry e
+    if constexpr (((I - G) & 1) == 0) {
+      constexpr int sc = (((I - G) >> 1) + 4) & 3;
+      constexpr int sp = (sc + 3) & 3;
+      m_phase<D, BK>(st, cx, e, ent[x - 1], ent[x], rg.v[sp], rg.k[sc]);
+    } else {
+      constexpr int se = ((I - G) >> 1) & 3;  // ring slot of block e
+      v_phase<D, BK>(st, cx, e, ent[x], rg.v[se]);
+    }
+  }
+  if (I & 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kDmaPerWave));
+  wg_barrier();
+}
+
+template <int D, int BK, int G>
+__device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
+                                          const Ring<D, BK>& rg) {
+  // The first round (t0 = -8) only issues the copies of key blocks 0 and 1
+  // (and, harmlessly, of block 0 into the two other slots): all copies come
+  // from this one loop body.
+  for (int32_t t0 = -8; t0 < cx.T; t0 += 8) {
+    // The list entries of these 8 intervals, loaded (scalar) and waited for
+    // up front, so that no scalar load is outstanding while the phases wait
+    // on their LDS reads (the shared counter would force full waits).
+    int32_t ent[kEnt];
+#pragma unroll
+    for (int x = 0; x < kEnt; ++x) {
+      const int32_t idx = min(max(t0 / 2 - 1 + x, 0), cx.n_u - 1);
+      ent[x] = cx.lst[idx];
+    }
+#pragma unroll
+    for (int x = 0; x < kEnt; ++x) asm volatile("" : "+s"(ent[x]));
+    interval<D, BK, G, 0>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 1>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 2>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 3>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 4>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 5>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 6>(st, cx, rg, t0, ent);
+    interval<D, BK, G, 7>(st, cx, rg, t0, ent);
+  }
+}
+
+// Ping-pong schedule.  The 8 wavefronts form two groups (waves 0-3 and 4-7;
+// each SIMD holds one wave of each).  Per key block e a wave runs an MFMA
+// phase M(e) = { O += P(e-1) V(e-1) ; S(e) = K(e) Q^T } and a VALU phase
+// V(e) = { online softmax of S(e) -> P(e) }.  Group 1 runs one phase behind
+// group 0 and phases are separated by workgroup barriers, so in every
+// interval one wave per SIMD issues matrix work while the other issues the
+// softmax.  Key block e is copied HBM -> LDS at interval 2e - 4, two key
+// blocks ahead of its first use, and is read during intervals 2e .. 2e+3.
 template <int D, int BK>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-            const __bf16* __restrict__ v, __bf16* __restrict__ out,
+            const __bf16* __restrict__ vt, __bf16* __restrict__ out,
             const int32_t* __restrict__ list, const int32_t* __restrict__ count,
             const int32_t* __restrict__ order, int32_t groups, int32_t nb, int32_t Npad,
             int32_t last_valid, float c_log2) {
   using C = Cfg<D, BK>;
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
-  constexpr int kS = D / 16;    // MFMA K-steps over the head dimension
-  constexpr int kDT = D / 32;   // 32-row tiles of O^T
+  __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
+      k2[C::kTileBytes], k3[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v0[C::kTileBytes], v1[C::kTileBytes],
+      v2[C::kTileBytes], v3[C::kTileBytes];
+  const Ring<D, BK> rg{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
+  constexpr int kS = D / 16, kDT = D / 32;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int qb = wave / C::kWavesPerBlock;                 // query block inside the group
-  const int sub = wave % C::kWavesPerBlock;                // 32-row slice inside the block
-  const int l32 = lane & 31, hh = lane >> 5;
+  Ctx cx;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  cx.lane = tid & 63;
+  const int grp = cx.wave >> 2;                             // ping-pong group
+  cx.qb = BK == 64 ? (cx.wave & 3) : cx.wave;               // query block inside the item
+  const int sub = BK == 64 ? grp : 0;                       // 32-row slice inside the block
+  cx.l32 = cx.lane & 31;
+  cx.hh = cx.lane >> 5;
 
   const int64_t item = order[blockIdx.x];
   const int64_t bh = item / groups;
-  const int32_t g = (int32_t)(item % groups);
-  const int32_t iq = g * C::kGroup + qb;
-  const bool wave_has_rows = iq < nb;
-  const int32_t n_u = count[item];
-  const int32_t* lst = list + item * nb;
-
+  const int32_t gi = (int32_t)(item % groups);
+  const int32_t iq = gi * C::kGroup + cx.qb;
+  cx.has_rows = iq < nb;
+  cx.n_u = count[item];
+  // intervals 0 .. 2 n_u + 1 carry work; the count is rounded up to whole
+  // rounds of 8 (the extra intervals do nothing); an empty union runs none
+  cx.T = cx.n_u > 0 ? (2 * cx.n_u + 2 + 7) & ~7 : 0;
+  cx.nb = nb;
+  cx.last_valid = last_valid;
+  cx.c_log2 = c_log2;
+  cx.lst = list + item * nb;
+  // raw buffer resources over this head's K and V^T (byte range Npad * D * 2,
+  // below 2^31 by the host checks; dword 3 = 0x00020000: raw 32-bit data)
+  const int32_t head_bytes = Npad * D * 2;
+  cx.k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(k + bh * (int64_t)Npad * D), (short)0,
+                                                head_bytes, 0x00020000);
+  cx.vt_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + bh * (int64_t)Npad * D), (short)0,
+                                                 head_bytes, 0x00020000);
   const __bf16* qh = q + bh * (int64_t)Npad * D;
-  const __bf16* kh = k + bh * (int64_t)Npad * D;
-  const __bf16* vh = v + bh * (int64_t)Npad * D;
   __bf16* oh = out + bh * (int64_t)Npad * D;
 
-  Stage<D, BK> stg;
-  if (n_u > 0) stg.load(kh, vh, lst[0] & 0xffffff, tid);
+#pragma unroll
+  for (int u = 0; u < C::kDmaPerWave; ++u) cx.dma_off[u] = copy_src_off<D, BK>(cx.wave, cx.lane, u);
 
-  const int32_t qrow = (wave_has_rows ? iq : nb - 1) * BK + sub * 32 + l32;
-  bf16x8 qreg[kS];
+  WaveState<D, BK> st;
+  const int32_t qrow = (cx.has_rows ? iq : nb - 1) * BK + sub * 32 + cx.l32;
 #pragma unroll
   for (int s = 0; s < kS; ++s)
-    qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * D + 16 * s + 8 * hh);
-
-  f32x16 oacc[kDT];
+    st.qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * D + 16 * s + 8 * cx.hh);
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int r = 0; r < 16; ++r) st.oacc[dt][r] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.o_alpha = 1.f;
+  st.o_rescale = false;
+  // Q operands are in place before the loop
+#pragma unroll
+  for (int s = 0; s < kS; ++s) asm volatile("" ::"v"(st.qreg[s]));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  wg_barrier();
 
-  if (n_u > 0) stg.store(lds, tid);
-  __syncthreads();
+  if (grp == 0) run_group<D, BK, 0>(st, cx, rg);
+  else run_group<D, BK, 1>(st, cx, rg);
 
-  for (int32_t e = 0; e < n_u; ++e) {
-    const int32_t ent = lst[e];
-    const int32_t j = ent & 0xffffff;
-    const uint32_t who = (uint32_t)ent >> 24;
-    // prefetch the next key block (the last iteration reloads its own block
-    // into the idle buffer, which keeps the loop free of divergent branches)
-    stg.load(kh, vh, lst[min(e + 1, n_u - 1)] & 0xffffff, tid);
-
-    const char* ks = lds + (e & 1) * C::kStageBytes;
-    const char* vs = ks + C::kTileBytes;
-    if (wave_has_rows && ((who >> qb) & 1u)) {
-      // S^T[kv][q] = sum_d K[kv][d] Q[q][d]
-      f32x16 sacc[C::kSTiles];
-#pragma unroll
-      for (int c = 0; c < C::kSTiles; ++c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[c][r] = 0.f;
-        const int row = 32 * c + l32;
-        bf16x8 kf[kS];
-#pragma unroll
-        for (int s = 0; s < kS; ++s) {
-          const int cc = 2 * s + hh;
-          kf[s] = *reinterpret_cast<const bf16x8*>(ks + row * C::kRowBytes +
-                                                   ((cc ^ k_swz<D>(row)) << 4));
-        }
-#pragma unroll
-        for (int s = 0; s < kS; ++s)
-          sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qreg[s], sacc[c], 0, 0, 0);
-      }
-      // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
-      if (j == nb - 1 && last_valid < BK) {
-#pragma unroll
-        for (int c = 0; c < C::kSTiles; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kv = 32 * c + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (kv >= last_valid) sacc[c][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int c = 0; c < C::kSTiles; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[c][r], sacc[c][r + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxs = mx * c_log2;
-      // lazy rescale: move the running max only when it grows by > kLazy
-      const bool need = mxs > m_run + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mxs : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int c = 0; c < C::kSTiles; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c][r], c_log2, -m_run));
-          sacc[c][r] = p;
-          rs += p;
-        }
-      l_run += rs;
-      // P^T as the bf16 B operand of step s: keys 16 s + 4 hh + {0..3, 8..11}
-      bf16x8 pk[C::kPSteps];
-#pragma unroll
-      for (int s = 0; s < C::kPSteps; ++s)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) pk[s][x] = (__bf16)sacc[s >> 1][8 * (s & 1) + x];
-      // O^T[d][q] += sum_kv V^T[d][kv] P^T[kv][q]; the A operand of step s for
-      // lane (d = 32 dt + l32, hh) is keys 16 s + 4 hh + {0..3} and {8..11},
-      // two transposed 4x16 reads of the row-major V tile
-      const int grp = lane >> 4, jj = lane & 15;
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        const int dcol = 32 * dt + 16 * (grp & 1) + 4 * (jj & 3);
-#pragma unroll
-        for (int s = 0; s < C::kPSteps; ++s) {
-          bf16x8 a;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int row = 16 * s + 8 * half + 4 * hh + (jj >> 2);
-            const int lc = dcol >> 3;
-            const int off = row * C::kRowBytes + ((lc ^ v_swz<D>(row)) << 4) + 2 * (dcol & 7);
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vs + off));
-            const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) a[4 * half + x] = tb[x];
-          }
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[s], oacc[dt], 0, 0, 0);
-        }
-      }
-    }
-    stg.store(lds + ((e + 1) & 1) * C::kStageBytes, tid);
-    __syncthreads();
-  }
-
-  if (!wave_has_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!cx.has_rows) return;
+  const float l_tot = st.l_run + swap_halves(st.l_run, cx.lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   __bf16* orow = oh + (int64_t)qrow * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * dt + 8 * rq + 4 * hh;
+      const int d0 = 32 * dt + 8 * rq + 4 * cx.hh;
       bf16x4 o;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) o[x] = (__bf16)(oacc[dt][4 * rq + x] * inv);
+      for (int x = 0; x < 4; ++x) o[x] = (__bf16)(st.oacc[dt][4 * rq + x] * inv);
       *reinterpret_cast<bf16x4*>(orow + d0) = o;
     }
 }
 
 template <int D, int BK>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
-                       const int32_t* count, const int32_t* order, const AttnWs& w, const Geom& g,
-                       float c_log2, hipStream_t stream) {
-  using C = Cfg<D, BK>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+                       const int32_t* count, const int32_t* order, __bf16* vt, int32_t bh,
+                       const AttnWs& w, const Geom& g, float c_log2, hipStream_t stream) {
+  hipLaunchKernelGGL((vt_kernel<D, BK>), dim3((uint32_t)((int64_t)bh * g.nb)), dim3(kVtThreads), 0,
+                     stream, (const __bf16*)v, vt, g.nb, g.Npad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int32_t last_valid = g.N - (g.nb - 1) * BK;
-  hipLaunchKernelGGL((attn_kernel<D, BK>), dim3((uint32_t)w.items), dim3(kThreads), C::kLdsBytes,
-                     stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)out,
-                     list, count, order, w.groups, g.nb, g.Npad, last_valid, c_log2);
+  hipLaunchKernelGGL((attn_kernel<D, BK>), dim3((uint32_t)w.items), dim3(kThreads), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
+                     count, order, w.groups, g.nb, g.Npad, last_valid, c_log2);
   return hipGetLastError();
 }
 
@@ -407,6 +662,8 @@ AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk) {
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
   w.order_off = off;
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
+  w.vt_off = off;
+  off = align_up(off + (size_t)bh * nb * Bk * kMaxHeadDim * 2, 256);  // V^T (bf16)
   w.total = off;
   return w;
 }
@@ -423,6 +680,7 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
   int32_t* count = reinterpret_cast<int32_t*>(base + w.count_off);
   int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
+  __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
 
   hipLaunchKernelGGL(union_kernel, dim3((uint32_t)w.items), dim3(kSchedThreads),
                      (size_t)g.nb * sizeof(uint32_t), stream, row_ptr, col_idx, list, count, g.nb,
@@ -436,12 +694,12 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
 
   const float c_log2 = scale * 1.4426950408889634f;
   if (head_dim == 128 && g.Bk == 64)
-    return launch_attn<128, 64>(q, k, v, out, list, count, order, w, g, c_log2, stream);
+    return launch_attn<128, 64>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
   if (head_dim == 64 && g.Bk == 64)
-    return launch_attn<64, 64>(q, k, v, out, list, count, order, w, g, c_log2, stream);
+    return launch_attn<64, 64>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
   if (head_dim == 128 && g.Bk == 32)
-    return launch_attn<128, 32>(q, k, v, out, list, count, order, w, g, c_log2, stream);
-  return launch_attn<64, 32>(q, k, v, out, list, count, order, w, g, c_log2, stream);
+    return launch_attn<128, 32>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
+  return launch_attn<64, 32>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
 }
 
 }  // namespace svsa

@@ -146,7 +146,9 @@ SVSA_API int svsa_block_mask(const double* qbar, const double* kbar, int32_t bat
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * Workspace (device bytes) needed by svsa_block_sparse_attn.  Returns 0 if the
+ * Workspace (device bytes) needed by svsa_block_sparse_attn: the per-group
+ * union lists and work queues, plus a transposed copy of V (sized for
+ * head_dim 128, so the figure does not depend on head_dim).  Returns 0 if the
  * sizes are invalid.
  */
 SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* g);
@@ -166,8 +168,10 @@ SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const sv
  *   overlap q, k or v.  A query block with an empty list gets zeros.
  * row_ptr / col_idx: CSR as produced by svsa_block_mask (rows (b,h,i); each
  *   column in [0, nb)).  Columns outside [0, nb) are ignored.
- * head_dim: 64 or 128.  Products are bf16 x bf16 on the matrix cores with
- *   float32 accumulation; the softmax runs in float32.
+ * head_dim: 64 or 128; tile volume Bk: 32 or 64; N_pad * head_dim * 2 bytes
+ *   per (b, h) below 2^31 (else SVSA_E_UNSUPPORTED).  Products are bf16 x bf16
+ *   on the matrix cores with float32 accumulation; the softmax runs in
+ *   float32.
  * workspace: at least svsa_attn_workspace_bytes(batch, heads, g) bytes.
  */
 SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
