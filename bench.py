@@ -281,7 +281,7 @@ def main():
         "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
         "dense": dense,
         "roofline": {
-            "kernel": "svsa_block_sparse_attn (union_kernel + order_kernel + vt_kernel + "
+            "kernel": "svsa_block_sparse_attn (union_kernel + queue_kernel + vt_kernel + "
                       "attn_kernel; attn_kernel is >99% of it)",
             "bound": "mfma",
             "achieved": attn_tflops,

@@ -15,8 +15,10 @@
 //    workgroup streams the UNION of their lists through LDS once and every
 //    wavefront whose block keeps the current key block computes on it.
 //  * The schedule kernel merges the group's CSR rows into that union list,
-//    with a "who keeps it" bit mask per entry, and orders the work items
-//    longest first.
+//    with a "who keeps it" bit mask per entry.  Items go to one work queue
+//    per XCD, a whole (b, h) per queue, so that the workgroups of one XCD
+//    share the head's key blocks in its L2; a persistent kernel drains its
+//    own XCD's queue first, then the others.
 //  * V is transposed once per call (vt_kernel), so both MFMA A operands (K
 //    rows for S^T, V^T rows for O^T) are plain 16-byte LDS reads.
 //  * Key blocks reach LDS through a 4-slot ring filled by MUBUF buffer loads
@@ -111,43 +113,64 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   if (t == 0) count[item] = off;
 }
 
-// order[] = items sorted by union length, longest first (counting sort; the
-// order among equal lengths is arbitrary and does not affect any result).
-constexpr int kOrderThreads = 1024;
+// Work queues.  The items of one (b, h) all go to one of kQueues queues (one
+// per XCD of the chip), filled in (b, h) order and, inside a (b, h), in query
+// group order, so the workgroups running on one XCD at a time work on
+// neighbouring query groups of the same head and share its key blocks in that
+// XCD's L2.  Each (b, h) goes to the queue with the least work so far (work =
+// union lengths plus a per-item constant).  meta = {base[8], len[8], head[8]};
+// head[] (the take counters) is zeroed here, before every attention launch.
+constexpr int kQueues = 8;
+constexpr int kQueueThreads = 1024;
+constexpr int kQueueMaxBh = 4096;   // (b, h) pairs placed by work; beyond, by bh % 8
+constexpr int kItemCost = 4;        // fixed cost of one item, in key blocks
 
-__global__ void __launch_bounds__(kOrderThreads)
-order_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ order, int64_t items,
-             int32_t nb) {
-  extern __shared__ int32_t hist[];  // [nb + 1]
-  __shared__ int32_t buf[kOrderThreads];
+__global__ void __launch_bounds__(kQueueThreads)
+queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
+             int32_t* __restrict__ meta, int32_t bh_count, int32_t groups) {
+  __shared__ int64_t work[kQueueMaxBh];
+  __shared__ int32_t qof[kQueueMaxBh];   // queue of each (b, h)
+  __shared__ int32_t off[kQueueMaxBh];   // its first position inside that queue
+  __shared__ int32_t len[kQueues], base[kQueues];
   const int t = threadIdx.x;
-  for (int32_t c = t; c <= nb; c += kOrderThreads) hist[c] = 0;
-  __syncthreads();
-  for (int64_t it = t; it < items; it += kOrderThreads) atomicAdd(&hist[min(count[it], nb)], 1);
-  __syncthreads();
-  // start[c] = number of items longer than c (bins scanned in descending order)
-  int32_t carry = 0;
-  for (int32_t base = 0; base <= nb; base += kOrderThreads) {
-    const int32_t c = nb - (base + t);
-    const int32_t v = c >= 0 ? hist[c] : 0;
-    buf[t] = v;
-    __syncthreads();
-    for (int s = 1; s < kOrderThreads; s <<= 1) {
-      const int32_t add = t >= s ? buf[t - s] : 0;
-      __syncthreads();
-      buf[t] += add;
-      __syncthreads();
+  const bool by_work = bh_count <= kQueueMaxBh;
+  if (by_work) {
+    for (int32_t b = t; b < bh_count; b += kQueueThreads) {
+      int64_t w = 0;
+      for (int32_t g = 0; g < groups; ++g) w += count[(int64_t)b * groups + g] + kItemCost;
+      work[b] = w;
     }
-    const int32_t excl = carry + buf[t] - v;
-    const int32_t chunk = buf[kOrderThreads - 1];
-    __syncthreads();
-    if (c >= 0) hist[c] = excl;
-    carry += chunk;
-    __syncthreads();
   }
-  for (int64_t it = t; it < items; it += kOrderThreads) {
-    const int32_t pos = atomicAdd(&hist[min(count[it], nb)], 1);
-    order[pos] = (int32_t)it;
+  __syncthreads();
+  if (t == 0) {
+    int64_t load[kQueues];
+    for (int x = 0; x < kQueues; ++x) { load[x] = 0; len[x] = 0; }
+    for (int32_t b = 0; b < (by_work ? bh_count : 0); ++b) {
+      int best = 0;
+      for (int x = 1; x < kQueues; ++x) if (load[x] < load[best]) best = x;
+      qof[b] = best;
+      off[b] = len[best];
+      len[best] += groups;
+      load[best] += work[b];
+    }
+    if (!by_work)
+      for (int x = 0; x < kQueues; ++x)
+        len[x] = ((bh_count - x + kQueues - 1) / kQueues) * groups;
+    int32_t acc = 0;
+    for (int x = 0; x < kQueues; ++x) { base[x] = acc; acc += len[x]; }
+    for (int x = 0; x < kQueues; ++x) {
+      meta[x] = base[x];
+      meta[kQueues + x] = len[x];
+      meta[2 * kQueues + x] = 0;
+    }
+  }
+  __syncthreads();
+  const int64_t items = (int64_t)bh_count * groups;
+  for (int64_t it = t; it < items; it += kQueueThreads) {
+    const int32_t b = (int32_t)(it / groups), g = (int32_t)(it % groups);
+    const int x = by_work ? qof[b] : b % kQueues;
+    const int32_t o = by_work ? off[b] : (b / kQueues) * groups;
+    queue[base[x] + o + g] = (int32_t)it;
   }
 }
 
@@ -544,19 +567,16 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
 // interval one wave per SIMD issues matrix work while the other issues the
 // softmax.  Key block e is copied HBM -> LDS at interval 2e - 4, two key
 // blocks ahead of its first use, and is read during intervals 2e .. 2e+3.
+// One work item: query group gi of head bh, whose union list is list[item].
 template <int D, int BK>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-            const __bf16* __restrict__ vt, __bf16* __restrict__ out,
-            const int32_t* __restrict__ list, const int32_t* __restrict__ count,
-            const int32_t* __restrict__ order, int32_t groups, int32_t nb, int32_t Npad,
-            int32_t last_valid, float c_log2) {
+__device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
+                                         const __bf16* __restrict__ k,
+                                         const __bf16* __restrict__ vt, __bf16* __restrict__ out,
+                                         const int32_t* __restrict__ list,
+                                         const int32_t* __restrict__ count, int64_t item,
+                                         int32_t groups, int32_t nb, int32_t Npad,
+                                         int32_t last_valid, float c_log2, const Ring<D, BK>& rg) {
   using C = Cfg<D, BK>;
-  __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
-      k2[C::kTileBytes], k3[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v0[C::kTileBytes], v1[C::kTileBytes],
-      v2[C::kTileBytes], v3[C::kTileBytes];
-  const Ring<D, BK> rg{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
   constexpr int kS = D / 16, kDT = D / 32;
 
   const int tid = threadIdx.x;
@@ -569,7 +589,6 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   cx.l32 = cx.lane & 31;
   cx.hh = cx.lane >> 5;
 
-  const int64_t item = order[blockIdx.x];
   const int64_t bh = item / groups;
   const int32_t gi = (int32_t)(item % groups);
   const int32_t iq = gi * C::kGroup + cx.qb;
@@ -633,18 +652,86 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
 }
 
+// Persistent kernel: one workgroup per CU slot takes items from the queue of
+// the XCD it runs on (hardware register XCC_ID), then from the other queues;
+// it exits once every queue is drained.
+template <int D, int BK>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+            const __bf16* __restrict__ vt, __bf16* __restrict__ out,
+            const int32_t* __restrict__ list, const int32_t* __restrict__ count,
+            const int32_t* __restrict__ queue, int32_t* __restrict__ meta, int32_t groups,
+            int32_t nb, int32_t Npad, int32_t last_valid, float c_log2) {
+  using C = Cfg<D, BK>;
+  __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
+      k2[C::kTileBytes], k3[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v0[C::kTileBytes], v1[C::kTileBytes],
+      v2[C::kTileBytes], v3[C::kTileBytes];
+  __shared__ int32_t s_item;
+  const Ring<D, BK> rg{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
+  const int home = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1);  // XCC_ID
+  int probe = 0;  // thread 0: queues home, home + 1, ... found empty so far
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int32_t it = -1;
+      while (probe < kQueues) {
+        const int x = (home + probe) & (kQueues - 1);
+        const int32_t pos = atomicAdd(&meta[2 * kQueues + x], 1);
+        if (pos < meta[kQueues + x]) {
+          it = queue[meta[x] + pos];
+          break;
+        }
+        ++probe;
+      }
+      s_item = it;
+    }
+    __syncthreads();
+    const int32_t item = s_item;
+    __syncthreads();
+    if (item < 0) break;
+    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, Npad, last_valid, c_log2, rg);
+  }
+}
+
+// Workgroups of the persistent attention kernel: every CU slot of the device
+// (CU count x resident workgroups per CU), at most one per item.
+template <int D, int BK>
+hipError_t attn_grid(int64_t items, uint32_t* grid) {
+  static int cached[64] = {0};  // per device: CU count x resident workgroups per CU
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int slots = (dev >= 0 && dev < 64) ? cached[dev] : 0;
+  if (slots <= 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK>, kThreads, 0);
+    if (e != hipSuccess) return e;
+    slots = cus * (per_cu > 0 ? per_cu : 1);
+    if (slots <= 0) slots = 1;
+    if (dev >= 0 && dev < 64) cached[dev] = slots;
+  }
+  *grid = (uint32_t)(items < slots ? items : slots);
+  return hipSuccess;
+}
+
 template <int D, int BK>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
-                       const int32_t* count, const int32_t* order, __bf16* vt, int32_t bh,
-                       const AttnWs& w, const Geom& g, float c_log2, hipStream_t stream) {
+                       const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
+                       int32_t bh, const AttnWs& w, const Geom& g, float c_log2,
+                       hipStream_t stream) {
   hipLaunchKernelGGL((vt_kernel<D, BK>), dim3((uint32_t)((int64_t)bh * g.nb)), dim3(kVtThreads), 0,
                      stream, (const __bf16*)v, vt, g.nb, g.Npad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  uint32_t grid = 0;
+  e = attn_grid<D, BK>(w.items, &grid);
+  if (e != hipSuccess) return e;
   const int32_t last_valid = g.N - (g.nb - 1) * BK;
-  hipLaunchKernelGGL((attn_kernel<D, BK>), dim3((uint32_t)w.items), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<D, BK>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
-                     count, order, w.groups, g.nb, g.Npad, last_valid, c_log2);
+                     count, queue, meta, w.groups, g.nb, g.Npad, last_valid, c_log2);
   return hipGetLastError();
 }
 
@@ -660,8 +747,10 @@ AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk) {
   off = align_up(off + (size_t)w.items * nb * sizeof(int32_t), 256);
   w.count_off = off;
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
-  w.order_off = off;
+  w.queue_off = off;
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
+  w.meta_off = off;
+  off = align_up(off + 3 * kQueues * sizeof(int32_t), 256);
   w.vt_off = off;
   off = align_up(off + (size_t)bh * nb * Bk * kMaxHeadDim * 2, 256);  // V^T (bf16)
   w.total = off;
@@ -679,7 +768,8 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   char* base = static_cast<char*>(ws);
   int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
   int32_t* count = reinterpret_cast<int32_t*>(base + w.count_off);
-  int32_t* order = reinterpret_cast<int32_t*>(base + w.order_off);
+  int32_t* queue = reinterpret_cast<int32_t*>(base + w.queue_off);
+  int32_t* meta = reinterpret_cast<int32_t*>(base + w.meta_off);
   __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
 
   hipLaunchKernelGGL(union_kernel, dim3((uint32_t)w.items), dim3(kSchedThreads),
@@ -687,19 +777,22 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
                      w.groups, w.group_size);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads),
-                     (size_t)(g.nb + 1) * sizeof(int32_t), stream, count, order, w.items, g.nb);
+  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
+                     w.groups);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const float c_log2 = scale * 1.4426950408889634f;
   if (head_dim == 128 && g.Bk == 64)
-    return launch_attn<128, 64>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
+    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+                                stream);
   if (head_dim == 64 && g.Bk == 64)
-    return launch_attn<64, 64>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
+    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+                               stream);
   if (head_dim == 128 && g.Bk == 32)
-    return launch_attn<128, 32>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
-  return launch_attn<64, 32>(q, k, v, out, list, count, order, vt, bh, w, g, c_log2, stream);
+    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+                                stream);
+  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2, stream);
 }
 
 }  // namespace svsa

@@ -32,7 +32,7 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
 
 // Attention workspace layout.
 struct AttnWs {
-  size_t list_off, count_off, order_off, vt_off, total;
+  size_t list_off, count_off, queue_off, meta_off, vt_off, total;
   int64_t items;
   int32_t groups;      // query-block groups per (b, h)
   int32_t group_size;  // query blocks per group (256 query rows per group)

@@ -190,8 +190,8 @@ def test_whole_path_bitwise_deterministic():
 
 
 def test_attention_edge_cases_custom_csr():
-    """Empty row -> zeros; out-of-range columns ignored; one block per row is
-    local attention; the tail block's padded keys never contribute."""
+    """Empty row -> zeros (also a whole 4-block query group with nothing to
+    do); out-of-range columns ignored; one block per row is local attention."""
     import block_sparse_attention_17_amd as m
     cfg = get_config("small")
     run, orun = gc.gpu_run("small"), gc.oracle_run("small")
@@ -199,8 +199,8 @@ def test_attention_edge_cases_custom_csr():
     rows_cols = []
     for h in range(H):
         for i in range(nb):
-            if (h, i) == (0, 5):
-                rows_cols.append([])                      # empty
+            if (h, i) == (0, 5) or (h == 2 and 8 <= i < 12):
+                rows_cols.append([])                      # empty (head 2: a whole group)
             elif (h, i) == (1, 7):
                 rows_cols.append([-3, 2, 7, nb + 4])      # out-of-range ignored
             else:
@@ -211,11 +211,13 @@ def test_attention_edge_cases_custom_csr():
     out_bits = run.attention(rp, ci)
     zero_blk = orc.widen(out_bits[0, 0, 5 * 64: 6 * 64])
     assert np.all(zero_blk == 0)
+    assert np.all(orc.widen(out_bits[0, 2, 8 * 64: 12 * 64]) == 0)
     clean = [[c for c in cs if 0 <= c < nb] for cs in rows_cols]
     rp2 = np.zeros_like(rp)
     rp2[1:] = np.cumsum([len(c) for c in clean])
     ci2 = np.array([c for cs in clean for c in cs], np.int32)
-    rows = [(0, h, i) for h in range(H) for i in range(nb) if (h, i) != (0, 5)]
+    rows = [(0, h, i) for h in range(H) for i in range(nb)
+            if (h, i) != (0, 5) and not (h == 2 and 8 <= i < 12)]
     ref = orun.attention_blocks(rp2, ci2, rows)
     max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
