@@ -114,15 +114,17 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
 }
 
 // Work queues.  The items of one (b, h) all go to one of kQueues queues (one
-// per XCD of the chip), filled in (b, h) order and, inside a (b, h), in query
-// group order, so the workgroups running on one XCD at a time work on
-// neighbouring query groups of the same head and share its key blocks in that
-// XCD's L2.  Each (b, h) goes to the queue with the least work so far (work =
-// union lengths plus a per-item constant).  meta = {base[8], len[8], head[8]};
-// head[] (the take counters) is zeroed here, before every attention launch.
+// per XCD of the chip) and, inside it, stay in query group order, so the
+// workgroups running on one XCD at a time work on neighbouring query groups of
+// the same head and share its key blocks in that XCD's L2.  (b, h) pairs are
+// taken heaviest first (work = union lengths plus a per-item constant) and
+// each goes to the queue with the least work so far, so every queue ends with
+// its lightest heads and the last items of the launch are short.
+// meta = {base[8], len[8], take[8]}; take[] is zeroed here, before every
+// attention launch.
 constexpr int kQueues = 8;
 constexpr int kQueueThreads = 1024;
-constexpr int kQueueMaxBh = 4096;   // (b, h) pairs placed by work; beyond, by bh % 8
+constexpr int kQueueMaxBh = 2048;   // (b, h) pairs placed by work; beyond, by bh % 8
 constexpr int kItemCost = 4;        // fixed cost of one item, in key blocks
 
 __global__ void __launch_bounds__(kQueueThreads)
@@ -131,6 +133,7 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   __shared__ int64_t work[kQueueMaxBh];
   __shared__ int32_t qof[kQueueMaxBh];   // queue of each (b, h)
   __shared__ int32_t off[kQueueMaxBh];   // its first position inside that queue
+  __shared__ int32_t by_rank[kQueueMaxBh];  // (b, h) pairs, heaviest first
   __shared__ int32_t len[kQueues], base[kQueues];
   const int t = threadIdx.x;
   const bool by_work = bh_count <= kQueueMaxBh;
@@ -140,12 +143,20 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
       for (int32_t g = 0; g < groups; ++g) w += count[(int64_t)b * groups + g] + kItemCost;
       work[b] = w;
     }
+    __syncthreads();
+    for (int32_t b = t; b < bh_count; b += kQueueThreads) {
+      int32_t rank = 0;
+      for (int32_t o = 0; o < bh_count; ++o)
+        rank += (work[o] > work[b]) || (work[o] == work[b] && o < b);
+      by_rank[rank] = b;
+    }
   }
   __syncthreads();
   if (t == 0) {
     int64_t load[kQueues];
     for (int x = 0; x < kQueues; ++x) { load[x] = 0; len[x] = 0; }
-    for (int32_t b = 0; b < (by_work ? bh_count : 0); ++b) {
+    for (int32_t k = 0; k < (by_work ? bh_count : 0); ++k) {
+      const int32_t b = by_rank[k];
       int best = 0;
       for (int x = 1; x < kQueues; ++x) if (load[x] < load[best]) best = x;
       qof[b] = best;
@@ -312,7 +323,8 @@ __device__ __forceinline__ uint32_t copy_src_off(int wave, int lane, int u) {
 // counting of LDS reads exact: with a FLAT copy in flight it would wait for
 // every outstanding LDS read before each use.)
 template <int D, int BK>
-__device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kdst, char* vdst) {
+__device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kdst, char* vdst,
+                                             int32_t wave_off) {
   using C = Cfg<D, BK>;
   const int32_t boff = j * C::kTileBytes;
 #pragma unroll
@@ -325,22 +337,22 @@ __device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kds
       constexpr int kPerWaveK = C::kDmaPerTile / kWaves;
       if (u < kPerWaveK)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + ld * 1024), 16,
+            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + wave_off + u * kWaves * 1024), 16,
             (int)cx.dma_off[u], boff, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             cx.vt_rsrc,
-            (__attribute__((address_space(3))) void*)(vdst + (ld - C::kDmaPerTile) * 1024), 16,
+            (__attribute__((address_space(3))) void*)(vdst + wave_off + (u * kWaves - C::kDmaPerTile) * 1024), 16,
             (int)cx.dma_off[u], boff, 0, 0);
     } else {
       if (ld < C::kDmaPerTile)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + ld * 1024), 16,
+            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + wave_off + u * kWaves * 1024), 16,
             (int)cx.dma_off[u], boff, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             cx.vt_rsrc,
-            (__attribute__((address_space(3))) void*)(vdst + (ld - C::kDmaPerTile) * 1024), 16,
+            (__attribute__((address_space(3))) void*)(vdst + wave_off + (u * kWaves - C::kDmaPerTile) * 1024), 16,
             (int)cx.dma_off[u], boff, 0, 0);
     }
   }
@@ -439,19 +451,29 @@ __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int
   if (!(e < cx.n_u && active(cx, ent))) return;
   // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
   if ((ent & 0xffffff) == cx.nb - 1 && cx.last_valid < BK) {
+    // lane-dependent limit, computed here (an opaque value keeps the 32
+    // compares out of loop-invariant code motion, where they would pin 32
+    // SGPR-pair lane masks for the whole loop)
+    int lim = cx.last_valid - 4 * cx.hh;
+    asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int c = 0; c < C::kSTiles; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kv = 32 * c + 8 * (r >> 2) + 4 * cx.hh + (r & 3);
-        if (kv >= cx.last_valid) st.sacc[c][r] = -INFINITY;
+        const int kv = 32 * c + 8 * (r >> 2) + (r & 3);  // key index minus 4 hh
+        if (kv >= lim) st.sacc[c][r] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  // row max: two chains of 3-input maxima
+  float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
   for (int c = 0; c < C::kSTiles; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(st.sacc[c][r], st.sacc[c][r + 1]));
+    for (int r = 0; r < 16; r += 4) {
+      m0 = fmaxf(fmaxf(m0, st.sacc[c][r]), st.sacc[c][r + 1]);
+      m1 = fmaxf(fmaxf(m1, st.sacc[c][r + 2]), st.sacc[c][r + 3]);
+    }
+  float mx = fmaxf(m0, m1);
   mx = fmaxf(mx, swap_halves(mx, cx.lane));
   const float mxs = mx * cx.c_log2;
   // lazy rescale: the running max moves only when it grows by > kLazy; O itself
@@ -503,7 +525,7 @@ struct Ring {
 // ent[x] is list entry t0 / 2 - 1 + x.
 template <int D, int BK, int G, int I>
 __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, const Ring<D, BK>& rg,
-                                         int32_t t0, const int32_t (&ent)[kEnt]) {
+                                         int32_t t0, const int32_t (&ent)[kEnt], int32_t wave_off) {
   using C = Cfg<D, BK>;
   const int32_t t = t0 + I;
   if ((I & 1) == 0) {
@@ -511,7 +533,7 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     // clamped) into a slot that is no longer read: unconditional copies keep
     // the per-wave count of copies in flight fixed.
     constexpr int slot = (I / 2 + 2) & 3;
-    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xffffff, rg.k[slot], rg.v[slot]);
+    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xffffff, rg.k[slot], rg.v[slot], wave_off);
   }
   const int32_t ph = t - G;
   if (ph >= 0 && cx.has_rows) {
@@ -526,8 +548,10 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
       v_phase<D, BK>(st, cx, e, ent[x], rg.v[se]);
     }
   }
-  if (I & 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kDmaPerWave));
-  wg_barrier();
+  if (I & 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kDmaPerWave));
+    wg_barrier();
+  }
 }
 
 template <int D, int BK, int G>
@@ -548,14 +572,19 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
     }
 #pragma unroll
     for (int x = 0; x < kEnt; ++x) asm volatile("" : "+s"(ent[x]));
-    interval<D, BK, G, 0>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 1>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 2>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 3>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 4>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 5>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 6>(st, cx, rg, t0, ent);
-    interval<D, BK, G, 7>(st, cx, rg, t0, ent);
+    // LDS offset of this wave's copies, re-materialised every round (kept
+    // out of loop-invariant code motion, which would pin one SGPR per copy
+    // destination and spill)
+    int32_t wave_off = cx.wave * 1024;
+    asm volatile("" : "+s"(wave_off));
+    interval<D, BK, G, 0>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 1>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 2>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 3>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 4>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 5>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 6>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, G, 7>(st, cx, rg, t0, ent, wave_off);
   }
 }
 
