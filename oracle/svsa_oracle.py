@@ -32,6 +32,12 @@ Readings taken where the pages are silent (each is pinned by a test):
   toward the mass.  Fixed mode keeps ceil(f_h * nb) blocks instead.
 * Attention excludes padded keys (their logits are -inf) and leaves padded
   query rows unspecified (they are not compared).
+* Stripe masks ([PSA] Alg. 1) are evaluated at tile granularity: a tile has
+  coordinates (t', s') = (tile's t index, h index * nW + w index) in the tile
+  grid (nT, nH, nW), the six parameters are in tile units (as PSA's search
+  ranges are in PSABlock units), a stride <= 0 stands for infinity, and a
+  query block keeps a key block when some tile of the first attends to some
+  tile of the second.  The diagonal band of the top-p path can be added.
 
 parity pins: see tests/test_oracle_*.py; every public function is pinned.
 """
@@ -43,6 +49,7 @@ __all__ = [
     "num_blocks", "tile_order", "permute_fwd", "permute_inv", "block_valid_counts",
     "pool", "block_logits", "block_scores", "select_row", "block_mask",
     "attention", "attention_rows", "dense_attention", "kept_flops", "widen",
+    "psa_attends", "block_tiles", "stripe_row", "stripe_mask",
 ]
 
 
@@ -282,3 +289,87 @@ def kept_flops(row_ptr, col_idx, N, Bk, D, nrows_per_head=None):
         cols = col_idx[row_ptr[r]: row_ptr[r + 1]]
         total += int(n[i]) * int(n[cols].sum())
     return 4 * D * total
+
+
+# --------------------------------------------------------------------------
+# Stripe masks.  [PSA] Sec. 3.2 "Unified Representation": six integers
+# M(Tw, To, Ts, Sw, So, Ss) give the width, offset and stride of the
+# inter-frame and intra-frame diagonal bands; [PSA] Alg. 1 ("PSA Mask
+# Definition") decides whether position i attends to position j from
+# (t, s) = (i div (H*W), i mod (H*W)); masking is applied per PSABlock.
+# Reading: positions are tiles of the tile grid, so H*W becomes nH*nW; an
+# infinite stride (here any value <= 0) reduces that axis to one band.
+# --------------------------------------------------------------------------
+def _band_cond(delta, width, offset, stride):
+    d = np.abs(delta - offset)
+    if stride > 0:
+        d = d % stride
+    return d <= width - 1
+
+
+def psa_attends(ti, si, tj, sj, params):
+    """[PSA] Alg. 1 on tile coordinates: inter-frame condition on the frame
+    (tile-slab) distance, then intra-frame condition on the in-frame distance.
+    Arrays broadcast; params = (Tw, To, Ts, Sw, So, Ss)."""
+    Tw, To, Ts, Sw, So, Ss = (int(x) for x in params)
+    inter = _band_cond(np.asarray(tj) - np.asarray(ti), Tw, To, Ts)
+    intra = _band_cond(np.asarray(sj) - np.asarray(si), Sw, So, Ss)
+    return inter & intra
+
+
+def block_tiles(grid, tile):
+    """For every block, the distinct tiles its valid tokens belong to, as a
+    list of (t', s') int64 arrays (s' = h' * nW + w')."""
+    T, H, W = grid
+    tt, th, tw = tile
+    nH, nW = -(-H // th), -(-W // tw)
+    N = T * H * W
+    Bk = tt * th * tw
+    nb = num_blocks(N, Bk)
+    pi = tile_order(grid, tile)
+    t, rem = np.divmod(pi, H * W)
+    h, w = np.divmod(rem, W)
+    tp, sp = t // tt, (h // th) * nW + (w // tw)
+    out = []
+    for b in range(nb):
+        sl = slice(b * Bk, min((b + 1) * Bk, N))
+        pairs = np.unique(np.stack([tp[sl], sp[sl]], axis=1), axis=0)
+        out.append((pairs[:, 0], pairs[:, 1]))
+    return out
+
+
+def stripe_row(tiles, i, params, band):
+    """Kept key blocks of query block i (ascending): some tile of block i
+    attends to some tile of block j under [PSA] Alg. 1, or |i - j| <= band-1."""
+    nb = len(tiles)
+    ti, si = tiles[i]
+    kept = np.zeros(nb, dtype=bool)
+    for j in range(nb):
+        tj, sj = tiles[j]
+        kept[j] = bool(np.any(psa_attends(ti[:, None], si[:, None], tj[None, :], sj[None, :],
+                                          params)))
+    kept |= np.abs(np.arange(nb) - i) <= band - 1
+    return np.nonzero(kept)[0].astype(np.int32)
+
+
+def stripe_mask(grid, tile, params, band, batch=1, rows=None):
+    """CSR over rows r = (b*Hh + h)*nb + i with the stripe mask of head h
+    (params: [Hh, 6]).  rows: optional list of (b, h, i) to evaluate; then the
+    result is a dict {(b, h, i): cols} instead of a CSR."""
+    tiles = block_tiles(grid, tile)
+    nb = len(tiles)
+    params = np.asarray(params, dtype=np.int64)
+    Hh = params.shape[0]
+    if rows is not None:
+        return {(b, h, i): stripe_row(tiles, i, params[h], band) for (b, h, i) in rows}
+    counts, cols = [], []
+    for b in range(batch):
+        for h in range(Hh):
+            for i in range(nb):
+                c = stripe_row(tiles, i, params[h], band)
+                cols.append(c)
+                counts.append(c.size)
+    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
+    return row_ptr, col_idx

@@ -7,6 +7,7 @@ from oracle import svsa_oracle as orc
 import tests.test_oracle_attention as ta
 import tests.test_oracle_permute as tp
 import tests.test_oracle_select as ts
+import tests.test_oracle_stripe as tst
 
 
 def _scores_no_scale(qbar, kbar, scale):
@@ -72,6 +73,41 @@ def _attention_rows_v_is_k(qp, kp, vp, b, h, i, cols, N, Bk, scale):
 
 _orig_rows = orc.attention_rows
 
+
+_orig_band = orc._band_cond
+
+
+def _band_wider(delta, width, offset, stride):
+    return _orig_band(delta, width + 1, offset, stride)
+
+
+def _band_no_stride(delta, width, offset, stride):
+    return _orig_band(delta, width, offset, 0)
+
+
+def _attends_reversed(ti, si, tj, sj, params):
+    Tw, To, Ts, Sw, So, Ss = (int(x) for x in params)
+    return (orc._band_cond(np.asarray(ti) - np.asarray(tj), Tw, To, Ts)
+            & orc._band_cond(np.asarray(si) - np.asarray(sj), Sw, So, Ss))
+
+
+def _block_tiles_nh(grid, tile):
+    T, H, W = grid
+    tt, th, tw = tile
+    nH = -(-H // th)
+    N = T * H * W
+    Bk = tt * th * tw
+    pi = orc.tile_order(grid, tile)
+    t, rem = np.divmod(pi, H * W)
+    h, w = np.divmod(rem, W)
+    tp, sp = t // tt, (h // th) * nH + (w // tw)
+    out = []
+    for b in range(-(-N // Bk)):
+        sl = slice(b * Bk, min((b + 1) * Bk, N))
+        pairs = np.unique(np.stack([tp[sl], sp[sl]], axis=1), axis=0)
+        out.append((pairs[:, 0], pairs[:, 1]))
+    return out
+
 MUTATIONS = [
     ("block_scores", _scores_no_scale, ts.test_scores_closed_form_one_channel, ()),
     ("block_scores", _scores_transposed, ts.test_scores_closed_form_one_channel, ()),
@@ -82,6 +118,10 @@ MUTATIONS = [
     ("attention_rows", _attention_rows_with_pads, ta.test_padded_keys_are_excluded, ()),
     ("attention_rows", _attention_rows_v_is_k, ta.test_all_blocks_kept_equals_dense_sdpa,
      ("grid_tile",)),
+    ("_band_cond", _band_wider, tst.test_stripe_svg_special_case_is_a_plain_window, ()),
+    ("_band_cond", _band_no_stride, tst.test_stripe_stride_repeats_the_band, ()),
+    ("psa_attends", _attends_reversed, tst.test_stripe_offset_direction, ()),
+    ("block_tiles", _block_tiles_nh, tst.test_stripe_hand_worked_examples, ("golden",)),
 ]
 
 
