@@ -38,6 +38,9 @@ def parse():
                     choices=["tiny", "small", "wan480", "wan720", "hv720"])
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--fixed", action="store_true", help="per-head keep-fraction mode")
+    ap.add_argument("--stripe", action="store_true",
+                    help="PSA stripe masks instead of top-p: per-head parameters drawn from PSA's "
+                         "Wan 2.1 search ranges (seeded), no pooling stage")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -140,7 +143,7 @@ def main():
         sys.exit(2)
     import torch
     import block_sparse_attention_17_amd as m
-    from svsa_synth import get_config, make_inputs
+    from svsa_synth import get_config, make_inputs, stripe_params
 
     cfg = get_config(args.workload)
     geom = m.Geometry(*cfg.grid, *cfg.tile)
@@ -162,16 +165,23 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
     stage_names = ["permute_qkv", "pool", "mask", "attention", "permute_out"]
 
+    stripe = stripe_params(cfg.heads, seed=args.seed) if args.stripe else None
+
     def step(record=None):
         marks = [ev() for _ in range(6)] if record is not None else None
         if marks: marks[0].record(stream)
         bsa.permute_in(q, k, v)
         if marks: marks[1].record(stream)
-        m.svsa_pool(bsa.qt, bsa.qbar, geom)
-        m.svsa_pool(bsa.kt, bsa.kbar, geom)
+        if stripe is None:
+            m.svsa_pool(bsa.qt, bsa.qbar, geom)
+            m.svsa_pool(bsa.kt, bsa.kbar, geom)
         if marks: marks[2].record(stream)
-        m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
-                          bsa.mask_ws, top_p=tp, keep_frac=kf, band_width=cfg.band)
+        if stripe is None:
+            m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
+                              bsa.col_idx, bsa.mask_ws, top_p=tp, keep_frac=kf,
+                              band_width=cfg.band)
+        else:
+            bsa.build_stripe_mask(stripe, band_width=cfg.band)
         if marks: marks[3].record(stream)
         bsa.attend()
         if marks: marks[4].record(stream)
@@ -212,6 +222,9 @@ def main():
     dense = None
     if not args.no_dense:
         # same kernel with every block kept, same inputs
+        if stripe is not None:   # the stripe steps never pooled
+            m.svsa_pool(bsa.qt, bsa.qbar, geom)
+            m.svsa_pool(bsa.kt, bsa.kbar, geom)
         m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
                           bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
         bsa.attend()
@@ -239,7 +252,7 @@ def main():
         del a, b
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.stripe:
         head = 0
         inp1 = make_inputs(cfg, seed=args.seed, heads=[head])
         cpu = cpu_baseline(cfg, inp1, top_p if not args.fixed else 0.9, args.cpu_budget_s,
@@ -264,7 +277,9 @@ def main():
             "workload": (f"{cfg.name}: grid {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]} "
                          f"({cfg.N} tokens), tiles {cfg.tile[0]}x{cfg.tile[1]}x{cfg.tile[2]}, "
                          f"{cfg.nb} blocks, {cfg.heads} heads, head_dim {cfg.head_dim}, batch "
-                         f"{cfg.batch}, " + ("fixed keep-fraction mode" if args.fixed
+                         f"{cfg.batch}, " + ("PSA stripe masks (seeded per-head parameters "
+                                             "from PSA's Wan 2.1 search ranges)" if args.stripe
+                                             else "fixed keep-fraction mode" if args.fixed
                                              else f"top-p {top_p}") + f", band {cfg.band}"),
             "global_batch": cfg.batch,
             "seq_len": cfg.N,
@@ -288,7 +303,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / BF16_PEAK_TFLOPS,
-            "traffic": None if args.fixed or args.top_p not in (None, 0.9)
+            "traffic": None if args.fixed or args.stripe or args.top_p not in (None, 0.9)
             else measured_traffic(args.workload),
         },
         "cpu_baseline": cpu,

@@ -81,6 +81,9 @@ def _load():
         "svsa_block_mask_workspace_bytes": (sz, [i32, i32, i32]),
         "svsa_block_mask": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, dbl, fp, fp, i32, vp, vp,
                                            i64, vp, sz, vp]),
+        "svsa_stripe_mask_workspace_bytes": (sz, [i32, i32, gp]),
+        "svsa_stripe_mask": (ctypes.c_int, [gp, i32, i32, ctypes.POINTER(ctypes.c_int32), i32, vp,
+                                            vp, i64, vp, sz, vp]),
         "svsa_attn_workspace_bytes": (sz, [i32, i32, gp]),
         "svsa_block_sparse_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp, vp,
                                                   vp, sz, vp]),
@@ -97,8 +100,9 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
-            "svsa_block_mask", "svsa_attn_workspace_bytes", "svsa_block_sparse_attn",
-            "svsa_status_string", "svsa_version")
+            "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
+            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_status_string",
+            "svsa_version")
 
 
 def library_path():
@@ -200,6 +204,26 @@ def svsa_block_mask(qbar, kbar, softmax_scale, row_ptr, col_idx, workspace, top_
         _ptr(col_idx, "col_idx", (torch.int32,)), col_idx.numel(),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
     del tp_arr, kf_arr
+    return row_ptr, col_idx
+
+
+def svsa_stripe_mask_workspace_bytes(batch, heads, geom):
+    return int(_lib.svsa_stripe_mask_workspace_bytes(batch, heads, ctypes.byref(geom.c())))
+
+
+def svsa_stripe_mask(geom, batch, params, row_ptr, col_idx, workspace, band_width=0,
+                     stream=None):
+    """CSR of the PSA stripe mask; params: [heads, 6] ints (Tw, To, Ts, Sw, So, Ss)."""
+    import torch
+    arr = np.ascontiguousarray(np.asarray(params, dtype=np.int32).reshape(-1, 6))
+    heads = arr.shape[0]
+    _check("svsa_stripe_mask", _lib.svsa_stripe_mask(
+        ctypes.byref(geom.c()), int(batch), int(heads),
+        arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(band_width),
+        _ptr(row_ptr, "row_ptr", (torch.int32,)), _ptr(col_idx, "col_idx", (torch.int32,)),
+        col_idx.numel(), _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+        _stream(stream)))
+    del arr
     return row_ptr, col_idx
 
 

@@ -130,6 +130,31 @@ int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32
                                           col_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t svsa_stripe_mask_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
+  Geom g;
+  if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;
+  return svsa::stripe_ws_layout((int64_t)batch * heads * g.nb, g).total;
+}
+
+int svsa_stripe_mask(const svsa_geom* gin, int32_t batch, int32_t heads, const int32_t* params,
+                     int32_t band_width, int32_t* row_ptr, int32_t* col_idx,
+                     int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  if (!params || !row_ptr || !col_idx || batch < 1 || heads < 1 || band_width < 0 ||
+      !make_geom(gin, &g))
+    return SVSA_E_INVALID;
+  for (int32_t h = 0; h < heads && h < svsa::kStripeMaxHeads; ++h)
+    if (params[h * 6 + 0] < 1 || params[h * 6 + 3] < 1) return SVSA_E_INVALID;
+  if (heads > svsa::kStripeMaxHeads || g.nb > kMaxNb || g.Bk > 1024) return SVSA_E_UNSUPPORTED;
+  const int64_t worst = (int64_t)batch * heads * g.nb * g.nb;
+  if (worst >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (col_capacity < worst) return SVSA_E_CAPACITY;
+  if (!workspace || ws_bytes < svsa_stripe_mask_workspace_bytes(batch, heads, gin))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_stripe_mask(g, batch * heads, heads, params, band_width, row_ptr,
+                                           col_idx, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
   Geom g;
   if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;

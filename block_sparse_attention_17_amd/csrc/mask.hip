@@ -412,6 +412,18 @@ compact_kernel(const uint32_t* __restrict__ bits, const int32_t* __restrict__ ro
 
 }  // namespace
 
+hipError_t launch_csr_from_bits(const uint32_t* bits, const int32_t* counts, int32_t* row_ptr,
+                                int32_t* col_idx, int64_t rows, int32_t words,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t cblocks = (rows + kCThreads / 64 - 1) / (kCThreads / 64);
+  hipLaunchKernelGGL(compact_kernel, dim3((uint32_t)cblocks), dim3(kCThreads), 0, stream, bits,
+                     row_ptr, col_idx, rows, words);
+  return hipGetLastError();
+}
+
 MaskWs mask_ws_layout(int64_t rows, int32_t nb) {
   MaskWs m{};
   m.words = (nb + 31) / 32;
@@ -468,13 +480,7 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                        m.words, band, mode, hp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr, rows);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t cblocks = (rows + kCThreads / 64 - 1) / (kCThreads / 64);
-  hipLaunchKernelGGL(compact_kernel, dim3((uint32_t)cblocks), dim3(kCThreads), 0, stream, bits,
-                     row_ptr, col_idx, rows, m.words);
-  return hipGetLastError();
+  return launch_csr_from_bits(bits, counts, row_ptr, col_idx, rows, m.words, stream);
 }
 
 }  // namespace svsa

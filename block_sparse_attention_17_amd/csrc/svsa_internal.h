@@ -30,6 +30,22 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                              const float* keep_frac, int32_t band, int32_t* row_ptr,
                              int32_t* col_idx, void* ws, hipStream_t stream);
 
+// Row bitmaps (words uint32 per row) + row counts -> CSR (row_ptr, col_idx).
+hipError_t launch_csr_from_bits(const uint32_t* bits, const int32_t* counts, int32_t* row_ptr,
+                                int32_t* col_idx, int64_t rows, int32_t words,
+                                hipStream_t stream);
+
+// Stripe-mask workspace layout and launcher.
+constexpr int kStripeMaxHeads = 128;
+struct StripeWs {
+  size_t tiles_off, ntiles_off, bits_off, counts_off, total;
+  int32_t words;
+};
+StripeWs stripe_ws_layout(int64_t rows, const Geom& g);
+hipError_t launch_stripe_mask(const Geom& g, int32_t bh, int32_t heads, const int32_t* params,
+                              int32_t band, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                              hipStream_t stream);
+
 // Attention workspace layout.
 struct AttnWs {
   size_t list_off, count_off, queue_off, meta_off, vt_off, total;

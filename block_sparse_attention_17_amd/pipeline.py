@@ -46,6 +46,16 @@ class BlockSparseAttention:
                           self.col_idx, self.mask_ws, top_p=top_p, keep_frac=keep_frac,
                           band_width=band_width, stream=stream)
 
+    def build_stripe_mask(self, params, band_width=0, stream=None):
+        """CSR of the PSA stripe mask (params: [heads, 6], tile units) into
+        row_ptr / col_idx; the stripe workspace is allocated on first use."""
+        if getattr(self, "stripe_ws", None) is None:
+            self.stripe_ws = torch.empty(
+                B.svsa_stripe_mask_workspace_bytes(self.batch, self.heads, self.geom),
+                dtype=torch.uint8, device=self.row_ptr.device)
+        B.svsa_stripe_mask(self.geom, self.batch, params, self.row_ptr, self.col_idx,
+                           self.stripe_ws, band_width=band_width, stream=stream)
+
     def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None):
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
         B.svsa_block_sparse_attn(self.qt, self.kt, self.vt, self.ot, self.geom, scale,

@@ -146,6 +146,40 @@ SVSA_API int svsa_block_mask(const double* qbar, const double* kbar, int32_t bat
                     void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Workspace (device bytes) needed by svsa_stripe_mask.  Returns 0 if the
+ * sizes are invalid.
+ */
+SVSA_API size_t svsa_stripe_mask_workspace_bytes(int32_t batch, int32_t heads,
+                                                 const svsa_geom* g);
+
+/*
+ * Stripe mask -> CSR.  [PSA] Sec. 3.2 "Unified Representation" and Alg. 1
+ * "PSA Mask Definition": six integers M(Tw, To, Ts, Sw, So, Ss) per head;
+ * position q attends to position k when
+ *   ((|dt - To|) mod Ts) <= Tw - 1  and  ((|ds - So|) mod Ss) <= Sw - 1,
+ * dt = t_k - t_q (frame distance), ds = s_k - s_q (in-frame distance); PSA
+ * applies the mask per PSABlock.  Here positions are the tiles of the tile
+ * grid (nT, nH, nW): t = tile t index, s = tile h index * nW + tile w index,
+ * so the parameters are in tile units; a stride <= 0 means infinity (no
+ * modulo).  Query block i keeps key block j when some tile of block i attends
+ * to some tile of block j (blocks made of partial edge tiles hold several),
+ * or |i - j| <= band_width - 1 (band_width 0: no band).
+ *
+ * params: HOST int32 [heads][6] (Tw, To, Ts, Sw, So, Ss); Tw, Sw >= 1, else
+ *   SVSA_E_INVALID.  heads <= 128, nb <= 4096, tile volume <= 1024, else
+ *   SVSA_E_UNSUPPORTED.
+ * row_ptr / col_idx / col_capacity: as svsa_block_mask (rows (b, h, i),
+ *   ascending columns, capacity >= batch*heads*nb*nb).
+ * workspace: at least svsa_stripe_mask_workspace_bytes(batch, heads, g).
+ * The CSR feeds svsa_block_sparse_attn unchanged.  Integer-only: the lists
+ * are exact and deterministic.
+ */
+SVSA_API int svsa_stripe_mask(const svsa_geom* g, int32_t batch, int32_t heads,
+                              const int32_t* params, int32_t band_width, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_capacity, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/*
  * Workspace (device bytes) needed by svsa_block_sparse_attn: the per-group
  * union lists and work queues, plus a transposed copy of V (sized for
  * head_dim 128, so the figure does not depend on head_dim).  Returns 0 if the

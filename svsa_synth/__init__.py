@@ -6,7 +6,7 @@ contains none of the method's arithmetic: no permutation, pooling, scoring,
 selection or attention.
 """
 from .configs import CONFIGS, Config, get_config
-from .gen import Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits
+from .gen import Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits, stripe_params
 
 __all__ = ["CONFIGS", "Config", "get_config", "Inputs", "make_inputs",
-           "bf16_bits_to_f32", "f32_to_bf16_bits"]
+           "bf16_bits_to_f32", "f32_to_bf16_bits", "stripe_params"]

@@ -157,3 +157,22 @@ def make_inputs(cfg, seed=0, heads=None, keep_f32=None, threads=None):
     sel = np.array(head_list)
     return Inputs(cfg, seed, out["q"], out["k"], out["v"], scales[sel], fmuls[sel], keep[sel],
                   *( (f32["q"], f32["k"], f32["v"]) if f32 is not None else (None, None, None)))
+
+
+_STRIPE_ID = 200
+
+
+def stripe_params(heads, seed=0, stream=0):
+    """Seeded per-head stripe-mask parameters (Tw, To, Ts, Sw, So, Ss), int32
+    [heads, 6], drawn uniformly from the search ranges the PSA paper lists for
+    Wan 2.1 (App., PSA-Search settings): Tw < 7, To in {0, +-1, +-2}, Ts in
+    {1, 2, 3, inf}, Sw < 5, So in {0, +-1}, Ss in {1, 3, 5, 6, inf}; inf is
+    encoded as 0.  Draws only: the mask itself is built elsewhere."""
+    g = _rng(seed, _STRIPE_ID, stream)
+    tw = g.integers(1, 7, size=heads)
+    to = g.choice([0, 1, -1, 2, -2], size=heads)
+    ts = g.choice([1, 2, 3, 0], size=heads)
+    sw = g.integers(1, 5, size=heads)
+    so = g.choice([0, 1, -1], size=heads)
+    ss = g.choice([1, 3, 5, 6, 0], size=heads)
+    return np.stack([tw, to, ts, sw, so, ss], axis=1).astype(np.int32)

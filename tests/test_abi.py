@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -117,3 +117,24 @@ def test_binding_refuses_host_tensors(mod):
     y = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mod.svsa_tile_permute(x, y, G)
+
+
+def test_stripe_mask_argument_errors(mod):
+    lib = mod.library()
+    g = mod.Geometry(4, 8, 8, 2, 4, 4)
+    nb = g.nb
+    prm = (ctypes.c_int32 * 6)(1, 0, 0, 1, 0, 0)
+    bad = (ctypes.c_int32 * 6)(0, 0, 0, 1, 0, 0)        # Tw = 0
+    cap = nb * nb
+    ws = mod.svsa_stripe_mask_workspace_bytes(1, 1, g)
+    assert ws > 0
+    assert mod.svsa_stripe_mask_workspace_bytes(0, 1, g) == 0
+    call = lambda p, band=0, c=cap, w=ws, geo=g, heads=1: lib.svsa_stripe_mask(
+        ctypes.byref(geo.c()), 1, heads, p, band, FAKE, FAKE2, c, FAKE, w, None)
+    assert call(None) == -1
+    assert call(bad) == -1
+    assert call(prm, band=-1) == -1
+    assert call(prm, c=cap - 1) == -4
+    assert call(prm, w=ws - 1) == -3
+    many = (ctypes.c_int32 * (6 * 129))(*([1, 0, 0, 1, 0, 0] * 129))
+    assert call(many, heads=129) == -2

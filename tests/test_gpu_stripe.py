@@ -1,0 +1,80 @@
+"""PSA stripe masks on the GPU (svsa_stripe_mask) against the oracle: the CSR
+is integer work and must match exactly; attention over a stripe CSR must match
+the oracle's attention over the same lists."""
+import numpy as np
+import pytest
+
+from oracle import svsa_oracle as orc
+from svsa_synth import get_config, stripe_params
+import tests.gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+HAND = [
+    [1, 0, 0, 1, 0, 0],      # diagonal only (SVG with width 1)
+    [2, 0, 0, 3, 0, 0],      # SVG window
+    [1, 1, 0, 2, 0, 0],      # one-frame offset
+    [2, 0, 2, 1, 1, 3],      # strides on both axes, intra offset
+    [3, -2, 3, 4, -1, 5],    # negative offsets
+]
+
+
+def _gpu_stripe(cfg, params, band):
+    import torch
+    import block_sparse_attention_17_amd as m
+    g = gc.geometry(cfg)
+    params = np.asarray(params, np.int32).reshape(-1, 6)
+    heads = params.shape[0]
+    rows = cfg.batch * heads * cfg.nb
+    rp = torch.empty(rows + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(rows * cfg.nb, dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.svsa_stripe_mask_workspace_bytes(cfg.batch, heads, g), dtype=torch.uint8,
+                     device="cuda")
+    gc.log(f"{cfg.name}: stripe mask on the GPU, {heads} heads, band {band}")
+    m.svsa_stripe_mask(g, cfg.batch, params, rp, ci, ws, band_width=band)
+    torch.cuda.synchronize()
+    rph = rp.cpu().numpy().astype(np.int64)
+    return rph, ci[: int(rph[-1])].cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_stripe_mask_matches_oracle_whole(name):
+    cfg = get_config(name)
+    sets = [np.array([p] * cfg.heads) for p in HAND] + [stripe_params(cfg.heads, seed=5)]
+    for params in sets:
+        for band in (0, 1):
+            rp, ci = _gpu_stripe(cfg, params, band)
+            rp_o, ci_o = orc.stripe_mask(cfg.grid, cfg.tile, params, band, batch=cfg.batch)
+            assert np.array_equal(rp, rp_o), (name, params[0], band)
+            assert np.array_equal(ci, ci_o), (name, params[0], band)
+
+
+@pytest.mark.parametrize("name", ["wan480", "wan720"])
+def test_stripe_mask_matches_oracle_sampled(name):
+    """Full-size CSR on the GPU; seeded sample of rows (first, last, random) of
+    eight heads recomputed by the oracle.  Wan-480p has 239 blocks made of
+    several partial tiles."""
+    cfg = get_config(name)
+    params = stripe_params(cfg.heads, seed=0)
+    rp, ci = _gpu_stripe(cfg, params, 1)
+    rng = np.random.default_rng(11)
+    rows = []
+    for h in range(0, cfg.heads, max(1, cfg.heads // 8)):
+        pick = {0, cfg.nb - 1} | set(rng.choice(cfg.nb, size=4, replace=False).tolist())
+        rows += [(0, h, i) for i in sorted(pick)]
+    ref = orc.stripe_mask(cfg.grid, cfg.tile, params, 1, rows=rows)
+    for (b, h, i), cols in ref.items():
+        r = (b * cfg.heads + h) * cfg.nb + i
+        assert np.array_equal(ci[rp[r]:rp[r + 1]], cols), (name, h, i)
+
+
+def test_attention_on_stripe_mask_small():
+    cfg = get_config("small")
+    run, orun = gc.gpu_run("small"), gc.oracle_run("small")
+    params = stripe_params(cfg.heads, seed=2)
+    rp, ci = _gpu_stripe(cfg, params, 1)
+    out_bits = run.attention(rp, ci)
+    rows = [(0, h, i) for h in range(cfg.heads) for i in range(cfg.nb)]
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
+    gc.log(f"[gpu-case] small stripe: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
