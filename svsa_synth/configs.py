@@ -5,7 +5,8 @@ grids 21x45x80 and 33x45x80 are the DiT shapes given in the PSA paper
 (Parameterized Stripe Attention for Efficient Video Generation), App. C.2
 "Initialization of Mask Candidates", and heads x head_dim (40x128 for Wan2.1-14B, 24x128
 for HunyuanVideo) are the ones that reproduce the dense TFLOP column of PSA
-Table 2 (4*N^2*D*heads).  The tiny and small cases are CPU-checkable shapes.
+Table 2 (4*N^2*D*heads).  The tiny and small cases are CPU-checkable shapes; small_b2 is the small shape
+with batch 2.
 """
 from dataclasses import dataclass, field
 from math import ceil
@@ -56,6 +57,9 @@ CONFIGS = {
                      (0.9, 0.8, 0.95), pe_scale="uniform"),
     "hv720": Config("hv720", 5, 1, 24, 128, (33, 45, 80), (4, 4, 4), "bf16", (0.9,),
                     pe_scale="uniform", fixed_mode=True),
+    # two independent samples of the small shape in one call (batch > 1)
+    "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
+                       pe_freq="per_head"),
 }
 
 

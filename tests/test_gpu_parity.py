@@ -91,7 +91,7 @@ def test_pool_f32_partial_tail():
 # ---------------------------------------------------------------- stage 3
 MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
               ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
-              ("hv720", 0.9, None), ("hv720", None, "keep")]
+              ("hv720", 0.9, None), ("hv720", None, "keep"), ("small_b2", 0.9, None)]
 
 
 @pytest.mark.parametrize("name,p,mode", MASK_CASES)
@@ -107,7 +107,7 @@ def test_block_mask_matches_oracle(name, p, mode):
     tol, bad = gc.mask_mismatch(cfg, orun.S, g_rp, g_ci, o_rp, o_ci, top_p=top_p,
                                 keep_frac=keep, band=cfg.band)
     gc.log(f"{name} p={p} mode={mode}: {len(tol)} tolerated rows, {len(bad)} failing, "
-           f"kept fraction {o_rp[-1] / (heads * cfg.nb ** 2):.4f}")
+           f"kept fraction {o_rp[-1] / (cfg.batch * heads * cfg.nb ** 2):.4f}")
     assert not bad, f"rows {bad[:10]} differ beyond the threshold tolerance"
     # every GPU row ascending and unique
     for r in range(0, len(g_rp) - 1, max(1, (len(g_rp) - 1) // 997)):
@@ -130,7 +130,8 @@ def test_block_mask_band_and_limits():
 
 
 # ---------------------------------------------------------------- stage 4
-ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2)]
+ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
+              ("small_b2", None)]
 
 
 @pytest.mark.parametrize("name,per_head", ATTN_CASES)
