@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan720",
-                    choices=["tiny", "small", "wan480", "wan720", "hv720"])
+                    choices=["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa"])
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--fixed", action="store_true", help="per-head keep-fraction mode")
     ap.add_argument("--stripe", action="store_true",

@@ -158,7 +158,8 @@ int svsa_stripe_mask(const svsa_geom* gin, int32_t batch, int32_t heads, const i
 size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
   Geom g;
   if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;
-  return svsa::attn_ws_layout(batch * heads, g.nb, g.Bk).total;
+  if (g.Bk % 32 != 0) return 0;
+  return svsa::attn_ws_layout(batch * heads, g).total;
 }
 
 int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
@@ -170,10 +171,13 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
       head_dim < 1 || !make_geom(gin, &g) || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
   if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
-  if ((g.Bk != 64 && g.Bk != 32) || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  if (g.Bk % 32 != 0 || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int32_t sub = g.Bk % 64 == 0 ? 64 : 32;
+  const int64_t nbs = ((int64_t)g.N + sub - 1) / sub;   // sub-blocks seen by the kernels
+  if (nbs > kMaxNb) return SVSA_E_UNSUPPORTED;
   if ((int64_t)g.Npad * head_dim * 2 >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
   const int64_t bh = (int64_t)batch * heads;
-  if (bh * g.nb * (int64_t)g.nb >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (bh * nbs * nbs >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
   const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;
   if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
       overlaps(out, tbytes, v, tbytes))

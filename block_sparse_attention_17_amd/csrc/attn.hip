@@ -9,8 +9,12 @@
 // kernel grouping.
 //
 // Design for CDNA4 (not a port of the Hopper producer/consumer pipeline):
+//  * The kernels see the sequence as sub-blocks of 64 tokens (32 when the block
+//    size is an odd multiple of 32); a block of Bk tokens is Bk / 64
+//    consecutive sub-blocks, each with the block's list (so PSA-shaped
+//    3x8x16 = 384-token blocks run unchanged).
 //  * A workgroup is 8 wavefronts (32 query rows each) and owns 256 consecutive
-//    query rows of one (b, h): 4 blocks of 64 tokens, or 8 blocks of 32.
+//    query rows of one (b, h): 4 sub-blocks of 64 tokens, or 8 of 32.
 //    Neighbouring query blocks keep largely the same key blocks, so the
 //    workgroup streams the UNION of their lists through LDS once and every
 //    wavefront whose block keeps the current key block computes on it.
@@ -68,10 +72,13 @@ constexpr int kPre = 4;   // P V operands read before the barrier that opens an 
 // ---------------------------------------------------------------------------
 constexpr int kSchedThreads = 256;
 
+// The attention kernels work on sub-blocks of S = 64 (or 32) tokens; a block
+// of Bk = ratio * S tokens is `ratio` consecutive sub-blocks, so block-level
+// lists expand to sub-block lists here (nb: sub-blocks, nb_blk: blocks).
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t groups,
-             int32_t group_size) {
+             int32_t group_size, int32_t ratio, int32_t nb_blk) {
   extern __shared__ uint32_t mask[];  // [nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
   const int64_t item = blockIdx.x;
@@ -81,13 +88,17 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   for (int32_t j = t; j < nb; j += kSchedThreads) mask[j] = 0u;
   __syncthreads();
   for (int m = 0; m < group_size; ++m) {
-    const int32_t i = g * group_size + m;
+    const int32_t i = g * group_size + m;   // query sub-block
     if (i >= nb) break;
-    const int64_t row = bh * nb + i;
+    const int64_t row = bh * nb_blk + i / ratio;
     const int32_t e0 = row_ptr[row], e1 = row_ptr[row + 1];
     for (int32_t e = e0 + t; e < e1; e += kSchedThreads) {
-      const int32_t j = col_idx[e];
-      if (j >= 0 && j < nb) atomicOr(&mask[j], 1u << m);
+      const int32_t jb = col_idx[e];
+      if (jb < 0 || jb >= nb_blk) continue;
+      for (int32_t r = 0; r < ratio; ++r) {
+        const int32_t j = jb * ratio + r;
+        if (j < nb) atomicOr(&mask[j], 1u << m);
+      }
     }
   }
   __syncthreads();
@@ -766,14 +777,17 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
 
 }  // namespace
 
-AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk) {
+AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
   AttnWs w{};
-  w.group_size = kRowsPerItem / Bk;
-  w.groups = (nb + w.group_size - 1) / w.group_size;
+  w.sub = g.Bk % 64 == 0 ? 64 : 32;
+  w.ratio = g.Bk / w.sub;
+  w.nbs = (g.N + w.sub - 1) / w.sub;
+  w.group_size = kRowsPerItem / w.sub;
+  w.groups = (w.nbs + w.group_size - 1) / w.group_size;
   w.items = (int64_t)bh * w.groups;
   size_t off = 0;
   w.list_off = off;
-  off = align_up(off + (size_t)w.items * nb * sizeof(int32_t), 256);
+  off = align_up(off + (size_t)w.items * w.nbs * sizeof(int32_t), 256);
   w.count_off = off;
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
   w.queue_off = off;
@@ -781,7 +795,7 @@ AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk) {
   w.meta_off = off;
   off = align_up(off + 3 * kQueues * sizeof(int32_t), 256);
   w.vt_off = off;
-  off = align_up(off + (size_t)bh * nb * Bk * kMaxHeadDim * 2, 256);  // V^T (bf16)
+  off = align_up(off + (size_t)bh * g.Npad * kMaxHeadDim * 2, 256);  // V^T (bf16)
   w.total = off;
   return w;
 }
@@ -790,9 +804,13 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
                                     hipStream_t stream) {
-  if (g.Bk != 32 && g.Bk != 64) return hipErrorInvalidValue;
+  if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
-  const AttnWs w = attn_ws_layout(bh, g.nb, g.Bk);
+  const AttnWs w = attn_ws_layout(bh, g);
+  // the attention kernels see the sequence as w.nbs sub-blocks of w.sub tokens
+  Geom gs = g;
+  gs.Bk = w.sub;
+  gs.nb = w.nbs;   // gs.Npad stays the tensor's row count (head stride)
   if (w.items > 0x7fffffff) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
@@ -802,8 +820,8 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
 
   hipLaunchKernelGGL(union_kernel, dim3((uint32_t)w.items), dim3(kSchedThreads),
-                     (size_t)g.nb * sizeof(uint32_t), stream, row_ptr, col_idx, list, count, g.nb,
-                     w.groups, w.group_size);
+                     (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
+                     w.nbs, w.groups, w.group_size, w.ratio, g.nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
@@ -812,16 +830,16 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   if (e != hipSuccess) return e;
 
   const float c_log2 = scale * 1.4426950408889634f;
-  if (head_dim == 128 && g.Bk == 64)
-    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+  if (head_dim == 128 && gs.Bk == 64)
+    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
                                 stream);
-  if (head_dim == 64 && g.Bk == 64)
-    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+  if (head_dim == 64 && gs.Bk == 64)
+    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
                                stream);
-  if (head_dim == 128 && g.Bk == 32)
-    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2,
+  if (head_dim == 128 && gs.Bk == 32)
+    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
                                 stream);
-  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, g, c_log2, stream);
+  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2, stream);
 }
 
 }  // namespace svsa

@@ -50,10 +50,13 @@ hipError_t launch_stripe_mask(const Geom& g, int32_t bh, int32_t heads, const in
 struct AttnWs {
   size_t list_off, count_off, queue_off, meta_off, vt_off, total;
   int64_t items;
-  int32_t groups;      // query-block groups per (b, h)
-  int32_t group_size;  // query blocks per group (256 query rows per group)
+  int32_t groups;      // query sub-block groups per (b, h)
+  int32_t group_size;  // query sub-blocks per group (256 query rows per group)
+  int32_t sub;         // sub-block size seen by the attention kernels (64 or 32)
+  int32_t ratio;       // sub-blocks per block (Bk / sub)
+  int32_t nbs;         // sub-blocks of the sequence, ceil(N / sub)
 };
-AttnWs attn_ws_layout(int32_t bh, int32_t nb, int32_t Bk);
+AttnWs attn_ws_layout(int32_t bh, const Geom& g);
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,

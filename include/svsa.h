@@ -202,8 +202,11 @@ SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const sv
  *   overlap q, k or v.  A query block with an empty list gets zeros.
  * row_ptr / col_idx: CSR as produced by svsa_block_mask (rows (b,h,i); each
  *   column in [0, nb)).  Columns outside [0, nb) are ignored.
- * head_dim: 64 or 128; tile volume Bk: 32 or 64; N_pad * head_dim * 2 bytes
- *   per (b, h) below 2^31 (else SVSA_E_UNSUPPORTED).  Products are bf16 x bf16
+ * head_dim: 64 or 128; tile volume Bk: any multiple of 32 (blocks are run as
+ *   consecutive sub-blocks of 64 tokens, or 32 when Bk is an odd multiple of
+ *   32; a block's list applies to each of its sub-blocks); ceil(N / sub) <= 4096
+ *   and N_pad * head_dim * 2 bytes per (b, h) below 2^31 (else
+ *   SVSA_E_UNSUPPORTED).  Products are bf16 x bf16
  *   on the matrix cores with float32 accumulation; the softmax runs in
  *   float32.
  * workspace: at least svsa_attn_workspace_bytes(batch, heads, g) bytes.

@@ -57,6 +57,10 @@ CONFIGS = {
                      (0.9, 0.8, 0.95), pe_scale="uniform"),
     "hv720": Config("hv720", 5, 1, 24, 128, (33, 45, 80), (4, 4, 4), "bf16", (0.9,),
                     pe_scale="uniform", fixed_mode=True),
+    # the Wan2.1-720p shape with PSA's PSABlock shape 3x8x16 (384 tokens) as the
+    # tile ([PSA] App. C.2), tail padding only: 197 blocks of 384
+    "wan720_psa": Config("wan720_psa", 7, 1, 40, 128, (21, 45, 80), (3, 8, 16), "bf16", (0.9,),
+                         pe_scale="uniform"),
     # two independent samples of the small shape in one call (batch > 1)
     "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
                        pe_freq="per_head"),

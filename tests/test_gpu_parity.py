@@ -14,7 +14,7 @@ from tests import gpu_cases as gc  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-ALL = ["tiny", "small", "wan480", "wan720", "hv720"]
+ALL = ["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa"]
 
 
 @pytest.fixture(autouse=True)
@@ -91,7 +91,8 @@ def test_pool_f32_partial_tail():
 # ---------------------------------------------------------------- stage 3
 MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
               ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
-              ("hv720", 0.9, None), ("hv720", None, "keep"), ("small_b2", 0.9, None)]
+              ("hv720", 0.9, None), ("hv720", None, "keep"), ("small_b2", 0.9, None),
+              ("wan720_psa", 0.9, None)]
 
 
 @pytest.mark.parametrize("name,p,mode", MASK_CASES)
@@ -148,6 +149,19 @@ def test_attention_matches_oracle(name, per_head):
     ref = orun.attention_blocks(o_rp, o_ci, rows)
     max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
     gc.log(f"{name}: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_attention_psa_block_shape_wan720():
+    """384-token blocks (PSA's 3x8x16 PSABlock shape): the attention kernel runs
+    them as six 64-token sub-blocks; rows of five heads, incl. the tail block."""
+    cfg = get_config("wan720_psa")
+    run, orun = gc.gpu_run("wan720_psa"), gc.oracle_run("wan720_psa")
+    o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, 0.9, np.float32), band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    rows = gc.sample_rows(cfg, o_rp, 1, seed=9, heads=[0, 7, 13, 21, 33])
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+    gc.log(f"wan720_psa: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
