@@ -38,6 +38,11 @@ Readings taken where the pages are silent (each is pinned by a test):
   ranges are in PSABlock units), a stride <= 0 stands for infinity, and a
   query block keeps a key block when some tile of the first attends to some
   tile of the second.  The diagonal band of the top-p path can be added.
+* 3D padding ([PSA] Sec. 4.1 / App. C.2: the latent grid is padded so that
+  every PSABlock is full): every tile is its own block of Bk slots, nb =
+  nT*nH*nW; its valid tokens fill the first slots (row-major (t, h, w) order)
+  and the remaining slots are padding, excluded like the tail padding.  The
+  order of tokens inside a block does not change any block-level quantity.
 
 parity pins: see tests/test_oracle_*.py; every public function is pinned.
 """
@@ -49,7 +54,7 @@ __all__ = [
     "num_blocks", "tile_order", "permute_fwd", "permute_inv", "block_valid_counts",
     "pool", "block_logits", "block_scores", "select_row", "block_mask",
     "attention", "attention_rows", "dense_attention", "kept_flops", "widen",
-    "psa_attends", "block_tiles", "stripe_row", "stripe_mask",
+    "psa_attends", "block_tiles", "stripe_row", "stripe_mask", "block_layout",
 ]
 
 
@@ -92,31 +97,65 @@ def tile_order(grid, tile):
     return natural[order].astype(np.int64)
 
 
-def permute_fwd(x, grid, tile):
-    """X'[..., j, :] = X[..., pi(j), :] for j < N; rows N..nb*Bk-1 are zero.
+def permute_fwd(x, grid, tile, pad3d=False):
+    """X'[..., j, :] = X[..., slot(j), :] for every valid slot j; padding slots
+    are zero (see block_layout).
 
     x: [B, Hh, N, D] in natural order (any float dtype or bf16 bits).
     Returns float64 [B, Hh, nb*Bk, D].
     """
     xf = widen(x)
     B, Hh, N, D = xf.shape
-    Bk = int(np.prod(tile))
-    nb = num_blocks(N, Bk)
-    pi = tile_order(grid, tile)
-    assert pi.shape[0] == N
-    out = np.zeros((B, Hh, nb * Bk, D))
-    out[:, :, :N, :] = xf[:, :, pi, :]
+    slots, _ = block_layout(grid, tile, pad3d)
+    valid = slots >= 0
+    assert int(valid.sum()) == N
+    out = np.zeros((B, Hh, slots.size, D))
+    out[:, :, valid, :] = xf[:, :, slots[valid], :]
     return out
 
 
-def permute_inv(xp, grid, tile):
-    """O[..., pi(j), :] = O'[..., j, :] for j < N (the padded tail is dropped)."""
+def permute_inv(xp, grid, tile, pad3d=False):
+    """O[..., slot(j), :] = O'[..., j, :] for every valid slot j (padding dropped)."""
     xf = widen(xp)
     N = int(np.prod(grid))
-    pi = tile_order(grid, tile)
+    slots, _ = block_layout(grid, tile, pad3d)
+    valid = slots >= 0
     out = np.empty(xf.shape[:2] + (N, xf.shape[3]))
-    out[:, :, pi, :] = xf[:, :, :N, :]
+    out[:, :, slots[valid], :] = xf[:, :, valid, :]
     return out
+
+
+def block_layout(grid, tile, pad3d=False):
+    """(slots, counts): slots int64 [nb*Bk] = natural index of the token in each
+    tiled slot or -1 for padding; counts int64 [nb] = valid tokens of each
+    block (always the first slots of the block).
+
+    pad3d=False: the tile order of tile_order(), cut into consecutive Bk-token
+    blocks, padding only at the tail.  pad3d=True: one block per tile (tiles
+    row-major over the tile grid), the tile's tokens first, padding after."""
+    T, H, W = grid
+    tt, th, tw = tile
+    N, Bk = T * H * W, tt * th * tw
+    if not pad3d:
+        nb = num_blocks(N, Bk)
+        slots = np.full(nb * Bk, -1, dtype=np.int64)
+        slots[:N] = tile_order(grid, tile)
+        return slots, block_valid_counts(N, Bk)
+    nT, nH, nW = -(-T // tt), -(-H // th), -(-W // tw)
+    nb = nT * nH * nW
+    slots = np.full(nb * Bk, -1, dtype=np.int64)
+    counts = np.zeros(nb, dtype=np.int64)
+    for a in range(nT):
+        for b in range(nH):
+            for c in range(nW):
+                k = (a * nH + b) * nW + c
+                t, h, w = np.meshgrid(np.arange(a * tt, min((a + 1) * tt, T)),
+                                      np.arange(b * th, min((b + 1) * th, H)),
+                                      np.arange(c * tw, min((c + 1) * tw, W)), indexing="ij")
+                nat = ((t * H + h) * W + w).ravel()
+                slots[k * Bk: k * Bk + nat.size] = nat
+                counts[k] = nat.size
+    return slots, counts
 
 
 def block_valid_counts(N, Bk):
@@ -133,13 +172,17 @@ def block_valid_counts(N, Bk):
 # importance is scored at the level of token groups.  Reading: the summary of
 # a block is the arithmetic mean of its valid tokens.
 # --------------------------------------------------------------------------
-def pool(xp, N, Bk):
-    """Xbar_i = (1/n_i) * sum of the valid rows of block i.  -> [B, Hh, nb, D]."""
+def pool(xp, N, Bk, counts=None):
+    """Xbar_i = (1/n_i) * sum of the valid rows of block i.  -> [B, Hh, nb, D].
+
+    counts: valid tokens per block (the first rows of each block); default the
+    tail-padded layout's."""
     xf = widen(xp)
     B, Hh, Np, D = xf.shape
-    nb = num_blocks(N, Bk)
+    if counts is None:
+        counts = block_valid_counts(N, Bk)
+    nb = len(counts)
     assert Np == nb * Bk
-    counts = block_valid_counts(N, Bk)
     out = np.empty((B, Hh, nb, D))
     for i in range(nb):
         rows = xf[:, :, i * Bk: i * Bk + counts[i], :]
@@ -228,16 +271,19 @@ def block_mask(S, band, top_p=None, keep_frac=None):
 # The oracle evaluates the same quantity directly: one softmax over the union
 # of the kept blocks' valid keys (what the blockwise accumulation equals).
 # --------------------------------------------------------------------------
-def attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale):
+def attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
     """Output rows of query block i of (b, h) as float64 [n_i, D].
 
     qp, kp, vp: tiled [B, Hh, nb*Bk, D] arrays (bf16 bits or float).
-    cols: kept key blocks of this row.
+    cols: kept key blocks of this row.  counts: valid tokens per block (a
+    prefix of each block); default the tail-padded layout's.
     """
-    nb = num_blocks(N, Bk)
-    n_i = min(Bk, N - i * Bk)
+    if counts is None:
+        counts = block_valid_counts(N, Bk)
+    nb = len(counts)
+    n_i = int(counts[i])
     q = widen(qp[b, h, i * Bk: i * Bk + n_i])
-    keys = np.concatenate([np.arange(j * Bk, min((j + 1) * Bk, N)) for j in cols])
+    keys = np.concatenate([np.arange(j * Bk, j * Bk + int(counts[j])) for j in cols])
     assert all(0 <= j < nb for j in cols)
     k = widen(kp[b, h, keys])
     v = widen(vp[b, h, keys])
@@ -247,22 +293,25 @@ def attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale):
     return wgt @ v
 
 
-def attention(qp, kp, vp, row_ptr, col_idx, N, Bk, scale, rows=None):
+def attention(qp, kp, vp, row_ptr, col_idx, N, Bk, scale, rows=None, counts=None):
     """O' (tiled, float64 [B, Hh, nb*Bk, D]) for the listed query blocks.
 
     rows: optional iterable of (b, h, i); default all.  Rows not computed and
     padded query rows are NaN.
     """
     B, Hh, Np, D = qp.shape
-    nb = num_blocks(N, Bk)
+    if counts is None:
+        counts = block_valid_counts(N, Bk)
+    nb = len(counts)
     out = np.full((B, Hh, Np, D), np.nan)
     if rows is None:
         rows = [(b, h, i) for b in range(B) for h in range(Hh) for i in range(nb)]
     for (b, h, i) in rows:
         r = (b * Hh + h) * nb + i
         cols = col_idx[row_ptr[r]: row_ptr[r + 1]]
-        n_i = min(Bk, N - i * Bk)
-        out[b, h, i * Bk: i * Bk + n_i] = attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale)
+        n_i = int(counts[i])
+        out[b, h, i * Bk: i * Bk + n_i] = attention_rows(qp, kp, vp, b, h, i, cols, N, Bk, scale,
+                                                         counts)
     return out
 
 
@@ -275,13 +324,13 @@ def dense_attention(q, k, v, scale):
     return np.matmul(wgt, vf)
 
 
-def kept_flops(row_ptr, col_idx, N, Bk, D, nrows_per_head=None):
+def kept_flops(row_ptr, col_idx, N, Bk, D, nrows_per_head=None, counts=None):
     """Algorithmic FLOPs of block-sparse attention: 4*D*sum_(i,j kept) n_i*n_j.
 
     This is the accounting of [PSA] Table 2, whose dense rows equal 4*N^2*D*heads.
     """
-    nb = num_blocks(N, Bk)
-    n = block_valid_counts(N, Bk)
+    n = block_valid_counts(N, Bk) if counts is None else np.asarray(counts)
+    nb = len(n)
     total = 0
     nrows = len(row_ptr) - 1
     for r in range(nrows):
@@ -317,12 +366,15 @@ def psa_attends(ti, si, tj, sj, params):
     return inter & intra
 
 
-def block_tiles(grid, tile):
+def block_tiles(grid, tile, pad3d=False):
     """For every block, the distinct tiles its valid tokens belong to, as a
     list of (t', s') int64 arrays (s' = h' * nW + w')."""
     T, H, W = grid
     tt, th, tw = tile
     nH, nW = -(-H // th), -(-W // tw)
+    if pad3d:   # one block per tile
+        nT = -(-T // tt)
+        return [(np.array([k // (nH * nW)]), np.array([k % (nH * nW)])) for k in range(nT * nH * nW)]
     N = T * H * W
     Bk = tt * th * tw
     nb = num_blocks(N, Bk)
@@ -352,11 +404,11 @@ def stripe_row(tiles, i, params, band):
     return np.nonzero(kept)[0].astype(np.int32)
 
 
-def stripe_mask(grid, tile, params, band, batch=1, rows=None):
+def stripe_mask(grid, tile, params, band, batch=1, rows=None, pad3d=False):
     """CSR over rows r = (b*Hh + h)*nb + i with the stripe mask of head h
     (params: [Hh, 6]).  rows: optional list of (b, h, i) to evaluate; then the
     result is a dict {(b, h, i): cols} instead of a CSR."""
-    tiles = block_tiles(grid, tile)
+    tiles = block_tiles(grid, tile, pad3d)
     nb = len(tiles)
     params = np.asarray(params, dtype=np.int64)
     Hh = params.shape[0]

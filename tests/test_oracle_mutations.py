@@ -8,6 +8,7 @@ import tests.test_oracle_attention as ta
 import tests.test_oracle_permute as tp
 import tests.test_oracle_select as ts
 import tests.test_oracle_stripe as tst
+import tests.test_oracle_pad3d as tpd
 
 
 def _scores_no_scale(qbar, kbar, scale):
@@ -57,7 +58,7 @@ def _select_strict(s_row, i, band, top_p=None, keep_frac=None):
     return np.nonzero(kept)[0]
 
 
-def _attention_rows_with_pads(qp, kp, vp, b, h, i, cols, N, Bk, scale):
+def _attention_rows_with_pads(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
     n_i = min(Bk, N - i * Bk)
     q = orc.widen(qp[b, h, i * Bk: i * Bk + n_i])
     keys = np.concatenate([np.arange(j * Bk, (j + 1) * Bk) for j in cols])
@@ -67,11 +68,52 @@ def _attention_rows_with_pads(qp, kp, vp, b, h, i, cols, N, Bk, scale):
     return (w / w.sum(1, keepdims=True)) @ v
 
 
-def _attention_rows_v_is_k(qp, kp, vp, b, h, i, cols, N, Bk, scale):
-    return _orig_rows(qp, kp, kp, b, h, i, cols, N, Bk, scale)
+def _attention_rows_v_is_k(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
+    return _orig_rows(qp, kp, kp, b, h, i, cols, N, Bk, scale, counts)
 
 
 _orig_rows = orc.attention_rows
+
+
+_orig_pool = orc.pool
+
+
+def _pool_ignores_counts(xp, N, Bk, counts=None):
+    xf = orc.widen(xp)
+    nb = xf.shape[2] // Bk
+    return xf.reshape(xf.shape[0], xf.shape[1], nb, Bk, xf.shape[3]).mean(axis=3)
+
+
+def _rows_ignore_counts(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
+    q = orc.widen(qp[b, h, i * Bk: i * Bk + int(counts[i])])
+    keys = np.concatenate([np.arange(j * Bk, (j + 1) * Bk) for j in cols])
+    lg = q @ orc.widen(kp[b, h, keys]).T * scale
+    w = np.exp(lg - lg.max(1, keepdims=True))
+    return (w / w.sum(1, keepdims=True)) @ orc.widen(vp[b, h, keys])
+
+
+_orig_layout = orc.block_layout
+
+
+def _layout_pads_in_place(grid, tile, pad3d=False):
+    if not pad3d:
+        return _orig_layout(grid, tile, pad3d)
+    T, H, W = grid
+    tt, th, tw = tile
+    nT, nH, nW = -(-T // tt), -(-H // th), -(-W // tw)
+    Bk = tt * th * tw
+    slots = np.full(nT * nH * nW * Bk, -1, dtype=np.int64)
+    counts = np.zeros(nT * nH * nW, dtype=np.int64)
+    for a in range(nT):
+        for b in range(nH):
+            for c in range(nW):
+                k = (a * nH + b) * nW + c
+                for x in range(Bk):   # slot x <-> in-tile (t, h, w), padding where off-grid
+                    t, h, w = a * tt + x // (th * tw), b * th + (x // tw) % th, c * tw + x % tw
+                    if t < T and h < H and w < W:
+                        slots[k * Bk + x] = (t * H + h) * W + w
+                        counts[k] += 1
+    return slots, counts
 
 
 _orig_band = orc._band_cond
@@ -91,7 +133,7 @@ def _attends_reversed(ti, si, tj, sj, params):
             & orc._band_cond(np.asarray(si) - np.asarray(sj), Sw, So, Ss))
 
 
-def _block_tiles_nh(grid, tile):
+def _block_tiles_nh(grid, tile, pad3d=False):
     T, H, W = grid
     tt, th, tw = tile
     nH = -(-H // th)
@@ -122,6 +164,9 @@ MUTATIONS = [
     ("_band_cond", _band_no_stride, tst.test_stripe_stride_repeats_the_band, ()),
     ("psa_attends", _attends_reversed, tst.test_stripe_offset_direction, ()),
     ("block_tiles", _block_tiles_nh, tst.test_stripe_hand_worked_examples, ("golden",)),
+    ("pool", _pool_ignores_counts, tpd.test_pad3d_pool_is_the_mean_of_each_tile, ()),
+    ("attention_rows", _rows_ignore_counts, tpd.test_pad3d_full_attention_equals_dense, ()),
+    ("block_layout", _layout_pads_in_place, tpd.test_pad3d_hand_worked_layouts, ("golden",)),
 ]
 
 
