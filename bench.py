@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan720",
-                    choices=["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa"])
+                    choices=["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa",
+                             "wan720_psa3d"])
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--fixed", action="store_true", help="per-head keep-fraction mode")
     ap.add_argument("--stripe", action="store_true",
@@ -78,10 +79,10 @@ def measured_traffic(workload):
         return None
 
 
-def kept_flops_from_csr(rp, ci, N, Bk, nb, D):
-    """4*D*sum n_i*n_j from host copies of the CSR (vectorised bookkeeping)."""
-    n = np.full(nb, Bk, np.int64)
-    n[-1] = N - (nb - 1) * Bk
+def kept_flops_from_csr(rp, ci, n, D):
+    """4*D*sum n_i*n_j from host copies of the CSR (vectorised bookkeeping);
+    n = valid tokens per block."""
+    nb = len(n)
     rows = len(rp) - 1
     counts = np.diff(rp)
     row_i = np.repeat(np.arange(rows) % nb, counts)
@@ -100,20 +101,20 @@ def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
     N, Bk, nb, D = cfg.N, cfg.Bk, cfg.nb, cfg.head_dim
     scale = 1 / sqrt(D)
     t0 = time.perf_counter()
-    qp = orc.permute_fwd(inp_head.q, cfg.grid, cfg.tile)
-    kp = orc.permute_fwd(inp_head.k, cfg.grid, cfg.tile)
-    vp = orc.permute_fwd(inp_head.v, cfg.grid, cfg.tile)
-    S = orc.block_scores(orc.pool(qp, N, Bk), orc.pool(kp, N, Bk), scale)
+    _, n = orc.block_layout(cfg.grid, cfg.tile, cfg.pad3d)
+    qp = orc.permute_fwd(inp_head.q, cfg.grid, cfg.tile, cfg.pad3d)
+    kp = orc.permute_fwd(inp_head.k, cfg.grid, cfg.tile, cfg.pad3d)
+    vp = orc.permute_fwd(inp_head.v, cfg.grid, cfg.tile, cfg.pad3d)
+    S = orc.block_scores(orc.pool(qp, N, Bk, n), orc.pool(kp, N, Bk, n), scale)
     rp, ci = orc.block_mask(S, cfg.band, top_p=np.array([top_p], np.float32))
     t_mask = time.perf_counter() - t0
     rng = np.random.default_rng(11)
     order = rng.permutation(nb)
     t1 = time.perf_counter()
     done, flops = 0, 0
-    n = orc.block_valid_counts(N, Bk)
     for i in order:
         cols = ci[rp[i]: rp[i + 1]]
-        orc.attention_rows(qp, kp, vp, 0, 0, int(i), cols, N, Bk, scale)
+        orc.attention_rows(qp, kp, vp, 0, 0, int(i), cols, N, Bk, scale, n)
         flops += 4 * D * int(n[i]) * int(n[cols].sum())
         done += 1
         if time.perf_counter() - t1 > budget_s:
@@ -146,7 +147,7 @@ def main():
     from svsa_synth import get_config, make_inputs, stripe_params
 
     cfg = get_config(args.workload)
-    geom = m.Geometry(*cfg.grid, *cfg.tile)
+    geom = m.Geometry.from_config(cfg)
     top_p = args.top_p if args.top_p is not None else cfg.top_p[0]
     t0 = time.perf_counter()
     inp = make_inputs(cfg, seed=args.seed)
@@ -210,7 +211,7 @@ def main():
 
     rp = bsa.row_ptr.cpu().numpy().astype(np.int64)
     ci = bsa.col_idx[: int(rp[-1])].cpu().numpy()
-    flops = kept_flops_from_csr(rp, ci, cfg.N, cfg.Bk, cfg.nb, cfg.head_dim)
+    flops = kept_flops_from_csr(rp, ci, geom.valid_counts(), cfg.head_dim)
     dense_flops = 4 * cfg.N * cfg.N * cfg.head_dim * cfg.heads * cfg.batch
     kept_frac = flops / dense_flops
     counts = np.diff(rp).reshape(cfg.batch * cfg.heads, cfg.nb)

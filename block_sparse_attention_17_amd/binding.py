@@ -28,18 +28,20 @@ class SvsaError(RuntimeError):
 
 
 class _Geom(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "W", "tt", "th", "tw")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "W", "tt", "th", "tw", "pad3d")]
 
 
 @dataclass(frozen=True)
 class Geometry:
-    """Latent grid (T, H, W) and tile shape (tt, th, tw)."""
+    """Latent grid (T, H, W), tile shape (tt, th, tw) and block layout (pad3d:
+    one block per tile with padding inside the sequence, else tail padding)."""
     T: int
     H: int
     W: int
     tt: int
     th: int
     tw: int
+    pad3d: bool = False
 
     @property
     def N(self):
@@ -50,19 +52,37 @@ class Geometry:
         return self.tt * self.th * self.tw
 
     @property
+    def tile_grid(self):
+        return (-(-self.T // self.tt), -(-self.H // self.th), -(-self.W // self.tw))
+
+    @property
     def nb(self):
+        if self.pad3d:
+            nT, nH, nW = self.tile_grid
+            return nT * nH * nW
         return -(-self.N // self.Bk)
 
     @property
     def N_pad(self):
         return self.nb * self.Bk
 
+    def valid_counts(self):
+        """int64 [nb]: valid tokens of each block (its first slots)."""
+        if not self.pad3d:
+            n = np.full(self.nb, self.Bk, np.int64)
+            n[-1] = self.N - (self.nb - 1) * self.Bk
+            return n
+        nT, nH, nW = self.tile_grid
+        ext = lambda L, t, n: np.minimum(t, L - np.arange(n) * t)
+        return (ext(self.T, self.tt, nT)[:, None, None] * ext(self.H, self.th, nH)[None, :, None]
+                * ext(self.W, self.tw, nW)[None, None, :]).astype(np.int64).ravel()
+
     def c(self):
-        return _Geom(self.T, self.H, self.W, self.tt, self.th, self.tw)
+        return _Geom(self.T, self.H, self.W, self.tt, self.th, self.tw, int(bool(self.pad3d)))
 
     @staticmethod
     def from_config(cfg):
-        return Geometry(*cfg.grid, *cfg.tile)
+        return Geometry(*cfg.grid, *cfg.tile, pad3d=getattr(cfg, "pad3d", False))
 
 
 def _load():

@@ -17,17 +17,21 @@ constexpr int32_t kMaxNb = 4096;
 bool make_geom(const svsa_geom* in, Geom* g) {
   if (!in) return false;
   if (in->T < 1 || in->H < 1 || in->W < 1 || in->tt < 1 || in->th < 1 || in->tw < 1) return false;
+  if (in->pad3d != 0 && in->pad3d != 1) return false;
   const int64_t N = (int64_t)in->T * in->H * in->W;
   const int64_t Bk = (int64_t)in->tt * in->th * in->tw;
   if (N >= (1ll << 30) || Bk >= 65536) return false;
   g->T = in->T; g->H = in->H; g->W = in->W;
   g->tt = in->tt; g->th = in->th; g->tw = in->tw;
+  g->pad3d = in->pad3d;
   g->nT = (in->T + in->tt - 1) / in->tt;
   g->nH = (in->H + in->th - 1) / in->th;
   g->nW = (in->W + in->tw - 1) / in->tw;
   g->N = (int32_t)N;
   g->Bk = (int32_t)Bk;
-  g->nb = (int32_t)((N + Bk - 1) / Bk);
+  const int64_t nb = in->pad3d ? (int64_t)g->nT * g->nH * g->nW : (N + Bk - 1) / Bk;
+  if (nb >= (1ll << 30)) return false;
+  g->nb = (int32_t)nb;
   const int64_t Npad = (int64_t)g->nb * Bk;
   if (Npad >= (1ll << 30)) return false;
   g->Npad = (int32_t)Npad;
@@ -52,7 +56,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 extern "C" {
 
-int svsa_version(void) { return 100; }
+int svsa_version(void) { return 101; }
 
 const char* svsa_status_string(int status) {
   switch (status) {
@@ -173,7 +177,8 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
   if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
   if (g.Bk % 32 != 0 || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
   const int32_t sub = g.Bk % 64 == 0 ? 64 : 32;
-  const int64_t nbs = ((int64_t)g.N + sub - 1) / sub;   // sub-blocks seen by the kernels
+  // sub-blocks seen by the kernels
+  const int64_t nbs = g.pad3d ? (int64_t)g.nb * (g.Bk / sub) : ((int64_t)g.N + sub - 1) / sub;
   if (nbs > kMaxNb) return SVSA_E_UNSUPPORTED;
   if ((int64_t)g.Npad * head_dim * 2 >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
   const int64_t bh = (int64_t)batch * heads;

@@ -66,19 +66,27 @@ constexpr int kWin = 8;   // LDS operand reads in flight ahead of the MFMA strea
 constexpr int kPre = 4;   // P V operands read before the barrier that opens an M phase
 
 // ---------------------------------------------------------------------------
-// Schedule: per item (b, h, group of query blocks) the ascending union of the
-// group's kept key blocks; entry = j | (mask << 24), bit m of mask set when the
-// m-th query block of the group keeps j.
+// Schedule: per item (b, h, group of query sub-blocks) the ascending union of
+// the group's kept key sub-blocks; entry = j | (valid << 12) | (mask << 24):
+// j the key sub-block (< 4096), valid its valid tokens (its first slots; key
+// sub-blocks with none are left out), bit m of mask set when the m-th query
+// sub-block of the group keeps j.
 // ---------------------------------------------------------------------------
 constexpr int kSchedThreads = 256;
 
 // The attention kernels work on sub-blocks of S = 64 (or 32) tokens; a block
 // of Bk = ratio * S tokens is `ratio` consecutive sub-blocks, so block-level
 // lists expand to sub-block lists here (nb: sub-blocks, nb_blk: blocks).
+__device__ __forceinline__ int32_t sub_valid(const Geom& g, int32_t j, int32_t ratio, int32_t sub) {
+  const int32_t v = block_valid(g, j / ratio) - (j % ratio) * sub;
+  return v < 0 ? 0 : (v > sub ? sub : v);
+}
+
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t groups,
-             int32_t group_size, int32_t ratio, int32_t nb_blk) {
+             int32_t group_size, int32_t ratio, int32_t sub, Geom gb) {
+  const int32_t nb_blk = gb.nb;
   extern __shared__ uint32_t mask[];  // [nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
   const int64_t item = blockIdx.x;
@@ -90,6 +98,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   for (int m = 0; m < group_size; ++m) {
     const int32_t i = g * group_size + m;   // query sub-block
     if (i >= nb) break;
+    if (sub_valid(gb, i, ratio, sub) == 0) continue;   // padding only: nothing to compute
     const int64_t row = bh * nb_blk + i / ratio;
     const int32_t e0 = row_ptr[row], e1 = row_ptr[row + 1];
     for (int32_t e = e0 + t; e < e1; e += kSchedThreads) {
@@ -97,7 +106,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
       if (jb < 0 || jb >= nb_blk) continue;
       for (int32_t r = 0; r < ratio; ++r) {
         const int32_t j = jb * ratio + r;
-        if (j < nb) atomicOr(&mask[j], 1u << m);
+        if (j < nb && sub_valid(gb, j, ratio, sub) > 0) atomicOr(&mask[j], 1u << m);
       }
     }
   }
@@ -117,7 +126,8 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
       if (k < wv) wbase += wave_tot[k];
       tot += wave_tot[k];
     }
-    if (m != 0u) out[off + wbase + before] = j | (int32_t)(m << 24);
+    if (m != 0u)
+      out[off + wbase + before] = j | (sub_valid(gb, j, ratio, sub) << 12) | (int32_t)(m << 24);
     off += tot;
     __syncthreads();
   }
@@ -304,7 +314,7 @@ struct Ctx {
   __amdgpu_buffer_rsrc_t k_rsrc;   // K of this (b, h)
   __amdgpu_buffer_rsrc_t vt_rsrc;  // V^T blocks of this (b, h)
   const int32_t* lst;
-  int32_t n_u, T, nb, last_valid;
+  int32_t n_u, T, nb;
   float c_log2;
   int wave, lane, qb, l32, hh;
   uint32_t dma_off[4];  // per-lane source offsets of this wave's copies
@@ -461,11 +471,12 @@ __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int
   using C = Cfg<D, BK>;
   if (!(e < cx.n_u && active(cx, ent))) return;
   // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
-  if ((ent & 0xffffff) == cx.nb - 1 && cx.last_valid < BK) {
+  const int32_t nvalid = (ent >> 12) & 127;   // valid keys: the first nvalid
+  if (nvalid < BK) {
     // lane-dependent limit, computed here (an opaque value keeps the 32
     // compares out of loop-invariant code motion, where they would pin 32
     // SGPR-pair lane masks for the whole loop)
-    int lim = cx.last_valid - 4 * cx.hh;
+    int lim = nvalid - 4 * cx.hh;
     asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int c = 0; c < C::kSTiles; ++c)
@@ -544,7 +555,7 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     // clamped) into a slot that is no longer read: unconditional copies keep
     // the per-wave count of copies in flight fixed.
     constexpr int slot = (I / 2 + 2) & 3;
-    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xffffff, rg.k[slot], rg.v[slot], wave_off);
+    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xfff, rg.k[slot], rg.v[slot], wave_off);
   }
   const int32_t ph = t - G;
   if (ph >= 0 && cx.has_rows) {
@@ -615,7 +626,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const int32_t* __restrict__ list,
                                          const int32_t* __restrict__ count, int64_t item,
                                          int32_t groups, int32_t nb, int32_t Npad,
-                                         int32_t last_valid, float c_log2, const Ring<D, BK>& rg) {
+                                         float c_log2, const Ring<D, BK>& rg) {
   using C = Cfg<D, BK>;
   constexpr int kS = D / 16, kDT = D / 32;
 
@@ -638,7 +649,6 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   // rounds of 8 (the extra intervals do nothing); an empty union runs none
   cx.T = cx.n_u > 0 ? (2 * cx.n_u + 2 + 7) & ~7 : 0;
   cx.nb = nb;
-  cx.last_valid = last_valid;
   cx.c_log2 = c_log2;
   cx.lst = list + item * nb;
   // raw buffer resources over this head's K and V^T (byte range Npad * D * 2,
@@ -701,7 +711,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
             const int32_t* __restrict__ list, const int32_t* __restrict__ count,
             const int32_t* __restrict__ queue, int32_t* __restrict__ meta, int32_t groups,
-            int32_t nb, int32_t Npad, int32_t last_valid, float c_log2) {
+            int32_t nb, int32_t Npad, float c_log2) {
   using C = Cfg<D, BK>;
   __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
       k2[C::kTileBytes], k3[C::kTileBytes];
@@ -729,7 +739,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int32_t item = s_item;
     __syncthreads();
     if (item < 0) break;
-    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, Npad, last_valid, c_log2, rg);
+    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, Npad, c_log2, rg);
   }
 }
 
@@ -768,10 +778,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
   uint32_t grid = 0;
   e = attn_grid<D, BK>(w.items, &grid);
   if (e != hipSuccess) return e;
-  const int32_t last_valid = g.N - (g.nb - 1) * BK;
   hipLaunchKernelGGL((attn_kernel<D, BK>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
-                     count, queue, meta, w.groups, g.nb, g.Npad, last_valid, c_log2);
+                     count, queue, meta, w.groups, g.nb, g.Npad, c_log2);
   return hipGetLastError();
 }
 
@@ -781,7 +790,7 @@ AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
   AttnWs w{};
   w.sub = g.Bk % 64 == 0 ? 64 : 32;
   w.ratio = g.Bk / w.sub;
-  w.nbs = (g.N + w.sub - 1) / w.sub;
+  w.nbs = g.pad3d ? g.nb * w.ratio : (g.N + w.sub - 1) / w.sub;
   w.group_size = kRowsPerItem / w.sub;
   w.groups = (w.nbs + w.group_size - 1) / w.group_size;
   w.items = (int64_t)bh * w.groups;
@@ -821,7 +830,7 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
 
   hipLaunchKernelGGL(union_kernel, dim3((uint32_t)w.items), dim3(kSchedThreads),
                      (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
-                     w.nbs, w.groups, w.group_size, w.ratio, g.nb);
+                     w.nbs, w.groups, w.group_size, w.ratio, w.sub, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,

@@ -9,8 +9,10 @@
 // The tiled offset of tile (a,b,c) with extents (sa,sb,sc) is
 //   a*tt*H*W + sa*(b*th)*W + sa*sb*(c*tw)
 // because every tile before it in the walk is full along the axes that are
-// already complete.  Rows are copied 16 bytes per lane, so both the gather
-// side and the scatter side move whole contiguous rows.
+// already complete (packed layout), or tile_index * Bk (3D-padded layout,
+// [PSA] App. C.2: every tile owns a whole block, padding after its tokens).
+// Rows are copied 16 bytes per lane, so both the gather side and the scatter
+// side move whole contiguous rows.
 #include "svsa_internal.h"
 
 namespace svsa {
@@ -18,13 +20,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// floor(n / d) for n, d < 2^16 via a 32-bit reciprocal: m = ceil(2^32 / d)
-// gives the exact quotient because n * (m*d - 2^32) < 2^16 * d <= 2^32.
-__device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t m) {
-  return __umulhi(n, m);
+// floor(n / d) for n, d < 2^16 via a reciprocal m = ceil(2^32 / d): the
+// quotient (n * m) >> 32 is exact because n * (m*d - 2^32) < n * d < 2^32.
+// m needs 33 bits (d = 1 gives 2^32), so it is kept in 64 bits.
+__device__ __forceinline__ uint32_t div_small(uint32_t n, uint64_t m) {
+  return (uint32_t)(((uint64_t)n * m) >> 32);
 }
-__device__ __forceinline__ uint32_t recip_small(uint32_t d) {
-  return (uint32_t)((0x100000000ull + d - 1) / d);
+__device__ __forceinline__ uint64_t recip_small(uint32_t d) {
+  return (0x100000000ull + d - 1) / d;
 }
 
 // chunks_per_row = head_dim * element_bytes / 16 is a power of two (2^chunk_shift).
@@ -43,10 +46,12 @@ tile_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int3
   const int32_t sb = min(g.th, g.H - b * g.th);
   const int32_t sc = min(g.tw, g.W - c * g.tw);
   const int32_t vol = sa * sb * sc;
-  const int64_t tiled0 = (int64_t)a * g.tt * g.H * g.W + (int64_t)sa * (b * g.th) * g.W +
-                         (int64_t)sa * sb * (c * g.tw);
+  // packed layout: tiles back to back; 3D-padded layout: one Bk-slot block per tile
+  const int64_t tiled0 = g.pad3d ? (int64_t)tile * g.Bk
+                                 : (int64_t)a * g.tt * g.H * g.W + (int64_t)sa * (b * g.th) * g.W +
+                                       (int64_t)sa * sb * (c * g.tw);
   const int64_t nat0 = ((int64_t)(a * g.tt) * g.H + b * g.th) * g.W + c * g.tw;
-  const uint32_t m_sc = recip_small(sc), m_plane = recip_small(sb * sc);
+  const uint64_t m_sc = recip_small(sc), m_plane = recip_small(sb * sc);
 
   const int64_t nat_rows = (int64_t)g.N, tiled_rows = (int64_t)g.Npad;
   const uint4* sbase = src + bh * (kInverse ? tiled_rows : nat_rows) * chunks_per_row;
@@ -68,8 +73,15 @@ tile_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int3
       dbase[til * chunks_per_row + ch] = sbase[nat * chunks_per_row + ch];
     }
   }
-  // The workgroup of the last tile also clears the padded tail (forward only).
-  if (!kInverse && tile == ntiles - 1) {
+  // Padding slots are cleared (forward only): the rest of each partial tile's
+  // block in the 3D-padded layout, the sequence tail (by the last tile's
+  // workgroup) in the packed one.
+  if (!kInverse && g.pad3d && vol < g.Bk) {
+    const int32_t pad_chunks = (g.Bk - vol) * chunks_per_row;
+    uint4* pad = dbase + (tiled0 + vol) * chunks_per_row;
+    for (int32_t e = threadIdx.x; e < pad_chunks; e += kThreads) pad[e] = make_uint4(0, 0, 0, 0);
+  }
+  if (!kInverse && !g.pad3d && tile == ntiles - 1) {
     const int32_t pad_chunks = (g.Npad - g.N) * chunks_per_row;
     uint4* tail = dbase + (int64_t)g.N * chunks_per_row;
     for (int32_t e = threadIdx.x; e < pad_chunks; e += kThreads) tail[e] = make_uint4(0, 0, 0, 0);

@@ -28,7 +28,7 @@ pool_kernel(const uint4* __restrict__ x, double* __restrict__ out, int32_t head_
   const int32_t nb = g.nb;
   const int64_t bh = blockIdx.x / nb;
   const int32_t blk = blockIdx.x % nb;
-  const int32_t n_valid = min(g.Bk, g.N - blk * g.Bk);
+  const int32_t n_valid = block_valid(g, blk);
   const int32_t chunks = head_dim / kPer;         // chunks per row
   const int32_t groups = kThreads / chunks;       // row groups
   const int32_t ch = threadIdx.x % chunks;

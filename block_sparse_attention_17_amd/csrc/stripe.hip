@@ -36,6 +36,11 @@ __global__ void __launch_bounds__(kTilesThreads)
 block_tiles_kernel(int2* __restrict__ tiles, int32_t* __restrict__ ntiles, Geom g) {
   const int32_t b = blockIdx.x * kTilesThreads + threadIdx.x;
   if (b >= g.nb) return;
+  if (g.pad3d) {   // one block per tile
+    tiles[(int64_t)b * g.Bk] = make_int2(b / (g.nH * g.nW), b % (g.nH * g.nW));
+    ntiles[b] = 1;
+    return;
+  }
   const int64_t HW = (int64_t)g.H * g.W;
   int64_t p = (int64_t)b * g.Bk;
   const int64_t end = min((int64_t)(b + 1) * g.Bk, (int64_t)g.N);

@@ -10,7 +10,21 @@ struct Geom {
   int32_t T, H, W, tt, th, tw;
   int32_t nT, nH, nW;   // tile grid
   int32_t N, Bk, nb, Npad;
+  int32_t pad3d;        // 1: one block per tile (padding inside the sequence)
 };
+
+// Valid tokens of block b (the block's first slots).
+__host__ __device__ inline int32_t block_valid(const Geom& g, int32_t b) {
+  if (!g.pad3d) {
+    const int32_t r = g.N - b * g.Bk;
+    return r < g.Bk ? r : g.Bk;
+  }
+  const int32_t a = b / (g.nH * g.nW), c_h = (b / g.nW) % g.nH, c_w = b % g.nW;
+  const int32_t sa = g.T - a * g.tt < g.tt ? g.T - a * g.tt : g.tt;
+  const int32_t sb = g.H - c_h * g.th < g.th ? g.H - c_h * g.th : g.th;
+  const int32_t sc = g.W - c_w * g.tw < g.tw ? g.W - c_w * g.tw : g.tw;
+  return sa * sb * sc;
+}
 
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,

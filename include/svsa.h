@@ -55,10 +55,21 @@
 extern "C" {
 #endif
 
-/* Latent grid (T,H,W) and tile shape (tt,th,tw); all must be >= 1. */
+/*
+ * Latent grid (T,H,W), tile shape (tt,th,tw) (all >= 1) and block layout.
+ * pad3d = 0: tiles walked row-major over the tile grid, tokens inside a tile
+ *   row-major (t,h,w), edge tiles partial; the sequence is cut into
+ *   consecutive blocks of Bk = tt*th*tw tokens, padding only at the tail:
+ *   nb = ceil(N / Bk).
+ * pad3d = 1: [PSA] App. C.2 ("3D-Padding"): one block per tile, nb = nT*nH*nW
+ *   (tile grid ceil(T/tt) x ceil(H/th) x ceil(W/tw)); the tile's tokens fill
+ *   the first slots of its block, the rest of the block is padding.
+ * In both layouts every block's valid tokens are its first slots.
+ */
 typedef struct svsa_geom {
   int32_t T, H, W;
   int32_t tt, th, tw;
+  int32_t pad3d;
 } svsa_geom;
 
 enum svsa_dtype { SVSA_BF16 = 0, SVSA_F32 = 1 };

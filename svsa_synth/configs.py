@@ -6,7 +6,8 @@ grids 21x45x80 and 33x45x80 are the DiT shapes given in the PSA paper
 "Initialization of Mask Candidates", and heads x head_dim (40x128 for Wan2.1-14B, 24x128
 for HunyuanVideo) are the ones that reproduce the dense TFLOP column of PSA
 Table 2 (4*N^2*D*heads).  The tiny and small cases are CPU-checkable shapes; small_b2 is the small shape
-with batch 2.
+with batch 2.  The *_pad3d / *_psa3d cases use PSA's 3D padding (one block per
+tile, padding inside the sequence; PSA App. C.2).
 """
 from dataclasses import dataclass, field
 from math import ceil
@@ -27,6 +28,7 @@ class Config:
     pe_scale: str = "fixed"      # "fixed" (1.5) or "uniform" (U[0.5, 3.0] per head)
     pe_freq: str = "unit"        # "unit" or "per_head" (2^U[-2,0] per head)
     fixed_mode: bool = False     # also run the per-head keep-fraction mode
+    pad3d: bool = False          # one block per tile, padding inside the sequence
 
     @property
     def N(self):
@@ -40,6 +42,9 @@ class Config:
 
     @property
     def nb(self):
+        if self.pad3d:
+            return ceil(self.grid[0] / self.tile[0]) * ceil(self.grid[1] / self.tile[1]) * \
+                ceil(self.grid[2] / self.tile[2])
         return ceil(self.N / self.Bk)
 
     @property
@@ -61,6 +66,17 @@ CONFIGS = {
     # tile ([PSA] App. C.2), tail padding only: 197 blocks of 384
     "wan720_psa": Config("wan720_psa", 7, 1, 40, 128, (21, 45, 80), (3, 8, 16), "bf16", (0.9,),
                          pe_scale="uniform"),
+    # the same with PSA's 3D padding (the grid padded to 21x48x80, one block per
+    # PSABlock: 7 x 6 x 5 = 210 blocks of 384 slots)
+    "wan720_psa3d": Config("wan720_psa3d", 8, 1, 40, 128, (21, 45, 80), (3, 8, 16), "bf16",
+                           (0.9,), pe_scale="uniform", pad3d=True),
+    # a small 3D-padded case with partial tiles on every axis
+    "small_pad3d": Config("small_pad3d", 9, 1, 4, 64, (5, 7, 9), (2, 4, 4), "bf16", (0.9,),
+                          pad3d=True),
+    # 3D padding with 128-slot blocks (two 64-token sub-blocks; edge tiles hold
+    # as few as 4 tokens, so whole sub-blocks are padding)
+    "tiny_pad3d": Config("tiny_pad3d", 10, 1, 2, 128, (3, 9, 20), (2, 4, 16), "bf16", (0.9,),
+                         pad3d=True),
     # two independent samples of the small shape in one call (batch > 1)
     "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
                        pe_freq="per_head"),

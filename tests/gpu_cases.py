@@ -39,7 +39,7 @@ def dev_to_bits(t):
 
 def geometry(cfg):
     import block_sparse_attention_17_amd as m
-    return m.Geometry(*cfg.grid, *cfg.tile)
+    return m.Geometry.from_config(cfg)
 
 
 @lru_cache(maxsize=8)
@@ -101,20 +101,20 @@ class OracleRun:
         self.cfg = cfg = get_config(name)
         self.inp = inp = inputs(name, seed)
         log(f"{name}: oracle tile order / pool / scores")
-        self.pi = orc.tile_order(cfg.grid, cfg.tile)
+        self.slots, self.counts = orc.block_layout(cfg.grid, cfg.tile, cfg.pad3d)
         self.qt_bits = self._permute_bits(inp.q)
         self.kt_bits = self._permute_bits(inp.k)
         self.vt_bits = self._permute_bits(inp.v)
-        self.qbar = np.concatenate([orc.pool(self.qt_bits[:, h:h + 1], cfg.N, cfg.Bk)
+        self.qbar = np.concatenate([orc.pool(self.qt_bits[:, h:h + 1], cfg.N, cfg.Bk, self.counts)
                                     for h in range(cfg.heads)], axis=1)
-        self.kbar = np.concatenate([orc.pool(self.kt_bits[:, h:h + 1], cfg.N, cfg.Bk)
+        self.kbar = np.concatenate([orc.pool(self.kt_bits[:, h:h + 1], cfg.N, cfg.Bk, self.counts)
                                     for h in range(cfg.heads)], axis=1)
         self.S = orc.block_scores(self.qbar, self.kbar, 1 / sqrt(cfg.head_dim))
 
     def _permute_bits(self, x):
-        cfg = self.cfg
-        out = np.zeros(x.shape[:2] + (cfg.N_pad, x.shape[3]), np.uint16)
-        out[:, :, : cfg.N] = x[:, :, self.pi]
+        valid = self.slots >= 0
+        out = np.zeros(x.shape[:2] + (self.slots.size, x.shape[3]), np.uint16)
+        out[:, :, valid] = x[:, :, self.slots[valid]]
         return out
 
     def mask(self, top_p=None, keep_frac=None, band=1):
@@ -129,7 +129,7 @@ class OracleRun:
             r = (b * cfg.heads + h) * cfg.nb + i
             cols = ci[rp[r]: rp[r + 1]]
             res[(b, h, i)] = orc.attention_rows(self.qt_bits, self.kt_bits, self.vt_bits, b, h, i,
-                                                cols, cfg.N, cfg.Bk, scale)
+                                                cols, cfg.N, cfg.Bk, scale, self.counts)
         return res
 
 

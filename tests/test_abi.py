@@ -55,6 +55,19 @@ def test_permute_argument_errors(mod):
     assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 64, _g(mod, 0, 8, 8, 2, 4, 4), 0,
                                  None) == E_INV
     assert lib.svsa_tile_permute(FAKE, FAKE, 0, 1, 1, 64, g, 0, None) == E_INV    # in place
+    bad = mod.Geometry(4, 8, 8, 2, 4, 4).c()
+    bad.pad3d = 2                                                                  # not 0/1
+    assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 64, ctypes.byref(bad), 0, None) == E_INV
+
+
+def test_pad3d_geometry_counts(mod):
+    """Host-side layout bookkeeping of the 3D-padded layout (no GPU call)."""
+    G = mod.Geometry(21, 45, 80, 3, 8, 16, pad3d=True)
+    assert G.tile_grid == (7, 6, 5) and G.nb == 210 and G.N_pad == 210 * 384
+    n = G.valid_counts()
+    assert n.sum() == 21 * 45 * 80 and n.max() == 384 and n.min() == 3 * 5 * 16
+    P = mod.Geometry(21, 45, 80, 3, 8, 16)
+    assert P.nb == 197 and P.valid_counts().sum() == 21 * 45 * 80
 
 
 def test_pool_argument_errors(mod):

@@ -14,7 +14,8 @@ from tests import gpu_cases as gc  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-ALL = ["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa"]
+ALL = ["tiny", "small", "wan480", "wan720", "hv720", "wan720_psa", "small_pad3d", "tiny_pad3d",
+       "wan720_psa3d"]
 
 
 @pytest.fixture(autouse=True)
@@ -32,7 +33,7 @@ def test_permute_bit_exact(name):
         assert np.array_equal(g, o), f"{name}: permuted {tag} differs"
 
 
-@pytest.mark.parametrize("name", ["small", "wan720"])
+@pytest.mark.parametrize("name", ["small", "wan720", "small_pad3d", "wan720_psa3d"])
 def test_inverse_permute_round_trip(name):
     import block_sparse_attention_17_amd as m
     run = gc.gpu_run(name)
@@ -43,11 +44,13 @@ def test_inverse_permute_round_trip(name):
 
 
 @pytest.mark.parametrize("grid,tile,D", [((3, 5, 6), (2, 2, 4), 64), ((5, 7, 3), (4, 4, 4), 128),
-                                         ((21, 30, 52), (4, 4, 4), 64), ((1, 1, 1), (2, 2, 2), 64)])
+                                         ((21, 30, 52), (4, 4, 4), 64), ((1, 1, 1), (2, 2, 2), 64),
+                                         ((4, 6, 9), (2, 4, 4), 64), ((3, 1, 5), (2, 4, 4), 128)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_permute_partial_tiles_and_f32(grid, tile, D, dtype):
+@pytest.mark.parametrize("pad3d", [False, True])
+def test_permute_partial_tiles_and_f32(grid, tile, D, dtype, pad3d):
     import block_sparse_attention_17_amd as m
-    G = m.Geometry(*grid, *tile)
+    G = m.Geometry(*grid, *tile, pad3d=pad3d)
     rng = np.random.default_rng(7)
     N = G.N
     if dtype == "f32":
@@ -58,7 +61,7 @@ def test_permute_partial_tiles_and_f32(grid, tile, D, dtype):
         xd = gc.bits_to_dev(x)
     out = torch.full((2, 3, G.N_pad, D), 7, dtype=xd.dtype, device="cuda")
     m.svsa_tile_permute(xd, out, G)
-    ref = orc.permute_fwd(x, grid, tile)
+    ref = orc.permute_fwd(x, grid, tile, pad3d)
     got = out.float().cpu().numpy().astype(np.float64)
     assert np.array_equal(got, ref)
     back = torch.empty_like(xd)
@@ -92,7 +95,8 @@ def test_pool_f32_partial_tail():
 MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
               ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
               ("hv720", 0.9, None), ("hv720", None, "keep"), ("small_b2", 0.9, None),
-              ("wan720_psa", 0.9, None)]
+              ("wan720_psa", 0.9, None), ("small_pad3d", 0.9, None), ("tiny_pad3d", 0.9, None),
+              ("wan720_psa3d", 0.9, None)]
 
 
 @pytest.mark.parametrize("name,p,mode", MASK_CASES)
@@ -132,7 +136,7 @@ def test_block_mask_band_and_limits():
 
 # ---------------------------------------------------------------- stage 4
 ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
-              ("small_b2", None)]
+              ("small_b2", None), ("small_pad3d", None), ("tiny_pad3d", None)]
 
 
 @pytest.mark.parametrize("name,per_head", ATTN_CASES)
@@ -163,6 +167,34 @@ def test_attention_psa_block_shape_wan720():
     max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
     gc.log(f"wan720_psa: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_attention_psa_3d_padding_wan720():
+    """PSA's 3D-padded layout at full size: 210 blocks of 384 slots, the last
+    tile row holding 3x5x16 = 240 tokens (sub-blocks 4 and 5 padding only);
+    sampled rows include the padded tiles' rows."""
+    cfg = get_config("wan720_psa3d")
+    run, orun = gc.gpu_run("wan720_psa3d"), gc.oracle_run("wan720_psa3d")
+    o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, 0.9, np.float32), band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    rows = gc.sample_rows(cfg, o_rp, 1, seed=4, heads=[0, 11, 26, 39])
+    rows += [(0, 5, i) for i in (25, 29, 209)]    # tiles of the padded last tile row
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+    gc.log(f"wan720_psa3d: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_whole_path_pad3d_equals_dense_attention():
+    """3D-padded layout, every block kept: the whole path (permute, pool, mask,
+    attention, inverse permute) equals dense attention in natural order."""
+    cfg = get_config("tiny_pad3d")
+    run = gc.gpu_run("tiny_pad3d")
+    out = run.bsa(run.q_dev, run.k_dev, run.v_dev, top_p=np.ones(cfg.heads, np.float32))
+    torch.cuda.synchronize()
+    got = orc.widen(gc.dev_to_bits(out))
+    ref = orc.dense_attention(run.inp.q, run.inp.k, run.inp.v, 1 / np.sqrt(cfg.head_dim))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert np.abs(got - ref).max() <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
 def test_attention_fixed_mode_hv720():

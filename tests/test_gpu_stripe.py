@@ -37,19 +37,20 @@ def _gpu_stripe(cfg, params, band):
     return rph, ci[: int(rph[-1])].cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["tiny", "small"])
+@pytest.mark.parametrize("name", ["tiny", "small", "small_pad3d", "tiny_pad3d"])
 def test_stripe_mask_matches_oracle_whole(name):
     cfg = get_config(name)
     sets = [np.array([p] * cfg.heads) for p in HAND] + [stripe_params(cfg.heads, seed=5)]
     for params in sets:
         for band in (0, 1):
             rp, ci = _gpu_stripe(cfg, params, band)
-            rp_o, ci_o = orc.stripe_mask(cfg.grid, cfg.tile, params, band, batch=cfg.batch)
+            rp_o, ci_o = orc.stripe_mask(cfg.grid, cfg.tile, params, band, batch=cfg.batch,
+                                         pad3d=cfg.pad3d)
             assert np.array_equal(rp, rp_o), (name, params[0], band)
             assert np.array_equal(ci, ci_o), (name, params[0], band)
 
 
-@pytest.mark.parametrize("name", ["wan480", "wan720"])
+@pytest.mark.parametrize("name", ["wan480", "wan720", "wan720_psa3d"])
 def test_stripe_mask_matches_oracle_sampled(name):
     """Full-size CSR on the GPU; seeded sample of rows (first, last, random) of
     eight heads recomputed by the oracle.  Wan-480p has 239 blocks made of
@@ -62,7 +63,7 @@ def test_stripe_mask_matches_oracle_sampled(name):
     for h in range(0, cfg.heads, max(1, cfg.heads // 8)):
         pick = {0, cfg.nb - 1} | set(rng.choice(cfg.nb, size=4, replace=False).tolist())
         rows += [(0, h, i) for i in sorted(pick)]
-    ref = orc.stripe_mask(cfg.grid, cfg.tile, params, 1, rows=rows)
+    ref = orc.stripe_mask(cfg.grid, cfg.tile, params, 1, rows=rows, pad3d=cfg.pad3d)
     for (b, h, i), cols in ref.items():
         r = (b * cfg.heads + h) * cfg.nb + i
         assert np.array_equal(ci[rp[r]:rp[r + 1]], cols), (name, h, i)
@@ -77,4 +78,16 @@ def test_attention_on_stripe_mask_small():
     rows = [(0, h, i) for h in range(cfg.heads) for i in range(cfg.nb)]
     max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
     gc.log(f"[gpu-case] small stripe: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_attention_on_stripe_mask_pad3d():
+    cfg = get_config("tiny_pad3d")
+    run, orun = gc.gpu_run("tiny_pad3d"), gc.oracle_run("tiny_pad3d")
+    params = stripe_params(cfg.heads, seed=3)
+    rp, ci = _gpu_stripe(cfg, params, 1)
+    out_bits = run.attention(rp, ci)
+    rows = [(0, h, i) for h in range(cfg.heads) for i in range(cfg.nb)]
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
+    gc.log(f"tiny_pad3d stripe: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
