@@ -42,6 +42,11 @@ def parse():
     ap.add_argument("--stripe", action="store_true",
                     help="PSA stripe masks instead of top-p: per-head parameters drawn from PSA's "
                          "Wan 2.1 search ranges (seeded), no pooling stage")
+    ap.add_argument("--snr", default=None, metavar="PMIN,TAU",
+                    help="also run the whole path over an SNR-guided top-p schedule")
+    ap.add_argument("--snr-steps", type=int, default=50)
+    ap.add_argument("--snr-first", type=int, default=10, help="first sparse denoising step")
+    ap.add_argument("--snr-shift", type=float, default=5.0, help="flow-matching time shift")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -144,7 +149,7 @@ def main():
         sys.exit(2)
     import torch
     import block_sparse_attention_17_amd as m
-    from svsa_synth import get_config, make_inputs, stripe_params
+    from svsa_synth import flow_sigmas, get_config, make_inputs, stripe_params
 
     cfg = get_config(args.workload)
     geom = m.Geometry.from_config(cfg)
@@ -245,6 +250,38 @@ def main():
                  "speedup_step": (step_ms - attn_ms + dense_ms) / step_ms}
         print(f"[bench] dense attention {dense_ms:.3f} ms", file=sys.stderr, flush=True)
 
+    snr = None
+    if args.snr:
+        # one whole step per denoising step at that step's top-p (all heads alike)
+        p_min, tau = (float(x) for x in args.snr.split(","))
+        sig = flow_sigmas(args.snr_steps, args.snr_shift)
+        sched = m.svsa_snr_top_p(sig, args.snr_first, p_min, tau)
+        s_ms, s_kept = [], []
+        for p_k in sched:
+            a, b = ev(), ev()
+            a.record(stream)
+            bsa.permute_in(q, k, v)
+            m.svsa_pool(bsa.qt, bsa.qbar, geom)
+            m.svsa_pool(bsa.kt, bsa.kbar, geom)
+            m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
+                              bsa.col_idx, bsa.mask_ws,
+                              top_p=np.full(cfg.heads, p_k, np.float32), band_width=cfg.band)
+            bsa.attend()
+            bsa.permute_out()
+            b.record(stream)
+            torch.cuda.synchronize()
+            s_ms.append(a.elapsed_time(b))
+            s_kept.append(int(bsa.row_ptr[-1].item()) / (cfg.batch * cfg.heads * cfg.nb ** 2))
+        snr = {"p_min": p_min, "tau": tau, "steps": args.snr_steps, "first_sparse": args.snr_first,
+               "shift": args.snr_shift, "top_p": [round(float(x), 5) for x in sched],
+               "step_ms": [round(x, 3) for x in s_ms],
+               "kept_block_fraction": [round(x, 4) for x in s_kept],
+               "total_ms": float(np.sum(s_ms)),
+               "dense_total_ms": float(np.mean(s_ms[: args.snr_first]) * args.snr_steps)
+               if args.snr_first > 0 else None}
+        print(f"[bench] SNR schedule ({p_min}, {tau}): {snr['total_ms']:.1f} ms over "
+              f"{args.snr_steps} steps", file=sys.stderr, flush=True)
+
     if args.calibrate_copy:
         a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         b = torch.empty_like(a)
@@ -309,6 +346,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if snr is not None:
+        out["snr_schedule"] = snr
     print(json.dumps(out))
 
 

@@ -6,12 +6,13 @@ Importing fails loudly when the library has not been built.
 from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, library, library_path,
                       status_string, svsa_attn_workspace_bytes, svsa_block_mask,
                       svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
-                      svsa_status_string, svsa_stripe_mask, svsa_stripe_mask_workspace_bytes,
-                      svsa_tile_permute, svsa_version)
+                      svsa_snr_top_p, svsa_status_string, svsa_stripe_mask,
+                      svsa_stripe_mask_workspace_bytes, svsa_tile_permute, svsa_version)
 from .pipeline import BlockSparseAttention
 
 __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
            "library_path", "status_string", "svsa_attn_workspace_bytes", "svsa_block_mask",
            "svsa_block_mask_workspace_bytes", "svsa_block_sparse_attn", "svsa_pool",
-           "svsa_status_string", "svsa_stripe_mask", "svsa_stripe_mask_workspace_bytes",
-           "svsa_tile_permute", "svsa_version", "BlockSparseAttention"]
+           "svsa_snr_top_p", "svsa_status_string", "svsa_stripe_mask",
+           "svsa_stripe_mask_workspace_bytes", "svsa_tile_permute", "svsa_version",
+           "BlockSparseAttention"]

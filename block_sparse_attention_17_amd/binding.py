@@ -107,6 +107,8 @@ def _load():
         "svsa_attn_workspace_bytes": (sz, [i32, i32, gp]),
         "svsa_block_sparse_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp, vp,
                                                   vp, sz, vp]),
+        "svsa_snr_top_p": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), i32, i32, flt, flt,
+                                          fp]),
         "svsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "svsa_version": (ctypes.c_int, []),
     }
@@ -121,8 +123,8 @@ _lib = _load()
 
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
             "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
-            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_status_string",
-            "svsa_version")
+            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_snr_top_p",
+            "svsa_status_string", "svsa_version")
 
 
 def library_path():
@@ -197,6 +199,16 @@ def svsa_pool(x_tiled, out, geom, stream=None):
     _check("svsa_pool", _lib.svsa_pool(
         _ptr(x_tiled, "x_tiled", (torch.bfloat16, torch.float32)), _dtype_code(x_tiled),
         _ptr(out, "out", (torch.float64,)), B, Hh, D, ctypes.byref(geom.c()), _stream(stream)))
+    return out
+
+
+def svsa_snr_top_p(sigmas, first_sparse, p_min, tau):
+    """float32 [steps] per-step top-p from the noise levels (host call, no GPU)."""
+    sig = np.ascontiguousarray(np.asarray(sigmas, dtype=np.float64).ravel())
+    out = np.empty(sig.size, np.float32)
+    _check("svsa_snr_top_p", _lib.svsa_snr_top_p(
+        sig.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), sig.size, int(first_sparse),
+        float(p_min), float(tau), out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
     return out
 
 

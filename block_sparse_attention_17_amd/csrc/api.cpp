@@ -56,7 +56,34 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 extern "C" {
 
-int svsa_version(void) { return 101; }
+int svsa_version(void) { return 102; }
+
+// [iCATS] Sec. 4.2 / App. A: per-step top-p from the log-SNR of the noise
+// schedule.  With x = (1 - s) x0 + s eps, SNR = ((1 - s) / s)^2 and
+// sigmoid(-logSNR) = 1 / (1 + SNR) = s^2 / (s^2 + (1 - s)^2), written here in
+// the form that stays finite at s = 0 and s = 1 (the denominator is >= 1/2).
+int svsa_snr_top_p(const double* sigmas, int32_t steps, int32_t first_sparse, float p_min,
+                   float tau, float* top_p) {
+  if (!sigmas || !top_p || steps < 1 || first_sparse < 0 || first_sparse > steps)
+    return SVSA_E_INVALID;
+  if (!(p_min > 0.0f && p_min <= tau && tau <= 1.0f)) return SVSA_E_INVALID;
+  for (int32_t k = 0; k < steps; ++k)
+    if (!(sigmas[k] >= 0.0 && sigmas[k] <= 1.0)) return SVSA_E_INVALID;
+  auto w = [&](int32_t k) {
+    const double s = sigmas[k], r = 1.0 - s;
+    return s * s / (s * s + r * r);
+  };
+  for (int32_t k = 0; k < first_sparse; ++k) top_p[k] = 1.0f;
+  if (first_sparse == steps) return SVSA_OK;
+  const double w_first = w(first_sparse), w_last = w(steps - 1);
+  const double span = w_first - w_last;
+  for (int32_t k = first_sparse; k < steps; ++k) {
+    double u = span != 0.0 ? (w(k) - w_last) / span : 1.0;
+    u = u < 0.0 ? 0.0 : (u > 1.0 ? 1.0 : u);
+    top_p[k] = (float)((double)p_min + ((double)tau - (double)p_min) * u);
+  }
+  return SVSA_OK;
+}
 
 const char* svsa_status_string(int status) {
   switch (status) {

@@ -228,6 +228,31 @@ SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * SNR-guided top-p schedule ([iCATS] Sec. 4.2 "SNR-Guided Sparsity" and
+ * App. A; the per-model pmin and tau of App. B).  Host-only: no GPU call,
+ * no allocation; the result feeds the top_p array of svsa_block_mask, one
+ * denoising step at a time.
+ * The pages fix the shape of the schedule (dense before the first sparse
+ * step; top-p lowered through the middle of denoising and nearly flat early
+ * and late; a smooth function of log-SNR, computed offline from the noise
+ * schedule) but print no formula.  This library's reading, for the
+ * flow-matching noise level s_k in [0, 1] (x = (1 - s) x0 + s eps):
+ *   logSNR_k = 2 ln((1 - s_k) / s_k),  w_k = sigmoid(-logSNR_k)
+ *                                          (1 at pure noise, 0 at clean data)
+ *   top_p[k] = 1                                            k < first_sparse
+ *   top_p[k] = p_min + (tau - p_min) * clamp((w_k - w_L) / (w_F - w_L), 0, 1)
+ *                                                           otherwise,
+ * F = first_sparse, L = steps - 1 (tau when w_F == w_L): tau is the top-p of
+ * the first sparse step and p_min that of the last.
+ * sigmas: host float64 [steps]; top_p: host float32 [steps] (output).
+ * Errors (SVSA_E_INVALID, nothing written): NULL pointer, steps < 1,
+ * first_sparse outside [0, steps], a sigma outside [0, 1] or NaN, or not
+ * 0 < p_min <= tau <= 1.
+ */
+SVSA_API int svsa_snr_top_p(const double* sigmas, int32_t steps, int32_t first_sparse,
+                            float p_min, float tau, float* top_p);
+
 /* Static description of a status code (never NULL). */
 SVSA_API const char* svsa_status_string(int status);
 

@@ -43,6 +43,13 @@ Readings taken where the pages are silent (each is pinned by a test):
   nT*nH*nW; its valid tokens fill the first slots (row-major (t, h, w) order)
   and the remaining slots are padding, excluded like the tail padding.  The
   order of tokens inside a block does not change any block-level quantity.
+* SNR-guided top-p ([iCATS] Sec. 4.2, App. A): the pages give the schedule's
+  shape and its two parameters (pmin, tau) but no formula.  Reading: with the
+  flow-matching noise level s (x = (1 - s) x0 + s eps), logSNR = 2 ln((1-s)/s)
+  and w = sigmoid(-logSNR); steps before the first sparse one are dense
+  (p = 1); later steps interpolate linearly in w from tau (first sparse step)
+  to pmin (last step).  The formula itself is parity unpinned (the pins fix
+  this reading, not the pages' unprinted formula).
 
 parity pins: see tests/test_oracle_*.py; every public function is pinned.
 """
@@ -54,7 +61,7 @@ __all__ = [
     "num_blocks", "tile_order", "permute_fwd", "permute_inv", "block_valid_counts",
     "pool", "block_logits", "block_scores", "select_row", "block_mask",
     "attention", "attention_rows", "dense_attention", "kept_flops", "widen",
-    "psa_attends", "block_tiles", "stripe_row", "stripe_mask", "block_layout",
+    "psa_attends", "block_tiles", "stripe_row", "stripe_mask", "block_layout", "snr_top_p",
 ]
 
 
@@ -425,3 +432,31 @@ def stripe_mask(grid, tile, params, band, batch=1, rows=None, pad3d=False):
     row_ptr[1:] = np.cumsum(counts)
     col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
     return row_ptr, col_idx
+
+
+# --------------------------------------------------------------------------
+# SNR-guided sparsity.  [iCATS] Sec. 4.2 and App. A: top-p changes over the
+# denoising steps as a smooth function of the log signal-to-noise ratio of
+# the noise schedule -- dense before the first sparse step, lowered through
+# the middle of denoising, nearly flat early and late; pmin and tau per model
+# in App. B.  Reading (the formula is not on the pages): w = sigmoid(-logSNR),
+# linear in w between tau at the first sparse step and pmin at the last.
+# --------------------------------------------------------------------------
+def snr_top_p(sigmas, first_sparse, p_min, tau):
+    """float64 [steps] top-p per denoising step.
+
+    sigmas: flow-matching noise levels s_k in [0, 1] (x = (1 - s) x0 + s eps).
+    Steps k < first_sparse are dense (1.0)."""
+    s = np.asarray(sigmas, dtype=np.float64)
+    steps = s.size
+    with np.errstate(divide="ignore"):
+        log_snr = 2.0 * (np.log(1.0 - s) - np.log(s))       # -inf at s = 1, +inf at s = 0
+    w = 1.0 / (1.0 + np.exp(log_snr))                       # sigmoid(-logSNR)
+    p = np.ones(steps)
+    if first_sparse >= steps:
+        return p
+    w_first, w_last = w[first_sparse], w[steps - 1]
+    for k in range(first_sparse, steps):
+        u = 1.0 if w_first == w_last else (w[k] - w_last) / (w_first - w_last)
+        p[k] = p_min + (tau - p_min) * min(1.0, max(0.0, u))
+    return p

@@ -6,7 +6,8 @@ contains none of the method's arithmetic: no permutation, pooling, scoring,
 selection or attention.
 """
 from .configs import CONFIGS, Config, get_config
-from .gen import Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits, stripe_params
+from .gen import (Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits, stripe_params,
+                  flow_sigmas)
 
 __all__ = ["CONFIGS", "Config", "get_config", "Inputs", "make_inputs",
-           "bf16_bits_to_f32", "f32_to_bf16_bits", "stripe_params"]
+           "bf16_bits_to_f32", "f32_to_bf16_bits", "stripe_params", "flow_sigmas"]

@@ -176,3 +176,12 @@ def stripe_params(heads, seed=0, stream=0):
     so = g.choice([0, 1, -1], size=heads)
     ss = g.choice([1, 3, 5, 6, 0], size=heads)
     return np.stack([tw, to, ts, sw, so, ss], axis=1).astype(np.int32)
+
+
+def flow_sigmas(steps, shift=5.0):
+    """Noise levels of a flow-matching sampler (x = (1 - s) x0 + s eps) with a
+    time shift: t_k = 1 - k / steps, s_k = shift t / (1 + (shift - 1) t).  An
+    input of the SNR-guided top-p schedule (the pages give no noise schedule;
+    this stands in for the denoising loop of a rectified-flow video model)."""
+    t = 1.0 - np.arange(steps, dtype=np.float64) / steps
+    return shift * t / (1.0 + (shift - 1.0) * t)

@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -151,3 +151,49 @@ def test_stripe_mask_argument_errors(mod):
     assert call(prm, w=ws - 1) == -3
     many = (ctypes.c_int32 * (6 * 129))(*([1, 0, 0, 1, 0, 0] * 129))
     assert call(many, heads=129) == -2
+
+
+def test_snr_top_p_matches_the_oracle(mod):
+    """Host entry point (no GPU): float32 result within one rounding of the fp64
+    oracle, on hand-worked schedules and on 50-step shifted flow schedules."""
+    import json
+    import numpy as np
+    from oracle import svsa_oracle as orc
+    with open(os.path.join(ROOT, "tests", "golden", "snr_schedule.json")) as f:
+        cases = json.load(f)["cases"]
+    runs = [(c["sigmas"], c["first_sparse"], c["p_min"], c["tau"]) for c in cases]
+    for shift in (1.0, 3.0, 5.0, 8.0):
+        t = 1.0 - np.arange(50) / 50
+        runs.append((shift * t / (1 + (shift - 1) * t), 10, 0.7, 0.999))
+        runs.append((shift * t / (1 + (shift - 1) * t), 0, 0.65, 0.97))
+    for sig, first, pmin, tau in runs:
+        got = mod.svsa_snr_top_p(sig, first, pmin, tau)
+        ref = orc.snr_top_p(sig, first, float(np.float32(pmin)), float(np.float32(tau)))
+        assert got.dtype == np.float32
+        np.testing.assert_allclose(got, ref, rtol=2 ** -23, atol=0)
+
+
+def test_snr_top_p_argument_errors(mod):
+    import numpy as np
+    lib = mod.library()
+    sig = np.array([1.0, 0.5, 0.2])
+    out = np.full(3, -1.0, np.float32)
+    dp = sig.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    fp = out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    E_INV = -1
+    assert lib.svsa_snr_top_p(None, 3, 0, 0.7, 0.9, fp) == E_INV
+    assert lib.svsa_snr_top_p(dp, 0, 0, 0.7, 0.9, fp) == E_INV          # no steps
+    assert lib.svsa_snr_top_p(dp, 3, 4, 0.7, 0.9, fp) == E_INV          # first_sparse > steps
+    assert lib.svsa_snr_top_p(dp, 3, -1, 0.7, 0.9, fp) == E_INV
+    assert lib.svsa_snr_top_p(dp, 3, 0, 0.95, 0.9, fp) == E_INV         # p_min > tau
+    assert lib.svsa_snr_top_p(dp, 3, 0, 0.0, 0.9, fp) == E_INV          # p_min = 0
+    assert lib.svsa_snr_top_p(dp, 3, 0, 0.7, 1.5, fp) == E_INV          # tau > 1
+    bad = np.array([1.0, float("nan"), 0.2])
+    assert lib.svsa_snr_top_p(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 3, 0, 0.7,
+                              0.9, fp) == E_INV
+    bad = np.array([1.2, 0.5, 0.2])
+    assert lib.svsa_snr_top_p(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 3, 0, 0.7,
+                              0.9, fp) == E_INV
+    assert np.all(out == -1.0)                                            # nothing written
+    with pytest.raises(mod.SvsaError):
+        mod.svsa_snr_top_p([0.5, 2.0], 0, 0.7, 0.9)

@@ -134,6 +134,29 @@ def test_block_mask_band_and_limits():
             assert not bad
 
 
+def test_block_mask_over_snr_schedule():
+    """Per-step top-p from svsa_snr_top_p ([iCATS] Sec. 4.2 reading) drives the
+    mask: every step's CSR equals the oracle's mask at the oracle's schedule."""
+    import block_sparse_attention_17_amd as m
+    from svsa_synth import flow_sigmas
+    cfg = get_config("small")
+    run, orun = gc.gpu_run("small"), gc.oracle_run("small")
+    sig = flow_sigmas(8, 5.0)
+    sched = m.svsa_snr_top_p(sig, 2, 0.7, 0.999)
+    ref = orc.snr_top_p(sig, 2, float(np.float32(0.7)), float(np.float32(0.999)))
+    np.testing.assert_allclose(sched, ref, rtol=2 ** -23, atol=0)
+    kept = []
+    for p_k in sched:
+        tp = np.full(cfg.heads, p_k, np.float32)
+        g_rp, g_ci = run.mask(top_p=tp, band=cfg.band)
+        o_rp, o_ci = orun.mask(top_p=tp, band=cfg.band)
+        tol, bad = gc.mask_mismatch(cfg, orun.S, g_rp, g_ci, o_rp, o_ci, top_p=tp, band=cfg.band)
+        assert not bad
+        kept.append(int(g_rp[-1]))
+    gc.log(f"small SNR schedule: top-p {np.round(sched, 4).tolist()} kept blocks {kept}")
+    assert all(a >= b for a, b in zip(kept, kept[1:]))     # top-p never rises
+
+
 # ---------------------------------------------------------------- stage 4
 ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
               ("small_b2", None), ("small_pad3d", None), ("tiny_pad3d", None)]

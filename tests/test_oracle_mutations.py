@@ -9,6 +9,9 @@ import tests.test_oracle_permute as tp
 import tests.test_oracle_select as ts
 import tests.test_oracle_stripe as tst
 import tests.test_oracle_pad3d as tpd
+import tests.test_oracle_snr as tsnr
+
+_SNR = orc.snr_top_p   # the unmutated schedule, for mutations built on top of it
 
 
 def _scores_no_scale(qbar, kbar, scale):
@@ -150,6 +153,32 @@ def _block_tiles_nh(grid, tile, pad3d=False):
         out.append((pairs[:, 0], pairs[:, 1]))
     return out
 
+def _snr_linear_in_log_snr(sigmas, first_sparse, p_min, tau):
+    # interpolates in logSNR itself instead of sigmoid(-logSNR)
+    s = np.asarray(sigmas, float)
+    with np.errstate(divide="ignore"):
+        lam = 2.0 * (np.log(1.0 - s) - np.log(s))
+    p = np.ones(s.size)
+    for k in range(first_sparse, s.size):
+        u = (lam[k] - lam[-1]) / (lam[first_sparse] - lam[-1])
+        p[k] = p_min + (tau - p_min) * min(1.0, max(0.0, u))
+    return p
+
+
+def _snr_unsquared(sigmas, first_sparse, p_min, tau):
+    # SNR = (1 - s) / s (amplitude ratio) instead of its square: w = s
+    s = np.asarray(sigmas, float)
+    p = np.ones(s.size)
+    for k in range(first_sparse, s.size):
+        u = 1.0 if s[first_sparse] == s[-1] else (s[k] - s[-1]) / (s[first_sparse] - s[-1])
+        p[k] = p_min + (tau - p_min) * min(1.0, max(0.0, u))
+    return p
+
+
+def _snr_no_warmup(sigmas, first_sparse, p_min, tau):
+    return _SNR(sigmas, 0, p_min, tau)
+
+
 MUTATIONS = [
     ("block_scores", _scores_no_scale, ts.test_scores_closed_form_one_channel, ()),
     ("block_scores", _scores_transposed, ts.test_scores_closed_form_one_channel, ()),
@@ -167,6 +196,9 @@ MUTATIONS = [
     ("pool", _pool_ignores_counts, tpd.test_pad3d_pool_is_the_mean_of_each_tile, ()),
     ("attention_rows", _rows_ignore_counts, tpd.test_pad3d_full_attention_equals_dense, ()),
     ("block_layout", _layout_pads_in_place, tpd.test_pad3d_hand_worked_layouts, ("golden",)),
+    ("snr_top_p", _snr_linear_in_log_snr, tsnr.test_snr_hand_worked_schedules, ("golden",)),
+    ("snr_top_p", _snr_unsquared, tsnr.test_snr_hand_worked_schedules, ("golden",)),
+    ("snr_top_p", _snr_no_warmup, tsnr.test_snr_hand_worked_schedules, ("golden",)),
 ]
 
 
