@@ -43,6 +43,24 @@ Readings taken where the pages are silent (each is pinned by a test):
   nT*nH*nW; its valid tokens fill the first slots (row-major (t, h, w) order)
   and the remaining slots are padding, excluded like the tail padding.  The
   order of tokens inside a block does not change any block-level quantity.
+* Variable-size blocks from query / key clustering ([iCATS] Sec. 3.1, 4.1;
+  [SVOO] "online bidirectional QK co-clustering"; the pages give the idea,
+  not the algorithm).  Reading: replacing a query q by its centroid mu moves
+  its logit against a key k by (q - mu).k, so the summed squared change over
+  the keys is the quadratic form (q - mu)^T G (q - mu) with G = sum_k k k^T,
+  approximated from the key clusters as G = sum_j n_j kappa_j kappa_j^T (and
+  symmetrically for keys with the query clusters).  Clustering is Lloyd's
+  k-means under that fixed metric: each iteration assigns every token to the
+  centroid of least quadratic-form distance (ties: lowest index) and moves
+  every non-empty centroid to the mean of its members (an empty one stays).
+  G = I is plain feature-space k-means (the first sparse step).  Initial
+  centroids and iteration counts are inputs.  Clusters are laid out one after
+  another, each starting on a multiple of the alignment, members in natural
+  order, padding zero.  Cluster scores are the row softmax over key clusters
+  of scale * mu_i . kappa_j + ln n_j (the mass of n_j keys that all equal
+  kappa_j; empty key clusters get none); top-p / fixed fraction as for
+  blocks, no band.  A query token attends to every token of its cluster's
+  kept key clusters.
 * SNR-guided top-p ([iCATS] Sec. 4.2, App. A): the pages give the schedule's
   shape and its two parameters (pmin, tau) but no formula.  Reading: with the
   flow-matching noise level s (x = (1 - s) x0 + s eps), logSNR = 2 ln((1-s)/s)
@@ -62,6 +80,9 @@ __all__ = [
     "pool", "block_logits", "block_scores", "select_row", "block_mask",
     "attention", "attention_rows", "dense_attention", "kept_flops", "widen",
     "psa_attends", "block_tiles", "stripe_row", "stripe_mask", "block_layout", "snr_top_p",
+    "cluster_means", "quad_distances", "kmeans_assign", "kmeans", "cluster_metric",
+    "cluster_layout", "cluster_permute", "cluster_unpermute", "cluster_scores", "cluster_mask",
+    "cluster_attention_rows",
 ]
 
 
@@ -460,3 +481,157 @@ def snr_top_p(sigmas, first_sparse, p_min, tau):
         u = 1.0 if w_first == w_last else (w[k] - w_last) / (w_first - w_last)
         p[k] = p_min + (tau - p_min) * min(1.0, max(0.0, u))
     return p
+
+
+# --------------------------------------------------------------------------
+# Variable-size blocks: query / key clustering.  [iCATS] Sec. 3.1 and 4.1:
+# clustering should minimise the error of the query-key interactions, which
+# is written as a quadratic form in the feature space so that the full
+# interaction matrix is never built; query clusters start in plain feature
+# space and later use the key clusters' metric, and the query clusters in
+# turn guide the key clustering.  [SVOO]: online bidirectional QK
+# co-clustering into blocks.  The steps below are this module's reading.
+# --------------------------------------------------------------------------
+def cluster_means(x, labels, C):
+    """(means float64 [B, Hh, C, D], sizes int64 [B, Hh, C]): the mean of each
+    cluster's member tokens (NaN rows for empty clusters)."""
+    xf = widen(x)
+    B, Hh, N, D = xf.shape
+    lab = np.asarray(labels)
+    means = np.full((B, Hh, C, D), np.nan)
+    sizes = np.zeros((B, Hh, C), np.int64)
+    for b in range(B):
+        for h in range(Hh):
+            for c in range(C):
+                members = xf[b, h, lab[b, h] == c]
+                sizes[b, h, c] = members.shape[0]
+                if members.shape[0]:
+                    means[b, h, c] = members.sum(axis=0) / members.shape[0]
+    return means, sizes
+
+
+def quad_distances(x, cents, G=None):
+    """float64 [N, C]: (x_n - c)^T G (x_n - c) for one head (G = I if None).
+
+    x: [N, D] tokens, cents: [C, D]."""
+    xf = widen(x)
+    c = np.asarray(cents, dtype=np.float64)
+    diff = xf[:, None, :] - c[None, :, :]                 # [N, C, D]
+    if G is None:
+        return np.einsum("ncd,ncd->nc", diff, diff)
+    return np.einsum("ncd,de,nce->nc", diff, np.asarray(G, np.float64), diff)
+
+
+def kmeans_assign(x, cents, G=None):
+    """int32 [N]: index of the centroid of least quadratic-form distance
+    (lowest index among equal distances)."""
+    return np.argmin(quad_distances(x, cents, G), axis=1).astype(np.int32)
+
+
+def kmeans(x, cents0, iters, G=None):
+    """Lloyd iterations for one head: assign, then move every non-empty
+    centroid to its members' mean.  Returns (centroids float64 [C, D], sizes
+    int64 [C], labels int32 [N] of the last assignment); the centroids are the
+    means of those labels (empty clusters keep their previous centroid)."""
+    xf = widen(x)
+    c = np.array(cents0, dtype=np.float64)
+    C = c.shape[0]
+    labels = np.zeros(xf.shape[0], np.int32)
+    sizes = np.zeros(C, np.int64)
+    for _ in range(iters):
+        labels = kmeans_assign(xf, c, G)
+        m, sz = cluster_means(xf[None, None], labels[None, None], C)
+        sizes = sz[0, 0]
+        keep = sizes > 0
+        c[keep] = m[0, 0, keep]
+    return c, sizes, labels
+
+
+def cluster_metric(cents, sizes):
+    """G = sum_c n_c c c^T (float64 [D, D]) for one head: the quadratic form
+    that the clusters of one side induce on the other side's tokens."""
+    c = np.asarray(cents, dtype=np.float64)
+    n = np.asarray(sizes, dtype=np.float64)
+    return (c * n[:, None]).T @ c
+
+
+def cluster_layout(labels, C, align):
+    """Padded layout of one head's clusters.
+
+    Returns (start int64 [C+1], slot int64 [N], token int64 [start[C]]):
+    cluster c owns slots start[c] .. start[c] + n_c - 1 (its members in
+    ascending natural index), start[0] = 0 and start[c+1] = start[c] +
+    align * ceil(n_c / align); slot[t] = the slot of token t; token[s] = the
+    token in slot s or -1 for padding."""
+    lab = np.asarray(labels)
+    sizes = np.bincount(lab, minlength=C)[:C]
+    start = np.zeros(C + 1, np.int64)
+    start[1:] = np.cumsum(-(-sizes // align) * align)
+    slot = np.empty(lab.size, np.int64)
+    token = np.full(int(start[C]), -1, np.int64)
+    for c in range(C):
+        members = np.nonzero(lab == c)[0]            # ascending natural index
+        slot[members] = start[c] + np.arange(members.size)
+        token[start[c]: start[c] + members.size] = members
+    return start, slot, token
+
+
+def cluster_permute(x, token):
+    """X'[s] = X[token[s]] (zero for padding slots) for one head [N, D] -> [L, D]."""
+    xf = widen(x)
+    out = np.zeros((token.size, xf.shape[1]))
+    ok = token >= 0
+    out[ok] = xf[token[ok]]
+    return out
+
+
+def cluster_unpermute(xp, slot):
+    """O[t] = O'[slot[t]] for one head."""
+    return widen(xp)[np.asarray(slot)]
+
+
+def cluster_scores(qbar, kbar, ksizes, scale):
+    """float64 [nq, nk] for one head: row softmax over the key clusters of
+    scale * qbar_i . kbar_j + ln n_j; empty key clusters score 0."""
+    L = (np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T) * scale
+    n = np.asarray(ksizes)
+    with np.errstate(divide="ignore"):
+        L = L + np.where(n > 0, np.log(np.maximum(n, 1).astype(np.float64)), -np.inf)[None, :]
+    w = np.exp(L - L.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def cluster_mask(S, top_p=None, keep_frac=None):
+    """CSR over rows r = (b*Hh + h)*nq + i of kept key clusters (no band).
+
+    S: [B, Hh, nq, nk] cluster scores; top_p / keep_frac per head."""
+    B, Hh, nq, nk = S.shape
+    counts, cols = [], []
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nq):
+                if keep_frac is not None:
+                    c = select_row(S[b, h, i], i, 0, keep_frac=keep_frac[h])
+                else:
+                    c = select_row(S[b, h, i], i, 0, top_p=top_p[h])
+                cols.append(c)
+                counts.append(c.size)
+    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
+    return row_ptr, col_idx
+
+
+def cluster_attention_rows(q, k, v, qlab, klab, i, cols, scale):
+    """Attention of the query tokens of cluster i (one head, natural order)
+    over every key token of the listed key clusters: (tokens int64, float64
+    [m_i, D]).  q, k, v: [N, D]; qlab, klab: [N] cluster labels."""
+    toks = np.nonzero(np.asarray(qlab) == i)[0]
+    keys = np.nonzero(np.isin(np.asarray(klab), np.asarray(cols)))[0]
+    if toks.size == 0:
+        return toks, np.zeros((0, widen(q).shape[1]))
+    qf, kf, vf = widen(q)[toks], widen(k)[keys], widen(v)[keys]
+    logits = (qf @ kf.T) * scale
+    wgt = np.exp(logits - logits.max(axis=1, keepdims=True))
+    wgt /= wgt.sum(axis=1, keepdims=True)
+    return toks, wgt @ vf

@@ -10,8 +10,13 @@ import tests.test_oracle_select as ts
 import tests.test_oracle_stripe as tst
 import tests.test_oracle_pad3d as tpd
 import tests.test_oracle_snr as tsnr
+import tests.test_oracle_cluster as tcl
 
 _SNR = orc.snr_top_p   # the unmutated schedule, for mutations built on top of it
+_MEANS = orc.cluster_means
+_ASSIGN = orc.kmeans_assign
+_LAYOUT = orc.cluster_layout
+_ROWS = orc.cluster_attention_rows
 
 
 def _scores_no_scale(qbar, kbar, scale):
@@ -179,6 +184,42 @@ def _snr_no_warmup(sigmas, first_sparse, p_min, tau):
     return _SNR(sigmas, 0, p_min, tau)
 
 
+def _kmeans_empty_becomes_nan(x, cents0, iters, G=None):
+    xf = orc.widen(x)
+    c = np.array(cents0, dtype=np.float64)
+    labels = np.zeros(xf.shape[0], np.int32)
+    sizes = np.zeros(c.shape[0], np.int64)
+    for _ in range(iters):
+        labels = _ASSIGN(xf, c, G)
+        m, sz = _MEANS(xf[None, None], labels[None, None], c.shape[0])
+        c, sizes = m[0, 0], sz[0, 0]
+    return c, sizes, labels
+
+
+def _quad_ignores_metric(x, cents, G=None):
+    diff = orc.widen(x)[:, None, :] - np.asarray(cents, np.float64)[None]
+    return np.einsum("ncd,ncd->nc", diff, diff)
+
+
+def _scores_without_size(qbar, kbar, ksizes, scale):
+    L = (np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T) * scale
+    w = np.exp(L - L.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def _layout_unpadded(labels, C, align):
+    return _LAYOUT(labels, C, 1)
+
+
+def _metric_without_sizes(cents, sizes):
+    c = np.asarray(cents, np.float64)
+    return c.T @ c
+
+
+def _cluster_rows_query_labels(q, k, v, qlab, klab, i, cols, scale):
+    return _ROWS(q, k, v, qlab, qlab, i, cols, scale)
+
+
 MUTATIONS = [
     ("block_scores", _scores_no_scale, ts.test_scores_closed_form_one_channel, ()),
     ("block_scores", _scores_transposed, ts.test_scores_closed_form_one_channel, ()),
@@ -199,6 +240,15 @@ MUTATIONS = [
     ("snr_top_p", _snr_linear_in_log_snr, tsnr.test_snr_hand_worked_schedules, ("golden",)),
     ("snr_top_p", _snr_unsquared, tsnr.test_snr_hand_worked_schedules, ("golden",)),
     ("snr_top_p", _snr_no_warmup, tsnr.test_snr_hand_worked_schedules, ("golden",)),
+    ("kmeans", _kmeans_empty_becomes_nan, tcl.test_kmeans_euclidean_equals_scipy, (1, 3)),
+    ("quad_distances", _quad_ignores_metric, tcl.test_quad_distances_equal_squared_mahalanobis,
+     ()),
+    ("cluster_scores", _scores_without_size, tcl.test_cluster_scores_weight_by_size, ()),
+    ("cluster_layout", _layout_unpadded, tcl.test_cluster_layout_hand_worked, ("golden",)),
+    ("cluster_metric", _metric_without_sizes, tcl.test_cluster_metric_is_the_interaction_error,
+     ()),
+    ("cluster_attention_rows", _cluster_rows_query_labels,
+     tcl.test_cluster_attention_all_kept_equals_dense_sdpa, ()),
 ]
 
 
@@ -208,7 +258,7 @@ def test_pin_catches_planted_mistake(monkeypatch, golden_dir, name, fn, pin, arg
     monkeypatch.setattr(orc, name, fn)
     call = []
     for a in args:
-        call.append(golden_dir if a == "golden" else None)
+        call.append(golden_dir if a == "golden" else a)
     if args == ("grid_tile",):
         call = [(4, 8, 8), (2, 4, 4)]
     with pytest.raises(AssertionError):
