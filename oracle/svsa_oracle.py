@@ -593,10 +593,11 @@ def cluster_unpermute(xp, slot):
 def cluster_scores(qbar, kbar, ksizes, scale):
     """float64 [nq, nk] for one head: row softmax over the key clusters of
     scale * qbar_i . kbar_j + ln n_j; empty key clusters score 0."""
-    L = (np.asarray(qbar, np.float64) @ np.asarray(kbar, np.float64).T) * scale
     n = np.asarray(ksizes)
-    with np.errstate(divide="ignore"):
-        L = L + np.where(n > 0, np.log(np.maximum(n, 1).astype(np.float64)), -np.inf)[None, :]
+    # an empty key cluster has no tokens (its centroid may be undefined): no mass
+    kb = np.where((n > 0)[:, None], np.asarray(kbar, np.float64), 0.0)
+    L = (np.asarray(qbar, np.float64) @ kb.T) * scale
+    L = np.where(n > 0, L + np.log(np.maximum(n, 1).astype(np.float64))[None, :], -np.inf)
     w = np.exp(L - L.max(axis=1, keepdims=True))
     return w / w.sum(axis=1, keepdims=True)
 

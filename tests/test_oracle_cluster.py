@@ -128,6 +128,19 @@ def test_cluster_scores_weight_by_size():
     assert abs(S[0, 0] - 1 / (1 + np.exp(-2.0))) < 1e-15
 
 
+def test_cluster_scores_ignore_undefined_empty_centroids():
+    """Empty key clusters score 0 even when their centroid is undefined (the
+    NaN mean of no tokens), and leave the other scores as without them."""
+    rng = np.random.default_rng(13)
+    qbar, kbar = rng.standard_normal((2, 3)), rng.standard_normal((4, 3))
+    kb = kbar.copy()
+    kb[1] = np.nan
+    S = orc.cluster_scores(qbar, kb, np.array([3, 0, 2, 5]), 0.4)
+    ref = orc.cluster_scores(qbar, kbar[[0, 2, 3]], np.array([3, 2, 5]), 0.4)
+    assert np.all(S[:, 1] == 0.0) and np.all(np.isfinite(S))
+    np.testing.assert_allclose(S[:, [0, 2, 3]], ref, rtol=1e-14)
+
+
 def test_cluster_mask_top_p_on_size_fractions():
     S = np.tile([0.5, 0.3, 0.0, 0.2], (1, 1, 2, 1))
     rp, ci = orc.cluster_mask(S, top_p=np.array([0.7], np.float32))
