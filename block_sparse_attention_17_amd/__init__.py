@@ -3,16 +3,25 @@
 Python face of ``libsvsa.so`` (HIP kernels behind a C ABI, ``include/svsa.h``).
 Importing fails loudly when the library has not been built.
 """
+from .binding import (svsa_cluster_attn, svsa_cluster_attn_workspace_bytes,
+                      svsa_cluster_capacity, svsa_cluster_layout, svsa_cluster_mask,
+                      svsa_cluster_means, svsa_cluster_means_workspace_bytes,
+                      svsa_cluster_mask_workspace_bytes, svsa_cluster_metric, svsa_cluster_permute,
+                      svsa_kmeans, svsa_kmeans_workspace_bytes)
 from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, library, library_path,
                       status_string, svsa_attn_workspace_bytes, svsa_block_mask,
                       svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
                       svsa_snr_top_p, svsa_status_string, svsa_stripe_mask,
                       svsa_stripe_mask_workspace_bytes, svsa_tile_permute, svsa_version)
-from .pipeline import BlockSparseAttention
+from .pipeline import BlockSparseAttention, ClusteredAttention
 
 __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
            "library_path", "status_string", "svsa_attn_workspace_bytes", "svsa_block_mask",
            "svsa_block_mask_workspace_bytes", "svsa_block_sparse_attn", "svsa_pool",
            "svsa_snr_top_p", "svsa_status_string", "svsa_stripe_mask",
            "svsa_stripe_mask_workspace_bytes", "svsa_tile_permute", "svsa_version",
-           "BlockSparseAttention"]
+           "BlockSparseAttention", "ClusteredAttention", "svsa_cluster_attn",
+           "svsa_cluster_attn_workspace_bytes", "svsa_cluster_capacity", "svsa_cluster_layout",
+           "svsa_cluster_mask", "svsa_cluster_mask_workspace_bytes", "svsa_cluster_metric",
+           "svsa_cluster_permute", "svsa_kmeans", "svsa_kmeans_workspace_bytes",
+           "svsa_cluster_means", "svsa_cluster_means_workspace_bytes"]

@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libsvsa.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("SVSA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "permute.hip", "pool.hip", "mask.hip", "stripe.hip", "attn.hip"]
+SOURCES = ["api.cpp", "permute.hip", "pool.hip", "mask.hip", "stripe.hip", "attn.hip",
+           "cluster.hip"]
 
 
 def hipcc():

@@ -109,6 +109,23 @@ def _load():
                                                   vp, sz, vp]),
         "svsa_snr_top_p": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), i32, i32, flt, flt,
                                           fp]),
+        "svsa_kmeans_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "svsa_kmeans": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz,
+                                       vp]),
+        "svsa_cluster_metric": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, vp, vp]),
+        "svsa_cluster_means_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "svsa_cluster_means": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz,
+                                              vp]),
+        "svsa_cluster_capacity": (i64, [i32, i32, i32]),
+        "svsa_cluster_layout": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "svsa_cluster_permute": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                                                i32, vp]),
+        "svsa_cluster_mask_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "svsa_cluster_mask": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, dbl, fp, fp, vp,
+                                             vp, i64, vp, sz, vp]),
+        "svsa_cluster_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "svsa_cluster_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32,
+                                             i32, vp, vp, i32, flt, vp, vp, vp, sz, vp]),
         "svsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "svsa_version": (ctypes.c_int, []),
     }
@@ -124,6 +141,11 @@ _lib = _load()
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
             "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
             "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_snr_top_p",
+            "svsa_kmeans_workspace_bytes", "svsa_kmeans", "svsa_cluster_metric",
+            "svsa_cluster_means_workspace_bytes", "svsa_cluster_means",
+            "svsa_cluster_capacity", "svsa_cluster_layout", "svsa_cluster_permute",
+            "svsa_cluster_mask_workspace_bytes", "svsa_cluster_mask",
+            "svsa_cluster_attn_workspace_bytes", "svsa_cluster_attn",
             "svsa_status_string", "svsa_version")
 
 
@@ -274,4 +296,118 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
         ctypes.byref(geom.c()), float(softmax_scale), _ptr(row_ptr, "row_ptr", (torch.int32,)),
         _ptr(col_idx, "col_idx", (torch.int32,)), _ptr(workspace, "workspace", (torch.uint8,)),
         workspace.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Variable-size blocks (clusters)
+# ---------------------------------------------------------------------------
+def svsa_kmeans_workspace_bytes(batch, heads, n, clusters, head_dim):
+    return int(_lib.svsa_kmeans_workspace_bytes(batch, heads, n, clusters, head_dim))
+
+
+def svsa_kmeans(x, centroids, labels, sizes, workspace, iters, metric=None, stream=None):
+    """Lloyd iterations under the quadratic form `metric` (None: identity);
+    centroids float64 [B, Hh, C, D] are updated in place."""
+    import torch
+    B_, Hh, N, D = x.shape
+    C = centroids.shape[2]
+    _check("svsa_kmeans", _lib.svsa_kmeans(
+        _ptr(x, "x", (torch.bfloat16,)), B_, Hh, N, D,
+        _ptr(metric, "metric", (torch.float64,)), _ptr(centroids, "centroids", (torch.float64,)),
+        C, int(iters), _ptr(labels, "labels", (torch.int32,)),
+        _ptr(sizes, "sizes", (torch.int32,)), _ptr(workspace, "workspace", (torch.uint8,)),
+        workspace.numel(), _stream(stream)))
+    return centroids, labels, sizes
+
+
+def svsa_cluster_means_workspace_bytes(batch, heads, n, clusters):
+    return int(_lib.svsa_cluster_means_workspace_bytes(batch, heads, n, clusters))
+
+
+def svsa_cluster_means(x, labels, centroids, sizes, workspace, stream=None):
+    """centroids (float64 [B, Hh, C, D]) <- means of the tokens of each label."""
+    import torch
+    B_, Hh, N, D = x.shape
+    C = centroids.shape[2]
+    _check("svsa_cluster_means", _lib.svsa_cluster_means(
+        _ptr(x, "x", (torch.bfloat16,)), _ptr(labels, "labels", (torch.int32,)), B_, Hh, N, D, C,
+        _ptr(centroids, "centroids", (torch.float64,)), _ptr(sizes, "sizes", (torch.int32,)),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+    return centroids, sizes
+
+
+def svsa_cluster_metric(centroids, sizes, metric, stream=None):
+    import torch
+    B_, Hh, C, D = centroids.shape
+    _check("svsa_cluster_metric", _lib.svsa_cluster_metric(
+        _ptr(centroids, "centroids", (torch.float64,)), _ptr(sizes, "sizes", (torch.int32,)),
+        B_, Hh, C, D, _ptr(metric, "metric", (torch.float64,)), _stream(stream)))
+    return metric
+
+
+def svsa_cluster_capacity(n, clusters, align):
+    return int(_lib.svsa_cluster_capacity(n, clusters, align))
+
+
+def svsa_cluster_layout(labels, clusters, align, start, sizes, slot, token, stream=None):
+    import torch
+    B_, Hh, N = labels.shape
+    i32 = (torch.int32,)
+    _check("svsa_cluster_layout", _lib.svsa_cluster_layout(
+        _ptr(labels, "labels", i32), B_, Hh, N, int(clusters), int(align),
+        _ptr(start, "start", i32), _ptr(sizes, "sizes", i32), _ptr(slot, "slot", i32),
+        _ptr(token, "token", i32), _stream(stream)))
+    return start, sizes, slot, token
+
+
+def svsa_cluster_permute(src, dst, n, clusters, align, map_, start, inverse=False, stream=None):
+    import torch
+    B_, Hh, _, D = src.shape
+    _check("svsa_cluster_permute", _lib.svsa_cluster_permute(
+        _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
+        _dtype_code(src), B_, Hh, int(n), D, int(clusters), int(align),
+        _ptr(map_, "map", (torch.int32,)), _ptr(start, "start", (torch.int32,)),
+        int(bool(inverse)), _stream(stream)))
+    return dst
+
+
+def svsa_cluster_mask_workspace_bytes(batch, heads, nq, nk):
+    return int(_lib.svsa_cluster_mask_workspace_bytes(batch, heads, nq, nk))
+
+
+def svsa_cluster_mask(qbar, kbar, ksizes, softmax_scale, row_ptr, col_idx, workspace,
+                      top_p=None, keep_frac=None, stream=None):
+    import torch
+    B_, Hh, nq, D = qbar.shape
+    nk = kbar.shape[2]
+    tp_arr, tp = _host_f32(top_p, Hh, "top_p")
+    kf_arr, kf = _host_f32(keep_frac, Hh, "keep_frac")
+    _check("svsa_cluster_mask", _lib.svsa_cluster_mask(
+        _ptr(qbar, "qbar", (torch.float64,)), _ptr(kbar, "kbar", (torch.float64,)),
+        _ptr(ksizes, "ksizes", (torch.int32,)), B_, Hh, nq, nk, D, float(softmax_scale), tp, kf,
+        _ptr(row_ptr, "row_ptr", (torch.int32,)), _ptr(col_idx, "col_idx", (torch.int32,)),
+        col_idx.numel(), _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+        _stream(stream)))
+    del tp_arr, kf_arr
+    return row_ptr, col_idx
+
+
+def svsa_cluster_attn_workspace_bytes(batch, heads, n_q, nq, n_k, nk, align):
+    return int(_lib.svsa_cluster_attn_workspace_bytes(batch, heads, n_q, nq, n_k, nk, align))
+
+
+def svsa_cluster_attn(q, k, v, out, n_q, q_start, q_size, n_k, k_start, k_size, align,
+                      softmax_scale, row_ptr, col_idx, workspace, stream=None):
+    """out (bf16, query cluster layout) <- attention over the kept key clusters."""
+    import torch
+    B_, Hh, _, D = q.shape
+    bf, i32 = (torch.bfloat16,), (torch.int32,)
+    nq, nk = q_size.shape[-1], k_size.shape[-1]
+    _check("svsa_cluster_attn", _lib.svsa_cluster_attn(
+        _ptr(q, "q", bf), _ptr(k, "k", bf), _ptr(v, "v", bf), _ptr(out, "out", bf), B_, Hh, D,
+        int(n_q), int(nq), _ptr(q_start, "q_start", i32), _ptr(q_size, "q_size", i32), int(n_k),
+        int(nk), _ptr(k_start, "k_start", i32), _ptr(k_size, "k_size", i32), int(align),
+        float(softmax_scale), _ptr(row_ptr, "row_ptr", i32), _ptr(col_idx, "col_idx", i32),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
     return out

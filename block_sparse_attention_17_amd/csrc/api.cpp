@@ -85,6 +85,121 @@ int svsa_snr_top_p(const double* sigmas, int32_t steps, int32_t first_sparse, fl
   return SVSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Variable-size blocks ([iCATS] Sec. 4.1; [SVOO] QK co-clustering).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int32_t kMaxClusters = 4096;
+
+bool cluster_sizes_ok(int32_t batch, int32_t heads, int32_t n, int32_t C, int32_t D) {
+  if (batch < 1 || heads < 1 || n < 1 || C < 1 || C > kMaxClusters) return false;
+  const int64_t bh = (int64_t)batch * heads;
+  return bh <= 65535 && bh * n < (1ll << 31) && bh * C * (int64_t)D < (1ll << 31);
+}
+}  // namespace
+
+size_t svsa_kmeans_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t clusters,
+                                   int32_t head_dim) {
+  if (!cluster_sizes_ok(batch, heads, n, clusters, head_dim) || head_dim < 1) return 0;
+  return svsa::kmeans_ws_layout(batch * heads, n, clusters, head_dim).total;
+}
+
+int svsa_kmeans(const void* x, int32_t batch, int32_t heads, int32_t n, int32_t head_dim,
+                const double* metric, double* centroids, int32_t clusters, int32_t iters,
+                int32_t* labels, int32_t* sizes, void* workspace, size_t ws_bytes,
+                void* stream) {
+  if (!x || !centroids || !labels || !sizes || !workspace || iters < 1 || head_dim < 1 ||
+      !cluster_sizes_ok(batch, heads, n, clusters, head_dim))
+    return SVSA_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
+  const int32_t bh = batch * heads;
+  if (ws_bytes < svsa::kmeans_ws_layout(bh, n, clusters, head_dim).total) return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_kmeans(x, bh, n, head_dim, metric, centroids, clusters, iters,
+                                      labels, sizes, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t svsa_cluster_means_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                          int32_t clusters) {
+  if (!cluster_sizes_ok(batch, heads, n, clusters, 1)) return 0;
+  return svsa::kmeans_ws_layout(batch * heads, n, clusters, 0).total;
+}
+
+int svsa_cluster_means(const void* x, const int32_t* labels, int32_t batch, int32_t heads,
+                       int32_t n, int32_t head_dim, int32_t clusters, double* centroids,
+                       int32_t* sizes, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !labels || !centroids || !sizes || !workspace || head_dim < 1 ||
+      !cluster_sizes_ok(batch, heads, n, clusters, head_dim))
+    return SVSA_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
+  const int32_t bh = batch * heads;
+  const svsa::KmeansWs w = svsa::kmeans_ws_layout(bh, n, clusters, 0);
+  if (ws_bytes < w.total) return SVSA_E_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  int32_t* start = reinterpret_cast<int32_t*>(base + w.start_off);
+  int32_t* token = reinterpret_cast<int32_t*>(base + w.token_off);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = svsa::launch_cluster_layout(labels, bh, n, clusters, 1, start, sizes, nullptr,
+                                             token, st);
+  if (e == hipSuccess)
+    e = svsa::launch_cluster_means(x, start, sizes, token, centroids, bh, n, clusters, head_dim,
+                                   n, st);
+  return from_hip(e);
+}
+
+int svsa_cluster_metric(const double* centroids, const int32_t* sizes, int32_t batch,
+                        int32_t heads, int32_t clusters, int32_t head_dim, double* metric,
+                        void* stream) {
+  if (!centroids || !sizes || !metric || head_dim < 1 ||
+      !cluster_sizes_ok(batch, heads, 1, clusters, head_dim))
+    return SVSA_E_INVALID;
+  if (head_dim % 16 != 0 || head_dim > 256) return SVSA_E_UNSUPPORTED;
+  return from_hip(svsa::launch_cluster_metric(centroids, sizes, metric, batch * heads, clusters,
+                                              head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int64_t svsa_cluster_capacity(int32_t n, int32_t clusters, int32_t align) {
+  if (n < 1 || clusters < 1 || clusters > kMaxClusters || align < 1 || align > 1024 ||
+      !is_pow2(align))
+    return 0;
+  return svsa::cluster_lcap(n, clusters, align);
+}
+
+int svsa_cluster_layout(const int32_t* labels, int32_t batch, int32_t heads, int32_t n,
+                        int32_t clusters, int32_t align, int32_t* start, int32_t* sizes,
+                        int32_t* slot, int32_t* token, void* stream) {
+  if (!labels || !start || !sizes || !token || !cluster_sizes_ok(batch, heads, n, clusters, 1))
+    return SVSA_E_INVALID;
+  const int64_t lcap = svsa_cluster_capacity(n, clusters, align);
+  if (lcap == 0) return SVSA_E_INVALID;
+  if ((int64_t)batch * heads * lcap >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
+  return from_hip(svsa::launch_cluster_layout(labels, batch * heads, n, clusters, align, start,
+                                              sizes, slot, token,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int svsa_cluster_permute(const void* src, void* dst, int32_t dtype, int32_t batch, int32_t heads,
+                         int32_t n, int32_t head_dim, int32_t clusters, int32_t align,
+                         const int32_t* map, const int32_t* start, int32_t inverse,
+                         void* stream) {
+  if (!src || !dst || !map || !start || head_dim < 1 ||
+      !cluster_sizes_ok(batch, heads, n, clusters, 1))
+    return SVSA_E_INVALID;
+  const int64_t lcap = svsa_cluster_capacity(n, clusters, align);
+  if (lcap == 0) return SVSA_E_INVALID;
+  const int eb = elt_bytes(dtype);
+  if (!eb) return SVSA_E_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)head_dim * eb;
+  if (row_bytes % 16 != 0 || !is_pow2(row_bytes / 16) || row_bytes > 4096)
+    return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  const size_t nat = (size_t)bh * n * row_bytes, pad = (size_t)bh * lcap * row_bytes;
+  if (overlaps(src, inverse ? pad : nat, dst, inverse ? nat : pad)) return SVSA_E_INVALID;
+  return from_hip(svsa::launch_cluster_permute(src, dst, eb, (int32_t)bh, n, head_dim, clusters,
+                                               lcap, map, start, inverse != 0,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 const char* svsa_status_string(int status) {
   switch (status) {
     case SVSA_OK: return "ok";
@@ -161,6 +276,35 @@ int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32
                                           col_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t svsa_cluster_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nq, int32_t nk) {
+  if (batch < 1 || heads < 1 || nq < 1 || nk < 1) return 0;
+  return svsa::mask_ws_layout((int64_t)batch * heads * nq, nk).total;
+}
+
+int svsa_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,
+                      int32_t batch, int32_t heads, int32_t nq, int32_t nk, int32_t head_dim,
+                      double softmax_scale, const float* top_p, const float* keep_frac,
+                      int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  if (!qbar || !kbar || !ksizes || !row_ptr || !col_idx || batch < 1 || heads < 1 || nq < 1 ||
+      nk < 1 || head_dim < 1 || !isfinite(softmax_scale))
+    return SVSA_E_INVALID;
+  if ((top_p == nullptr) == (keep_frac == nullptr)) return SVSA_E_INVALID;
+  const float* par = top_p ? top_p : keep_frac;
+  for (int32_t h = 0; h < heads && h < kMaxHeadsMask; ++h)
+    if (!(par[h] > 0.f && par[h] <= 1.f)) return SVSA_E_INVALID;
+  if (heads > kMaxHeadsMask || nk > kMaxNb || nq > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int64_t worst = (int64_t)batch * heads * nq * nk;
+  if (worst >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (col_capacity < worst) return SVSA_E_CAPACITY;
+  if (!workspace || ws_bytes < svsa_cluster_mask_workspace_bytes(batch, heads, nq, nk))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_cluster_mask(qbar, kbar, ksizes, batch * heads, heads, nq, nk,
+                                            head_dim, softmax_scale, top_p, keep_frac, 0,
+                                            row_ptr, col_idx, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t svsa_stripe_mask_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* gin) {
   Geom g;
   if (batch < 1 || heads < 1 || !make_geom(gin, &g)) return 0;
@@ -219,6 +363,51 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
   return from_hip(svsa::launch_block_sparse_attn(q, k, v, out, (int32_t)bh, head_dim, g,
                                                  softmax_scale, row_ptr, col_idx, workspace,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t svsa_cluster_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q, int32_t nq,
+                                         int32_t n_k, int32_t nk, int32_t align) {
+  if (batch < 1 || heads < 1 || (align != 32 && align != 64)) return 0;
+  const int64_t cap_q = svsa_cluster_capacity(n_q, nq, align);
+  const int64_t cap_k = svsa_cluster_capacity(n_k, nk, align);
+  if (cap_q == 0 || cap_k == 0) return 0;
+  return svsa::cluster_attn_ws_layout(batch * heads, align, cap_q, cap_k).total;
+}
+
+int svsa_cluster_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                      int32_t heads, int32_t head_dim, int32_t n_q, int32_t nq,
+                      const int32_t* q_start, const int32_t* q_size, int32_t n_k, int32_t nk,
+                      const int32_t* k_start, const int32_t* k_size, int32_t align,
+                      float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !out || !q_start || !q_size || !k_start || !k_size || !row_ptr ||
+      !col_idx || batch < 1 || heads < 1 || head_dim < 1 || !isfinite(softmax_scale))
+    return SVSA_E_INVALID;
+  if (align != 32 && align != 64) return SVSA_E_INVALID;
+  const int64_t cap_q = svsa_cluster_capacity(n_q, nq, align);
+  const int64_t cap_k = svsa_cluster_capacity(n_k, nk, align);
+  if (cap_q == 0 || cap_k == 0) return SVSA_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  // key sub-blocks fit the 13-bit index of the schedule entries; one head's
+  // rows fit a 32-bit buffer range
+  if (cap_k / align > 8192 || cap_q * head_dim * 2 >= (1ll << 31) ||
+      cap_k * head_dim * 2 >= (1ll << 31) || bh > 65535)
+    return SVSA_E_UNSUPPORTED;
+  const int64_t groups = (cap_q / align + 256 / align - 1) / (256 / align);
+  if (bh * groups * (cap_k / align) >= 0x7fffffff || bh * nq * nk >= 0x7fffffff)
+    return SVSA_E_UNSUPPORTED;
+  const size_t qbytes = (size_t)bh * cap_q * head_dim * 2, kbytes = (size_t)bh * cap_k * head_dim * 2;
+  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kbytes) ||
+      overlaps(out, qbytes, v, kbytes))
+    return SVSA_E_INVALID;
+  if (!workspace ||
+      ws_bytes < svsa_cluster_attn_workspace_bytes(batch, heads, n_q, nq, n_k, nk, align))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_cluster_attn(q, k, v, out, (int32_t)bh, head_dim, align, cap_q,
+                                            cap_k, q_start, q_size, nq, k_start, k_size, nk,
+                                            softmax_scale, row_ptr, col_idx, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

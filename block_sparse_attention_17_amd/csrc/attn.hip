@@ -67,8 +67,8 @@ constexpr int kPre = 4;   // P V operands read before the barrier that opens an 
 
 // ---------------------------------------------------------------------------
 // Schedule: per item (b, h, group of query sub-blocks) the ascending union of
-// the group's kept key sub-blocks; entry = j | (valid << 12) | (mask << 24):
-// j the key sub-block (< 4096), valid its valid tokens (its first slots; key
+// the group's kept key sub-blocks; entry = j | (valid << 13) | (mask << 24):
+// j the key sub-block (< 8192), valid its valid tokens (its first slots; key
 // sub-blocks with none are left out), bit m of mask set when the m-th query
 // sub-block of the group keeps j.
 // ---------------------------------------------------------------------------
@@ -76,17 +76,76 @@ constexpr int kSchedThreads = 256;
 
 // The attention kernels work on sub-blocks of S = 64 (or 32) tokens; a block
 // of Bk = ratio * S tokens is `ratio` consecutive sub-blocks, so block-level
-// lists expand to sub-block lists here (nb: sub-blocks, nb_blk: blocks).
-__device__ __forceinline__ int32_t sub_valid(const Geom& g, int32_t j, int32_t ratio, int32_t sub) {
-  const int32_t v = block_valid(g, j / ratio) - (j % ratio) * sub;
+// lists expand to sub-block lists here (nb: key sub-blocks, nq: query
+// sub-blocks).  Two sources of blocks:
+//   GeomSched   fixed-size tiles (packed or 3D-padded), CSR rows = blocks;
+//   TableSched  clusters of any size, each starting on a sub-block boundary
+//               (start[c], size[c] per head), CSR rows = query clusters and
+//               columns = key clusters.
+__device__ __forceinline__ int32_t clamp_valid(int32_t v, int32_t sub) {
   return v < 0 ? 0 : (v > sub ? sub : v);
 }
 
+struct GeomSched {
+  Geom g;
+  int32_t ratio, sub;
+  __device__ int32_t ncols() const { return g.nb; }
+  __device__ int32_t qvalid(int64_t, int32_t i) const {
+    return clamp_valid(block_valid(g, i / ratio) - (i % ratio) * sub, sub);
+  }
+  __device__ int64_t row(int64_t bh, int32_t i) const { return bh * g.nb + i / ratio; }
+  __device__ void keys(int64_t, int32_t jb, int32_t* j0, int32_t* j1) const {
+    *j0 = jb * ratio;
+    *j1 = *j0 + ratio;
+  }
+  __device__ int32_t kvalid(int64_t bh, int32_t j) const { return qvalid(bh, j); }
+};
+
+// last cluster c in [0, n) with start[c] <= pos (the one whose slots hold pos)
+__device__ __forceinline__ int32_t owner_of(const int32_t* start, int32_t n, int32_t pos) {
+  int32_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct TableSched {
+  const int32_t *q_start, *q_size, *k_start, *k_size;
+  int32_t nq, nk, sub;
+  __device__ int32_t ncols() const { return nk; }
+  __device__ int32_t qvalid(int64_t bh, int32_t i) const {
+    const int32_t* st = q_start + bh * (nq + 1);
+    const int32_t pos = i * sub;
+    if (pos >= st[nq]) return 0;
+    const int32_t c = owner_of(st, nq, pos);
+    return clamp_valid(st[c] + q_size[bh * nq + c] - pos, sub);
+  }
+  __device__ int64_t row(int64_t bh, int32_t i) const {
+    return bh * nq + owner_of(q_start + bh * (nq + 1), nq, i * sub);
+  }
+  __device__ void keys(int64_t bh, int32_t jc, int32_t* j0, int32_t* j1) const {
+    const int32_t s0 = k_start[bh * (nk + 1) + jc];
+    *j0 = s0 / sub;
+    *j1 = (s0 + k_size[bh * nk + jc] + sub - 1) / sub;
+  }
+  __device__ int32_t kvalid(int64_t bh, int32_t j) const {
+    const int32_t* st = k_start + bh * (nk + 1);
+    const int32_t pos = j * sub;
+    if (pos >= st[nk]) return 0;
+    const int32_t c = owner_of(st, nk, pos);
+    return clamp_valid(st[c] + k_size[bh * nk + c] - pos, sub);
+  }
+};
+
+template <typename Sched>
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-             int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t groups,
-             int32_t group_size, int32_t ratio, int32_t sub, Geom gb) {
-  const int32_t nb_blk = gb.nb;
+             int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t nq,
+             int32_t groups, int32_t group_size, Sched sc) {
+  const int32_t ncols = sc.ncols();
   extern __shared__ uint32_t mask[];  // [nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
   const int64_t item = blockIdx.x;
@@ -97,17 +156,17 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   __syncthreads();
   for (int m = 0; m < group_size; ++m) {
     const int32_t i = g * group_size + m;   // query sub-block
-    if (i >= nb) break;
-    if (sub_valid(gb, i, ratio, sub) == 0) continue;   // padding only: nothing to compute
-    const int64_t row = bh * nb_blk + i / ratio;
+    if (i >= nq) break;
+    if (sc.qvalid(bh, i) == 0) continue;     // padding only: nothing to compute
+    const int64_t row = sc.row(bh, i);
     const int32_t e0 = row_ptr[row], e1 = row_ptr[row + 1];
     for (int32_t e = e0 + t; e < e1; e += kSchedThreads) {
       const int32_t jb = col_idx[e];
-      if (jb < 0 || jb >= nb_blk) continue;
-      for (int32_t r = 0; r < ratio; ++r) {
-        const int32_t j = jb * ratio + r;
-        if (j < nb && sub_valid(gb, j, ratio, sub) > 0) atomicOr(&mask[j], 1u << m);
-      }
+      if (jb < 0 || jb >= ncols) continue;
+      int32_t j0, j1;
+      sc.keys(bh, jb, &j0, &j1);
+      for (int32_t j = j0; j < j1; ++j)
+        if (j < nb && sc.kvalid(bh, j) > 0) atomicOr(&mask[j], 1u << m);
     }
   }
   __syncthreads();
@@ -127,7 +186,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
       tot += wave_tot[k];
     }
     if (m != 0u)
-      out[off + wbase + before] = j | (sub_valid(gb, j, ratio, sub) << 12) | (int32_t)(m << 24);
+      out[off + wbase + before] = j | (sc.kvalid(bh, j) << 13) | (int32_t)(m << 24);
     off += tot;
     __syncthreads();
   }
@@ -471,7 +530,7 @@ __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int
   using C = Cfg<D, BK>;
   if (!(e < cx.n_u && active(cx, ent))) return;
   // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
-  const int32_t nvalid = (ent >> 12) & 127;   // valid keys: the first nvalid
+  const int32_t nvalid = (ent >> 13) & 127;   // valid keys: the first nvalid
   if (nvalid < BK) {
     // lane-dependent limit, computed here (an opaque value keeps the 32
     // compares out of loop-invariant code motion, where they would pin 32
@@ -555,7 +614,7 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     // clamped) into a slot that is no longer read: unconditional copies keep
     // the per-wave count of copies in flight fixed.
     constexpr int slot = (I / 2 + 2) & 3;
-    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0xfff, rg.k[slot], rg.v[slot], wave_off);
+    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0x1fff, rg.k[slot], rg.v[slot], wave_off);
   }
   const int32_t ph = t - G;
   if (ph >= 0 && cx.has_rows) {
@@ -625,8 +684,9 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const __bf16* __restrict__ vt, __bf16* __restrict__ out,
                                          const int32_t* __restrict__ list,
                                          const int32_t* __restrict__ count, int64_t item,
-                                         int32_t groups, int32_t nb, int32_t Npad,
-                                         float c_log2, const Ring<D, BK>& rg) {
+                                         int32_t groups, int32_t nb, int32_t nq,
+                                         int32_t npad_q, int32_t npad_k, float c_log2,
+                                         const Ring<D, BK>& rg) {
   using C = Cfg<D, BK>;
   constexpr int kS = D / 16, kDT = D / 32;
 
@@ -643,7 +703,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   const int64_t bh = item / groups;
   const int32_t gi = (int32_t)(item % groups);
   const int32_t iq = gi * C::kGroup + cx.qb;
-  cx.has_rows = iq < nb;
+  cx.has_rows = iq < nq;
   cx.n_u = count[item];
   // intervals 0 .. 2 n_u + 1 carry work; the count is rounded up to whole
   // rounds of 8 (the extra intervals do nothing); an empty union runs none
@@ -651,21 +711,21 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   cx.nb = nb;
   cx.c_log2 = c_log2;
   cx.lst = list + item * nb;
-  // raw buffer resources over this head's K and V^T (byte range Npad * D * 2,
+  // raw buffer resources over this head's K and V^T (byte range npad_k * D * 2,
   // below 2^31 by the host checks; dword 3 = 0x00020000: raw 32-bit data)
-  const int32_t head_bytes = Npad * D * 2;
-  cx.k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(k + bh * (int64_t)Npad * D), (short)0,
+  const int32_t head_bytes = npad_k * D * 2;
+  cx.k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(k + bh * (int64_t)npad_k * D), (short)0,
                                                 head_bytes, 0x00020000);
-  cx.vt_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + bh * (int64_t)Npad * D), (short)0,
-                                                 head_bytes, 0x00020000);
-  const __bf16* qh = q + bh * (int64_t)Npad * D;
-  __bf16* oh = out + bh * (int64_t)Npad * D;
+  cx.vt_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + bh * (int64_t)npad_k * D),
+                                                 (short)0, head_bytes, 0x00020000);
+  const __bf16* qh = q + bh * (int64_t)npad_q * D;
+  __bf16* oh = out + bh * (int64_t)npad_q * D;
 
 #pragma unroll
   for (int u = 0; u < C::kDmaPerWave; ++u) cx.dma_off[u] = copy_src_off<D, BK>(cx.wave, cx.lane, u);
 
   WaveState<D, BK> st;
-  const int32_t qrow = (cx.has_rows ? iq : nb - 1) * BK + sub * 32 + cx.l32;
+  const int32_t qrow = (cx.has_rows ? iq : nq - 1) * BK + sub * 32 + cx.l32;
 #pragma unroll
   for (int s = 0; s < kS; ++s)
     st.qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * D + 16 * s + 8 * cx.hh);
@@ -711,7 +771,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
             const int32_t* __restrict__ list, const int32_t* __restrict__ count,
             const int32_t* __restrict__ queue, int32_t* __restrict__ meta, int32_t groups,
-            int32_t nb, int32_t Npad, float c_log2) {
+            int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2) {
   using C = Cfg<D, BK>;
   __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
       k2[C::kTileBytes], k3[C::kTileBytes];
@@ -739,7 +799,8 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int32_t item = s_item;
     __syncthreads();
     if (item < 0) break;
-    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, Npad, c_log2, rg);
+    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
+                    rg);
   }
 }
 
@@ -766,13 +827,15 @@ hipError_t attn_grid(int64_t items, uint32_t* grid) {
   return hipSuccess;
 }
 
+// nb / nq: key / query sub-blocks per head (nb is also the list stride);
+// npad_q / npad_k: rows per head of Q and O / of K and V.
 template <int D, int BK>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
-                       int32_t bh, const AttnWs& w, const Geom& g, float c_log2,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL((vt_kernel<D, BK>), dim3((uint32_t)((int64_t)bh * g.nb)), dim3(kVtThreads), 0,
-                     stream, (const __bf16*)v, vt, g.nb, g.Npad);
+                       int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
+                       int32_t npad_k, float c_log2, hipStream_t stream) {
+  hipLaunchKernelGGL((vt_kernel<D, BK>), dim3((uint32_t)((int64_t)bh * nb)), dim3(kVtThreads), 0,
+                     stream, (const __bf16*)v, vt, nb, npad_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint32_t grid = 0;
@@ -780,19 +843,20 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<D, BK>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
-                     count, queue, meta, w.groups, g.nb, g.Npad, c_log2);
+                     count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2);
   return hipGetLastError();
 }
 
 }  // namespace
 
-AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
+namespace {
+AttnWs ws_common(int32_t bh, int32_t sub, int32_t nbs_q, int32_t nbs_k, int64_t npad_k) {
   AttnWs w{};
-  w.sub = g.Bk % 64 == 0 ? 64 : 32;
-  w.ratio = g.Bk / w.sub;
-  w.nbs = g.pad3d ? g.nb * w.ratio : (g.N + w.sub - 1) / w.sub;
+  w.sub = sub;
+  w.nbs = nbs_k;
+  w.nbs_q = nbs_q;
   w.group_size = kRowsPerItem / w.sub;
-  w.groups = (w.nbs + w.group_size - 1) / w.group_size;
+  w.groups = (nbs_q + w.group_size - 1) / w.group_size;
   w.items = (int64_t)bh * w.groups;
   size_t off = 0;
   w.list_off = off;
@@ -804,8 +868,62 @@ AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
   w.meta_off = off;
   off = align_up(off + 3 * kQueues * sizeof(int32_t), 256);
   w.vt_off = off;
-  off = align_up(off + (size_t)bh * g.Npad * kMaxHeadDim * 2, 256);  // V^T (bf16)
+  off = align_up(off + (size_t)bh * npad_k * kMaxHeadDim * 2, 256);  // V^T (bf16)
   w.total = off;
+  return w;
+}
+
+// union lists, work queues, then the kernels for this head_dim / sub-block size
+template <typename Sched>
+hipError_t run_attention(const void* q, const void* k, const void* v, void* out, int32_t bh,
+                         int32_t head_dim, const AttnWs& w, const Sched& sc, int32_t npad_q,
+                         int32_t npad_k, float scale, const int32_t* row_ptr,
+                         const int32_t* col_idx, void* ws, hipStream_t stream) {
+  if (w.items > 0x7fffffff) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
+  int32_t* count = reinterpret_cast<int32_t*>(base + w.count_off);
+  int32_t* queue = reinterpret_cast<int32_t*>(base + w.queue_off);
+  int32_t* meta = reinterpret_cast<int32_t*>(base + w.meta_off);
+  __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
+
+  hipLaunchKernelGGL(union_kernel<Sched>, dim3((uint32_t)w.items), dim3(kSchedThreads),
+                     (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
+                     w.nbs, w.nbs_q, w.groups, w.group_size, sc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
+                     w.groups);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const float c_log2 = scale * 1.4426950408889634f;
+  if (head_dim == 128 && w.sub == 64)
+    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+                                w.nbs_q, npad_q, npad_k, c_log2, stream);
+  if (head_dim == 64 && w.sub == 64)
+    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+                               w.nbs_q, npad_q, npad_k, c_log2, stream);
+  if (head_dim == 128 && w.sub == 32)
+    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+                                w.nbs_q, npad_q, npad_k, c_log2, stream);
+  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
+                             npad_q, npad_k, c_log2, stream);
+}
+}  // namespace
+
+AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
+  const int32_t sub = g.Bk % 64 == 0 ? 64 : 32;
+  const int32_t ratio = g.Bk / sub;
+  const int32_t nbs = g.pad3d ? g.nb * ratio : (g.N + sub - 1) / sub;
+  AttnWs w = ws_common(bh, sub, nbs, nbs, g.Npad);
+  w.ratio = ratio;
+  return w;
+}
+
+AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t npad_k) {
+  AttnWs w = ws_common(bh, sub, (int32_t)(npad_q / sub), (int32_t)(npad_k / sub), npad_k);
+  w.ratio = 1;
   return w;
 }
 
@@ -816,39 +934,23 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = attn_ws_layout(bh, g);
-  // the attention kernels see the sequence as w.nbs sub-blocks of w.sub tokens
-  Geom gs = g;
-  gs.Bk = w.sub;
-  gs.nb = w.nbs;   // gs.Npad stays the tensor's row count (head stride)
-  if (w.items > 0x7fffffff) return hipErrorInvalidValue;
-  char* base = static_cast<char*>(ws);
-  int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
-  int32_t* count = reinterpret_cast<int32_t*>(base + w.count_off);
-  int32_t* queue = reinterpret_cast<int32_t*>(base + w.queue_off);
-  int32_t* meta = reinterpret_cast<int32_t*>(base + w.meta_off);
-  __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
+  const GeomSched sc{g, w.ratio, w.sub};
+  return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
+                       ws, stream);
+}
 
-  hipLaunchKernelGGL(union_kernel, dim3((uint32_t)w.items), dim3(kSchedThreads),
-                     (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
-                     w.nbs, w.groups, w.group_size, w.ratio, w.sub, g);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
-                     w.groups);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const float c_log2 = scale * 1.4426950408889634f;
-  if (head_dim == 128 && gs.Bk == 64)
-    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
-                                stream);
-  if (head_dim == 64 && gs.Bk == 64)
-    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
-                               stream);
-  if (head_dim == 128 && gs.Bk == 32)
-    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2,
-                                stream);
-  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, gs, c_log2, stream);
+hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void* out,
+                               int32_t bh, int32_t head_dim, int32_t sub, int64_t npad_q,
+                               int64_t npad_k, const int32_t* q_start, const int32_t* q_size,
+                               int32_t nq, const int32_t* k_start, const int32_t* k_size,
+                               int32_t nk, float scale, const int32_t* row_ptr,
+                               const int32_t* col_idx, void* ws, hipStream_t stream) {
+  if ((sub != 32 && sub != 64) || npad_q % sub || npad_k % sub) return hipErrorInvalidValue;
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  const AttnWs w = cluster_attn_ws_layout(bh, sub, npad_q, npad_k);
+  const TableSched sc{q_start, q_size, k_start, k_size, nq, nk, sub};
+  return run_attention(q, k, v, out, bh, head_dim, w, sc, (int32_t)npad_q, (int32_t)npad_k, scale,
+                       row_ptr, col_idx, ws, stream);
 }
 
 }  // namespace svsa

@@ -1,0 +1,443 @@
+// Variable-size blocks: query / key clustering and the cluster layout.
+//
+// [iCATS] "iCATS: Fast Video Generation via Interaction-Aware Sparse Attention
+// and Timestep-Adaptive Sparsity", Sec. 3.1 and 4.1: clustering targets the
+// error of the query-key interactions, written as a quadratic form in the
+// feature space; query clusters start in plain feature space, later use the
+// key clusters' metric, and guide the key clustering in turn.  [SVOO]
+// "Attention Sparsity is Input-Stable: ... Online QK Co-Clustering":
+// bidirectional co-clustering of queries and keys into blocks.
+//
+// Reading implemented here: replacing a token x by a centroid c changes its
+// logits against the other side's tokens y by (x - c).y, whose summed square
+// is (x - c)^T G (x - c) with G = sum_y y y^T, approximated from the other
+// side's clusters as G = sum_j n_j c_j c_j^T.  Lloyd iterations under that
+// fixed metric: assign every token to the centroid of least distance (ties:
+// lowest index), then move every non-empty centroid to its members' mean.
+//
+// Kernels:
+//   layout_kernel  one workgroup per (b, h): cluster sizes, padded starts,
+//                  a stable counting sort (members in ascending token order)
+//   means_kernel   one wavefront per cluster: float64 sum of the members in
+//                  that order, mean written only for non-empty clusters
+//   metric_kernel  G = sum_c n_c c c^T, 16 x 16 tile of G per workgroup
+//   prep_kernel    g_c = G c (float64) split into bf16 hi + lo, and c^T G c
+//   assign_kernel  MFMA: 256 tokens per workgroup against all centroids in
+//                  chunks of 32; d(x, c) - x^T G x = c^T G c - 2 x . g_c
+//   permute_kernel rows gathered into the padded cluster layout (padding
+//                  zero) or scattered back to token order
+#include "svsa_internal.h"
+
+namespace svsa {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// layout_kernel: start[c] (padded to `align`), sizes[c], slot[t] and
+// token[s].  Labels outside [0, C) are not placed (slot -1).
+// ---------------------------------------------------------------------------
+constexpr int kLayThreads = 256;
+
+__global__ void __launch_bounds__(kLayThreads)
+layout_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t align,
+              int32_t* __restrict__ start, int32_t* __restrict__ sizes,
+              int32_t* __restrict__ slot, int32_t* __restrict__ token, int64_t lcap) {
+  extern __shared__ int32_t sh[];
+  int32_t* cnt = sh;            // [C]
+  int32_t* cursor = sh + C;     // [C]
+  __shared__ int32_t lab_s[kLayThreads];
+  __shared__ int32_t part[kLayThreads];
+  const int64_t bh = blockIdx.x;
+  const int32_t tid = threadIdx.x;
+  const int32_t* lab = labels + bh * N;
+
+  for (int32_t c = tid; c < C; c += kLayThreads) cnt[c] = 0;
+  __syncthreads();
+  for (int32_t t = tid; t < N; t += kLayThreads) {
+    const int32_t c = lab[t];
+    if (c >= 0 && c < C) atomicAdd(&cnt[c], 1);
+  }
+  __syncthreads();
+
+  // exclusive scan of the padded sizes: each thread owns a contiguous range
+  const int32_t per = (C + kLayThreads - 1) / kLayThreads;
+  const int32_t c0 = tid * per, c1 = min(C, c0 + per);
+  int32_t local = 0;
+  for (int32_t c = c0; c < c1; ++c) local += (cnt[c] + align - 1) / align * align;
+  part[tid] = local;
+  __syncthreads();
+  for (int32_t off = 1; off < kLayThreads; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - local;
+  int32_t* st = start + bh * (int64_t)(C + 1);
+  for (int32_t c = c0; c < c1; ++c) {
+    cursor[c] = run;
+    st[c] = run;
+    sizes[bh * C + c] = cnt[c];
+    run += (cnt[c] + align - 1) / align * align;
+  }
+  const int32_t total = part[kLayThreads - 1];
+  if (tid == 0) st[C] = total;
+  int32_t* tok = token + bh * lcap;
+  for (int32_t s = tid; s < total; s += kLayThreads) tok[s] = -1;
+  __syncthreads();
+
+  // stable placement: chunk by chunk in token order; inside a chunk a token's
+  // rank is the number of earlier tokens of the chunk with the same label
+  int32_t* sl = slot ? slot + bh * N : nullptr;
+  for (int32_t base = 0; base < N; base += kLayThreads) {
+    const int32_t t = base + tid;
+    const int32_t c = t < N ? lab[t] : -1;
+    lab_s[tid] = c;
+    __syncthreads();
+    const bool ok = c >= 0 && c < C;
+    if (ok) {
+      int32_t rank = 0;
+      for (int32_t j = 0; j < tid; ++j) rank += lab_s[j] == c;
+      const int32_t s = cursor[c] + rank;
+      tok[s] = t;
+      if (sl) sl[t] = s;
+    } else if (t < N && sl) {
+      sl[t] = -1;
+    }
+    __syncthreads();
+    if (ok) atomicAdd(&cursor[c], 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// means_kernel: one wavefront per (b, h, c); members token[start .. start+n)
+// (ascending token order, from layout_kernel with align 1).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+means_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ start,
+             const int32_t* __restrict__ sizes, const int32_t* __restrict__ token,
+             double* __restrict__ cents, int32_t N, int32_t C, int32_t D, int64_t lcap,
+             int64_t total) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  if (w >= total) return;
+  const int32_t lane = threadIdx.x % 64;
+  const int64_t bh = w / C;
+  const int32_t c = (int32_t)(w % C);
+  const int32_t n = sizes[bh * C + c];
+  if (n == 0) return;  // empty: the centroid stays
+  const int32_t s0 = start[bh * (int64_t)(C + 1) + c];
+  const int32_t* tok = token + bh * lcap + s0;
+  const uint16_t* xb = x + bh * (int64_t)N * D;
+  double acc0 = 0.0, acc1 = 0.0;   // dims lane and lane + 64
+  for (int32_t m = 0; m < n; ++m) {
+    const uint16_t* row = xb + (int64_t)tok[m] * D;
+    if (lane < D) acc0 += (double)bf16_bits_to_float(row[lane]);
+    if (lane + 64 < D) acc1 += (double)bf16_bits_to_float(row[lane + 64]);
+  }
+  double* out = cents + (bh * C + c) * (int64_t)D;
+  if (lane < D) out[lane] = acc0 / n;
+  if (lane + 64 < D) out[lane + 64] = acc1 / n;
+}
+
+// ---------------------------------------------------------------------------
+// metric_kernel: G[d][e] = sum_c n_c cent[c][d] cent[c][e] (float64).
+// ---------------------------------------------------------------------------
+constexpr int kMt = 16, kMc = 64;
+
+__global__ void __launch_bounds__(256)
+metric_kernel(const double* __restrict__ cents, const int32_t* __restrict__ sizes,
+              double* __restrict__ G, int32_t C, int32_t D, int32_t tiles) {
+  __shared__ double sd[kMc][kMt + 1];
+  __shared__ double se[kMc][kMt + 1];
+  __shared__ double sn[kMc];
+  const int64_t bh = blockIdx.x / (tiles * tiles);
+  const int32_t t2 = blockIdx.x % (tiles * tiles);
+  const int32_t d0 = (t2 / tiles) * kMt, e0 = (t2 % tiles) * kMt;
+  const int32_t dl = threadIdx.x / kMt, el = threadIdx.x % kMt;
+  const double* cb = cents + bh * (int64_t)C * D;
+  double acc = 0.0;
+  for (int32_t cc = 0; cc < C; cc += kMc) {
+    for (int32_t i = threadIdx.x; i < kMc * kMt; i += 256) {
+      const int32_t r = i / kMt, k = i % kMt;
+      const bool ok = cc + r < C;
+      sd[r][k] = ok ? cb[(int64_t)(cc + r) * D + d0 + k] : 0.0;
+      se[r][k] = ok ? cb[(int64_t)(cc + r) * D + e0 + k] : 0.0;
+    }
+    if (threadIdx.x < kMc) sn[threadIdx.x] = cc + (int)threadIdx.x < C
+                                                  ? (double)sizes[bh * C + cc + threadIdx.x] : 0.0;
+    __syncthreads();
+    const int32_t lim = min(kMc, C - cc);
+    for (int32_t r = 0; r < lim; ++r) acc = fma(sn[r] * sd[r][dl], se[r][el], acc);
+    __syncthreads();
+  }
+  G[(bh * D + d0 + dl) * (int64_t)D + e0 + el] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// prep_kernel: per (b, h, c) g = G c (or c without a metric), q = c . g;
+// g is stored as bf16 hi + lo (hi = bf16(g), lo = bf16(g - hi)) for the MFMA.
+// One workgroup of D threads per centroid.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(128)
+prep_kernel(const double* __restrict__ cents, const double* __restrict__ G,
+            uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo, float* __restrict__ cq,
+            int32_t C, int32_t D) {
+  __shared__ double cv[128];
+  __shared__ double red[128];
+  const int64_t w = blockIdx.x;           // (b, h, c)
+  const int64_t bh = w / C;
+  const int32_t d = threadIdx.x;
+  const double* c = cents + w * D;
+  if (d < D) cv[d] = c[d];
+  __syncthreads();
+  double g = 0.0;
+  if (d < D) {
+    if (G) {
+      const double* Gr = G + (bh * D + d) * (int64_t)D;
+      for (int32_t e = 0; e < D; ++e) g = fma(Gr[e], cv[e], g);
+    } else {
+      g = cv[d];
+    }
+    const float gf = (float)g;
+    const uint32_t hi = float_to_bf16_bits(gf);
+    const uint32_t lo = float_to_bf16_bits(gf - bf16_bits_to_float(hi));
+    g_hi[w * D + d] = (uint16_t)hi;
+    g_lo[w * D + d] = (uint16_t)lo;
+  }
+  red[d] = d < D ? cv[d] * g : 0.0;
+  __syncthreads();
+  for (int32_t s = 64; s > 0; s >>= 1) {
+    if (d < s) red[d] += red[d + s];
+    __syncthreads();
+  }
+  if (d == 0) cq[w] = (float)red[0];
+}
+
+// ---------------------------------------------------------------------------
+// assign_kernel: label[t] = argmin_c (c^T G c - 2 x_t . g_c), ties to the
+// lowest c.  v_mfma_f32_32x32x16_bf16 with A = g (32 centroids x 16 dims,
+// from LDS) and B = x^T (16 dims x 32 tokens, registers): each lane then holds
+// one token column and 16 centroid rows of the 32 x 32 output.
+// ---------------------------------------------------------------------------
+constexpr int kAsWaves = 8, kAsTok = 32 * kAsWaves, kAsC = 32;
+
+template <int D>
+__global__ void __launch_bounds__(64 * kAsWaves)
+assign_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g_hi,
+              const uint16_t* __restrict__ g_lo, const float* __restrict__ cq,
+              int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t tiles) {
+  constexpr int kChunks = D / 8;              // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint4 ahi[2][kAsC * kChunks];
+  __shared__ __attribute__((aligned(16))) uint4 alo[2][kAsC * kChunks];
+  __shared__ float acq[2][kAsC];
+  const int64_t bh = blockIdx.x / tiles;
+  const int32_t t0 = (int32_t)(blockIdx.x % tiles) * kAsTok;
+  const int32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int32_t col = lane % 32, half = lane / 32;
+  const int32_t tok = t0 + wave * 32 + col;
+
+  // B operand: 8 consecutive dims of this lane's token per 16-dim step
+  bf16x8 xb[D / 16];
+  const uint4* xrow = reinterpret_cast<const uint4*>(x + (bh * N + (tok < N ? tok : 0)) * (int64_t)D);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    uint4 v = xrow[2 * ks + half];
+    if (tok >= N) v = make_uint4(0, 0, 0, 0);
+    xb[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  const uint4* ghi = reinterpret_cast<const uint4*>(g_hi + bh * (int64_t)C * D);
+  const uint4* glo = reinterpret_cast<const uint4*>(g_lo + bh * (int64_t)C * D);
+  const float* cqb = cq + bh * (int64_t)C;
+  const int32_t nchunk = (C + kAsC - 1) / kAsC;
+  // stage chunk k into buffer k & 1 (rows beyond C are zero, never selected);
+  // row r's 16-byte piece q lands at q ^ (r & 15) so the operand reads of 32
+  // rows at one column hit different banks
+  auto stage = [&](int32_t k) {
+    const int32_t buf = k & 1;
+    for (int32_t i = threadIdx.x; i < kAsC * kChunks; i += 64 * kAsWaves) {
+      const int32_t r = i / kChunks, q = i % kChunks;
+      const int32_t c = k * kAsC + r;
+      const int32_t dst = r * kChunks + (q ^ (r & (kChunks - 1) & 15));
+      ahi[buf][dst] = c < C ? ghi[(int64_t)c * kChunks + q] : make_uint4(0, 0, 0, 0);
+      alo[buf][dst] = c < C ? glo[(int64_t)c * kChunks + q] : make_uint4(0, 0, 0, 0);
+    }
+    if (threadIdx.x < kAsC) {
+      const int32_t c = k * kAsC + threadIdx.x;
+      acq[buf][threadIdx.x] = c < C ? cqb[c] : 0.0f;
+    }
+  };
+
+  float best = __builtin_huge_valf();
+  int32_t bidx = 0x7fffffff;
+  stage(0);
+  __syncthreads();
+  for (int32_t k = 0; k < nchunk; ++k) {
+    if (k + 1 < nchunk) stage(k + 1);
+    const int32_t buf = k & 1;
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int32_t q = 2 * ks + half;
+      const int32_t a_off = col * kChunks + (q ^ (col & (kChunks - 1) & 15));
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, ahi[buf][a_off]);
+      const bf16x8 al = __builtin_bit_cast(bf16x8, alo[buf][a_off]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[ks], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int32_t row = (r / 4) * 8 + half * 4 + (r % 4);
+      const int32_t c = k * kAsC + row;
+      const float s = acq[buf][row] - 2.0f * acc[r];
+      if (c < C && s < best) {   // rows ascend within a lane: strict < keeps the lowest
+        best = s;
+        bidx = c;
+      }
+    }
+    __syncthreads();
+  }
+  // the two lanes of a token column hold interleaved row sets: combine
+  const float ob = __shfl_xor(best, 32);
+  const int32_t oi = __shfl_xor(bidx, 32);
+  if (ob < best || (ob == best && oi < bidx)) {
+    best = ob;
+    bidx = oi;
+  }
+  if (half == 0 && tok < N) labels[bh * N + tok] = bidx;
+}
+
+// ---------------------------------------------------------------------------
+// permute_kernel: forward dst[s] = src[token[s]] (zero for padding) over the
+// slots s < start[C] of each (b, h); inverse dst[t] = src[slot[t]] (zero when
+// the token was not placed).  16-byte chunks.
+// ---------------------------------------------------------------------------
+template <int kInverse>
+__global__ void __launch_bounds__(256)
+cluster_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                       const int32_t* __restrict__ map, const int32_t* __restrict__ start,
+                       int32_t N, int32_t C, int64_t lcap, int32_t chunk_shift,
+                       int32_t rows_per_block) {
+  const int32_t chunks = 1 << chunk_shift;
+  const int64_t bh = blockIdx.y;
+  const int64_t rows = kInverse ? N : start[bh * (int64_t)(C + 1) + C];
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  if (r0 >= rows) return;
+  const int64_t r1 = min(rows, r0 + rows_per_block);
+  const int64_t src_rows = kInverse ? lcap : N, dst_rows = kInverse ? N : lcap;
+  const int32_t* m = map + bh * (kInverse ? (int64_t)N : lcap);
+  for (int64_t e = r0 * chunks + threadIdx.x; e < r1 * chunks; e += 256) {
+    const int64_t r = e >> chunk_shift;
+    const int32_t ch = (int32_t)(e & (chunks - 1));
+    const int32_t from = m[r];
+    dst[(bh * dst_rows + r) * chunks + ch] =
+        from >= 0 ? src[(bh * src_rows + from) * chunks + ch] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+}  // namespace
+
+int64_t cluster_lcap(int32_t N, int32_t C, int32_t align) {
+  return ((int64_t)N + (int64_t)C * (align - 1) + align - 1) / align * align;
+}
+
+hipError_t launch_cluster_layout(const int32_t* labels, int32_t bh, int32_t N, int32_t C,
+                                 int32_t align, int32_t* start, int32_t* sizes, int32_t* slot,
+                                 int32_t* token, hipStream_t stream) {
+  const size_t shmem = (size_t)2 * C * sizeof(int32_t);
+  hipLaunchKernelGGL(layout_kernel, dim3((uint32_t)bh), dim3(kLayThreads), shmem, stream, labels,
+                     N, C, align, start, sizes, slot, token, cluster_lcap(N, C, align));
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_means(const void* x, const int32_t* start, const int32_t* sizes,
+                                const int32_t* token, double* cents, int32_t bh, int32_t N,
+                                int32_t C, int32_t D, int64_t lcap, hipStream_t stream) {
+  const int64_t total = (int64_t)bh * C;
+  hipLaunchKernelGGL(means_kernel, dim3((uint32_t)((total + 3) / 4)), dim3(256), 0, stream,
+                     (const uint16_t*)x, start, sizes, token, cents, N, C, D, lcap, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_metric(const double* cents, const int32_t* sizes, double* G, int32_t bh,
+                                 int32_t C, int32_t D, hipStream_t stream) {
+  const int32_t tiles = D / kMt;
+  hipLaunchKernelGGL(metric_kernel, dim3((uint32_t)(bh * tiles * tiles)), dim3(256), 0, stream,
+                     cents, sizes, G, C, D, tiles);
+  return hipGetLastError();
+}
+
+KmeansWs kmeans_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t D) {
+  KmeansWs w{};
+  size_t off = 0;
+  w.g_hi_off = off; off = align_up(off + (size_t)bh * C * D * 2, 256);
+  w.g_lo_off = off; off = align_up(off + (size_t)bh * C * D * 2, 256);
+  w.cq_off = off;   off = align_up(off + (size_t)bh * C * 4, 256);
+  w.start_off = off; off = align_up(off + (size_t)bh * (C + 1) * 4, 256);
+  w.token_off = off; off = align_up(off + (size_t)bh * N * 4, 256);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_kmeans(const void* x, int32_t bh, int32_t N, int32_t D, const double* G,
+                         double* cents, int32_t C, int32_t iters, int32_t* labels,
+                         int32_t* sizes, void* ws, hipStream_t stream) {
+  const KmeansWs w = kmeans_ws_layout(bh, N, C, D);
+  char* base = static_cast<char*>(ws);
+  uint16_t* g_hi = reinterpret_cast<uint16_t*>(base + w.g_hi_off);
+  uint16_t* g_lo = reinterpret_cast<uint16_t*>(base + w.g_lo_off);
+  float* cq = reinterpret_cast<float*>(base + w.cq_off);
+  int32_t* start = reinterpret_cast<int32_t*>(base + w.start_off);
+  int32_t* token = reinterpret_cast<int32_t*>(base + w.token_off);
+  const int32_t tiles = (N + kAsTok - 1) / kAsTok;
+  for (int32_t it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL(prep_kernel, dim3((uint32_t)((int64_t)bh * C)), dim3(128), 0, stream,
+                       (const double*)cents, G, g_hi, g_lo, cq, C, D);
+    if (D == 128)
+      hipLaunchKernelGGL(assign_kernel<128>, dim3((uint32_t)((int64_t)bh * tiles)),
+                         dim3(64 * kAsWaves), 0, stream, (const uint16_t*)x, g_hi, g_lo, cq,
+                         labels, N, C, tiles);
+    else
+      hipLaunchKernelGGL(assign_kernel<64>, dim3((uint32_t)((int64_t)bh * tiles)),
+                         dim3(64 * kAsWaves), 0, stream, (const uint16_t*)x, g_hi, g_lo, cq,
+                         labels, N, C, tiles);
+    hipError_t e = launch_cluster_layout(labels, bh, N, C, 1, start, sizes, nullptr, token, stream);
+    if (e != hipSuccess) return e;
+    e = launch_cluster_means(x, start, sizes, token, cents, bh, N, C, D, N, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
+                                  int32_t N, int32_t D, int32_t C, int64_t lcap,
+                                  const int32_t* map, const int32_t* start, bool inverse,
+                                  hipStream_t stream) {
+  const int32_t chunks = D * elt_bytes / 16;
+  int32_t shift = 0;
+  while ((1 << shift) < chunks) ++shift;
+  if ((1 << shift) != chunks) return hipErrorInvalidValue;
+  constexpr int32_t kRows = 64;
+  const int64_t rows = inverse ? N : lcap;
+  const dim3 grid((uint32_t)((rows + kRows - 1) / kRows), (uint32_t)bh);
+  if (inverse)
+    hipLaunchKernelGGL(cluster_permute_kernel<1>, grid, dim3(256), 0, stream,
+                       (const uint4*)src, (uint4*)dst, map, start, N, C, lcap, shift, kRows);
+  else
+    hipLaunchKernelGGL(cluster_permute_kernel<0>, grid, dim3(256), 0, stream,
+                       (const uint4*)src, (uint4*)dst, map, start, N, C, lcap, shift, kRows);
+  return hipGetLastError();
+}
+
+}  // namespace svsa

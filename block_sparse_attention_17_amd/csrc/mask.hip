@@ -33,16 +33,19 @@ struct HeadParams {
 // ---------------------------------------------------------------------------
 constexpr int kTile = 64, kDc = 32, kLThreads = 256;
 
+// With ksizes (cluster mode) every logit of key cluster j gets + ln n_j, and
+// empty key clusters get -inf.
 __global__ void __launch_bounds__(kLThreads)
 logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
-              double* __restrict__ L, int32_t nb, int32_t D, double scale, int32_t tiles) {
+              const int32_t* __restrict__ ksizes, double* __restrict__ L, int32_t nq,
+              int32_t nk, int32_t D, double scale, int32_t tiles_q, int32_t tiles_k) {
   __shared__ double As[kDc][kTile + 1];
   __shared__ double Bs[kDc][kTile + 1];
-  const int64_t bh = blockIdx.x / (tiles * tiles);
-  const int32_t t2 = blockIdx.x % (tiles * tiles);
-  const int32_t i0 = (t2 / tiles) * kTile, j0 = (t2 % tiles) * kTile;
-  const double* qb = qbar + bh * nb * D;
-  const double* kb = kbar + bh * nb * D;
+  const int64_t bh = blockIdx.x / (tiles_q * tiles_k);
+  const int32_t t2 = blockIdx.x % (tiles_q * tiles_k);
+  const int32_t i0 = (t2 / tiles_k) * kTile, j0 = (t2 % tiles_k) * kTile;
+  const double* qb = qbar + bh * nq * D;
+  const double* kb = kbar + bh * nk * D;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   double acc[4][4];
 #pragma unroll
@@ -54,8 +57,8 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
     const int dl = threadIdx.x % kDc;
     for (int r = threadIdx.x / kDc; r < kTile; r += kLThreads / kDc) {
       const bool dok = dc + dl < D;
-      As[dl][r] = (i0 + r < nb && dok) ? qb[(int64_t)(i0 + r) * D + dc + dl] : 0.0;
-      Bs[dl][r] = (j0 + r < nb && dok) ? kb[(int64_t)(j0 + r) * D + dc + dl] : 0.0;
+      As[dl][r] = (i0 + r < nq && dok) ? qb[(int64_t)(i0 + r) * D + dc + dl] : 0.0;
+      Bs[dl][r] = (j0 + r < nk && dok) ? kb[(int64_t)(j0 + r) * D + dc + dl] : 0.0;
     }
     __syncthreads();
 #pragma unroll 4
@@ -75,11 +78,17 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int32_t i = i0 + ty + 16 * a;
-    if (i >= nb) continue;
+    if (i >= nq) continue;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int32_t j = j0 + tx + 16 * b;
-      if (j < nb) L[(bh * nb + i) * nb + j] = acc[a][b] * scale;
+      if (j >= nk) continue;
+      double v = acc[a][b] * scale;
+      if (ksizes) {
+        const int32_t n = ksizes[bh * nk + j];
+        v = n > 0 ? v + log((double)n) : -INFINITY;
+      }
+      L[(bh * nq + i) * nk + j] = v;
     }
   }
 }
@@ -126,11 +135,12 @@ struct RadixStep {
 };
 
 // mode: 0 = top-p, 1 = fixed fraction.  PER = elements per thread (nb <= 256 * PER).
+// Rows r = (bh, i) with nq rows per head; nb columns (key blocks or clusters).
 template <int PER>
 __global__ void __launch_bounds__(kSThreads)
 select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
-              int32_t* __restrict__ counts, int32_t nb, int32_t heads, int32_t words,
-              int32_t band, int32_t mode, HeadParams hp) {
+              int32_t* __restrict__ counts, int32_t nq, int32_t nb, int32_t heads,
+              int32_t words, int32_t band, int32_t mode, HeadParams hp) {
   __shared__ uint32_t hcnt[256];
   __shared__ unsigned long long hmass[256];
   __shared__ double red[kSThreads];
@@ -139,8 +149,8 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
   __shared__ RadixStep res;
 
   const int64_t r = blockIdx.x;
-  const int32_t i = (int32_t)(r % nb);
-  const int32_t h = (int32_t)((r / nb) % heads);
+  const int32_t i = (int32_t)(r % nq);
+  const int32_t h = (int32_t)((r / nq) % heads);
   const double* Lr = L + r * nb;
   const int t = threadIdx.x, lane = t & 63;
 
@@ -425,6 +435,7 @@ hipError_t launch_csr_from_bits(const uint32_t* bits, const int32_t* counts, int
 }
 
 MaskWs mask_ws_layout(int64_t rows, int32_t nb) {
+  // rows x nb logits (nb = columns: key blocks or key clusters)
   MaskWs m{};
   m.words = (nb + 31) / 32;
   size_t off = 0;
@@ -442,19 +453,28 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                              int32_t nb, int32_t head_dim, double scale, const float* top_p,
                              const float* keep_frac, int32_t band, int32_t* row_ptr,
                              int32_t* col_idx, void* ws, hipStream_t stream) {
+  return launch_cluster_mask(qbar, kbar, nullptr, bh, heads, nb, nb, head_dim, scale, top_p,
+                             keep_frac, band, row_ptr, col_idx, ws, stream);
+}
+
+hipError_t launch_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,
+                               int32_t bh, int32_t heads, int32_t nq, int32_t nb,
+                               int32_t head_dim, double scale, const float* top_p,
+                               const float* keep_frac, int32_t band, int32_t* row_ptr,
+                               int32_t* col_idx, void* ws, hipStream_t stream) {
   if (heads > kMaxHeads || nb > kMaxNb) return hipErrorInvalidValue;
-  const int64_t rows = (int64_t)bh * nb;
+  const int64_t rows = (int64_t)bh * nq;
   const MaskWs m = mask_ws_layout(rows, nb);
   char* w = static_cast<char*>(ws);
   double* L = reinterpret_cast<double*>(w + m.logits_off);
   uint32_t* bits = reinterpret_cast<uint32_t*>(w + m.bits_off);
   int32_t* counts = reinterpret_cast<int32_t*>(w + m.counts_off);
 
-  const int32_t tiles = (nb + kTile - 1) / kTile;
-  const int64_t lblocks = (int64_t)bh * tiles * tiles;
+  const int32_t tiles_q = (nq + kTile - 1) / kTile, tiles_k = (nb + kTile - 1) / kTile;
+  const int64_t lblocks = (int64_t)bh * tiles_q * tiles_k;
   if (lblocks > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(logits_kernel, dim3((uint32_t)lblocks), dim3(kLThreads), 0, stream, qbar,
-                     kbar, L, nb, head_dim, scale, tiles);
+                     kbar, ksizes, L, nq, nb, head_dim, scale, tiles_q, tiles_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -464,19 +484,19 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
   const int mode = top_p ? 0 : 1;
   const dim3 grid((uint32_t)rows), blk(kSThreads);
   if (nb <= kSThreads)
-    hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+    hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        m.words, band, mode, hp);
   else if (nb <= 2 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<2>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+    hipLaunchKernelGGL(select_kernel<2>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        m.words, band, mode, hp);
   else if (nb <= 4 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<4>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+    hipLaunchKernelGGL(select_kernel<4>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        m.words, band, mode, hp);
   else if (nb <= 8 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<8>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+    hipLaunchKernelGGL(select_kernel<8>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        m.words, band, mode, hp);
   else
-    hipLaunchKernelGGL(select_kernel<16>, grid, blk, 0, stream, L, bits, counts, nb, heads,
+    hipLaunchKernelGGL(select_kernel<16>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        m.words, band, mode, hp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -44,6 +44,14 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                              const float* keep_frac, int32_t band, int32_t* row_ptr,
                              int32_t* col_idx, void* ws, hipStream_t stream);
 
+// Rectangular variant: nq query rows per head against nb key clusters, with
+// + ln n_j on every logit of key cluster j when ksizes is given.
+hipError_t launch_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,
+                               int32_t bh, int32_t heads, int32_t nq, int32_t nb,
+                               int32_t head_dim, double scale, const float* top_p,
+                               const float* keep_frac, int32_t band, int32_t* row_ptr,
+                               int32_t* col_idx, void* ws, hipStream_t stream);
+
 // Row bitmaps (words uint32 per row) + row counts -> CSR (row_ptr, col_idx).
 hipError_t launch_csr_from_bits(const uint32_t* bits, const int32_t* counts, int32_t* row_ptr,
                                 int32_t* col_idx, int64_t rows, int32_t words,
@@ -68,13 +76,43 @@ struct AttnWs {
   int32_t group_size;  // query sub-blocks per group (256 query rows per group)
   int32_t sub;         // sub-block size seen by the attention kernels (64 or 32)
   int32_t ratio;       // sub-blocks per block (Bk / sub)
-  int32_t nbs;         // sub-blocks of the sequence, ceil(N / sub)
+  int32_t nbs;         // key sub-blocks per head (also the list stride)
+  int32_t nbs_q;       // query sub-blocks per head
 };
 AttnWs attn_ws_layout(int32_t bh, const Geom& g);
+AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t npad_k);
+hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void* out,
+                               int32_t bh, int32_t head_dim, int32_t sub, int64_t npad_q,
+                               int64_t npad_k, const int32_t* q_start, const int32_t* q_size,
+                               int32_t nq, const int32_t* k_start, const int32_t* k_size,
+                               int32_t nk, float scale, const int32_t* row_ptr,
+                               const int32_t* col_idx, void* ws, hipStream_t stream);
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
                                     hipStream_t stream);
+
+// Clustering (variable-size blocks).
+int64_t cluster_lcap(int32_t N, int32_t C, int32_t align);   // padded layout capacity
+struct KmeansWs {
+  size_t g_hi_off, g_lo_off, cq_off, start_off, token_off, total;
+};
+KmeansWs kmeans_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t D);
+hipError_t launch_kmeans(const void* x, int32_t bh, int32_t N, int32_t D, const double* G,
+                         double* cents, int32_t C, int32_t iters, int32_t* labels,
+                         int32_t* sizes, void* ws, hipStream_t stream);
+hipError_t launch_cluster_metric(const double* cents, const int32_t* sizes, double* G, int32_t bh,
+                                 int32_t C, int32_t D, hipStream_t stream);
+hipError_t launch_cluster_layout(const int32_t* labels, int32_t bh, int32_t N, int32_t C,
+                                 int32_t align, int32_t* start, int32_t* sizes, int32_t* slot,
+                                 int32_t* token, hipStream_t stream);
+hipError_t launch_cluster_means(const void* x, const int32_t* start, const int32_t* sizes,
+                                const int32_t* token, double* cents, int32_t bh, int32_t N,
+                                int32_t C, int32_t D, int64_t lcap, hipStream_t stream);
+hipError_t launch_cluster_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
+                                  int32_t N, int32_t D, int32_t C, int64_t lcap,
+                                  const int32_t* map, const int32_t* start, bool inverse,
+                                  hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

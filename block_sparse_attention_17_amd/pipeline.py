@@ -73,3 +73,112 @@ class BlockSparseAttention:
         self.build_mask(top_p, keep_frac, band_width, stream)
         self.attend(stream=stream)
         return self.permute_out(stream)
+
+
+class ClusteredAttention:
+    """Attention over variable-size blocks from query / key clustering
+    ([iCATS] Sec. 4.1; [SVOO] QK co-clustering), chaining the cluster entry
+    points: query k-means under the key clusters' metric (plain feature space
+    on the first call) -> key k-means under the updated query clusters'
+    metric -> padded cluster layouts -> permuted Q, K, V -> cluster mask ->
+    cluster attention -> token order.  Centroids persist between calls (warm
+    start across denoising steps); initial centroids are the caller's."""
+
+    def __init__(self, batch, heads, head_dim, n, q_clusters, k_clusters, align=64,
+                 q_iters=2, k_iters=2, device="cuda"):
+        self.batch, self.heads, self.head_dim, self.n = batch, heads, head_dim, n
+        self.nq, self.nk, self.align = q_clusters, k_clusters, align
+        self.q_iters, self.k_iters = q_iters, k_iters
+        dev = torch.device(device)
+        f64 = dict(dtype=torch.float64, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        bh = (batch, heads)
+        self.qcent = torch.empty(bh + (q_clusters, head_dim), **f64)
+        self.kcent = torch.empty(bh + (k_clusters, head_dim), **f64)
+        self.metric = torch.empty(bh + (head_dim, head_dim), **f64)
+        self.qlab = torch.empty(bh + (n,), **i32)
+        self.klab = torch.empty(bh + (n,), **i32)
+        self.qsize = torch.zeros(bh + (q_clusters,), **i32)
+        self.ksize = torch.zeros(bh + (k_clusters,), **i32)
+        self.cap_q = B.svsa_cluster_capacity(n, q_clusters, align)
+        self.cap_k = B.svsa_cluster_capacity(n, k_clusters, align)
+        self.q_start = torch.empty(bh + (q_clusters + 1,), **i32)
+        self.k_start = torch.empty(bh + (k_clusters + 1,), **i32)
+        self.q_slot = torch.empty(bh + (n,), **i32)
+        self.k_slot = torch.empty(bh + (n,), **i32)
+        self.q_token = torch.empty(bh + (self.cap_q,), **i32)
+        self.k_token = torch.empty(bh + (self.cap_k,), **i32)
+        self.qp = torch.empty(bh + (self.cap_q, head_dim), **bf)
+        self.kp = torch.empty(bh + (self.cap_k, head_dim), **bf)
+        self.vp = torch.empty(bh + (self.cap_k, head_dim), **bf)
+        self.op = torch.empty(bh + (self.cap_q, head_dim), **bf)
+        self.out = torch.empty(bh + (n, head_dim), **bf)
+        rows = batch * heads * q_clusters
+        self.row_ptr = torch.empty(rows + 1, **i32)
+        self.col_idx = torch.empty(rows * k_clusters, **i32)
+        km = max(B.svsa_kmeans_workspace_bytes(batch, heads, n, q_clusters, head_dim),
+                 B.svsa_kmeans_workspace_bytes(batch, heads, n, k_clusters, head_dim))
+        self.km_ws = torch.empty(km, dtype=torch.uint8, device=dev)
+        self.mask_ws = torch.empty(
+            B.svsa_cluster_mask_workspace_bytes(batch, heads, q_clusters, k_clusters),
+            dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(
+            B.svsa_cluster_attn_workspace_bytes(batch, heads, n, q_clusters, n, k_clusters, align),
+            dtype=torch.uint8, device=dev)
+        self.warm = False
+
+    def set_centroids(self, qcent, kcent):
+        """Initial centroids (float64 [B, Hh, C, D]); the next call clusters the
+        queries in plain feature space."""
+        self.qcent.copy_(qcent)
+        self.kcent.copy_(kcent)
+        self.warm = False
+
+    def cluster(self, q, k, stream=None):
+        if self.warm:
+            B.svsa_cluster_metric(self.kcent, self.ksize, self.metric, stream=stream)
+        B.svsa_kmeans(q, self.qcent, self.qlab, self.qsize, self.km_ws, self.q_iters,
+                      metric=self.metric if self.warm else None, stream=stream)
+        B.svsa_cluster_metric(self.qcent, self.qsize, self.metric, stream=stream)
+        B.svsa_kmeans(k, self.kcent, self.klab, self.ksize, self.km_ws, self.k_iters,
+                      metric=self.metric, stream=stream)
+        self.warm = True
+
+    def layout(self, q, k, v, stream=None):
+        a = self.align
+        B.svsa_cluster_layout(self.qlab, self.nq, a, self.q_start, self.qsize, self.q_slot,
+                              self.q_token, stream=stream)
+        B.svsa_cluster_layout(self.klab, self.nk, a, self.k_start, self.ksize, self.k_slot,
+                              self.k_token, stream=stream)
+        B.svsa_cluster_permute(q, self.qp, self.n, self.nq, a, self.q_token, self.q_start,
+                               stream=stream)
+        B.svsa_cluster_permute(k, self.kp, self.n, self.nk, a, self.k_token, self.k_start,
+                               stream=stream)
+        B.svsa_cluster_permute(v, self.vp, self.n, self.nk, a, self.k_token, self.k_start,
+                               stream=stream)
+
+    def build_mask(self, top_p=None, keep_frac=None, stream=None):
+        B.svsa_cluster_mask(self.qcent, self.kcent, self.ksize, 1.0 / sqrt(self.head_dim),
+                            self.row_ptr, self.col_idx, self.mask_ws, top_p=top_p,
+                            keep_frac=keep_frac, stream=stream)
+
+    def attend(self, row_ptr=None, col_idx=None, stream=None):
+        B.svsa_cluster_attn(self.qp, self.kp, self.vp, self.op, self.n, self.q_start, self.qsize,
+                            self.n, self.k_start, self.ksize, self.align,
+                            1.0 / sqrt(self.head_dim),
+                            self.row_ptr if row_ptr is None else row_ptr,
+                            self.col_idx if col_idx is None else col_idx, self.attn_ws,
+                            stream=stream)
+
+    def permute_out(self, stream=None):
+        B.svsa_cluster_permute(self.op, self.out, self.n, self.nq, self.align, self.q_slot,
+                               self.q_start, inverse=True, stream=stream)
+        return self.out
+
+    def __call__(self, q, k, v, top_p=None, keep_frac=None, stream=None):
+        self.cluster(q, k, stream)
+        self.layout(q, k, v, stream)
+        self.build_mask(top_p, keep_frac, stream)
+        self.attend(stream=stream)
+        return self.permute_out(stream)

@@ -228,6 +228,162 @@ SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Variable-size blocks: query / key clustering ([iCATS] Sec. 3.1 and 4.1,
+ * interaction-aware clustering; [SVOO] online bidirectional QK
+ * co-clustering).  The pages describe the idea; this library's reading:
+ * replacing a token x by a centroid c moves its logits against the other
+ * side's tokens y by (x - c).y, with summed square (x - c)^T G (x - c),
+ * G = sum_y y y^T, approximated from the other side's clusters as
+ * G = sum_j n_j c_j c_j^T (svsa_cluster_metric).  Clustering is Lloyd's
+ * k-means under that fixed metric (svsa_kmeans).  Clusters are then laid out
+ * contiguously, each padded to a multiple of the block alignment
+ * (svsa_cluster_layout, svsa_cluster_permute), scored and selected per
+ * cluster pair (svsa_cluster_mask) and attended (svsa_cluster_attn).
+ * ------------------------------------------------------------------------ */
+
+/* Workspace (device bytes) for svsa_kmeans; 0 if the sizes are invalid. */
+SVSA_API size_t svsa_kmeans_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                            int32_t clusters, int32_t head_dim);
+
+/*
+ * `iters` Lloyd iterations per (batch, head).  Each iteration assigns every
+ * token to the centroid c of least (x - c)^T G (x - c) (ties: lowest index)
+ * and then moves every non-empty centroid to the mean of its members (an
+ * empty cluster keeps its centroid).  On return `labels` is the last
+ * assignment, `sizes` its cluster sizes and `centroids` the means of those
+ * labels.  The distance comparison drops the common x^T G x term and is
+ * evaluated as c^T G c - 2 x . (G c) with bf16 MFMA on x and on a two-term
+ * bf16 split of G c (fp32 accumulation): choices between centroids whose
+ * distances differ by less than about 1e-4 of |x| |G c| may differ from an
+ * exact evaluation.  Means are float64 sums in token order.
+ *
+ * x: bf16 [batch, heads, n, head_dim] (natural token order), head_dim 64 or 128.
+ * metric: float64 [batch, heads, head_dim, head_dim] symmetric positive
+ *   semi-definite, or NULL for G = I (plain feature-space k-means).
+ * centroids: float64 [batch, heads, clusters, head_dim], in: the initial
+ *   centroids (e.g. seeded token picks, or the previous step's), out: final.
+ * labels: int32 [batch, heads, n] (out); sizes: int32 [batch, heads, clusters] (out).
+ * Limits: clusters <= 4096, batch*heads <= 65535, iters >= 1.
+ */
+SVSA_API int svsa_kmeans(const void* x, int32_t batch, int32_t heads, int32_t n,
+                         int32_t head_dim, const double* metric, double* centroids,
+                         int32_t clusters, int32_t iters, int32_t* labels, int32_t* sizes,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace (device bytes) for svsa_cluster_means; 0 if the sizes are invalid. */
+SVSA_API size_t svsa_cluster_means_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                                   int32_t clusters);
+
+/*
+ * Cluster summaries from given labels (the block means of variable-size
+ * blocks): centroids[b,h,c] = float64 mean of the tokens labelled c (summed in
+ * token order), sizes[b,h,c] their count; centroids of empty clusters are
+ * left unchanged.  x: bf16 [batch, heads, n, head_dim] (64 or 128); labels:
+ * int32 [batch, heads, n] (labels outside [0, clusters) are ignored).
+ */
+SVSA_API int svsa_cluster_means(const void* x, const int32_t* labels, int32_t batch,
+                                int32_t heads, int32_t n, int32_t head_dim, int32_t clusters,
+                                double* centroids, int32_t* sizes, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * metric[b,h] = sum_c sizes[b,h,c] * centroids[b,h,c] centroids[b,h,c]^T
+ * (float64 [batch, heads, head_dim, head_dim]): the quadratic form that one
+ * side's clusters induce on the other side's tokens.  head_dim a multiple of
+ * 16, at most 256.
+ */
+SVSA_API int svsa_cluster_metric(const double* centroids, const int32_t* sizes, int32_t batch,
+                                 int32_t heads, int32_t clusters, int32_t head_dim,
+                                 double* metric, void* stream);
+
+/*
+ * Rows of the padded cluster layout: n + clusters * (align - 1), rounded up to
+ * align (every layout fits).  align: a power of two <= 1024.  0 if invalid.
+ */
+SVSA_API int64_t svsa_cluster_capacity(int32_t n, int32_t clusters, int32_t align);
+
+/*
+ * Padded cluster layout per (batch, head): cluster c owns the slots start[c]
+ * .. start[c] + sizes[c] - 1, its members in ascending token order;
+ * start[0] = 0, start[c+1] = start[c] + align * ceil(sizes[c] / align), so
+ * start[clusters] is the padded length L (<= svsa_cluster_capacity).
+ * labels: int32 [batch, heads, n] in [0, clusters) (others are not placed:
+ *   their slot is -1).
+ * start: int32 [batch, heads, clusters + 1]; sizes: int32 [batch, heads, clusters];
+ * slot: int32 [batch, heads, n] (slot of each token; may be NULL);
+ * token: int32 [batch, heads, capacity] (token in each slot s < L, -1 for padding).
+ */
+SVSA_API int svsa_cluster_layout(const int32_t* labels, int32_t batch, int32_t heads, int32_t n,
+                                 int32_t clusters, int32_t align, int32_t* start,
+                                 int32_t* sizes, int32_t* slot, int32_t* token, void* stream);
+
+/*
+ * Rows into the cluster layout (inverse = 0: dst[s] = src[token[s]] for the
+ * slots s < start[clusters], zero for padding; dst is [batch, heads,
+ * capacity, head_dim]) or back to token order (inverse = 1: dst[t] =
+ * src[slot[t]], zero for tokens without a slot; dst is [batch, heads, n,
+ * head_dim]).  map = token (forward) or slot (inverse) from
+ * svsa_cluster_layout with the same clusters and align.
+ */
+SVSA_API int svsa_cluster_permute(const void* src, void* dst, int32_t dtype, int32_t batch,
+                                  int32_t heads, int32_t n, int32_t head_dim, int32_t clusters,
+                                  int32_t align, const int32_t* map, const int32_t* start,
+                                  int32_t inverse, void* stream);
+
+/* Workspace (device bytes) for svsa_cluster_mask; 0 if the sizes are invalid. */
+SVSA_API size_t svsa_cluster_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nq,
+                                                  int32_t nk);
+
+/*
+ * Cluster-level mask: per (batch, head, query cluster i) the key clusters
+ * kept by the rule of svsa_block_mask (top-p or fixed fraction, same
+ * tie-break, float64 throughout) applied to the row softmax over key
+ * clusters of  softmax_scale * <qbar_i, kbar_j> + ln ksizes_j  (the mass of
+ * ksizes_j keys that all equal kbar_j; empty key clusters score 0).  No
+ * diagonal band (query and key clusters are different partitions).
+ * qbar: float64 [batch, heads, nq, D] (query cluster means), kbar: float64
+ * [batch, heads, nk, D], ksizes: int32 [batch, heads, nk] (device).
+ * row_ptr: int32 [batch*heads*nq + 1]; col_idx capacity >= batch*heads*nq*nk.
+ * Limits: nq, nk <= 4096, heads <= 256.
+ */
+SVSA_API int svsa_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,
+                               int32_t batch, int32_t heads, int32_t nq, int32_t nk,
+                               int32_t head_dim, double softmax_scale, const float* top_p,
+                               const float* keep_frac, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t col_capacity, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+/* Workspace (device bytes) for svsa_cluster_attn; 0 if the sizes are invalid. */
+SVSA_API size_t svsa_cluster_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q,
+                                                  int32_t nq, int32_t n_k, int32_t nk,
+                                                  int32_t align);
+
+/*
+ * Attention over variable-size blocks: every query token of query cluster i
+ * attends, in one softmax, to every key token of the key clusters its CSR row
+ * keeps (the blockwise accumulation of [PSA] App. B, Alg. 2, with blocks of
+ * any size).  Inputs are in the padded cluster layouts of svsa_cluster_layout
+ * with the same align (32 or 64: every cluster starts on a sub-block of that
+ * many rows; padded key rows are masked).
+ * q: bf16 [batch, heads, cap_q, D], k, v: bf16 [batch, heads, cap_k, D] with
+ *   cap_q = svsa_cluster_capacity(n_q, nq, align), cap_k likewise.
+ * out: bf16 [batch, heads, cap_q, D]; rows of query tokens are written, padded
+ *   rows are unspecified; a query cluster with an empty row gets zeros.
+ * q_start / q_size: int32 [batch, heads, nq + 1] / [batch, heads, nq] (device),
+ *   k_start / k_size the same for the key clusters.
+ * row_ptr: int32 [batch*heads*nq + 1] over rows (b, h, i); col_idx: key
+ *   cluster indices (out-of-range entries are ignored).
+ * Limits: head_dim 64 or 128; cap_k / align <= 8192; cap * D * 2 < 2^31.
+ */
+SVSA_API int svsa_cluster_attn(const void* q, const void* k, const void* v, void* out,
+                               int32_t batch, int32_t heads, int32_t head_dim, int32_t n_q,
+                               int32_t nq, const int32_t* q_start, const int32_t* q_size,
+                               int32_t n_k, int32_t nk, const int32_t* k_start,
+                               const int32_t* k_size, int32_t align, float softmax_scale,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /*
  * SNR-guided top-p schedule ([iCATS] Sec. 4.2 "SNR-Guided Sparsity" and
  * App. A; the per-model pmin and tau of App. B).  Host-only: no GPU call,

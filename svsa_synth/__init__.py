@@ -7,7 +7,8 @@ selection or attention.
 """
 from .configs import CONFIGS, Config, get_config
 from .gen import (Inputs, make_inputs, bf16_bits_to_f32, f32_to_bf16_bits, stripe_params,
-                  flow_sigmas)
+                  flow_sigmas, cluster_seeds, cluster_labels)
 
 __all__ = ["CONFIGS", "Config", "get_config", "Inputs", "make_inputs",
-           "bf16_bits_to_f32", "f32_to_bf16_bits", "stripe_params", "flow_sigmas"]
+           "bf16_bits_to_f32", "f32_to_bf16_bits", "stripe_params", "flow_sigmas",
+           "cluster_seeds", "cluster_labels"]

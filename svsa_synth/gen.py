@@ -185,3 +185,29 @@ def flow_sigmas(steps, shift=5.0):
     this stands in for the denoising loop of a rectified-flow video model)."""
     t = 1.0 - np.arange(steps, dtype=np.float64) / steps
     return shift * t / (1.0 + (shift - 1.0) * t)
+
+
+_CLUSTER_ID = 300
+
+
+def cluster_seeds(n, clusters, batch, heads, seed=0, stream=0):
+    """Seeded initial centroid picks: int64 [batch, heads, clusters] distinct
+    token indices per (b, h), ascending (k-means starts from these tokens)."""
+    out = np.empty((batch, heads, clusters), np.int64)
+    for b in range(batch):
+        for h in range(heads):
+            g = _rng(seed, _CLUSTER_ID, stream, b, h)
+            out[b, h] = np.sort(g.choice(n, size=clusters, replace=False))
+    return out
+
+
+def cluster_labels(n, clusters, batch, heads, seed=0, stream=1, empty=0):
+    """Seeded labels int32 [batch, heads, n], uniform over the clusters except
+    `empty` seeded clusters per (b, h) that receive no token."""
+    out = np.empty((batch, heads, n), np.int32)
+    for b in range(batch):
+        for h in range(heads):
+            g = _rng(seed, _CLUSTER_ID, stream, b, h)
+            used = np.sort(g.choice(clusters, size=clusters - empty, replace=False))
+            out[b, h] = used[g.integers(0, used.size, size=n)]
+    return out
