@@ -47,6 +47,14 @@ def parse():
     ap.add_argument("--snr-steps", type=int, default=50)
     ap.add_argument("--snr-first", type=int, default=10, help="first sparse denoising step")
     ap.add_argument("--snr-shift", type=float, default=5.0, help="flow-matching time shift")
+    ap.add_argument("--cluster", action="store_true",
+                    help="variable-size blocks: query/key k-means, cluster mask and attention")
+    ap.add_argument("--q-clusters", type=int, default=400)
+    ap.add_argument("--k-clusters", type=int, default=1000)
+    ap.add_argument("--align", type=int, default=64, choices=[32, 64])
+    ap.add_argument("--iters", type=int, default=2, help="Lloyd iterations per side per step")
+    ap.add_argument("--cold-iters", type=int, default=10,
+                    help="Lloyd iterations of the first (feature-space) clustering")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -140,6 +148,104 @@ def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
     }
 
 
+def cluster_bench(args, cfg, m, inp, torch):
+    """Variable-size blocks: one step = query k-means under the key clusters'
+    metric, key k-means under the query clusters' metric, padded layouts and
+    permutation, cluster mask, cluster attention, token order.  Centroids are
+    warm across steps; the first (untimed) call clusters from seeded token
+    picks in feature space."""
+    from svsa_synth import cluster_seeds
+    B_, H, N, D = cfg.batch, cfg.heads, cfg.N, cfg.head_dim
+    nq, nk = args.q_clusters, args.k_clusters
+    top_p = args.top_p if args.top_p is not None else cfg.top_p[0]
+    tp = np.full(H, top_p, np.float32)
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    ca = m.ClusteredAttention(B_, H, D, N, nq, nk, align=args.align, q_iters=args.cold_iters,
+                              k_iters=args.cold_iters)
+    sq = cluster_seeds(N, nq, B_, H, seed=args.seed, stream=1)
+    sk = cluster_seeds(N, nk, B_, H, seed=args.seed, stream=2)
+    bh = np.arange(B_)[:, None, None], np.arange(H)[None, :, None]
+    widen = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ca.set_centroids(torch.from_numpy(widen(inp.q[bh[0], bh[1], sq])).cuda(),
+                     torch.from_numpy(widen(inp.k[bh[0], bh[1], sk])).cuda())
+    ca(q, k, v, top_p=tp)
+    torch.cuda.synchronize()
+    ca.q_iters = ca.k_iters = args.iters
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    names = ["cluster", "layout_permute", "mask", "attention", "permute_out"]
+
+    def step(rec=None):
+        mk = [ev() for _ in range(6)] if rec is not None else None
+        if mk: mk[0].record(stream)
+        ca.cluster(q, k)
+        if mk: mk[1].record(stream)
+        ca.layout(q, k, v)
+        if mk: mk[2].record(stream)
+        ca.build_mask(top_p=tp)
+        if mk: mk[3].record(stream)
+        ca.attend()
+        if mk: mk[4].record(stream)
+        ca.permute_out()
+        if mk:
+            mk[5].record(stream)
+            rec.append(mk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stage_ms = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]))
+                for i, n in enumerate(names)}
+    step_ms = float(np.mean([r[0].elapsed_time(r[5]) for r in recs]))
+    # kept FLOPs over real tokens, and the rows the kernel runs (sub-block padded)
+    rp = ca.row_ptr.cpu().numpy().astype(np.int64)
+    ci = ca.col_idx[: int(rp[-1])].cpu().numpy()
+    qs = ca.qsize.cpu().numpy().reshape(-1, nq)
+    ks = ca.ksize.cpu().numpy().reshape(-1, nk)
+    a = args.align
+    row_h = np.repeat(np.arange(B_ * H * nq) // nq, np.diff(rp))
+    row_i = np.repeat(np.arange(B_ * H * nq) % nq, np.diff(rp))
+    m_i, n_j = qs[row_h, row_i], ks[row_h, ci]
+    flops = 4 * D * int(np.sum(m_i.astype(np.int64) * n_j))
+    pad = lambda x: -(-x.astype(np.int64) // a) * a
+    padded = 4 * D * int(np.sum(pad(m_i) * pad(n_j)))
+    dense = 4 * N * N * D * H * B_
+    attn_tf = flops / (stage_ms["attention"] * 1e-3) / 1e12
+    return {
+        "metric": "kept-block attention TFLOP/s and % bf16 MFMA peak; speedup vs dense, 1 GPU",
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": step_ms, "wall_ms_per_step": wall_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + shared 3D sinusoidal positional term, bf16)",
+        "config": {"workload": (f"{cfg.name} variable-size blocks: {nq} query / {nk} key clusters "
+                                f"(k-means under the interaction metric, {args.iters} Lloyd "
+                                f"iterations per side per step, warm), align {a}, {H} heads, "
+                                f"head_dim {D}, top-p {top_p}"),
+                   "global_batch": B_, "seq_len": N, "parallelism": "single GPU"},
+        "kept_tflop_per_step": flops / 1e12,
+        "executed_tflop_per_step": padded / 1e12,
+        "dense_tflop": dense / 1e12,
+        "kept_fraction": flops / dense,
+        "stage_ms": stage_ms,
+        "attention_tflops": attn_tf,
+        "attention_frac_peak": attn_tf / BF16_PEAK_TFLOPS,
+        "attention_executed_tflops": padded / (stage_ms["attention"] * 1e-3) / 1e12,
+        "roofline": {"kernel": "svsa_cluster_attn (union_kernel + queue_kernel + vt_kernel + "
+                               "attn_kernel)",
+                     "bound": "mfma", "achieved": attn_tf, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tf / BF16_PEAK_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +264,9 @@ def main():
     inp = make_inputs(cfg, seed=args.seed)
     gen_s = time.perf_counter() - t0
     print(f"[bench] inputs {cfg.name} generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    if args.cluster:
+        print(json.dumps(cluster_bench(args, cfg, m, inp, torch)))
+        return
 
     def dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
