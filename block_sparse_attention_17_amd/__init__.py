@@ -4,7 +4,8 @@ Python face of ``libsvsa.so`` (HIP kernels behind a C ABI, ``include/svsa.h``).
 Importing fails loudly when the library has not been built.
 """
 from .binding import (svsa_cluster_attn, svsa_cluster_attn_workspace_bytes,
-                      svsa_cluster_capacity, svsa_cluster_layout, svsa_cluster_mask,
+                      svsa_cluster_capacity, svsa_cluster_layout,
+                      svsa_cluster_layout_workspace_bytes, svsa_cluster_mask,
                       svsa_cluster_means, svsa_cluster_means_workspace_bytes,
                       svsa_cluster_mask_workspace_bytes, svsa_cluster_metric, svsa_cluster_permute,
                       svsa_kmeans, svsa_kmeans_workspace_bytes)
@@ -24,4 +25,5 @@ __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "librar
            "svsa_cluster_attn_workspace_bytes", "svsa_cluster_capacity", "svsa_cluster_layout",
            "svsa_cluster_mask", "svsa_cluster_mask_workspace_bytes", "svsa_cluster_metric",
            "svsa_cluster_permute", "svsa_kmeans", "svsa_kmeans_workspace_bytes",
-           "svsa_cluster_means", "svsa_cluster_means_workspace_bytes"]
+           "svsa_cluster_means", "svsa_cluster_means_workspace_bytes",
+           "svsa_cluster_layout_workspace_bytes"]

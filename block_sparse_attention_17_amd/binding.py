@@ -117,7 +117,9 @@ def _load():
         "svsa_cluster_means": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz,
                                               vp]),
         "svsa_cluster_capacity": (i64, [i32, i32, i32]),
-        "svsa_cluster_layout": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "svsa_cluster_layout_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "svsa_cluster_layout": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                               sz, vp]),
         "svsa_cluster_permute": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
                                                 i32, vp]),
         "svsa_cluster_mask_workspace_bytes": (sz, [i32, i32, i32, i32]),
@@ -143,7 +145,8 @@ EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
             "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_snr_top_p",
             "svsa_kmeans_workspace_bytes", "svsa_kmeans", "svsa_cluster_metric",
             "svsa_cluster_means_workspace_bytes", "svsa_cluster_means",
-            "svsa_cluster_capacity", "svsa_cluster_layout", "svsa_cluster_permute",
+            "svsa_cluster_capacity", "svsa_cluster_layout_workspace_bytes",
+            "svsa_cluster_layout", "svsa_cluster_permute",
             "svsa_cluster_mask_workspace_bytes", "svsa_cluster_mask",
             "svsa_cluster_attn_workspace_bytes", "svsa_cluster_attn",
             "svsa_status_string", "svsa_version")
@@ -350,14 +353,20 @@ def svsa_cluster_capacity(n, clusters, align):
     return int(_lib.svsa_cluster_capacity(n, clusters, align))
 
 
-def svsa_cluster_layout(labels, clusters, align, start, sizes, slot, token, stream=None):
+def svsa_cluster_layout_workspace_bytes(batch, heads, n, clusters):
+    return int(_lib.svsa_cluster_layout_workspace_bytes(batch, heads, n, clusters))
+
+
+def svsa_cluster_layout(labels, clusters, align, start, sizes, slot, token, workspace,
+                        stream=None):
     import torch
     B_, Hh, N = labels.shape
     i32 = (torch.int32,)
     _check("svsa_cluster_layout", _lib.svsa_cluster_layout(
         _ptr(labels, "labels", i32), B_, Hh, N, int(clusters), int(align),
         _ptr(start, "start", i32), _ptr(sizes, "sizes", i32), _ptr(slot, "slot", i32),
-        _ptr(token, "token", i32), _stream(stream)))
+        _ptr(token, "token", i32), _ptr(workspace, "workspace", (torch.uint8,)),
+        workspace.numel(), _stream(stream)))
     return start, sizes, slot, token
 
 

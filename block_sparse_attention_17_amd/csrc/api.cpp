@@ -140,7 +140,7 @@ int svsa_cluster_means(const void* x, const int32_t* labels, int32_t batch, int3
   int32_t* token = reinterpret_cast<int32_t*>(base + w.token_off);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = svsa::launch_cluster_layout(labels, bh, n, clusters, 1, start, sizes, nullptr,
-                                             token, st);
+                                             token, base + w.layout_off, st);
   if (e == hipSuccess)
     e = svsa::launch_cluster_means(x, start, sizes, token, centroids, bh, n, clusters, head_dim,
                                    n, st);
@@ -165,16 +165,25 @@ int64_t svsa_cluster_capacity(int32_t n, int32_t clusters, int32_t align) {
   return svsa::cluster_lcap(n, clusters, align);
 }
 
+size_t svsa_cluster_layout_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                           int32_t clusters) {
+  if (!cluster_sizes_ok(batch, heads, n, clusters, 1)) return 0;
+  return svsa::layout_ws_bytes(batch * heads, n, clusters);
+}
+
 int svsa_cluster_layout(const int32_t* labels, int32_t batch, int32_t heads, int32_t n,
                         int32_t clusters, int32_t align, int32_t* start, int32_t* sizes,
-                        int32_t* slot, int32_t* token, void* stream) {
+                        int32_t* slot, int32_t* token, void* workspace, size_t ws_bytes,
+                        void* stream) {
   if (!labels || !start || !sizes || !token || !cluster_sizes_ok(batch, heads, n, clusters, 1))
     return SVSA_E_INVALID;
   const int64_t lcap = svsa_cluster_capacity(n, clusters, align);
   if (lcap == 0) return SVSA_E_INVALID;
   if ((int64_t)batch * heads * lcap >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
+  if (!workspace || ws_bytes < svsa::layout_ws_bytes(batch * heads, n, clusters))
+    return SVSA_E_WORKSPACE;
   return from_hip(svsa::launch_cluster_layout(labels, batch * heads, n, clusters, align, start,
-                                              sizes, slot, token,
+                                              sizes, slot, token, workspace,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -16,8 +16,10 @@
 // lowest index), then move every non-empty centroid to its members' mean.
 //
 // Kernels:
-//   layout_kernel  one workgroup per (b, h): cluster sizes, padded starts,
-//                  a stable counting sort (members in ascending token order)
+//   hist_kernel, offsets_kernel, place_kernel
+//                  the layout: per-tile cluster counts, padded starts and tile
+//                  offsets, then a stable counting sort inside each tile
+//                  (members in ascending token order)
 //   means_kernel   one wavefront per cluster: float64 sum of the members in
 //                  that order, mean written only for non-empty clusters
 //   metric_kernel  G = sum_c n_c c c^T, 16 x 16 tile of G per workgroup
@@ -43,37 +45,51 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------------------
-// layout_kernel: start[c] (padded to `align`), sizes[c], slot[t] and
-// token[s].  Labels outside [0, C) are not placed (slot -1).
+// Layout in three passes over tiles of kLayTile tokens (many workgroups per
+// head): tile histograms, then per (b, h) the padded cluster starts and each
+// tile's first slot per cluster, then a stable placement inside every tile.
+// Labels outside [0, C) are not placed (slot -1).
 // ---------------------------------------------------------------------------
-constexpr int kLayThreads = 256;
+constexpr int kLayThreads = 256, kLayTile = 2048;
 
 __global__ void __launch_bounds__(kLayThreads)
-layout_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t align,
-              int32_t* __restrict__ start, int32_t* __restrict__ sizes,
-              int32_t* __restrict__ slot, int32_t* __restrict__ token, int64_t lcap) {
-  extern __shared__ int32_t sh[];
-  int32_t* cnt = sh;            // [C]
-  int32_t* cursor = sh + C;     // [C]
-  __shared__ int32_t lab_s[kLayThreads];
-  __shared__ int32_t part[kLayThreads];
-  const int64_t bh = blockIdx.x;
-  const int32_t tid = threadIdx.x;
-  const int32_t* lab = labels + bh * N;
-
-  for (int32_t c = tid; c < C; c += kLayThreads) cnt[c] = 0;
+hist_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t tiles,
+            int32_t* __restrict__ tcount) {
+  extern __shared__ int32_t cnt[];  // [C]
+  const int64_t bh = blockIdx.y;
+  const int32_t tile = blockIdx.x;
+  for (int32_t c = threadIdx.x; c < C; c += kLayThreads) cnt[c] = 0;
   __syncthreads();
-  for (int32_t t = tid; t < N; t += kLayThreads) {
+  const int32_t* lab = labels + bh * N;
+  const int32_t t1 = min(N, (tile + 1) * kLayTile);
+  for (int32_t t = tile * kLayTile + threadIdx.x; t < t1; t += kLayThreads) {
     const int32_t c = lab[t];
     if (c >= 0 && c < C) atomicAdd(&cnt[c], 1);
   }
   __syncthreads();
+  int32_t* out = tcount + (bh * tiles + tile) * (int64_t)C;
+  for (int32_t c = threadIdx.x; c < C; c += kLayThreads) out[c] = cnt[c];
+}
 
-  // exclusive scan of the padded sizes: each thread owns a contiguous range
+// one workgroup per (b, h): sizes, padded starts, tile offsets (in place of
+// the tile counts) and -1 in every slot of the padded length
+__global__ void __launch_bounds__(kLayThreads)
+offsets_kernel(int32_t C, int32_t align, int32_t tiles, int32_t* __restrict__ tcount,
+               int32_t* __restrict__ start, int32_t* __restrict__ sizes,
+               int32_t* __restrict__ token, int64_t lcap) {
+  __shared__ int32_t part[kLayThreads];
+  const int64_t bh = blockIdx.x;
+  const int32_t tid = threadIdx.x;
+  int32_t* tc = tcount + bh * tiles * (int64_t)C;
   const int32_t per = (C + kLayThreads - 1) / kLayThreads;
   const int32_t c0 = tid * per, c1 = min(C, c0 + per);
   int32_t local = 0;
-  for (int32_t c = c0; c < c1; ++c) local += (cnt[c] + align - 1) / align * align;
+  for (int32_t c = c0; c < c1; ++c) {
+    int32_t n = 0;
+    for (int32_t t = 0; t < tiles; ++t) n += tc[(int64_t)t * C + c];
+    sizes[bh * C + c] = n;
+    local += (n + align - 1) / align * align;
+  }
   part[tid] = local;
   __syncthreads();
   for (int32_t off = 1; off < kLayThreads; off <<= 1) {
@@ -85,23 +101,41 @@ layout_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t 
   int32_t run = part[tid] - local;
   int32_t* st = start + bh * (int64_t)(C + 1);
   for (int32_t c = c0; c < c1; ++c) {
-    cursor[c] = run;
     st[c] = run;
-    sizes[bh * C + c] = cnt[c];
-    run += (cnt[c] + align - 1) / align * align;
+    int32_t cur = run;
+    for (int32_t t = 0; t < tiles; ++t) {
+      const int32_t n = tc[(int64_t)t * C + c];
+      tc[(int64_t)t * C + c] = cur;
+      cur += n;
+    }
+    run += (cur - run + align - 1) / align * align;
   }
   const int32_t total = part[kLayThreads - 1];
   if (tid == 0) st[C] = total;
   int32_t* tok = token + bh * lcap;
   for (int32_t s = tid; s < total; s += kLayThreads) tok[s] = -1;
-  __syncthreads();
+}
 
-  // stable placement: chunk by chunk in token order; inside a chunk a token's
-  // rank is the number of earlier tokens of the chunk with the same label
+// stable placement inside one tile: chunk by chunk in token order, a token's
+// rank is the number of earlier tokens of its chunk with the same label
+__global__ void __launch_bounds__(kLayThreads)
+place_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t tiles,
+             const int32_t* __restrict__ toff, int32_t* __restrict__ slot,
+             int32_t* __restrict__ token, int64_t lcap) {
+  extern __shared__ int32_t cursor[];  // [C]
+  __shared__ int32_t lab_s[kLayThreads];
+  const int64_t bh = blockIdx.y;
+  const int32_t tile = blockIdx.x, tid = threadIdx.x;
+  const int32_t* to = toff + (bh * tiles + tile) * (int64_t)C;
+  for (int32_t c = tid; c < C; c += kLayThreads) cursor[c] = to[c];
+  const int32_t* lab = labels + bh * N;
+  int32_t* tok = token + bh * lcap;
   int32_t* sl = slot ? slot + bh * N : nullptr;
-  for (int32_t base = 0; base < N; base += kLayThreads) {
+  const int32_t t1 = min(N, (tile + 1) * kLayTile);
+  __syncthreads();
+  for (int32_t base = tile * kLayTile; base < t1; base += kLayThreads) {
     const int32_t t = base + tid;
-    const int32_t c = t < N ? lab[t] : -1;
+    const int32_t c = t < t1 ? lab[t] : -1;
     lab_s[tid] = c;
     __syncthreads();
     const bool ok = c >= 0 && c < C;
@@ -111,7 +145,7 @@ layout_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t 
       const int32_t s = cursor[c] + rank;
       tok[s] = t;
       if (sl) sl[t] = s;
-    } else if (t < N && sl) {
+    } else if (t < t1 && sl) {
       sl[t] = -1;
     }
     __syncthreads();
@@ -122,7 +156,7 @@ layout_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C, int32_t 
 
 // ---------------------------------------------------------------------------
 // means_kernel: one wavefront per (b, h, c); members token[start .. start+n)
-// (ascending token order, from layout_kernel with align 1).
+// (ascending token order, from the layout with align 1).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 means_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ start,
@@ -139,11 +173,27 @@ means_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ start,
   const int32_t s0 = start[bh * (int64_t)(C + 1) + c];
   const int32_t* tok = token + bh * lcap + s0;
   const uint16_t* xb = x + bh * (int64_t)N * D;
-  double acc0 = 0.0, acc1 = 0.0;   // dims lane and lane + 64
-  for (int32_t m = 0; m < n; ++m) {
+  double acc0 = 0.0, acc1 = 0.0;   // dims lane and lane + 64, summed in member order
+  const int32_t d0 = lane < D ? lane : 0, d1 = lane + 64 < D ? lane + 64 : 0;
+  int32_t m = 0;
+  for (; m + 8 <= n; m += 8) {     // eight member rows in flight
+    float a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t* row = xb + (int64_t)tok[m + u] * D;
+      a[u] = bf16_bits_to_float(row[d0]);
+      b[u] = bf16_bits_to_float(row[d1]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc0 += (double)a[u];
+      acc1 += (double)b[u];
+    }
+  }
+  for (; m < n; ++m) {
     const uint16_t* row = xb + (int64_t)tok[m] * D;
-    if (lane < D) acc0 += (double)bf16_bits_to_float(row[lane]);
-    if (lane + 64 < D) acc1 += (double)bf16_bits_to_float(row[lane + 64]);
+    acc0 += (double)bf16_bits_to_float(row[d0]);
+    acc1 += (double)bf16_bits_to_float(row[d1]);
   }
   double* out = cents + (bh * C + c) * (int64_t)D;
   if (lane < D) out[lane] = acc0 / n;
@@ -187,41 +237,54 @@ metric_kernel(const double* __restrict__ cents, const int32_t* __restrict__ size
 // ---------------------------------------------------------------------------
 // prep_kernel: per (b, h, c) g = G c (or c without a metric), q = c . g;
 // g is stored as bf16 hi + lo (hi = bf16(g), lo = bf16(g - hi)) for the MFMA.
-// One workgroup of D threads per centroid.
+// kPrepC centroids per workgroup of 128 threads (thread d: component d); G is
+// symmetric, so thread d reads column d (coalesced across the workgroup).
 // ---------------------------------------------------------------------------
+constexpr int kPrepC = 8;
+
 __global__ void __launch_bounds__(128)
 prep_kernel(const double* __restrict__ cents, const double* __restrict__ G,
             uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo, float* __restrict__ cq,
-            int32_t C, int32_t D) {
-  __shared__ double cv[128];
-  __shared__ double red[128];
-  const int64_t w = blockIdx.x;           // (b, h, c)
-  const int64_t bh = w / C;
+            int32_t C, int32_t D, int32_t cgroups) {
+  __shared__ double cv[kPrepC][128];
+  __shared__ double red[kPrepC][128];
+  const int64_t bh = blockIdx.x / cgroups;
+  const int32_t c0 = (int32_t)(blockIdx.x % cgroups) * kPrepC;
   const int32_t d = threadIdx.x;
-  const double* c = cents + w * D;
-  if (d < D) cv[d] = c[d];
+  const int32_t nc = min(kPrepC, C - c0);
+  const double* cb = cents + (bh * C + c0) * (int64_t)D;
+  for (int32_t k = 0; k < kPrepC; ++k) cv[k][d] = (k < nc && d < D) ? cb[(int64_t)k * D + d] : 0.0;
   __syncthreads();
-  double g = 0.0;
-  if (d < D) {
-    if (G) {
-      const double* Gr = G + (bh * D + d) * (int64_t)D;
-      for (int32_t e = 0; e < D; ++e) g = fma(Gr[e], cv[e], g);
-    } else {
-      g = cv[d];
+  double g[kPrepC];
+#pragma unroll
+  for (int32_t k = 0; k < kPrepC; ++k) g[k] = G ? 0.0 : cv[k][d];
+  if (G && d < D) {
+    const double* Gb = G + bh * (int64_t)D * D;
+    for (int32_t e = 0; e < D; ++e) {
+      const double ge = Gb[(int64_t)e * D + d];
+#pragma unroll
+      for (int32_t k = 0; k < kPrepC; ++k) g[k] = fma(ge, cv[k][e], g[k]);
     }
-    const float gf = (float)g;
-    const uint32_t hi = float_to_bf16_bits(gf);
-    const uint32_t lo = float_to_bf16_bits(gf - bf16_bits_to_float(hi));
-    g_hi[w * D + d] = (uint16_t)hi;
-    g_lo[w * D + d] = (uint16_t)lo;
   }
-  red[d] = d < D ? cv[d] * g : 0.0;
+#pragma unroll
+  for (int32_t k = 0; k < kPrepC; ++k) {
+    if (k < nc && d < D) {
+      const int64_t w = (bh * C + c0 + k) * (int64_t)D + d;
+      const float gf = (float)g[k];
+      const uint32_t hi = float_to_bf16_bits(gf);
+      g_hi[w] = (uint16_t)hi;
+      g_lo[w] = (uint16_t)float_to_bf16_bits(gf - bf16_bits_to_float(hi));
+    }
+    red[k][d] = d < D ? cv[k][d] * g[k] : 0.0;
+  }
   __syncthreads();
-  for (int32_t s = 64; s > 0; s >>= 1) {
-    if (d < s) red[d] += red[d + s];
+  for (int32_t sft = 64; sft > 0; sft >>= 1) {
+    if (d < sft)
+#pragma unroll
+      for (int32_t k = 0; k < kPrepC; ++k) red[k][d] += red[k][d + sft];
     __syncthreads();
   }
-  if (d == 0) cq[w] = (float)red[0];
+  if (d < nc) cq[bh * C + c0 + d] = (float)red[d][0];
 }
 
 // ---------------------------------------------------------------------------
@@ -352,12 +415,24 @@ int64_t cluster_lcap(int32_t N, int32_t C, int32_t align) {
   return ((int64_t)N + (int64_t)C * (align - 1) + align - 1) / align * align;
 }
 
+size_t layout_ws_bytes(int32_t bh, int32_t N, int32_t C) {
+  const int64_t tiles = (N + kLayTile - 1) / kLayTile;
+  return align_up((size_t)bh * tiles * C * sizeof(int32_t), 256);
+}
+
 hipError_t launch_cluster_layout(const int32_t* labels, int32_t bh, int32_t N, int32_t C,
                                  int32_t align, int32_t* start, int32_t* sizes, int32_t* slot,
-                                 int32_t* token, hipStream_t stream) {
-  const size_t shmem = (size_t)2 * C * sizeof(int32_t);
-  hipLaunchKernelGGL(layout_kernel, dim3((uint32_t)bh), dim3(kLayThreads), shmem, stream, labels,
-                     N, C, align, start, sizes, slot, token, cluster_lcap(N, C, align));
+                                 int32_t* token, void* ws, hipStream_t stream) {
+  const int32_t tiles = (N + kLayTile - 1) / kLayTile;
+  const int64_t lcap = cluster_lcap(N, C, align);
+  int32_t* tcount = static_cast<int32_t*>(ws);
+  const size_t shmem = (size_t)C * sizeof(int32_t);
+  hipLaunchKernelGGL(hist_kernel, dim3((uint32_t)tiles, (uint32_t)bh), dim3(kLayThreads), shmem,
+                     stream, labels, N, C, tiles, tcount);
+  hipLaunchKernelGGL(offsets_kernel, dim3((uint32_t)bh), dim3(kLayThreads), 0, stream, C, align,
+                     tiles, tcount, start, sizes, token, lcap);
+  hipLaunchKernelGGL(place_kernel, dim3((uint32_t)tiles, (uint32_t)bh), dim3(kLayThreads), shmem,
+                     stream, labels, N, C, tiles, (const int32_t*)tcount, slot, token, lcap);
   return hipGetLastError();
 }
 
@@ -386,6 +461,7 @@ KmeansWs kmeans_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t D) {
   w.cq_off = off;   off = align_up(off + (size_t)bh * C * 4, 256);
   w.start_off = off; off = align_up(off + (size_t)bh * (C + 1) * 4, 256);
   w.token_off = off; off = align_up(off + (size_t)bh * N * 4, 256);
+  w.layout_off = off; off += layout_ws_bytes(bh, N, C);
   w.total = off;
   return w;
 }
@@ -400,10 +476,12 @@ hipError_t launch_kmeans(const void* x, int32_t bh, int32_t N, int32_t D, const 
   float* cq = reinterpret_cast<float*>(base + w.cq_off);
   int32_t* start = reinterpret_cast<int32_t*>(base + w.start_off);
   int32_t* token = reinterpret_cast<int32_t*>(base + w.token_off);
+  void* lay_ws = base + w.layout_off;
   const int32_t tiles = (N + kAsTok - 1) / kAsTok;
+  const int32_t cgroups = (C + kPrepC - 1) / kPrepC;
   for (int32_t it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(prep_kernel, dim3((uint32_t)((int64_t)bh * C)), dim3(128), 0, stream,
-                       (const double*)cents, G, g_hi, g_lo, cq, C, D);
+    hipLaunchKernelGGL(prep_kernel, dim3((uint32_t)((int64_t)bh * cgroups)), dim3(128), 0, stream,
+                       (const double*)cents, G, g_hi, g_lo, cq, C, D, cgroups);
     if (D == 128)
       hipLaunchKernelGGL(assign_kernel<128>, dim3((uint32_t)((int64_t)bh * tiles)),
                          dim3(64 * kAsWaves), 0, stream, (const uint16_t*)x, g_hi, g_lo, cq,
@@ -412,7 +490,8 @@ hipError_t launch_kmeans(const void* x, int32_t bh, int32_t N, int32_t D, const 
       hipLaunchKernelGGL(assign_kernel<64>, dim3((uint32_t)((int64_t)bh * tiles)),
                          dim3(64 * kAsWaves), 0, stream, (const uint16_t*)x, g_hi, g_lo, cq,
                          labels, N, C, tiles);
-    hipError_t e = launch_cluster_layout(labels, bh, N, C, 1, start, sizes, nullptr, token, stream);
+    hipError_t e =
+        launch_cluster_layout(labels, bh, N, C, 1, start, sizes, nullptr, token, lay_ws, stream);
     if (e != hipSuccess) return e;
     e = launch_cluster_means(x, start, sizes, token, cents, bh, N, C, D, N, stream);
     if (e != hipSuccess) return e;

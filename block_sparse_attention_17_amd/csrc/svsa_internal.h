@@ -95,8 +95,9 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
 // Clustering (variable-size blocks).
 int64_t cluster_lcap(int32_t N, int32_t C, int32_t align);   // padded layout capacity
 struct KmeansWs {
-  size_t g_hi_off, g_lo_off, cq_off, start_off, token_off, total;
+  size_t g_hi_off, g_lo_off, cq_off, start_off, token_off, layout_off, total;
 };
+size_t layout_ws_bytes(int32_t bh, int32_t N, int32_t C);   // svsa_cluster_layout scratch
 KmeansWs kmeans_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t D);
 hipError_t launch_kmeans(const void* x, int32_t bh, int32_t N, int32_t D, const double* G,
                          double* cents, int32_t C, int32_t iters, int32_t* labels,
@@ -105,7 +106,7 @@ hipError_t launch_cluster_metric(const double* cents, const int32_t* sizes, doub
                                  int32_t C, int32_t D, hipStream_t stream);
 hipError_t launch_cluster_layout(const int32_t* labels, int32_t bh, int32_t N, int32_t C,
                                  int32_t align, int32_t* start, int32_t* sizes, int32_t* slot,
-                                 int32_t* token, hipStream_t stream);
+                                 int32_t* token, void* ws, hipStream_t stream);
 hipError_t launch_cluster_means(const void* x, const int32_t* start, const int32_t* sizes,
                                 const int32_t* token, double* cents, int32_t bh, int32_t N,
                                 int32_t C, int32_t D, int64_t lcap, hipStream_t stream);

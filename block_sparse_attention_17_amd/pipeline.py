@@ -120,6 +120,10 @@ class ClusteredAttention:
         km = max(B.svsa_kmeans_workspace_bytes(batch, heads, n, q_clusters, head_dim),
                  B.svsa_kmeans_workspace_bytes(batch, heads, n, k_clusters, head_dim))
         self.km_ws = torch.empty(km, dtype=torch.uint8, device=dev)
+        self.layout_ws = torch.empty(
+            max(B.svsa_cluster_layout_workspace_bytes(batch, heads, n, q_clusters),
+                B.svsa_cluster_layout_workspace_bytes(batch, heads, n, k_clusters)),
+            dtype=torch.uint8, device=dev)
         self.mask_ws = torch.empty(
             B.svsa_cluster_mask_workspace_bytes(batch, heads, q_clusters, k_clusters),
             dtype=torch.uint8, device=dev)
@@ -148,9 +152,9 @@ class ClusteredAttention:
     def layout(self, q, k, v, stream=None):
         a = self.align
         B.svsa_cluster_layout(self.qlab, self.nq, a, self.q_start, self.qsize, self.q_slot,
-                              self.q_token, stream=stream)
+                              self.q_token, self.layout_ws, stream=stream)
         B.svsa_cluster_layout(self.klab, self.nk, a, self.k_start, self.ksize, self.k_slot,
-                              self.k_token, stream=stream)
+                              self.k_token, self.layout_ws, stream=stream)
         B.svsa_cluster_permute(q, self.qp, self.n, self.nq, a, self.q_token, self.q_start,
                                stream=stream)
         B.svsa_cluster_permute(k, self.kp, self.n, self.nk, a, self.k_token, self.k_start,

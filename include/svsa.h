@@ -313,10 +313,14 @@ SVSA_API int64_t svsa_cluster_capacity(int32_t n, int32_t clusters, int32_t alig
  * start: int32 [batch, heads, clusters + 1]; sizes: int32 [batch, heads, clusters];
  * slot: int32 [batch, heads, n] (slot of each token; may be NULL);
  * token: int32 [batch, heads, capacity] (token in each slot s < L, -1 for padding).
+ * workspace: device buffer of svsa_cluster_layout_workspace_bytes() bytes.
  */
+SVSA_API size_t svsa_cluster_layout_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                                    int32_t clusters);
 SVSA_API int svsa_cluster_layout(const int32_t* labels, int32_t batch, int32_t heads, int32_t n,
                                  int32_t clusters, int32_t align, int32_t* start,
-                                 int32_t* sizes, int32_t* slot, int32_t* token, void* stream);
+                                 int32_t* sizes, int32_t* slot, int32_t* token,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Rows into the cluster layout (inverse = 0: dst[s] = src[token[s]] for the

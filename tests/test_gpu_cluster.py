@@ -186,7 +186,9 @@ def _gpu_layout(labels, C, align):
     sizes = torch.empty((B, H, C), **i32)
     slot = torch.empty((B, H, N), **i32)
     token = torch.full((B, H, cap), -7, **i32)
-    m.svsa_cluster_layout(_dev(labels, torch.int32), C, align, start, sizes, slot, token)
+    ws = torch.empty(m.svsa_cluster_layout_workspace_bytes(B, H, N, C), dtype=torch.uint8,
+                     device="cuda")
+    m.svsa_cluster_layout(_dev(labels, torch.int32), C, align, start, sizes, slot, token, ws)
     torch.cuda.synchronize()
     return start, sizes, slot, token, cap
 
