@@ -61,6 +61,15 @@ Readings taken where the pages are silent (each is pinned by a test):
   kappa_j; empty key clusters get none); top-p / fixed fraction as for
   blocks, no band.  A query token attends to every token of its cluster's
   kept key clusters.
+* Tail merging ([iCATS] Sec. 4.3, App. E.1) of the query clusters of one
+  head, given their kept key-cluster sets and the block size b: (1) clusters
+  with identical kept sets merge into the lowest such index; (2) two rounds:
+  every non-empty cluster with a tail (size mod b > 0) finds its nearest
+  other such cluster by Jaccard similarity of the kept sets (ties: lowest
+  index); mutually nearest pairs whose tails fit one block move the smaller
+  tail (equal tails: the higher index's) -- the donor's last members in token
+  order -- to the other cluster, whose kept set becomes the union.  Emptied
+  clusters keep their index and occupy no rows.
 * SNR-guided top-p ([iCATS] Sec. 4.2, App. A): the pages give the schedule's
   shape and its two parameters (pmin, tau) but no formula.  Reading: with the
   flow-matching noise level s (x = (1 - s) x0 + s eps), logSNR = 2 ln((1-s)/s)
@@ -82,7 +91,7 @@ __all__ = [
     "psa_attends", "block_tiles", "stripe_row", "stripe_mask", "block_layout", "snr_top_p",
     "cluster_means", "quad_distances", "kmeans_assign", "kmeans", "cluster_metric",
     "cluster_layout", "cluster_permute", "cluster_unpermute", "cluster_scores", "cluster_mask",
-    "cluster_attention_rows",
+    "cluster_attention_rows", "tail_merge",
 ]
 
 
@@ -636,3 +645,58 @@ def cluster_attention_rows(q, k, v, qlab, klab, i, cols, scale):
     wgt = np.exp(logits - logits.max(axis=1, keepdims=True))
     wgt /= wgt.sum(axis=1, keepdims=True)
     return toks, wgt @ vf
+
+
+# --------------------------------------------------------------------------
+# Tail merging.  [iCATS] Sec. 4.3 and App. E.1: query clusters that attend to
+# the same key clusters merge without changing the attention pattern; then,
+# over two rounds, tail tokens move between mutually closest clusters whose
+# tails fit one block, the receiving cluster taking the union of both masks.
+# The similarity, the choice of donor and of its tail tokens are this
+# module's reading (see the header).
+# --------------------------------------------------------------------------
+def tail_merge(labels, kept, block, rounds=2):
+    """One head.  labels: int [N] query cluster of each token; kept: bool
+    [C, nk] kept key clusters of each query cluster; block: tokens per query
+    block.  Returns (labels int32 [N], kept bool [C, nk], sizes int64 [C])."""
+    lab = np.array(labels, dtype=np.int64)
+    R = np.array(kept, dtype=bool)
+    C = R.shape[0]
+    sizes = np.bincount(lab, minlength=C)[:C]
+    rep = np.arange(C)
+    for i in range(C):
+        if sizes[i] == 0:
+            continue
+        for j in range(i):
+            if sizes[j] > 0 and np.array_equal(R[j], R[i]):
+                rep[i] = j
+                break
+    lab = rep[lab]
+    for _ in range(rounds):
+        sizes = np.bincount(lab, minlength=C)[:C]
+        tail = sizes % block
+        part = [i for i in range(C) if sizes[i] > 0 and tail[i] > 0]
+        nearest = {}
+        for i in part:
+            best, bi, bu = -1, 0, 1
+            for j in part:
+                if j == i:
+                    continue
+                inter = int(np.sum(R[i] & R[j]))
+                uni = max(int(np.sum(R[i] | R[j])), 1)
+                if best < 0 or inter * bu > bi * uni:      # strictly more similar
+                    best, bi, bu = j, inter, uni
+            if best >= 0:
+                nearest[i] = best
+        moves = []
+        for i in part:
+            j = nearest.get(i, -1)
+            if j > i and nearest.get(j, -1) == i and tail[i] + tail[j] <= block:
+                donor, recv = (i, j) if tail[i] < tail[j] else (j, i)
+                moves.append((donor, recv))
+        for donor, recv in moves:
+            members = np.nonzero(lab == donor)[0]
+            lab[members[members.size - tail[donor]:]] = recv
+            R[recv] |= R[donor]
+    sizes = np.bincount(lab, minlength=C)[:C]
+    return lab.astype(np.int32), R, sizes

@@ -11,6 +11,7 @@ import tests.test_oracle_stripe as tst
 import tests.test_oracle_pad3d as tpd
 import tests.test_oracle_snr as tsnr
 import tests.test_oracle_cluster as tcl
+import tests.test_oracle_tail as ttl
 
 _SNR = orc.snr_top_p   # the unmutated schedule, for mutations built on top of it
 _MEANS = orc.cluster_means
@@ -220,6 +221,47 @@ def _cluster_rows_query_labels(q, k, v, qlab, klab, i, cols, scale):
     return _ROWS(q, k, v, qlab, qlab, i, cols, scale)
 
 
+def _tail_variant(one_sided=False, big_donor=False, no_union=False, head=False):
+    def fn(labels, kept, block, rounds=2):
+        lab = np.array(labels, dtype=np.int64)
+        R = np.array(kept, dtype=bool)
+        C = R.shape[0]
+        sizes = np.bincount(lab, minlength=C)[:C]
+        rep = np.arange(C)
+        for i in range(C):
+            for j in range(i):
+                if sizes[i] > 0 and sizes[j] > 0 and np.array_equal(R[j], R[i]):
+                    rep[i] = j
+                    break
+        lab = rep[lab]
+        for _ in range(rounds):
+            sizes = np.bincount(lab, minlength=C)[:C]
+            tail = sizes % block
+            part = [i for i in range(C) if sizes[i] > 0 and tail[i] > 0]
+            near = {}
+            for i in part:
+                cand = [(-(np.sum(R[i] & R[j]) / max(np.sum(R[i] | R[j]), 1)), j)
+                        for j in part if j != i]
+                if cand:
+                    near[i] = min(cand)[1]
+            moves, used = [], set()
+            for i in part:
+                j = near.get(i, -1)
+                ok = j >= 0 and (one_sided or (j > i and near.get(j, -1) == i))
+                if ok and i not in used and j not in used and tail[i] + tail[j] <= block:
+                    small = (i, j) if tail[i] < tail[j] else (j, i)
+                    moves.append(small[::-1] if big_donor else small)
+                    used |= {i, j}
+            for donor, recv in moves:
+                members = np.nonzero(lab == donor)[0]
+                take = members[:tail[donor]] if head else members[members.size - tail[donor]:]
+                lab[take] = recv
+                if not no_union:
+                    R[recv] |= R[donor]
+        return lab.astype(np.int32), R, np.bincount(lab, minlength=C)[:C]
+    return fn
+
+
 MUTATIONS = [
     ("block_scores", _scores_no_scale, ts.test_scores_closed_form_one_channel, ()),
     ("block_scores", _scores_transposed, ts.test_scores_closed_form_one_channel, ()),
@@ -249,6 +291,10 @@ MUTATIONS = [
      ()),
     ("cluster_attention_rows", _cluster_rows_query_labels,
      tcl.test_cluster_attention_all_kept_equals_dense_sdpa, ()),
+    ("tail_merge", _tail_variant(one_sided=True), ttl.test_tail_merge_hand_worked, ("golden",)),
+    ("tail_merge", _tail_variant(big_donor=True), ttl.test_tail_merge_hand_worked, ("golden",)),
+    ("tail_merge", _tail_variant(no_union=True), ttl.test_tail_merge_invariants, ()),
+    ("tail_merge", _tail_variant(head=True), ttl.test_tail_merge_hand_worked, ("golden",)),
 ]
 
 
