@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--k-clusters", type=int, default=1000)
     ap.add_argument("--align", type=int, default=64, choices=[32, 64])
     ap.add_argument("--iters", type=int, default=2, help="Lloyd iterations per side per step")
+    ap.add_argument("--tail-merge", action="store_true",
+                    help="tail merging of the query clusters before the attention")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="Lloyd iterations of the first (feature-space) clustering")
     ap.add_argument("--seed", type=int, default=0)
@@ -162,7 +164,7 @@ def cluster_bench(args, cfg, m, inp, torch):
     dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     ca = m.ClusteredAttention(B_, H, D, N, nq, nk, align=args.align, q_iters=args.cold_iters,
-                              k_iters=args.cold_iters)
+                              k_iters=args.cold_iters, tail_merge=args.tail_merge)
     sq = cluster_seeds(N, nq, B_, H, seed=args.seed, stream=1)
     sk = cluster_seeds(N, nk, B_, H, seed=args.seed, stream=2)
     bh = np.arange(B_)[:, None, None], np.arange(H)[None, :, None]
@@ -174,22 +176,25 @@ def cluster_bench(args, cfg, m, inp, torch):
     ca.q_iters = ca.k_iters = args.iters
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    names = ["cluster", "layout_permute", "mask", "attention", "permute_out"]
+    names = ["cluster", "mask", "tail_merge", "layout_permute", "attention", "permute_out"]
 
     def step(rec=None):
-        mk = [ev() for _ in range(6)] if rec is not None else None
+        mk = [ev() for _ in range(7)] if rec is not None else None
         if mk: mk[0].record(stream)
         ca.cluster(q, k)
         if mk: mk[1].record(stream)
-        ca.layout(q, k, v)
-        if mk: mk[2].record(stream)
         ca.build_mask(top_p=tp)
+        if mk: mk[2].record(stream)
+        if args.tail_merge:
+            ca.merge_tails()
         if mk: mk[3].record(stream)
-        ca.attend()
+        ca.layout(q, k, v)
         if mk: mk[4].record(stream)
+        ca.attend()
+        if mk: mk[5].record(stream)
         ca.permute_out()
         if mk:
-            mk[5].record(stream)
+            mk[6].record(stream)
             rec.append(mk)
 
     for _ in range(args.warmup):
@@ -203,10 +208,11 @@ def cluster_bench(args, cfg, m, inp, torch):
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     stage_ms = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]))
                 for i, n in enumerate(names)}
-    step_ms = float(np.mean([r[0].elapsed_time(r[5]) for r in recs]))
+    step_ms = float(np.mean([r[0].elapsed_time(r[6]) for r in recs]))
     # kept FLOPs over real tokens, and the rows the kernel runs (sub-block padded)
-    rp = ca.row_ptr.cpu().numpy().astype(np.int64)
-    ci = ca.col_idx[: int(rp[-1])].cpu().numpy()
+    rp_t, ci_t = (ca.row_ptr_m, ca.col_idx_m) if args.tail_merge else (ca.row_ptr, ca.col_idx)
+    rp = rp_t.cpu().numpy().astype(np.int64)
+    ci = ci_t[: int(rp[-1])].cpu().numpy()
     qs = ca.qsize.cpu().numpy().reshape(-1, nq)
     ks = ca.ksize.cpu().numpy().reshape(-1, nk)
     a = args.align
@@ -227,7 +233,8 @@ def cluster_bench(args, cfg, m, inp, torch):
         "data": "synthetic (seeded N(0,1) + shared 3D sinusoidal positional term, bf16)",
         "config": {"workload": (f"{cfg.name} variable-size blocks: {nq} query / {nk} key clusters "
                                 f"(k-means under the interaction metric, {args.iters} Lloyd "
-                                f"iterations per side per step, warm), align {a}, {H} heads, "
+                                f"iterations per side per step, warm), align {a}, "
+                                + ("tail merging, " if args.tail_merge else "") + f"{H} heads, "
                                 f"head_dim {D}, top-p {top_p}"),
                    "global_batch": B_, "seq_len": N, "parallelism": "single GPU"},
         "kept_tflop_per_step": flops / 1e12,

@@ -8,7 +8,8 @@ from .binding import (svsa_cluster_attn, svsa_cluster_attn_workspace_bytes,
                       svsa_cluster_layout_workspace_bytes, svsa_cluster_mask,
                       svsa_cluster_means, svsa_cluster_means_workspace_bytes,
                       svsa_cluster_mask_workspace_bytes, svsa_cluster_metric, svsa_cluster_permute,
-                      svsa_kmeans, svsa_kmeans_workspace_bytes)
+                      svsa_kmeans, svsa_kmeans_workspace_bytes, svsa_tail_merge,
+                      svsa_tail_merge_workspace_bytes)
 from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, library, library_path,
                       status_string, svsa_attn_workspace_bytes, svsa_block_mask,
                       svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
@@ -26,4 +27,5 @@ __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "librar
            "svsa_cluster_mask", "svsa_cluster_mask_workspace_bytes", "svsa_cluster_metric",
            "svsa_cluster_permute", "svsa_kmeans", "svsa_kmeans_workspace_bytes",
            "svsa_cluster_means", "svsa_cluster_means_workspace_bytes",
-           "svsa_cluster_layout_workspace_bytes"]
+           "svsa_cluster_layout_workspace_bytes", "svsa_tail_merge",
+           "svsa_tail_merge_workspace_bytes"]

@@ -125,6 +125,9 @@ def _load():
         "svsa_cluster_mask_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "svsa_cluster_mask": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, dbl, fp, fp, vp,
                                              vp, i64, vp, sz, vp]),
+        "svsa_tail_merge_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "svsa_tail_merge": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                           i64, vp, sz, vp]),
         "svsa_cluster_attn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "svsa_cluster_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32,
                                              i32, vp, vp, i32, flt, vp, vp, vp, sz, vp]),
@@ -149,6 +152,7 @@ EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
             "svsa_cluster_layout", "svsa_cluster_permute",
             "svsa_cluster_mask_workspace_bytes", "svsa_cluster_mask",
             "svsa_cluster_attn_workspace_bytes", "svsa_cluster_attn",
+            "svsa_tail_merge_workspace_bytes", "svsa_tail_merge",
             "svsa_status_string", "svsa_version")
 
 
@@ -420,3 +424,22 @@ def svsa_cluster_attn(q, k, v, out, n_q, q_start, q_size, n_k, k_start, k_size, 
         float(softmax_scale), _ptr(row_ptr, "row_ptr", i32), _ptr(col_idx, "col_idx", i32),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
     return out
+
+
+def svsa_tail_merge_workspace_bytes(batch, heads, n, nq, nk):
+    return int(_lib.svsa_tail_merge_workspace_bytes(batch, heads, n, nq, nk))
+
+
+def svsa_tail_merge(labels, nq, nk, block, row_ptr, col_idx, row_ptr_out, col_idx_out,
+                    workspace, rounds=2, stream=None):
+    """Query labels (in place) and the cluster mask after tail merging."""
+    import torch
+    B_, Hh, N = labels.shape
+    i32 = (torch.int32,)
+    _check("svsa_tail_merge", _lib.svsa_tail_merge(
+        _ptr(labels, "labels", i32), B_, Hh, N, int(nq), int(nk), int(block), int(rounds),
+        _ptr(row_ptr, "row_ptr", i32), _ptr(col_idx, "col_idx", i32),
+        _ptr(row_ptr_out, "row_ptr_out", i32), _ptr(col_idx_out, "col_idx_out", i32),
+        col_idx_out.numel(), _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(),
+        _stream(stream)))
+    return labels, row_ptr_out, col_idx_out

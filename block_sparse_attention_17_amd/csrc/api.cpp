@@ -209,6 +209,30 @@ int svsa_cluster_permute(const void* src, void* dst, int32_t dtype, int32_t batc
                                                static_cast<hipStream_t>(stream)));
 }
 
+size_t svsa_tail_merge_workspace_bytes(int32_t batch, int32_t heads, int32_t n, int32_t nq,
+                                       int32_t nk) {
+  if (!cluster_sizes_ok(batch, heads, n, nq, 1) || nk < 1 || nk > kMaxNb) return 0;
+  return svsa::tail_ws_layout(batch * heads, n, nq, nk).total;
+}
+
+int svsa_tail_merge(int32_t* labels, int32_t batch, int32_t heads, int32_t n, int32_t nq,
+                    int32_t nk, int32_t block, int32_t rounds, const int32_t* row_ptr,
+                    const int32_t* col_idx, int32_t* row_ptr_out, int32_t* col_idx_out,
+                    int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  if (!labels || !row_ptr || !col_idx || !row_ptr_out || !col_idx_out || block < 1 ||
+      rounds < 0 || rounds > 8 || nk < 1 || !cluster_sizes_ok(batch, heads, n, nq, 1))
+    return SVSA_E_INVALID;
+  if (nk > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int64_t worst = (int64_t)batch * heads * nq * nk;
+  if (worst >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (col_capacity < worst) return SVSA_E_CAPACITY;
+  if (!workspace || ws_bytes < svsa_tail_merge_workspace_bytes(batch, heads, n, nq, nk))
+    return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_tail_merge(labels, batch * heads, n, nq, nk, block, rounds,
+                                          row_ptr, col_idx, row_ptr_out, col_idx_out, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char* svsa_status_string(int status) {
   switch (status) {
     case SVSA_OK: return "ok";

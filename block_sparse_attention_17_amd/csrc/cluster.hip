@@ -28,6 +28,9 @@
 //                  chunks of 32; d(x, c) - x^T G x = c^T G c - 2 x . g_c
 //   permute_kernel rows gathered into the padded cluster layout (padding
 //                  zero) or scattered back to token order
+//   rows_to_bits_kernel, merge_kernel, relabel_kernel, pair_kernel,
+//   move_kernel, popcount_kernel
+//                  tail merging of the query clusters (see below)
 #include "svsa_internal.h"
 
 namespace svsa {
@@ -409,7 +412,252 @@ cluster_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tail merging ([iCATS] Sec. 4.3, App. E.1): query clusters with identical
+// kept key-cluster sets merge into the lowest index; then, per round, every
+// non-empty cluster with a tail (size mod block) finds its nearest other such
+// cluster by Jaccard similarity of the kept sets (compared exactly as integer
+// cross products; ties to the lowest index), and mutually nearest pairs whose
+// tails fit one block move the smaller tail (equal: the higher index's) to
+// the other cluster, which takes the union of both kept sets.  Kept sets are
+// row bitmaps of `words` uint32.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64)
+rows_to_bits_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                    uint32_t* __restrict__ bits, int32_t nk, int32_t words) {
+  const int64_t r = blockIdx.x;
+  uint32_t* b = bits + r * words;
+  for (int32_t w = threadIdx.x; w < words; w += 64) b[w] = 0u;
+  __syncthreads();
+  for (int32_t e = row_ptr[r] + threadIdx.x; e < row_ptr[r + 1]; e += 64) {
+    const int32_t j = col_idx[e];
+    if (j >= 0 && j < nk) atomicOr(&b[j >> 5], 1u << (j & 31));
+  }
+}
+
+__device__ __forceinline__ bool rows_equal(const uint32_t* a, const uint32_t* b, int32_t words) {
+  for (int32_t w = 0; w < words; ++w)
+    if (a[w] != b[w]) return false;
+  return true;
+}
+
+// The bitmaps of one (b, h) are read many times by the two per-head kernels
+// below: with kLds they are first copied into LDS (after the C counters).
+constexpr int kTailThreads = 1024;   // per-head kernels: many waves to hide LDS latency
+
+// The LDS copy uses an odd row stride (words | 1) so that the rows the lanes
+// of a wavefront read at one word offset fall in different banks.
+__host__ __device__ inline int32_t lds_stride(int32_t words) { return words | 1; }
+
+template <bool kLds>
+__device__ __forceinline__ const uint32_t* head_bits(const uint32_t* g, int32_t* sh, int32_t C,
+                                                      int32_t words, int32_t* stride) {
+  if (!kLds) {
+    *stride = words;
+    return g;
+  }
+  const int32_t ls = lds_stride(words);
+  uint32_t* l = reinterpret_cast<uint32_t*>(sh + C);
+  for (int32_t e = threadIdx.x; e < C * words; e += kTailThreads)
+    l[(e / words) * ls + e % words] = g[e];
+  __syncthreads();
+  *stride = ls;
+  return l;
+}
+
+// one workgroup per (b, h): rep[i] = lowest j <= i, both non-empty, with the
+// same kept set
+template <bool kLds>
+__global__ void __launch_bounds__(kTailThreads)
+merge_kernel(const int32_t* __restrict__ labels, int32_t N, int32_t C,
+             const uint32_t* __restrict__ bits, int32_t words, int32_t* __restrict__ rep) {
+  extern __shared__ int32_t cnt[];  // [C] (+ [C * words] bitmaps with kLds)
+  const int64_t bh = blockIdx.x;
+  for (int32_t c = threadIdx.x; c < C; c += kTailThreads) cnt[c] = 0;
+  __syncthreads();
+  const int32_t* lab = labels + bh * N;
+  for (int32_t t = threadIdx.x; t < N; t += kTailThreads) {
+    const int32_t c = lab[t];
+    if (c >= 0 && c < C) atomicAdd(&cnt[c], 1);
+  }
+  __syncthreads();
+  int32_t rs;
+  const uint32_t* bb = head_bits<kLds>(bits + bh * (int64_t)C * words, cnt, C, words, &rs);
+  for (int32_t i = threadIdx.x; i < C; i += kTailThreads) {
+    int32_t r = i;
+    if (cnt[i] > 0)
+      for (int32_t j = 0; j < i; ++j)
+        if (cnt[j] > 0 && rows_equal(bb + (int64_t)j * rs, bb + (int64_t)i * rs, words)) {
+          r = j;
+          break;
+        }
+    rep[bh * C + i] = r;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+relabel_kernel(int32_t* __restrict__ labels, const int32_t* __restrict__ rep, int32_t N,
+               int32_t C, int64_t total) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int32_t c = labels[e];
+  if (c >= 0 && c < C) labels[e] = rep[(e / N) * C + c];
+}
+
+// one workgroup per (b, h): the pairs of one round; move_to[d] = receiver of
+// donor d (else -1), cut[d] = members of d that stay (its first ones)
+template <bool kLds>
+__global__ void __launch_bounds__(kTailThreads)
+pair_kernel(const int32_t* __restrict__ sizes, int32_t C, uint32_t* __restrict__ bits,
+            int32_t words, int32_t block, int32_t* __restrict__ move_to,
+            int32_t* __restrict__ cut) {
+  extern __shared__ int32_t near[];  // [C] (+ [C * words] bitmaps with kLds)
+  const int64_t bh = blockIdx.x;
+  const int32_t* sz = sizes + bh * C;
+  uint32_t* bb = bits + bh * (int64_t)C * words;       // the unions go here
+  int32_t rs;
+  const uint32_t* rb = head_bits<kLds>(bb, near, C, words, &rs);
+  for (int32_t i = threadIdx.x; i < C; i += kTailThreads) {
+    int32_t best = -1;
+    if (sz[i] > 0 && sz[i] % block > 0) {
+      const uint32_t* bi = rb + (int64_t)i * rs;
+      int64_t b_in = 0, b_un = 1;
+      for (int32_t j = 0; j < C; ++j) {
+        if (j == i || sz[j] == 0 || sz[j] % block == 0) continue;
+        const uint32_t* bj = rb + (int64_t)j * rs;
+        int64_t in = 0, un = 0;
+        for (int32_t w = 0; w < words; ++w) {
+          in += __popc(bi[w] & bj[w]);
+          un += __popc(bi[w] | bj[w]);
+        }
+        if (un < 1) un = 1;
+        if (best < 0 || in * b_un > b_in * un) {
+          best = j;
+          b_in = in;
+          b_un = un;
+        }
+      }
+    }
+    near[i] = best;
+    move_to[bh * C + i] = -1;
+    cut[bh * C + i] = sz[i];
+  }
+  __syncthreads();
+  for (int32_t i = threadIdx.x; i < C; i += kTailThreads) {
+    const int32_t j = near[i];
+    if (j > i && near[j] == i) {
+      const int32_t ti = sz[i] % block, tj = sz[j] % block;
+      if (ti + tj <= block) {
+        const int32_t d = ti < tj ? i : j, r = ti < tj ? j : i;
+        move_to[bh * C + d] = r;
+        cut[bh * C + d] = sz[d] - (sz[d] % block);
+        uint32_t* br = bb + (int64_t)r * words;
+        const uint32_t* bd = rb + (int64_t)d * rs;
+        const uint32_t* bo = rb + (int64_t)r * rs;
+        for (int32_t w = 0; w < words; ++w) br[w] = bo[w] | bd[w];
+      }
+    }
+  }
+}
+
+// tokens of a donor at rank >= cut (its last members in token order) move
+__global__ void __launch_bounds__(256)
+move_kernel(int32_t* __restrict__ labels, const int32_t* __restrict__ slot,
+            const int32_t* __restrict__ start, const int32_t* __restrict__ move_to,
+            const int32_t* __restrict__ cut, int32_t N, int32_t C, int64_t total) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t bh = e / N;
+  const int32_t c = labels[e];
+  if (c < 0 || c >= C) return;
+  const int32_t to = move_to[bh * C + c];
+  if (to >= 0 && slot[e] - start[bh * (C + 1) + c] >= cut[bh * C + c]) labels[e] = to;
+}
+
+__global__ void __launch_bounds__(256)
+popcount_kernel(const uint32_t* __restrict__ bits, int32_t* __restrict__ counts, int32_t words,
+                int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  int32_t n = 0;
+  for (int32_t w = 0; w < words; ++w) n += __popc(bits[r * words + w]);
+  counts[r] = n;
+}
+
 }  // namespace
+
+TailWs tail_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t nk) {
+  TailWs w{};
+  w.words = (nk + 31) / 32;
+  size_t off = 0;
+  w.bits_off = off; off = align_up(off + (size_t)bh * C * w.words * 4, 256);
+  w.rep_off = off; off = align_up(off + (size_t)bh * C * 4, 256);
+  w.move_off = off; off = align_up(off + (size_t)bh * C * 4, 256);
+  w.cut_off = off; off = align_up(off + (size_t)bh * C * 4, 256);
+  w.counts_off = off; off = align_up(off + (size_t)bh * C * 4, 256);
+  w.start_off = off; off = align_up(off + (size_t)bh * (C + 1) * 4, 256);
+  w.sizes_off = off; off = align_up(off + (size_t)bh * C * 4, 256);
+  w.slot_off = off; off = align_up(off + (size_t)bh * N * 4, 256);
+  w.token_off = off; off = align_up(off + (size_t)bh * N * 4, 256);
+  w.layout_off = off; off += layout_ws_bytes(bh, N, C);
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_tail_merge(int32_t* labels, int32_t bh, int32_t N, int32_t C, int32_t nk,
+                             int32_t block, int32_t rounds, const int32_t* row_ptr,
+                             const int32_t* col_idx, int32_t* row_ptr_out, int32_t* col_idx_out,
+                             void* ws, hipStream_t stream) {
+  const TailWs w = tail_ws_layout(bh, N, C, nk);
+  char* base = static_cast<char*>(ws);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(base + w.bits_off);
+  int32_t* rep = reinterpret_cast<int32_t*>(base + w.rep_off);
+  int32_t* move_to = reinterpret_cast<int32_t*>(base + w.move_off);
+  int32_t* cut = reinterpret_cast<int32_t*>(base + w.cut_off);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts_off);
+  int32_t* start = reinterpret_cast<int32_t*>(base + w.start_off);
+  int32_t* sizes = reinterpret_cast<int32_t*>(base + w.sizes_off);
+  int32_t* slot = reinterpret_cast<int32_t*>(base + w.slot_off);
+  int32_t* token = reinterpret_cast<int32_t*>(base + w.token_off);
+  void* lay_ws = base + w.layout_off;
+  const int64_t rows = (int64_t)bh * C, total = (int64_t)bh * N;
+  const uint32_t tblocks = (uint32_t)((total + 255) / 256);
+  hipLaunchKernelGGL(rows_to_bits_kernel, dim3((uint32_t)rows), dim3(64), 0, stream, row_ptr,
+                     col_idx, bits, nk, w.words);
+  // bitmaps in LDS when the counters and one head's bitmaps fit in 64 KB
+  const size_t lds = (size_t)C * 4 * (1 + lds_stride(w.words));
+  const bool in_lds = lds <= 65536;
+  const size_t shmem = in_lds ? lds : (size_t)C * 4;
+  if (in_lds)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3((uint32_t)bh), dim3(kTailThreads), shmem, stream,
+                       (const int32_t*)labels, N, C, (const uint32_t*)bits, w.words, rep);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3((uint32_t)bh), dim3(kTailThreads), shmem, stream,
+                       (const int32_t*)labels, N, C, (const uint32_t*)bits, w.words, rep);
+  hipLaunchKernelGGL(relabel_kernel, dim3(tblocks), dim3(256), 0, stream, labels,
+                     (const int32_t*)rep, N, C, total);
+  for (int32_t r = 0; r < rounds; ++r) {
+    hipError_t e = launch_cluster_layout(labels, bh, N, C, 1, start, sizes, slot, token, lay_ws,
+                                         stream);
+    if (e != hipSuccess) return e;
+    if (in_lds)
+      hipLaunchKernelGGL(pair_kernel<true>, dim3((uint32_t)bh), dim3(kTailThreads), shmem,
+                         stream,
+                         (const int32_t*)sizes, C, bits, w.words, block, move_to, cut);
+    else
+      hipLaunchKernelGGL(pair_kernel<false>, dim3((uint32_t)bh), dim3(kTailThreads), shmem,
+                         stream,
+                         (const int32_t*)sizes, C, bits, w.words, block, move_to, cut);
+    hipLaunchKernelGGL(move_kernel, dim3(tblocks), dim3(256), 0, stream, labels,
+                       (const int32_t*)slot, (const int32_t*)start, (const int32_t*)move_to,
+                       (const int32_t*)cut, N, C, total);
+  }
+  hipLaunchKernelGGL(popcount_kernel, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, stream,
+                     (const uint32_t*)bits, counts, w.words, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_csr_from_bits(bits, counts, row_ptr_out, col_idx_out, rows, w.words, stream);
+}
 
 int64_t cluster_lcap(int32_t N, int32_t C, int32_t align) {
   return ((int64_t)N + (int64_t)C * (align - 1) + align - 1) / align * align;

@@ -115,6 +115,17 @@ hipError_t launch_cluster_permute(const void* src, void* dst, int elt_bytes, int
                                   const int32_t* map, const int32_t* start, bool inverse,
                                   hipStream_t stream);
 
+struct TailWs {
+  size_t bits_off, rep_off, move_off, cut_off, counts_off, start_off, sizes_off, slot_off,
+      token_off, layout_off, total;
+  int32_t words;
+};
+TailWs tail_ws_layout(int32_t bh, int32_t N, int32_t C, int32_t nk);
+hipError_t launch_tail_merge(int32_t* labels, int32_t bh, int32_t N, int32_t C, int32_t nk,
+                             int32_t block, int32_t rounds, const int32_t* row_ptr,
+                             const int32_t* col_idx, int32_t* row_ptr_out, int32_t* col_idx_out,
+                             void* ws, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace svsa

@@ -80,12 +80,13 @@ class ClusteredAttention:
     ([iCATS] Sec. 4.1; [SVOO] QK co-clustering), chaining the cluster entry
     points: query k-means under the key clusters' metric (plain feature space
     on the first call) -> key k-means under the updated query clusters'
-    metric -> padded cluster layouts -> permuted Q, K, V -> cluster mask ->
+    metric -> cluster mask -> optional tail merging of the query clusters
+    ([iCATS] Sec. 4.3) -> padded cluster layouts -> permuted Q, K, V ->
     cluster attention -> token order.  Centroids persist between calls (warm
     start across denoising steps); initial centroids are the caller's."""
 
     def __init__(self, batch, heads, head_dim, n, q_clusters, k_clusters, align=64,
-                 q_iters=2, k_iters=2, device="cuda"):
+                 q_iters=2, k_iters=2, tail_merge=False, tail_rounds=2, device="cuda"):
         self.batch, self.heads, self.head_dim, self.n = batch, heads, head_dim, n
         self.nq, self.nk, self.align = q_clusters, k_clusters, align
         self.q_iters, self.k_iters = q_iters, k_iters
@@ -130,6 +131,13 @@ class ClusteredAttention:
         self.attn_ws = torch.empty(
             B.svsa_cluster_attn_workspace_bytes(batch, heads, n, q_clusters, n, k_clusters, align),
             dtype=torch.uint8, device=dev)
+        self.tail_merge, self.tail_rounds = tail_merge, tail_rounds
+        if tail_merge:
+            self.row_ptr_m = torch.empty_like(self.row_ptr)
+            self.col_idx_m = torch.empty_like(self.col_idx)
+            self.tail_ws = torch.empty(
+                B.svsa_tail_merge_workspace_bytes(batch, heads, n, q_clusters, k_clusters),
+                dtype=torch.uint8, device=dev)
         self.warm = False
 
     def set_centroids(self, qcent, kcent):
@@ -167,12 +175,20 @@ class ClusteredAttention:
                             self.row_ptr, self.col_idx, self.mask_ws, top_p=top_p,
                             keep_frac=keep_frac, stream=stream)
 
+    def merge_tails(self, stream=None):
+        """[iCATS] Sec. 4.3 tail merging of the query clusters (labels in place;
+        the merged mask goes to row_ptr_m / col_idx_m)."""
+        B.svsa_tail_merge(self.qlab, self.nq, self.nk, self.align, self.row_ptr, self.col_idx,
+                          self.row_ptr_m, self.col_idx_m, self.tail_ws, rounds=self.tail_rounds,
+                          stream=stream)
+
     def attend(self, row_ptr=None, col_idx=None, stream=None):
+        if row_ptr is None:
+            row_ptr, col_idx = ((self.row_ptr_m, self.col_idx_m) if self.tail_merge
+                                else (self.row_ptr, self.col_idx))
         B.svsa_cluster_attn(self.qp, self.kp, self.vp, self.op, self.n, self.q_start, self.qsize,
                             self.n, self.k_start, self.ksize, self.align,
-                            1.0 / sqrt(self.head_dim),
-                            self.row_ptr if row_ptr is None else row_ptr,
-                            self.col_idx if col_idx is None else col_idx, self.attn_ws,
+                            1.0 / sqrt(self.head_dim), row_ptr, col_idx, self.attn_ws,
                             stream=stream)
 
     def permute_out(self, stream=None):
@@ -182,7 +198,9 @@ class ClusteredAttention:
 
     def __call__(self, q, k, v, top_p=None, keep_frac=None, stream=None):
         self.cluster(q, k, stream)
-        self.layout(q, k, v, stream)
         self.build_mask(top_p, keep_frac, stream)
+        if self.tail_merge:
+            self.merge_tails(stream)
+        self.layout(q, k, v, stream)
         self.attend(stream=stream)
         return self.permute_out(stream)

@@ -388,6 +388,34 @@ SVSA_API int svsa_cluster_attn(const void* q, const void* k, const void* v, void
                                const int32_t* row_ptr, const int32_t* col_idx, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Workspace (device bytes) for svsa_tail_merge; 0 if the sizes are invalid. */
+SVSA_API size_t svsa_tail_merge_workspace_bytes(int32_t batch, int32_t heads, int32_t n,
+                                                int32_t nq, int32_t nk);
+
+/*
+ * Tail merging of the query clusters ([iCATS] Sec. 4.3 and App. E.1), this
+ * library's reading: (1) query clusters of one (b, h) whose kept key-cluster
+ * sets are identical merge into the lowest such index (the attention pattern
+ * is unchanged); (2) `rounds` times: every non-empty cluster whose size is
+ * not a multiple of `block` (its tail: size mod block tokens) finds the other
+ * such cluster with the most similar kept set (Jaccard |A n B| / |A u B|,
+ * compared exactly; ties: lowest index); mutually nearest pairs whose tails
+ * fit one block move the smaller tail (equal tails: the higher index's) - the
+ * donor's last members in token order - to the other cluster, whose kept set
+ * becomes the union of both.  Every token keeps at least the key clusters it
+ * had; emptied clusters keep their index and own no rows.
+ * labels: int32 [batch, heads, n], rewritten in place.
+ * row_ptr / col_idx: the cluster mask (rows (b, h, i) over nq query
+ *   clusters, columns key clusters < nk); row_ptr_out / col_idx_out: the
+ *   merged mask (capacity >= batch*heads*nq*nk), ascending columns.
+ * Limits: nq <= 4096, nk <= 4096, rounds <= 8.
+ */
+SVSA_API int svsa_tail_merge(int32_t* labels, int32_t batch, int32_t heads, int32_t n,
+                             int32_t nq, int32_t nk, int32_t block, int32_t rounds,
+                             const int32_t* row_ptr, const int32_t* col_idx,
+                             int32_t* row_ptr_out, int32_t* col_idx_out, int64_t col_capacity,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /*
  * SNR-guided top-p schedule ([iCATS] Sec. 4.2 "SNR-Guided Sparsity" and
  * App. A; the per-model pmin and tau of App. B).  Host-only: no GPU call,

@@ -409,3 +409,69 @@ def test_clustered_attention_all_kept_equals_dense():
         assert int(ca.row_ptr[-1].item()) == B * H * nq * nk
         sizes = ca.qsize.cpu().numpy()
         assert sizes.sum() == B * H * N
+
+
+@pytest.mark.parametrize("N,nq,nk,block", [(3000, 40, 30, 64), (2048, 24, 40, 32),
+                                           (500, 12, 9, 8)])
+def test_tail_merge_bit_exact(N, nq, nk, block):
+    """Integer work: labels and merged kept sets equal the oracle's exactly, on
+    seeded labels and kept sets with planted identical rows."""
+    m = _m()
+    H = 3
+    rng = np.random.default_rng(N + nq)
+    labels = cluster_labels(N, nq, 1, H, seed=nq, stream=3, empty=2)
+    K = rng.random((H, nq, nk)) < 0.35
+    K[:, 5] = K[:, 2]
+    K[:, nq - 1] = K[:, 0]
+    rp = np.zeros(H * nq + 1, np.int64)
+    rp[1:] = np.cumsum(K.reshape(-1, nk).sum(1))
+    ci = np.concatenate([np.nonzero(r)[0] for r in K.reshape(-1, nk)]).astype(np.int32)
+    lab_d = _dev(labels, torch.int32)
+    rp2 = torch.empty(H * nq + 1, dtype=torch.int32, device="cuda")
+    ci2 = torch.empty(H * nq * nk, dtype=torch.int32, device="cuda")
+    ws = torch.empty(m.svsa_tail_merge_workspace_bytes(1, H, N, nq, nk), dtype=torch.uint8,
+                     device="cuda")
+    gc.log(f"tail merge on the GPU: {H} heads, {N} tokens, {nq} clusters, block {block}")
+    m.svsa_tail_merge(lab_d, nq, nk, block, _dev(rp.astype(np.int32), torch.int32),
+                      _dev(ci, torch.int32), rp2, ci2, ws)
+    torch.cuda.synchronize()
+    g_lab = lab_d.cpu().numpy()
+    g_rp = rp2.cpu().numpy().astype(np.int64)
+    g_ci = ci2[: int(g_rp[-1])].cpu().numpy()
+    moved = 0
+    for h in range(H):
+        o_lab, o_R, _ = orc.tail_merge(labels[0, h], K[h], block)
+        assert np.array_equal(g_lab[0, h], o_lab), h
+        for i in range(nq):
+            r = h * nq + i
+            assert np.array_equal(g_ci[g_rp[r]: g_rp[r + 1]], np.nonzero(o_R[i])[0]), (h, i)
+        moved += int(np.sum(o_lab != labels[0, h]))
+    gc.log(f"tail merge: {moved} tokens relabelled")
+    assert moved > 0
+
+
+def test_clustered_attention_tail_merge_all_kept_equals_dense():
+    """With every key cluster kept all kept sets are equal, so tail merging
+    folds each head into one query cluster; the output is still dense
+    attention."""
+    m = _m()
+    inp = gc.inputs("small")
+    B, H, N, D = inp.q.shape
+    nq, nk = 16, 32
+    ca = m.ClusteredAttention(B, H, D, N, nq, nk, align=64, q_iters=2, k_iters=2,
+                              tail_merge=True)
+    xq, xk = orc.widen(inp.q), orc.widen(inp.k)
+    sq = cluster_seeds(N, nq, B, H, seed=1, stream=1)
+    sk = cluster_seeds(N, nk, B, H, seed=1, stream=2)
+    qc = np.stack([np.stack([xq[b, h, sq[b, h]] for h in range(H)]) for b in range(B)])
+    kc = np.stack([np.stack([xk[b, h, sk[b, h]] for h in range(H)]) for b in range(B)])
+    ca.set_centroids(_dev(qc, torch.float64), _dev(kc, torch.float64))
+    ref = orc.dense_attention(inp.q, inp.k, inp.v, 1 / np.sqrt(D))
+    qd, kd, vd = (gc.bits_to_dev(a) for a in (inp.q, inp.k, inp.v))
+    out = ca(qd, kd, vd, top_p=np.ones(H, np.float32))
+    torch.cuda.synchronize()
+    got = orc.widen(gc.dev_to_bits(out))
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert np.abs(got - ref).max() <= gc.MAX_ABS and rel <= gc.REL_L2
+    sizes = ca.qsize.cpu().numpy().reshape(B * H, nq)
+    assert np.all(np.count_nonzero(sizes, axis=1) == 1)
