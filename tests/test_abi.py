@@ -197,3 +197,54 @@ def test_snr_top_p_argument_errors(mod):
     assert np.all(out == -1.0)                                            # nothing written
     with pytest.raises(mod.SvsaError):
         mod.svsa_snr_top_p([0.5, 2.0], 0, 0.7, 0.9)
+
+
+def test_cluster_entry_points_argument_errors(mod):
+    """Host-side validation of the cluster entry points (no GPU call)."""
+    lib = mod.library()
+    P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(8)]
+    E_INV, E_UNS, E_WS, E_CAP = -1, -2, -3, -4
+    # sizes and capacities
+    assert mod.svsa_cluster_capacity(100, 10, 64) == ((100 + 10 * 63 + 63) // 64) * 64
+    assert mod.svsa_cluster_capacity(100, 10, 48) == 0                       # not a power of two
+    assert mod.svsa_cluster_capacity(100, 5000, 64) == 0                     # > 4096 clusters
+    assert mod.svsa_kmeans_workspace_bytes(1, 2, 1000, 16, 64) > 0
+    assert mod.svsa_kmeans_workspace_bytes(1, 2, 1000, 0, 64) == 0
+    ws = mod.svsa_kmeans_workspace_bytes(1, 2, 1000, 16, 64)
+    km = lambda D=64, it=2, C=16, wsb=ws: lib.svsa_kmeans(P[0], 1, 2, 1000, D, None, P[1], C, it,
+                                                         P[2], P[3], P[4], wsb, None)
+    assert km(D=96) == E_UNS
+    assert km(it=0) == E_INV
+    assert km(C=5000) == E_INV
+    assert km(wsb=ws - 1) == E_WS
+    assert lib.svsa_cluster_metric(P[0], P[1], 1, 2, 16, 72, P[2], None) == E_UNS   # D % 16
+    lw = mod.svsa_cluster_layout_workspace_bytes(1, 2, 1000, 16)
+    assert lib.svsa_cluster_layout(P[0], 1, 2, 1000, 16, 3, P[1], P[2], None, P[3], P[4], lw,
+                                   None) == E_INV                                   # align 3
+    assert lib.svsa_cluster_layout(P[0], 1, 2, 1000, 16, 64, P[1], P[2], None, P[3], P[4],
+                                   lw - 1, None) == E_WS
+    assert lib.svsa_cluster_permute(P[0], P[0], 0, 1, 2, 1000, 64, 16, 64, P[1], P[2], 0,
+                                    None) == E_INV                                  # in place
+    mw = mod.svsa_cluster_mask_workspace_bytes(1, 2, 16, 32)
+    fa = (ctypes.c_float * 2)(0.9, 0.9)
+    cm = lambda cap=2 * 16 * 32, wsb=mw, tp=fa, kf=None: lib.svsa_cluster_mask(
+        P[0], P[1], P[2], 1, 2, 16, 32, 64, 0.125, tp, kf, P[3], P[4], cap, P[5], wsb, None)
+    assert cm(cap=2 * 16 * 32 - 1) == E_CAP
+    assert cm(wsb=mw - 1) == E_WS
+    assert cm(tp=None) == E_INV                                                      # no rule
+    assert cm(kf=fa) == E_INV                                                        # two rules
+    aw = mod.svsa_cluster_attn_workspace_bytes(1, 2, 1000, 16, 1000, 32, 64)
+    ca = lambda D=64, al=64, wsb=aw, out=P[3]: lib.svsa_cluster_attn(
+        P[0], P[1], P[2], out, 1, 2, D, 1000, 16, P[4], P[5], 1000, 32, P[6], P[7], al, 0.125,
+        FAKE, FAKE2, FAKE, wsb, None)
+    assert ca(D=96) == E_UNS
+    assert ca(al=16) == E_INV
+    assert ca(wsb=aw - 1) == E_WS
+    assert ca(out=P[0]) == E_INV                                                     # out aliases q
+    tw = mod.svsa_tail_merge_workspace_bytes(1, 2, 1000, 16, 32)
+    tm = lambda rounds=2, block=64, cap=2 * 16 * 32, wsb=tw: lib.svsa_tail_merge(
+        P[0], 1, 2, 1000, 16, 32, block, rounds, P[1], P[2], P[3], P[4], cap, P[5], wsb, None)
+    assert tm(rounds=9) == E_INV
+    assert tm(block=0) == E_INV
+    assert tm(cap=2 * 16 * 32 - 1) == E_CAP
+    assert tm(wsb=tw - 1) == E_WS
