@@ -475,3 +475,156 @@ def test_clustered_attention_tail_merge_all_kept_equals_dense():
     assert np.abs(got - ref).max() <= gc.MAX_ABS and rel <= gc.REL_L2
     sizes = ca.qsize.cpu().numpy().reshape(B * H, nq)
     assert np.all(np.count_nonzero(sizes, axis=1) == 1)
+
+
+# ---------------------------------------------------------------- full size
+def _wan720_heads(heads=(0, 17)):
+    inp = gc.inputs("wan720")
+    sel = list(heads)
+    return inp.q[:, sel], inp.k[:, sel], inp.v[:, sel]
+
+
+def test_kmeans_assignment_full_size_sampled():
+    """Wan-720p shape (75,600 tokens, D 128, 1000 centroids, metric): one
+    assignment; 3000 seeded tokens per head re-decided by the oracle."""
+    q, k, _ = _wan720_heads()
+    B, H, N, D = k.shape
+    C = 1000
+    seeds = cluster_seeds(N, C, B, H, seed=5)
+    xw = orc.widen(k)
+    cents0 = np.stack([np.stack([xw[b, h, seeds[b, h]] for h in range(H)]) for b in range(B)])
+    G = _metric(H, D, 8)
+    _, labels, sizes = _gpu_kmeans(k, cents0, 1, G)
+    assert sizes.sum() == B * H * N
+    rng = np.random.default_rng(14)
+    tolerated = 0
+    for h in range(H):
+        toks = np.sort(rng.choice(N, 3000, replace=False))
+        for part in np.array_split(toks, 12):
+            d = orc.quad_distances(xw[0, h, part], cents0[0, h], G[0, h])
+            lab_o = np.argmin(d, axis=1)
+            diff = np.nonzero(labels[0, h, part] != lab_o)[0]
+            tol = _assign_tolerance(xw[0, h, part], cents0[0, h], G[0, h])
+            gap = d[diff, labels[0, h, part][diff]] - d[diff, lab_o[diff]]
+            assert np.all(gap <= tol[diff])
+            tolerated += diff.size
+    gc.log(f"wan720 k-means sample: {tolerated} near-tie labels of {2 * 3000}")
+    assert tolerated <= 6
+
+
+def test_cluster_mask_and_attention_full_size_sampled():
+    """Wan-720p shape with 400 query / 1000 key clusters (seeded labels, ten
+    empty key clusters), align 64: GPU means and cluster mask against the
+    oracle's over all rows, attention with the oracle's mask on 12 sampled
+    query clusters per head, and tail merging of the oracle's mask."""
+    m = _m()
+    q, k, v = _wan720_heads()
+    B, H, N, D = q.shape
+    nq, nk, align = 400, 1000, 64
+    qlab = cluster_labels(N, nq, B, H, seed=31, stream=1)
+    klab = cluster_labels(N, nk, B, H, seed=31, stream=2, empty=10)
+    f64 = dict(dtype=torch.float64, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    qd, kd, vd = (gc.bits_to_dev(a) for a in (q, k, v))
+    qbar, kbar = torch.zeros((B, H, nq, D), **f64), torch.zeros((B, H, nk, D), **f64)
+    qs, ks = torch.empty((B, H, nq), **i32), torch.empty((B, H, nk), **i32)
+    ws = torch.empty(m.svsa_cluster_means_workspace_bytes(B, H, N, nk), dtype=torch.uint8,
+                     device="cuda")
+    gc.log("wan720 clusters: GPU means")
+    m.svsa_cluster_means(qd, _dev(qlab, torch.int32), qbar, qs, ws)
+    m.svsa_cluster_means(kd, _dev(klab, torch.int32), kbar, ks, ws)
+    torch.cuda.synchronize()
+    gc.log("wan720 clusters: oracle means and scores")
+    qbar_o, qs_o = orc.cluster_means(q, qlab, nq)
+    kbar_o, ks_o = orc.cluster_means(k, klab, nk)
+    assert np.array_equal(qs.cpu().numpy(), qs_o) and np.array_equal(ks.cpu().numpy(), ks_o)
+    np.testing.assert_allclose(qbar.cpu().numpy(), qbar_o, rtol=1e-13, atol=1e-15)
+    ne = ks_o > 0
+    np.testing.assert_allclose(kbar.cpu().numpy()[ne], kbar_o[ne], rtol=1e-13, atol=1e-15)
+    S = np.stack([np.stack([orc.cluster_scores(qbar_o[0, h], kbar_o[0, h], ks_o[0, h],
+                                               1 / np.sqrt(D)) for h in range(H)])])
+    tp = np.full(H, 0.9, np.float32)
+    o_rp, o_ci = orc.cluster_mask(S, top_p=tp)
+    # GPU mask over every row
+    rows = B * H * nq
+    rp = torch.empty(rows + 1, **i32)
+    ci = torch.empty(rows * nk, **i32)
+    mws = torch.empty(m.svsa_cluster_mask_workspace_bytes(B, H, nq, nk), dtype=torch.uint8,
+                      device="cuda")
+    m.svsa_cluster_mask(qbar, kbar, ks, 1 / np.sqrt(D), rp, ci, mws, top_p=tp)
+    torch.cuda.synchronize()
+    g_rp = rp.cpu().numpy().astype(np.int64)
+    g_ci = ci[: int(g_rp[-1])].cpu().numpy()
+    bad = _cluster_mask_failures(S, g_rp, g_ci, o_rp, o_ci, tp)
+    assert not bad, bad[:5]
+    # attention with the oracle's mask
+    lws = torch.empty(m.svsa_cluster_layout_workspace_bytes(B, H, N, nk), dtype=torch.uint8,
+                      device="cuda")
+    lay = {}
+    for tag, lab, C in (("q", qlab, nq), ("k", klab, nk)):
+        cap = m.svsa_cluster_capacity(N, C, align)
+        t = dict(start=torch.empty((B, H, C + 1), **i32), sizes=torch.empty((B, H, C), **i32),
+                 slot=torch.empty((B, H, N), **i32), token=torch.empty((B, H, cap), **i32),
+                 cap=cap)
+        m.svsa_cluster_layout(_dev(lab, torch.int32), C, align, t["start"], t["sizes"],
+                              t["slot"], t["token"], lws)
+        lay[tag] = t
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((B, H, lay["q"]["cap"], D), **bf)
+    kp = torch.empty((B, H, lay["k"]["cap"], D), **bf)
+    vp = torch.empty_like(kp)
+    op = torch.empty_like(qp)
+    m.svsa_cluster_permute(qd, qp, N, nq, align, lay["q"]["token"], lay["q"]["start"])
+    m.svsa_cluster_permute(kd, kp, N, nk, align, lay["k"]["token"], lay["k"]["start"])
+    m.svsa_cluster_permute(vd, vp, N, nk, align, lay["k"]["token"], lay["k"]["start"])
+    aws = torch.empty(m.svsa_cluster_attn_workspace_bytes(B, H, N, nq, N, nk, align),
+                      dtype=torch.uint8, device="cuda")
+    gc.log(f"wan720 clusters: attention on {int(o_rp[-1])} kept pairs")
+    m.svsa_cluster_attn(qp, kp, vp, op, N, lay["q"]["start"], lay["q"]["sizes"], N,
+                        lay["k"]["start"], lay["k"]["sizes"], align, 1 / np.sqrt(D),
+                        _dev(o_rp.astype(np.int32), torch.int32),
+                        _dev(o_ci.astype(np.int32), torch.int32), aws)
+    out = torch.empty_like(qd)
+    m.svsa_cluster_permute(op, out, N, nq, align, lay["q"]["slot"], lay["q"]["start"],
+                           inverse=True)
+    torch.cuda.synchronize()
+    out_bits = gc.dev_to_bits(out)
+    rng = np.random.default_rng(15)
+    g_all, r_all = [], []
+    for h in range(H):
+        counts = np.diff(o_rp)[h * nq:(h + 1) * nq]
+        pick = {int(np.argmax(counts)), int(np.argmin(counts))}
+        pick |= set(rng.choice(nq, 10, replace=False).tolist())
+        for i in sorted(pick):
+            r = h * nq + i
+            toks, ref = orc.cluster_attention_rows(q[0, h], k[0, h], v[0, h], qlab[0, h],
+                                                   klab[0, h], i, o_ci[o_rp[r]: o_rp[r + 1]],
+                                                   1 / np.sqrt(D))
+            g_all.append(orc.widen(out_bits[0, h, toks]).ravel())
+            r_all.append(ref.ravel())
+    g, r = np.concatenate(g_all), np.concatenate(r_all)
+    max_abs = float(np.abs(g - r).max())
+    rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    gc.log(f"wan720 clusters: attention max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+    # tail merging of the oracle's mask, bit-exact
+    lab_d = _dev(qlab, torch.int32)
+    rp2 = torch.empty(rows + 1, **i32)
+    ci2 = torch.empty(rows * nk, **i32)
+    tws = torch.empty(m.svsa_tail_merge_workspace_bytes(B, H, N, nq, nk), dtype=torch.uint8,
+                      device="cuda")
+    m.svsa_tail_merge(lab_d, nq, nk, align, _dev(o_rp.astype(np.int32), torch.int32),
+                      _dev(o_ci.astype(np.int32), torch.int32), rp2, ci2, tws)
+    torch.cuda.synchronize()
+    t_lab = lab_d.cpu().numpy()
+    t_rp = rp2.cpu().numpy().astype(np.int64)
+    t_ci = ci2[: int(t_rp[-1])].cpu().numpy()
+    for h in range(H):
+        K = np.zeros((nq, nk), bool)
+        for i in range(nq):
+            K[i, o_ci[o_rp[h * nq + i]: o_rp[h * nq + i + 1]]] = True
+        lab_o, R_o, _ = orc.tail_merge(qlab[0, h], K, align)
+        assert np.array_equal(t_lab[0, h], lab_o)
+        for i in range(nq):
+            r = h * nq + i
+            assert np.array_equal(t_ci[t_rp[r]: t_rp[r + 1]], np.nonzero(R_o[i])[0])
