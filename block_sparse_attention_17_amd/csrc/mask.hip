@@ -10,7 +10,8 @@
 // inside a band of width w when d <= w - 1.
 //
 // Kernels (all float64 arithmetic, all deterministic):
-//   logits_kernel   L = scale * Qbar Kbar^T, 64x64 output tile per workgroup
+//   logits_kernel   L = scale * Qbar Kbar^T on the float64 MFMA, 64x64 output
+//                   tile per workgroup
 //   select_kernel   one workgroup per row: softmax, radix select of the
 //                   boundary block over the score bits with fixed-point mass
 //                   histograms, kept bitmap, row count
@@ -29,9 +30,17 @@ struct HeadParams {
 };
 
 // ---------------------------------------------------------------------------
-// L[bh][i][j] = scale * sum_d qbar[bh][i][d] * kbar[bh][j][d]
+// L[bh][i][j] = scale * sum_d qbar[bh][i][d] * kbar[bh][j][d], a dense float64
+// contraction on the float64 matrix cores (v_mfma_f64_16x16x4f64).  64 x 64
+// output tile per workgroup; wave w owns rows 32 (w / 2) .. +31 and columns
+// 32 (w % 2) .. +31 as 2 x 2 tiles of 16 x 16.  Operand layout of the
+// instruction: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and
+// holds D[4 r + l / 16][l % 16] in its r-th result.  Q-bar and K-bar chunks of
+// kDc dims go through LDS with an odd row stride (no bank conflicts on the
+// 16-row operand reads).
 // ---------------------------------------------------------------------------
-constexpr int kTile = 64, kDc = 32, kLThreads = 256;
+constexpr int kTile = 64, kDc = 32, kLThreads = 256, kLdsStride = kDc + 1;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // With ksizes (cluster mode) every logit of key cluster j gets + ln n_j, and
 // empty key clusters get -inf.
@@ -39,58 +48,65 @@ __global__ void __launch_bounds__(kLThreads)
 logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
               const int32_t* __restrict__ ksizes, double* __restrict__ L, int32_t nq,
               int32_t nk, int32_t D, double scale, int32_t tiles_q, int32_t tiles_k) {
-  __shared__ double As[kDc][kTile + 1];
-  __shared__ double Bs[kDc][kTile + 1];
+  __shared__ double As[kTile * kLdsStride];
+  __shared__ double Bs[kTile * kLdsStride];
   const int64_t bh = blockIdx.x / (tiles_q * tiles_k);
   const int32_t t2 = blockIdx.x % (tiles_q * tiles_k);
   const int32_t i0 = (t2 / tiles_k) * kTile, j0 = (t2 % tiles_k) * kTile;
   const double* qb = qbar + bh * nq * D;
   const double* kb = kbar + bh * nk * D;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  double acc[4][4];
+  const int32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int32_t wr = 32 * (wave / 2), wc = 32 * (wave % 2);
+  const int32_t lr = lane % 16, lk = lane / 16;
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   for (int32_t dc = 0; dc < D; dc += kDc) {
-    const int dl = threadIdx.x % kDc;
-    for (int r = threadIdx.x / kDc; r < kTile; r += kLThreads / kDc) {
-      const bool dok = dc + dl < D;
-      As[dl][r] = (i0 + r < nq && dok) ? qb[(int64_t)(i0 + r) * D + dc + dl] : 0.0;
-      Bs[dl][r] = (j0 + r < nk && dok) ? kb[(int64_t)(j0 + r) * D + dc + dl] : 0.0;
+    // stage rows i0 .. i0 + 63 and j0 .. j0 + 63, dims dc .. dc + kDc - 1
+    for (int32_t e = threadIdx.x; e < kTile * kDc; e += kLThreads) {
+      const int32_t r = e / kDc, d = e % kDc;
+      const bool dok = dc + d < D;
+      As[r * kLdsStride + d] = (i0 + r < nq && dok) ? qb[(int64_t)(i0 + r) * D + dc + d] : 0.0;
+      Bs[r * kLdsStride + d] = (j0 + r < nk && dok) ? kb[(int64_t)(j0 + r) * D + dc + d] : 0.0;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int d = 0; d < kDc; ++d) {
-      double av[4], bv[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[d][ty + 16 * a];
+    for (int ks = 0; ks < kDc / 4; ++ks) {
+      const int32_t d = 4 * ks + lk;
+      double av[2], bv[2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[d][tx + 16 * b];
+      for (int a = 0; a < 2; ++a) av[a] = As[(wr + 16 * a + lr) * kLdsStride + d];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < 2; ++b) bv[b] = Bs[(wc + 16 * b + lr) * kLdsStride + d];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int32_t i = i0 + ty + 16 * a;
-    if (i >= nq) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int32_t j = j0 + tx + 16 * b;
-      if (j >= nk) continue;
-      double v = acc[a][b] * scale;
-      if (ksizes) {
-        const int32_t n = ksizes[bh * nk + j];
-        v = n > 0 ? v + log((double)n) : -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      const int32_t i = i0 + wr + 16 * a + 4 * r + lk;
+      if (i >= nq) continue;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int32_t j = j0 + wc + 16 * b + lr;
+        if (j >= nk) continue;
+        double v = acc[a][b][r] * scale;
+        if (ksizes) {
+          const int32_t n = ksizes[bh * nk + j];
+          v = n > 0 ? v + log((double)n) : -INFINITY;
+        }
+        L[(bh * nq + i) * nk + j] = v;
       }
-      L[(bh * nq + i) * nk + j] = v;
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
