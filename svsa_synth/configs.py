@@ -77,6 +77,9 @@ CONFIGS = {
     # as few as 4 tokens, so whole sub-blocks are padding)
     "tiny_pad3d": Config("tiny_pad3d", 10, 1, 2, 128, (3, 9, 20), (2, 4, 16), "bf16", (0.9,),
                          pad3d=True),
+    # the largest block count the attention and mask entry points accept: 4096
+    # blocks of 64 tokens (262,144 tokens, one head)
+    "maxnb": Config("maxnb", 11, 1, 1, 64, (16, 64, 256), (4, 4, 4), "bf16", (0.9,)),
     # two independent samples of the small shape in one call (batch > 1)
     "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
                        pe_freq="per_head"),

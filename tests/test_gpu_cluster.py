@@ -628,3 +628,31 @@ def test_cluster_mask_and_attention_full_size_sampled():
         for i in range(nq):
             r = h * nq + i
             assert np.array_equal(t_ci[t_rp[r]: t_rp[r + 1]], np.nonzero(R_o[i])[0])
+
+
+def test_cluster_attention_at_the_key_sub_block_limit():
+    """4096 key clusters over 262,144 tokens (align 64: 8,128 key sub-blocks,
+    near the 8,192 the schedule entries can index) and 512 query clusters:
+    the mask over every row and attention on sampled query clusters."""
+    c = _ClusterCase("maxnb", 512, 4096, 64, k_empty=0, seed=19)
+    assert c.cap_k // 64 > 8000
+    tp = np.full(c.H, 0.9, np.float32)
+    g_rp, g_ci = c.gpu_mask(tp)
+    o_rp, o_ci = orc.cluster_mask(c.S, top_p=tp)
+    assert not _cluster_mask_failures(c.S, g_rp, g_ci, o_rp, o_ci, tp)
+    out = c.gpu_attention(o_rp, o_ci)
+    rng = np.random.default_rng(20)
+    counts = np.diff(o_rp)
+    pick = {int(np.argmax(counts)), int(np.argmin(counts))} | set(rng.choice(512, 6, replace=False).tolist())
+    g_all, r_all = [], []
+    for i in sorted(pick):
+        toks, ref = orc.cluster_attention_rows(c.inp.q[0, 0], c.inp.k[0, 0], c.inp.v[0, 0],
+                                               c.qlab[0, 0], c.klab[0, 0], i,
+                                               o_ci[o_rp[i]: o_rp[i + 1]], 1 / np.sqrt(c.D))
+        g_all.append(orc.widen(out[0, 0, toks]).ravel())
+        r_all.append(ref.ravel())
+    g, r = np.concatenate(g_all), np.concatenate(r_all)
+    max_abs = float(np.abs(g - r).max())
+    rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    gc.log(f"maxnb clusters: attention max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2

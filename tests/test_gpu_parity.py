@@ -96,7 +96,7 @@ MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
               ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
               ("hv720", 0.9, None), ("hv720", None, "keep"), ("small_b2", 0.9, None),
               ("wan720_psa", 0.9, None), ("small_pad3d", 0.9, None), ("tiny_pad3d", 0.9, None),
-              ("wan720_psa3d", 0.9, None)]
+              ("wan720_psa3d", 0.9, None), ("maxnb", 0.9, None)]
 
 
 @pytest.mark.parametrize("name,p,mode", MASK_CASES)
@@ -159,7 +159,7 @@ def test_block_mask_over_snr_schedule():
 
 # ---------------------------------------------------------------- stage 4
 ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
-              ("small_b2", None), ("small_pad3d", None), ("tiny_pad3d", None)]
+              ("small_b2", None), ("small_pad3d", None), ("tiny_pad3d", None), ("maxnb", 12)]
 
 
 @pytest.mark.parametrize("name,per_head", ATTN_CASES)
