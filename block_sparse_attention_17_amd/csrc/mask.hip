@@ -31,15 +31,15 @@ struct HeadParams {
 
 // ---------------------------------------------------------------------------
 // L[bh][i][j] = scale * sum_d qbar[bh][i][d] * kbar[bh][j][d], a dense float64
-// contraction on the float64 matrix cores (v_mfma_f64_16x16x4f64).  64 x 64
-// output tile per workgroup; wave w owns rows 32 (w / 2) .. +31 and columns
-// 32 (w % 2) .. +31 as 2 x 2 tiles of 16 x 16.  Operand layout of the
+// contraction on the float64 matrix cores (v_mfma_f64_16x16x4f64).  128 x 128
+// output tile per workgroup of 8 waves; wave w owns rows 32 (w / 2) .. +31 and
+// columns 64 (w % 2) .. +63 as 2 x 4 tiles of 16 x 16.  Operand layout of the
 // instruction: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and
 // holds D[4 r + l / 16][l % 16] in its r-th result.  Q-bar and K-bar chunks of
 // kDc dims go through LDS with an odd row stride (no bank conflicts on the
 // 16-row operand reads).
 // ---------------------------------------------------------------------------
-constexpr int kTile = 64, kDc = 32, kLThreads = 256, kLdsStride = kDc + 1;
+constexpr int kTile = 128, kDc = 16, kLThreads = 512, kLdsStride = kDc + 1;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // With ksizes (cluster mode) every logit of key cluster j gets + ln n_j, and
@@ -56,13 +56,13 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
   const double* qb = qbar + bh * nq * D;
   const double* kb = kbar + bh * nk * D;
   const int32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int32_t wr = 32 * (wave / 2), wc = 32 * (wave % 2);
+  const int32_t wr = 32 * (wave / 2), wc = 64 * (wave % 2);
   const int32_t lr = lane % 16, lk = lane / 16;
-  f64x4 acc[2][2];
+  f64x4 acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   for (int32_t dc = 0; dc < D; dc += kDc) {
     // stage rows i0 .. i0 + 63 and j0 .. j0 + 63, dims dc .. dc + kDc - 1
@@ -76,15 +76,15 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 #pragma unroll
     for (int ks = 0; ks < kDc / 4; ++ks) {
       const int32_t d = 4 * ks + lk;
-      double av[2], bv[2];
+      double av[2], bv[4];
 #pragma unroll
       for (int a = 0; a < 2; ++a) av[a] = As[(wr + 16 * a + lr) * kLdsStride + d];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = Bs[(wc + 16 * b + lr) * kLdsStride + d];
+      for (int b = 0; b < 4; ++b) bv[b] = Bs[(wc + 16 * b + lr) * kLdsStride + d];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
@@ -96,7 +96,7 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
       const int32_t i = i0 + wr + 16 * a + 4 * r + lk;
       if (i >= nq) continue;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 4; ++b) {
         const int32_t j = j0 + wc + 16 * b + lr;
         if (j >= nk) continue;
         double v = acc[a][b][r] * scale;
