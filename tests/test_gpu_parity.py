@@ -179,6 +179,25 @@ def test_attention_matches_oracle(name, per_head):
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
+def test_attention_whole_heads_wan720():
+    """Full Wan-720p size, top-p 0.9: every query block of four whole heads
+    (the heaviest, the lightest and two median heads by kept blocks)."""
+    cfg = get_config("wan720")
+    run, orun = gc.gpu_run("wan720"), gc.oracle_run("wan720")
+    o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, 0.9, np.float32), band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    kept = np.diff(o_rp).reshape(cfg.heads, cfg.nb).sum(1)
+    order = np.argsort(kept, kind="stable")
+    heads = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]),
+                    int(order[len(order) // 2 - 1])})
+    for h in heads:
+        rows = [(0, h, i) for i in range(cfg.nb)]
+        max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+        gc.log(f"wan720 head {h} ({kept[h]} kept blocks), all {cfg.nb} q-blocks: "
+               f"max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
 def test_attention_psa_block_shape_wan720():
     """384-token blocks (PSA's 3x8x16 PSABlock shape): the attention kernel runs
     them as six 64-token sub-blocks; rows of five heads, incl. the tail block."""
