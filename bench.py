@@ -104,6 +104,17 @@ def kept_flops_from_csr(rp, ci, n, D):
     return 4 * D * int(np.sum(n[row_i] * n[ci[: rp[-1]]]))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
     """The oracle on a bounded sample: the full mask stages of one head plus the
     attention of seeded query blocks of that head, extrapolated to a whole step."""
@@ -142,6 +153,7 @@ def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
         "unit": "TFLOP/s",
         "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": (f"fp64 NumPy oracle: permute+pool+scores+top-p mask of 1 head "
                    f"({t_mask:.2f} s) and attention of {done}/{nb} seeded query blocks of that "
