@@ -80,6 +80,9 @@ CONFIGS = {
     # the largest block count the attention and mask entry points accept: 4096
     # blocks of 64 tokens (262,144 tokens, one head)
     "maxnb": Config("maxnb", 11, 1, 1, 64, (16, 64, 256), (4, 4, 4), "bf16", (0.9,)),
+    # more (batch, head) pairs than the work queues place by measured work
+    # (2100 > 2048): a tiny grid, batch 2100, one head
+    "manybh": Config("manybh", 12, 2100, 1, 64, (4, 8, 8), (4, 4, 4), "bf16", (0.9,)),
     # two independent samples of the small shape in one call (batch > 1)
     "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
                        pe_freq="per_head"),

@@ -179,6 +179,22 @@ def test_attention_matches_oracle(name, per_head):
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
+def test_more_pairs_than_the_queues_balance():
+    """2100 (batch, head) pairs (beyond the 2048 the work queues place by
+    measured work): mask equal to the oracle's, attention on sampled pairs."""
+    cfg = get_config("manybh")
+    run, orun = gc.gpu_run("manybh"), gc.oracle_run("manybh")
+    tp = np.full(cfg.heads, 0.9, np.float32)
+    g_rp, g_ci = run.mask(top_p=tp, band=cfg.band)
+    o_rp, o_ci = orun.mask(top_p=tp, band=cfg.band)
+    assert np.array_equal(g_rp, o_rp) and np.array_equal(g_ci, o_ci)
+    out_bits = run.attention(o_rp, o_ci)
+    rows = [(b, 0, i) for b in (0, 1, 777, 2047, 2048, 2099) for i in range(cfg.nb)]
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+    gc.log(f"manybh: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
 def test_attention_whole_heads_wan720():
     """Full Wan-720p size, top-p 0.9: every query block of four whole heads
     (the heaviest, the lightest and two median heads by kept blocks)."""
