@@ -66,8 +66,9 @@ constexpr int kWin = 8;   // LDS operand reads in flight ahead of the MFMA strea
 constexpr int kPre = 4;   // P V operands read before the barrier that opens an M phase
 
 // ---------------------------------------------------------------------------
-// Schedule: per item (b, h, group of query sub-blocks) the ascending union of
-// the group's kept key sub-blocks; entry = j | (valid << 13) | (mask << 24):
+// Schedule: per item (b, h, group of query sub-blocks) the union of the
+// group's kept key sub-blocks, ascending from the group's own diagonal key
+// sub-block and wrapping around (fixed-size blocks; cluster lists start at 0); entry = j | (valid << 13) | (mask << 24):
 // j the key sub-block (< 8192), valid its valid tokens (its first slots; key
 // sub-blocks with none are left out), bit m of mask set when the m-th query
 // sub-block of the group keeps j.
@@ -99,6 +100,7 @@ struct GeomSched {
     *j1 = *j0 + ratio;
   }
   __device__ int32_t kvalid(int64_t bh, int32_t j) const { return qvalid(bh, j); }
+  __device__ int32_t rotation(int32_t i) const { return i; }   // same layout both sides
 };
 
 // last cluster c in [0, n) with start[c] <= pos (the one whose slots hold pos)
@@ -138,6 +140,7 @@ struct TableSched {
     const int32_t c = owner_of(st, nk, pos);
     return clamp_valid(st[c] + k_size[bh * nk + c] - pos, sub);
   }
+  __device__ int32_t rotation(int32_t) const { return 0; }
 };
 
 template <typename Sched>
@@ -173,9 +176,14 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   int32_t* out = list + item * nb;
   int32_t off = 0;
   const int lane = t & 63, wv = t >> 6;
+  // the list starts at the group's own diagonal key sub-block and wraps
+  // around, so neighbouring query groups walk the same keys at the same time
+  int32_t j0 = sc.rotation(g * group_size);
+  j0 = j0 < nb ? j0 : 0;
   for (int32_t base = 0; base < nb; base += kSchedThreads) {
-    const int32_t j = base + t;
-    const uint32_t m = j < nb ? mask[j] : 0u;
+    const int32_t jj = base + t;
+    const int32_t j = jj < nb ? (jj + j0 < nb ? jj + j0 : jj + j0 - nb) : nb;
+    const uint32_t m = jj < nb ? mask[j] : 0u;
     const unsigned long long bal = __ballot(m != 0u);
     const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wave_tot[wv] = __popcll(bal);
