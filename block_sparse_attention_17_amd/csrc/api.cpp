@@ -40,6 +40,12 @@ bool make_geom(const svsa_geom* in, Geom* g) {
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Alignment the kernels rely on: 16 bytes for bf16 / f32 tensors (16-byte
+// vector loads and stores), 8 for float64 arrays, 4 for int32 arrays, 256 for
+// workspaces (carved into 256-byte aligned regions).  NULL passes here; the
+// NULL checks are separate.
+bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 int elt_bytes(int32_t dtype) {
   return dtype == SVSA_BF16 ? 2 : dtype == SVSA_F32 ? 4 : 0;
 }
@@ -108,6 +114,9 @@ int svsa_kmeans(const void* x, int32_t batch, int32_t heads, int32_t n, int32_t 
                 const double* metric, double* centroids, int32_t clusters, int32_t iters,
                 int32_t* labels, int32_t* sizes, void* workspace, size_t ws_bytes,
                 void* stream) {
+  if (!(al(x, 16) && al(metric, 8) && al(centroids, 8) && al(labels, 4) && al(sizes, 4) &&
+        al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!x || !centroids || !labels || !sizes || !workspace || iters < 1 || head_dim < 1 ||
       !cluster_sizes_ok(batch, heads, n, clusters, head_dim))
     return SVSA_E_INVALID;
@@ -128,6 +137,8 @@ size_t svsa_cluster_means_workspace_bytes(int32_t batch, int32_t heads, int32_t 
 int svsa_cluster_means(const void* x, const int32_t* labels, int32_t batch, int32_t heads,
                        int32_t n, int32_t head_dim, int32_t clusters, double* centroids,
                        int32_t* sizes, void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(x, 2) && al(labels, 4) && al(centroids, 8) && al(sizes, 4) && al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!x || !labels || !centroids || !sizes || !workspace || head_dim < 1 ||
       !cluster_sizes_ok(batch, heads, n, clusters, head_dim))
     return SVSA_E_INVALID;
@@ -150,6 +161,7 @@ int svsa_cluster_means(const void* x, const int32_t* labels, int32_t batch, int3
 int svsa_cluster_metric(const double* centroids, const int32_t* sizes, int32_t batch,
                         int32_t heads, int32_t clusters, int32_t head_dim, double* metric,
                         void* stream) {
+  if (!(al(centroids, 8) && al(sizes, 4) && al(metric, 8))) return SVSA_E_INVALID;
   if (!centroids || !sizes || !metric || head_dim < 1 ||
       !cluster_sizes_ok(batch, heads, 1, clusters, head_dim))
     return SVSA_E_INVALID;
@@ -175,6 +187,9 @@ int svsa_cluster_layout(const int32_t* labels, int32_t batch, int32_t heads, int
                         int32_t clusters, int32_t align, int32_t* start, int32_t* sizes,
                         int32_t* slot, int32_t* token, void* workspace, size_t ws_bytes,
                         void* stream) {
+  if (!(al(labels, 4) && al(start, 4) && al(sizes, 4) && al(slot, 4) && al(token, 4) &&
+        al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!labels || !start || !sizes || !token || !cluster_sizes_ok(batch, heads, n, clusters, 1))
     return SVSA_E_INVALID;
   const int64_t lcap = svsa_cluster_capacity(n, clusters, align);
@@ -191,6 +206,7 @@ int svsa_cluster_permute(const void* src, void* dst, int32_t dtype, int32_t batc
                          int32_t n, int32_t head_dim, int32_t clusters, int32_t align,
                          const int32_t* map, const int32_t* start, int32_t inverse,
                          void* stream) {
+  if (!(al(src, 16) && al(dst, 16) && al(map, 4) && al(start, 4))) return SVSA_E_INVALID;
   if (!src || !dst || !map || !start || head_dim < 1 ||
       !cluster_sizes_ok(batch, heads, n, clusters, 1))
     return SVSA_E_INVALID;
@@ -219,6 +235,9 @@ int svsa_tail_merge(int32_t* labels, int32_t batch, int32_t heads, int32_t n, in
                     int32_t nk, int32_t block, int32_t rounds, const int32_t* row_ptr,
                     const int32_t* col_idx, int32_t* row_ptr_out, int32_t* col_idx_out,
                     int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(labels, 4) && al(row_ptr, 4) && al(col_idx, 4) && al(row_ptr_out, 4) &&
+        al(col_idx_out, 4) && al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!labels || !row_ptr || !col_idx || !row_ptr_out || !col_idx_out || block < 1 ||
       rounds < 0 || rounds > 8 || nk < 1 || !cluster_sizes_ok(batch, heads, n, nq, 1))
     return SVSA_E_INVALID;
@@ -247,6 +266,7 @@ const char* svsa_status_string(int status) {
 
 int svsa_tile_permute(const void* src, void* dst, int32_t dtype, int32_t batch, int32_t heads,
                       int32_t head_dim, const svsa_geom* gin, int32_t inverse, void* stream) {
+  if (!(al(src, 16) && al(dst, 16))) return SVSA_E_INVALID;
   Geom g;
   if (!src || !dst || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
     return SVSA_E_INVALID;
@@ -266,6 +286,7 @@ int svsa_tile_permute(const void* src, void* dst, int32_t dtype, int32_t batch, 
 
 int svsa_pool(const void* x_tiled, int32_t dtype, double* out, int32_t batch, int32_t heads,
               int32_t head_dim, const svsa_geom* gin, void* stream) {
+  if (!(al(x_tiled, 16) && al(out, 8))) return SVSA_E_INVALID;
   Geom g;
   if (!x_tiled || !out || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
     return SVSA_E_INVALID;
@@ -291,6 +312,8 @@ int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32
                     const float* keep_frac, int32_t band_width, int32_t* row_ptr,
                     int32_t* col_idx, int64_t col_capacity, void* workspace, size_t ws_bytes,
                     void* stream) {
+  if (!(al(qbar, 8) && al(kbar, 8) && al(row_ptr, 4) && al(col_idx, 4) && al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!qbar || !kbar || !row_ptr || !col_idx || batch < 1 || heads < 1 || nb < 1 ||
       head_dim < 1 || band_width < 1 || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
@@ -319,6 +342,9 @@ int svsa_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksi
                       double softmax_scale, const float* top_p, const float* keep_frac,
                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(qbar, 8) && al(kbar, 8) && al(ksizes, 4) && al(row_ptr, 4) && al(col_idx, 4) &&
+        al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!qbar || !kbar || !ksizes || !row_ptr || !col_idx || batch < 1 || heads < 1 || nq < 1 ||
       nk < 1 || head_dim < 1 || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
@@ -347,6 +373,7 @@ size_t svsa_stripe_mask_workspace_bytes(int32_t batch, int32_t heads, const svsa
 int svsa_stripe_mask(const svsa_geom* gin, int32_t batch, int32_t heads, const int32_t* params,
                      int32_t band_width, int32_t* row_ptr, int32_t* col_idx,
                      int64_t col_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(row_ptr, 4) && al(col_idx, 4) && al(workspace, 256))) return SVSA_E_INVALID;
   Geom g;
   if (!params || !row_ptr || !col_idx || batch < 1 || heads < 1 || band_width < 0 ||
       !make_geom(gin, &g))
@@ -374,6 +401,9 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
                            int32_t heads, int32_t head_dim, const svsa_geom* gin,
                            float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
                            void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(q, 16) && al(k, 16) && al(v, 16) && al(out, 16) && al(row_ptr, 4) && al(col_idx, 4) &&
+        al(workspace, 256)))
+    return SVSA_E_INVALID;
   Geom g;
   if (!q || !k || !v || !out || !row_ptr || !col_idx || batch < 1 || heads < 1 ||
       head_dim < 1 || !make_geom(gin, &g) || !isfinite(softmax_scale))
@@ -413,6 +443,9 @@ int svsa_cluster_attn(const void* q, const void* k, const void* v, void* out, in
                       const int32_t* k_start, const int32_t* k_size, int32_t align,
                       float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
                       void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(q, 16) && al(k, 16) && al(v, 16) && al(out, 16) && al(q_start, 4) && al(q_size, 4) &&
+        al(k_start, 4) && al(k_size, 4) && al(row_ptr, 4) && al(col_idx, 4) && al(workspace, 256)))
+    return SVSA_E_INVALID;
   if (!q || !k || !v || !out || !q_start || !q_size || !k_start || !k_size || !row_ptr ||
       !col_idx || batch < 1 || heads < 1 || head_dim < 1 || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
@@ -430,7 +463,8 @@ int svsa_cluster_attn(const void* q, const void* k, const void* v, void* out, in
   const int64_t groups = (cap_q / align + 256 / align - 1) / (256 / align);
   if (bh * groups * (cap_k / align) >= 0x7fffffff || bh * nq * nk >= 0x7fffffff)
     return SVSA_E_UNSUPPORTED;
-  const size_t qbytes = (size_t)bh * cap_q * head_dim * 2, kbytes = (size_t)bh * cap_k * head_dim * 2;
+  const size_t qbytes = (size_t)bh * cap_q * head_dim * 2;
+  const size_t kbytes = (size_t)bh * cap_k * head_dim * 2;
   if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kbytes) ||
       overlaps(out, qbytes, v, kbytes))
     return SVSA_E_INVALID;

@@ -72,6 +72,11 @@ typedef struct svsa_geom {
   int32_t pad3d;
 } svsa_geom;
 
+/*
+ * Alignment (checked on the host, SVSA_E_INVALID otherwise): bf16 / f32 tensors
+ * 16 bytes, float64 arrays 8, int32 arrays 4, workspaces 256 (every torch
+ * allocation satisfies all of them).
+ */
 enum svsa_dtype { SVSA_BF16 = 0, SVSA_F32 = 1 };
 
 enum svsa_status {

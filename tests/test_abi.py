@@ -248,3 +248,21 @@ def test_cluster_entry_points_argument_errors(mod):
     assert tm(block=0) == E_INV
     assert tm(cap=2 * 16 * 32 - 1) == E_CAP
     assert tm(wsb=tw - 1) == E_WS
+
+
+def test_misaligned_pointers_are_refused(mod):
+    """Host checks of the alignment the kernels rely on (no GPU call)."""
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)
+    ok16, off8 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20008)
+    assert lib.svsa_tile_permute(off8, ok16, 0, 1, 1, 64, g, 0, None) == -1
+    assert lib.svsa_tile_permute(ok16, off8, 0, 1, 1, 64, g, 0, None) == -1
+    assert lib.svsa_pool(off8, 0, ok16, 1, 1, 64, g, None) == -1
+    G = mod.Geometry(8, 16, 16, 4, 4, 4)
+    ws = mod.svsa_attn_workspace_bytes(1, 2, G)
+    P = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(4)]
+    ws_off = ctypes.c_void_p(0x50000080)           # 128-byte aligned only
+    assert lib.svsa_block_sparse_attn(P[0], P[1], P[2], P[3], 1, 2, 64, ctypes.byref(G.c()),
+                                      0.125, FAKE, FAKE2, ws_off, ws, None) == -1
+    assert lib.svsa_block_sparse_attn(off8, P[1], P[2], P[3], 1, 2, 64, ctypes.byref(G.c()),
+                                      0.125, FAKE, FAKE2, FAKE, ws, None) == -1
