@@ -62,7 +62,7 @@ constexpr int kRowsPerItem = 32 * kWaves;  // query rows owned by one workgroup
 constexpr float kLazy = 8.0f;              // log2 of the largest unnormalised probability
 constexpr int kMaxHeadDim = 128;
 constexpr int kEnt = 7;                    // list entries used by one round of 8 intervals
-constexpr int kWin = 8;   // LDS operand reads in flight ahead of the MFMA stream
+constexpr int kWin = 10;  // LDS operand reads in flight ahead of the MFMA stream
 constexpr int kPre = 4;   // P V operands read before the barrier that opens an M phase
 
 // ---------------------------------------------------------------------------
