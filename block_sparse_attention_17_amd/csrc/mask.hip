@@ -116,25 +116,28 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 // fixed by its last element tau: every block scoring above tau is kept, and
 // of the blocks scoring exactly tau the lowest-index ones up to the boundary.
 // tau is found by an MSB-first radix select over the score bits (non-negative
-// doubles order like their bit patterns), 8 bits per pass, with a per-bin
-// histogram of counts and of probability mass.  Mass is accumulated in 2^-63
-// fixed point with integer atomics, so the result is independent of the
-// order of the atomics (bitwise deterministic); it differs from a float64
-// running sum by at most nb * 2^-63.  Most rows resolve in 2-3 passes (the
-// boundary bin holds a single block).
+// doubles order like their bit patterns), 8 bits per pass starting below the
+// bits that all of the row's keys share, with a per-bin histogram of counts
+// and of probability mass.  Mass is accumulated in 2^-63 fixed point with
+// integer atomics, so the result is independent of the order of the atomics
+// (bitwise deterministic); it differs from a float64 running sum by at most
+// nb * 2^-63.  Most rows resolve in 2-3 passes (the boundary bin holds a
+// single block).
 // ---------------------------------------------------------------------------
 constexpr int kSThreads = 256;
 
+// Fixed-order reduction over the kSThreads (= 4 wavefronts) partial values: a
+// butterfly inside each wavefront (every lane ends with the same value, as
+// the operations are commutative), then the four wavefront results in index
+// order.
+static_assert(kSThreads == 256, "block_reduce combines four wavefronts");
 template <typename T, typename Op>
 __device__ T block_reduce(T v, T* scratch, Op op) {
-  // fixed-order tree over the kSThreads partial values
-  scratch[threadIdx.x] = v;
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) v = op(v, __shfl_xor(v, s, 64));
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = kSThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) scratch[threadIdx.x] = op(scratch[threadIdx.x], scratch[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const T r = scratch[0];
+  const T r = op(op(scratch[0], scratch[1]), op(scratch[2], scratch[3]));
   __syncthreads();
   return r;
 }
@@ -159,7 +162,7 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
               int32_t words, int32_t band, int32_t mode, HeadParams hp) {
   __shared__ uint32_t hcnt[256];
   __shared__ unsigned long long hmass[256];
-  __shared__ double red[kSThreads];
+  __shared__ double red[4];   // one partial value per wavefront
   __shared__ uint32_t flag[kMaxNb / 32];
   __shared__ uint32_t tie[kMaxNb / 32];
   __shared__ RadixStep res;
@@ -209,22 +212,42 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
     P = (uint64_t)ceil(pval * 9223372036854775808.0);
   }
 
-  // 3. radix select of the boundary element
-  uint64_t prefix = 0, A = 0;
+  // 3. radix select of the boundary element.  The scores of a row share their
+  // leading key bits (sign and high exponent bits), so the digits start below
+  // the bits common to the row's smallest and largest key: 8-bit digits, the
+  // last one narrower.  Keys of non-negative doubles have bit 63 clear, so at
+  // least one bit is common.  A row of equal keys runs no pass and goes to the
+  // tie rule with every element in the boundary bin.
+  uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = t + k * kSThreads;
+    if (j < nb) {
+      kmin = key[k] < kmin ? key[k] : kmin;
+      kmax = key[k] > kmax ? key[k] : kmax;
+    }
+  }
+  unsigned long long* ured = reinterpret_cast<unsigned long long*>(red);
+  kmin = block_reduce((unsigned long long)kmin, ured,
+                      [](unsigned long long a, unsigned long long b) { return a < b ? a : b; });
+  kmax = block_reduce((unsigned long long)kmax, ured,
+                      [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+  int shift = kmin == kmax ? 0 : 64 - __clzll((long long)(kmin ^ kmax));
+  uint64_t prefix = kmax >> shift, A = 0;
   uint32_t C = 0;
-  int shift = 64;
   bool resolved = false;
-  uint32_t last_cnt = 0;
+  uint32_t last_cnt = (uint32_t)nb;
   while (!keep_all && shift > 0) {
-    shift -= 8;
+    const int w = shift < 8 ? shift : 8;   // digit width
+    shift -= w;
     hcnt[t] = 0u;
     hmass[t] = 0ull;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int32_t j = t + k * kSThreads;
-      if (j < nb && (shift == 56 || (key[k] >> (shift + 8)) == prefix)) {
-        const uint32_t b = (uint32_t)(key[k] >> shift) & 255u;
+      if (j < nb && (key[k] >> (shift + w)) == prefix) {
+        const uint32_t b = (uint32_t)(key[k] >> shift) & ((1u << w) - 1u);
         atomicAdd(&hcnt[b], 1u);
         atomicAdd(&hmass[b], (unsigned long long)mass[k]);
       }
@@ -281,7 +304,7 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
       keep_all = true;
       break;
     }
-    prefix = (prefix << 8) | (uint64_t)st.bin;
+    prefix = (prefix << w) | (uint64_t)st.bin;
     A = st.above_mass;
     C = st.above_cnt;
     last_cnt = st.bin_cnt;
