@@ -134,6 +134,55 @@ def test_block_mask_band_and_limits():
             assert not bad
 
 
+@pytest.mark.parametrize("nb", [200, 300])
+def test_block_mask_equal_and_few_distinct_scores(nb):
+    """Crafted block summaries whose rows hold exactly equal scores (no radix
+    pass; the tie rule alone decides), two or three distinct values (long
+    common key prefixes, ties at the boundary), scores that underflow to zero,
+    and many ties at row-dependent scales: the lists equal the oracle's up to
+    the near-threshold rule, in top-p and fixed-fraction modes."""
+    import types
+    import torch
+    from block_sparse_attention_17_amd import binding as B
+    H, D = 5, 16
+    scale = 1.0 / np.sqrt(D)
+    j = np.arange(nb)
+    logit = np.zeros((H, nb))
+    logit[1] = np.where(j % 3 == 0, 2.0, 0.0)
+    logit[2] = np.where(j % 5 == 0, 3.0, np.where(j % 7 == 0, 1.5, 0.0))
+    logit[3] = np.where(j < 40, 0.0, -1000.0)          # exp underflows to 0.0
+    logit[4] = np.round(np.random.default_rng(11).normal(size=nb) * 2) / 2
+    qbar = np.zeros((1, H, nb, D))
+    kbar = np.zeros((1, H, nb, D))
+    qbar[0, :, :, 0] = 1.0 / scale
+    qbar[0, 4, :, 0] *= 1 + (j % 3)                   # row-dependent scale, same ties
+    kbar[0, :, :, 0] = logit
+    S = orc.block_scores(qbar, kbar, scale)
+    dq, dk = torch.from_numpy(qbar).cuda(), torch.from_numpy(kbar).cuda()
+    rows = H * nb
+    rp_d = torch.empty(rows + 1, dtype=torch.int32, device="cuda")
+    ci_d = torch.empty(rows * nb, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.svsa_block_mask_workspace_bytes(1, H, nb), dtype=torch.uint8,
+                     device="cuda")
+    cfg = types.SimpleNamespace(nb=nb, heads=H)
+    settings = [dict(top_p=np.full(H, p, np.float32)) for p in (1e-6, 0.5, 0.9, 0.999)]
+    settings += [dict(keep_frac=np.full(H, f, np.float32)) for f in (0.1, 0.5)]
+    for kw in settings:
+        for band in (1, 2):
+            B.svsa_block_mask(dq, dk, scale, rp_d, ci_d, ws, band_width=band, **kw)
+            torch.cuda.synchronize()
+            g_rp = rp_d.cpu().numpy().astype(np.int64)
+            g_ci = ci_d[: int(g_rp[-1])].cpu().numpy()
+            o_rp, o_ci = orc.block_mask(S, band, **kw)
+            tol, bad = gc.mask_mismatch(cfg, S, g_rp, g_ci, o_rp, o_ci, band=band, **kw)
+            gc.log(f"crafted nb={nb} {list(kw)[0]}={float(list(kw.values())[0][0])} "
+                   f"band={band}: {len(tol)} tolerated, {len(bad)} failing")
+            assert not bad, f"rows {bad[:10]} differ beyond the threshold tolerance"
+            for r in range(rows):
+                row = g_ci[g_rp[r]: g_rp[r + 1]]
+                assert row.size >= 1 and np.all(np.diff(row) > 0)
+
+
 def test_block_mask_over_snr_schedule():
     """Per-step top-p from svsa_snr_top_p ([iCATS] Sec. 4.2 reading) drives the
     mask: every step's CSR equals the oracle's mask at the oracle's schedule."""
