@@ -9,10 +9,12 @@
 // kernel grouping.
 //
 // Design for CDNA4 (not a port of the Hopper producer/consumer pipeline):
-//  * The kernels see the sequence as sub-blocks of 64 tokens (32 when the block
-//    size is an odd multiple of 32); a block of Bk tokens is Bk / 64
-//    consecutive sub-blocks, each with the block's list (so PSA-shaped
-//    3x8x16 = 384-token blocks run unchanged).
+//  * The schedule sees the sequence as sub-blocks of 64 tokens (32 when the
+//    block size is an odd multiple of 32, or for 32-aligned clusters); a block
+//    of Bk tokens is Bk / 64 consecutive sub-blocks, each with the block's
+//    list (so PSA-shaped 3x8x16 = 384-token blocks run unchanged).  Key tiles
+//    are always 64 keys: with 32-token sub-blocks the kernel streams two list
+//    entries per tile (paired mode), each half copied from its own block.
 //  * A workgroup is 8 wavefronts (32 query rows each) and owns 256 consecutive
 //    query rows of one (b, h): 4 sub-blocks of 64 tokens, or 8 of 32.
 //    Neighbouring query blocks keep largely the same key blocks, so the
@@ -323,8 +325,6 @@ struct Cfg {
   static constexpr int kDmaPerWave = 2 * kDmaPerTile / kWaves;   // K + V, split over the waves
   static constexpr int kSTiles = BK / 32;    // 32-key tiles of S^T
   static constexpr int kPSteps = BK / 16;    // 16-key MFMA steps of P V
-  static constexpr int kWavesPerBlock = BK / 32;
-  static constexpr int kGroup = kWaves / kWavesPerBlock;  // query blocks per item
   static_assert(kDmaPerWave >= 1 && kDmaPerWave <= 4 && (2 * kDmaPerTile) % kWaves == 0,
                 "copies must split");
 };
@@ -340,7 +340,8 @@ __device__ __forceinline__ int k_swz(int row) {
 // V^T A-operand pattern) hit distinct banks.
 template <int BK>
 __device__ __forceinline__ int vt_swz(int row) {
-  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  static_assert(BK == 64, "key tiles are 64 keys");
+  return (row >> 1) & 7;
 }
 
 // Cross-half exchange: the value held by lane (lane ^ 32).
@@ -381,11 +382,21 @@ struct Ctx {
   __amdgpu_buffer_rsrc_t k_rsrc;   // K of this (b, h)
   __amdgpu_buffer_rsrc_t vt_rsrc;  // V^T blocks of this (b, h)
   const int32_t* lst;
-  int32_t n_u, T, nb;
+  int32_t n_u, T, nb;   // n_u: key tiles streamed (list entries, or pairs of them)
+  int32_t n_list;       // list entries
   float c_log2;
   int wave, lane, qb, l32, hh;
   uint32_t dma_off[4];  // per-lane source offsets of this wave's copies
+  uint32_t vt_sel[4];   // paired mode: all ones where a lane's V^T copy comes from entry b
   bool has_rows;
+};
+
+// List data of one key tile.  Plain mode: one entry (a) per tile of BK keys.
+// Paired mode (32-token list entries streamed two at a time as the halves of
+// a 64-key tile, query sub-blocks of 32 rows, one per wavefront): entries a
+// and b; an entry past the end of the list has its keep mask cleared.
+struct TileEnt {
+  int32_t a, b;
 };
 
 // Per-lane source byte offset, inside one key block, of this wavefront's u-th
@@ -410,11 +421,36 @@ __device__ __forceinline__ uint32_t copy_src_off(int wave, int lane, int u) {
 // (A MUBUF copy, unlike the FLAT global_load_lds form, leaves the compiler's
 // counting of LDS reads exact: with a FLAT copy in flight it would wait for
 // every outstanding LDS read before each use.)
-template <int D, int BK>
-__device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kdst, char* vdst,
+template <int D, int BK, bool PR>
+__device__ __forceinline__ void issue_copies(const Ctx& cx, TileEnt te, char* kdst, char* vdst,
                                              int32_t wave_off) {
   using C = Cfg<D, BK>;
-  const int32_t boff = j * C::kTileBytes;
+  if constexpr (PR) {
+    // Paired mode: K copies lie within one half of the tile, so their block
+    // offset is wave-uniform (the half's row offset is folded into dma_off);
+    // each lane of a V^T copy takes its 16 bytes from entry a's or b's block.
+    static_assert(BK == 64 && C::kDmaPerTile % kWaves == 0, "paired tiles are 64 keys");
+    constexpr int32_t kHalfBytes = 32 * D * 2;
+    constexpr int kPerWaveK = C::kDmaPerTile / kWaves;
+    const int32_t ja = (te.a & 0x1fff) * kHalfBytes, jb = (te.b & 0x1fff) * kHalfBytes;
+#pragma unroll
+    for (int u = 0; u < C::kDmaPerWave; ++u) {
+      if (u < kPerWaveK) {
+        const bool hb = (cx.wave + u * kWaves) * 1024 >= kHalfBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.k_rsrc, (__attribute__((address_space(3))) void*)(kdst + wave_off + u * kWaves * 1024), 16,
+            (int)cx.dma_off[u], hb ? jb : ja, 0, 0);
+      } else {
+        const uint32_t base = (cx.vt_sel[u] & (uint32_t)jb) | (~cx.vt_sel[u] & (uint32_t)ja);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cx.vt_rsrc,
+            (__attribute__((address_space(3))) void*)(vdst + wave_off + (u * kWaves - C::kDmaPerTile) * 1024), 16,
+            (int)(cx.dma_off[u] + base), 0, 0, 0);
+      }
+    }
+    return;
+  }
+  const int32_t boff = (te.a & 0x1fff) * C::kTileBytes;
 #pragma unroll
   for (int u = 0; u < C::kDmaPerWave; ++u) {
     const int ld = cx.wave + u * kWaves;
@@ -447,8 +483,13 @@ __device__ __forceinline__ void issue_copies(const Ctx& cx, int32_t j, char* kds
 }
 
 // Does this wavefront's query block keep the key block of list entry `ent`?
-__device__ __forceinline__ bool active(const Ctx& cx, int32_t ent) {
+__device__ __forceinline__ bool keeps(const Ctx& cx, int32_t ent) {
   return ((((uint32_t)ent) >> 24) >> cx.qb) & 1u;
+}
+// ... any key of the tile (paired mode: either half)?
+template <bool PR>
+__device__ __forceinline__ bool active(const Ctx& cx, TileEnt te) {
+  return PR ? (keeps(cx, te.a) || keeps(cx, te.b)) : keeps(cx, te.a);
 }
 
 // V^T A operand of P V job i (step s = i / (D / 32), d tile dt = i % (D / 32);
@@ -477,9 +518,9 @@ __device__ __forceinline__ bf16x8 k_operand(const Ctx& cx, const char* kt, int j
 // One stream of MFMA jobs: the P V jobs (if PV) followed by the S^T jobs (if
 // QK), with LDS operand reads kWin jobs ahead of their MFMA.  The operands of
 // the first kPre P V jobs were read at the end of the previous phase.
-template <int D, int BK, bool PV, bool QK>
+template <int D, int BK, bool PV, bool QK, bool PR>
 __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx, const char* vprev,
-                                            const char* kcur) {
+                                            const char* kcur, bool ha, bool hb) {
   using C = Cfg<D, BK>;
   constexpr int kNpv = PV ? (D / 32) * C::kPSteps : 0;
   constexpr int kNqk = QK ? (D / 16) * C::kSTiles : 0;
@@ -499,47 +540,70 @@ __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx,
   for (int i = 0; i < kN; ++i) {
     const bf16x8 a = win[i % kWin];
     if (i + kWin < kN) win[i % kWin] = rd(i + kWin);
+    // paired mode: ha / hb say whether the wave keeps the tile's first / second
+    // 32 keys (P V steps 0-1 / 2-3, S^T tile 0 / 1); a skipped half is masked
+    // in the softmax and contributes nothing
     if (i < kNpv) {
       const int s = i / (D / 32), dt = i % (D / 32);
-      st.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pk[s], st.oacc[dt], 0, 0, 0);
+      if (!PR || ((s >> 1) ? hb : ha))
+        st.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pk[s], st.oacc[dt], 0, 0, 0);
     } else {
       const int j = i - kNpv;
       const int s = j / C::kSTiles, c = j % C::kSTiles;
       const f32x16 acc = s == 0 ? f32x16{} : st.sacc[c];  // S^T starts at 0
-      st.sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[s], acc, 0, 0, 0);
+      if (!PR || (c ? hb : ha))
+        st.sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[s], acc, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // M phase for key block e: O += P(e-1) V(e-1); S(e) = K(e) Q^T.
-template <int D, int BK>
+template <int D, int BK, bool PR>
 __device__ __forceinline__ void m_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
-                                        int32_t ent_prev, int32_t ent, const char* vprev,
+                                        TileEnt ent_prev, TileEnt ent, const char* vprev,
                                         const char* kcur) {
   using C = Cfg<D, BK>;
   constexpr int kDT = D / 32;
-  const bool pv = e >= 1 && e <= cx.n_u && active(cx, ent_prev);
-  const bool qk = e < cx.n_u && active(cx, ent);
+  const bool pv = e >= 1 && e <= cx.n_u && active<PR>(cx, ent_prev);
+  const bool qk = e < cx.n_u && active<PR>(cx, ent);
   __builtin_amdgcn_s_setprio(1);
   if (pv && st.o_rescale) {
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) st.oacc[dt] = st.oacc[dt] * st.o_alpha;
   }
-  if (pv) mfma_stream<D, BK, true, false>(st, cx, vprev, kcur);
-  if (qk) mfma_stream<D, BK, false, true>(st, cx, vprev, kcur);
+  if (pv)
+    mfma_stream<D, BK, true, false, PR>(st, cx, vprev, kcur, keeps(cx, ent_prev.a),
+                                        keeps(cx, ent_prev.b));
+  if (qk) mfma_stream<D, BK, false, true, PR>(st, cx, vprev, kcur, keeps(cx, ent.a), keeps(cx, ent.b));
   __builtin_amdgcn_s_setprio(0);
 }
 
 // V phase for key block e: online softmax of S(e) -> P(e).
-template <int D, int BK>
+template <int D, int BK, bool PR>
 __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
-                                        int32_t ent, const char* vcur) {
+                                        TileEnt te, const char* vcur) {
   using C = Cfg<D, BK>;
-  if (!(e < cx.n_u && active(cx, ent))) return;
+  if (!(e < cx.n_u && active<PR>(cx, te))) return;
   // lane holds keys kv = 32 c + 8 (r / 4) + 4 hh + (r % 4) of query column l32
-  const int32_t nvalid = (ent >> 13) & 127;   // valid keys: the first nvalid
-  if (nvalid < BK) {
+  if constexpr (PR) {
+    // per 32-key half: its valid keys (the first ones) if the wave keeps it, else none
+    const int32_t la = keeps(cx, te.a) ? (te.a >> 13) & 127 : 0;
+    const int32_t lb = keeps(cx, te.b) ? (te.b >> 13) & 127 : 0;
+    if (la < 32 || lb < 32) {
+      int lim0 = la - 4 * cx.hh, lim1 = lb - 4 * cx.hh;
+      asm volatile("" : "+v"(lim0), "+v"(lim1));
+#pragma unroll
+      for (int c = 0; c < C::kSTiles; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = 8 * (r >> 2) + (r & 3);  // key index in the half minus 4 hh
+          if (kv >= (c ? lim1 : lim0)) st.sacc[c][r] = -INFINITY;
+        }
+    }
+  }
+  const int32_t nvalid = PR ? BK : (te.a >> 13) & 127;   // valid keys: the first nvalid
+  if (!PR && nvalid < BK) {
     // lane-dependent limit, computed here (an opaque value keeps the 32
     // compares out of loop-invariant code motion, where they would pin 32
     // SGPR-pair lane masks for the whole loop)
@@ -612,9 +676,9 @@ struct Ring {
 //  * odd t: wait for this wave's copies of block (t + 1) / 2 before the
 //    barrier, so the block is complete when group 0 reads it at t + 1.
 // ent[x] is list entry t0 / 2 - 1 + x.
-template <int D, int BK, int G, int I>
+template <int D, int BK, bool PR, int G, int I>
 __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, const Ring<D, BK>& rg,
-                                         int32_t t0, const int32_t (&ent)[kEnt], int32_t wave_off) {
+                                         int32_t t0, const TileEnt (&ent)[kEnt], int32_t wave_off) {
   using C = Cfg<D, BK>;
   const int32_t t = t0 + I;
   if ((I & 1) == 0) {
@@ -622,7 +686,7 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     // clamped) into a slot that is no longer read: unconditional copies keep
     // the per-wave count of copies in flight fixed.
     constexpr int slot = (I / 2 + 2) & 3;
-    issue_copies<D, BK>(cx, ent[I / 2 + 3] & 0x1fff, rg.k[slot], rg.v[slot], wave_off);
+    issue_copies<D, BK, PR>(cx, ent[I / 2 + 3], rg.k[slot], rg.v[slot], wave_off);
   }
   const int32_t ph = t - G;
   if (ph >= 0 && cx.has_rows) {
@@ -631,10 +695,10 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     if constexpr (((I - G) & 1) == 0) {
       constexpr int sc = (((I - G) >> 1) + 4) & 3;
       constexpr int sp = (sc + 3) & 3;
-      m_phase<D, BK>(st, cx, e, ent[x - 1], ent[x], rg.v[sp], rg.k[sc]);
+      m_phase<D, BK, PR>(st, cx, e, ent[x - 1], ent[x], rg.v[sp], rg.k[sc]);
     } else {
       constexpr int se = ((I - G) >> 1) & 3;  // ring slot of block e
-      v_phase<D, BK>(st, cx, e, ent[x], rg.v[se]);
+      v_phase<D, BK, PR>(st, cx, e, ent[x], rg.v[se]);
     }
   }
   if (I & 1) {
@@ -643,7 +707,7 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
   }
 }
 
-template <int D, int BK, int G>
+template <int D, int BK, bool PR, int G>
 __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
                                           const Ring<D, BK>& rg) {
   // The first round (t0 = -8) only issues the copies of key blocks 0 and 1
@@ -653,27 +717,38 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
     // The list entries of these 8 intervals, loaded (scalar) and waited for
     // up front, so that no scalar load is outstanding while the phases wait
     // on their LDS reads (the shared counter would force full waits).
-    int32_t ent[kEnt];
+    TileEnt ent[kEnt];
 #pragma unroll
     for (int x = 0; x < kEnt; ++x) {
-      const int32_t idx = min(max(t0 / 2 - 1 + x, 0), cx.n_u - 1);
-      ent[x] = cx.lst[idx];
+      const int32_t tile = t0 / 2 - 1 + x;
+      if constexpr (PR) {
+        const int32_t ia = 2 * tile, ib = 2 * tile + 1;
+        ent[x].a = cx.lst[min(max(ia, 0), cx.n_list - 1)];
+        const int32_t eb = cx.lst[min(max(ib, 0), cx.n_list - 1)];
+        ent[x].b = ib >= 0 && ib < cx.n_list ? eb : eb & 0x00ffffff;  // past the end: kept by none
+      } else {
+        ent[x].a = cx.lst[min(max(tile, 0), cx.n_u - 1)];
+        ent[x].b = 0;
+      }
     }
 #pragma unroll
-    for (int x = 0; x < kEnt; ++x) asm volatile("" : "+s"(ent[x]));
+    for (int x = 0; x < kEnt; ++x) {
+      if constexpr (PR) asm volatile("" : "+s"(ent[x].a), "+s"(ent[x].b));
+      else asm volatile("" : "+s"(ent[x].a));
+    }
     // LDS offset of this wave's copies, re-materialised every round (kept
     // out of loop-invariant code motion, which would pin one SGPR per copy
     // destination and spill)
     int32_t wave_off = cx.wave * 1024;
     asm volatile("" : "+s"(wave_off));
-    interval<D, BK, G, 0>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 1>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 2>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 3>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 4>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 5>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 6>(st, cx, rg, t0, ent, wave_off);
-    interval<D, BK, G, 7>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 0>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 1>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 2>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 3>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 4>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 5>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 6>(st, cx, rg, t0, ent, wave_off);
+    interval<D, BK, PR, G, 7>(st, cx, rg, t0, ent, wave_off);
   }
 }
 
@@ -686,7 +761,7 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
 // softmax.  Key block e is copied HBM -> LDS at interval 2e - 4, two key
 // blocks ahead of its first use, and is read during intervals 2e .. 2e+3.
 // One work item: query group gi of head bh, whose union list is list[item].
-template <int D, int BK>
+template <int D, int BK, bool PR>
 __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ vt, __bf16* __restrict__ out,
@@ -703,16 +778,22 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   cx.lane = tid & 63;
   const int grp = cx.wave >> 2;                             // ping-pong group
-  cx.qb = BK == 64 ? (cx.wave & 3) : cx.wave;               // query block inside the item
-  const int sub = BK == 64 ? grp : 0;                       // 32-row slice inside the block
+  // query block inside the item (paired mode: one 32-row block per wave) and
+  // the wave's 32-row slice inside it
+  constexpr bool kSplitBlock = !PR;
+  cx.qb = kSplitBlock ? (cx.wave & 3) : cx.wave;
+  const int sub = kSplitBlock ? grp : 0;
+  constexpr int kQRows = kSplitBlock ? 64 : 32;             // rows of one query block
+  constexpr int kQGroup = kRowsPerItem / kQRows;            // query blocks per item
   cx.l32 = cx.lane & 31;
   cx.hh = cx.lane >> 5;
 
   const int64_t bh = item / groups;
   const int32_t gi = (int32_t)(item % groups);
-  const int32_t iq = gi * C::kGroup + cx.qb;
+  const int32_t iq = gi * kQGroup + cx.qb;
   cx.has_rows = iq < nq;
-  cx.n_u = count[item];
+  cx.n_list = count[item];
+  cx.n_u = PR ? (cx.n_list + 1) / 2 : cx.n_list;            // key tiles streamed
   // intervals 0 .. 2 n_u + 1 carry work; the count is rounded up to whole
   // rounds of 8 (the extra intervals do nothing); an empty union runs none
   cx.T = cx.n_u > 0 ? (2 * cx.n_u + 2 + 7) & ~7 : 0;
@@ -730,10 +811,28 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   __bf16* oh = out + bh * (int64_t)npad_q * D;
 
 #pragma unroll
-  for (int u = 0; u < C::kDmaPerWave; ++u) cx.dma_off[u] = copy_src_off<D, BK>(cx.wave, cx.lane, u);
+  for (int u = 0; u < C::kDmaPerWave; ++u) {
+    cx.dma_off[u] = copy_src_off<D, BK>(cx.wave, cx.lane, u);
+    cx.vt_sel[u] = 0u;
+    if constexpr (PR) {
+      // paired mode: the source of each 32-key half is its own list entry's
+      // block of 32 keys (K: 32 rows of 2 D bytes; V^T: D rows of 64 bytes)
+      constexpr int32_t kHalfBytes = 32 * D * 2;
+      const int ld = cx.wave + u * kWaves;
+      if (ld < C::kDmaPerTile) {
+        if (ld * 1024 >= kHalfBytes) cx.dma_off[u] -= kHalfBytes;   // rows 32..63: entry b
+      } else {
+        const int byte = (ld - C::kDmaPerTile) * 1024 + cx.lane * 16;
+        const int row = byte / C::kVtRowBytes;
+        const int lc = ((byte % C::kVtRowBytes) >> 4) ^ vt_swz<BK>(row);  // source chunk 0..7
+        cx.dma_off[u] = (uint32_t)(row * 64 + (lc & 3) * 16);
+        cx.vt_sel[u] = lc >= 4 ? ~0u : 0u;
+      }
+    }
+  }
 
   WaveState<D, BK> st;
-  const int32_t qrow = (cx.has_rows ? iq : nq - 1) * BK + sub * 32 + cx.l32;
+  const int32_t qrow = (cx.has_rows ? iq : nq - 1) * kQRows + sub * 32 + cx.l32;
 #pragma unroll
   for (int s = 0; s < kS; ++s)
     st.qreg[s] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * D + 16 * s + 8 * cx.hh);
@@ -751,8 +850,8 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   wg_barrier();
 
-  if (grp == 0) run_group<D, BK, 0>(st, cx, rg);
-  else run_group<D, BK, 1>(st, cx, rg);
+  if (grp == 0) run_group<D, BK, PR, 0>(st, cx, rg);
+  else run_group<D, BK, PR, 1>(st, cx, rg);
 
   if (!cx.has_rows) return;
   const float l_tot = st.l_run + swap_halves(st.l_run, cx.lane);
@@ -773,7 +872,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
 // Persistent kernel: one workgroup per CU slot takes items from the queue of
 // the XCD it runs on (hardware register XCC_ID), then from the other queues;
 // it exits once every queue is drained.
-template <int D, int BK>
+template <int D, int BK, bool PR>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
@@ -807,14 +906,14 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int32_t item = s_item;
     __syncthreads();
     if (item < 0) break;
-    run_item<D, BK>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
+    run_item<D, BK, PR>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
                     rg);
   }
 }
 
 // Workgroups of the persistent attention kernel: every CU slot of the device
 // (CU count x resident workgroups per CU), at most one per item.
-template <int D, int BK>
+template <int D, int BK, bool PR>
 hipError_t attn_grid(int64_t items, uint32_t* grid) {
   static int cached[64] = {0};  // per device: CU count x resident workgroups per CU
   int dev = 0;
@@ -825,7 +924,7 @@ hipError_t attn_grid(int64_t items, uint32_t* grid) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK, PR>, kThreads, 0);
     if (e != hipSuccess) return e;
     slots = cus * (per_cu > 0 ? per_cu : 1);
     if (slots <= 0) slots = 1;
@@ -837,19 +936,21 @@ hipError_t attn_grid(int64_t items, uint32_t* grid) {
 
 // nb / nq: key / query sub-blocks per head (nb is also the list stride);
 // npad_q / npad_k: rows per head of Q and O / of K and V.
-template <int D, int BK>
+// PR: paired mode (32-key schedule entries streamed two per 64-key tile; V^T
+// is laid out per 32-key sub-block)
+template <int D, int BK, bool PR>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
                        int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
                        int32_t npad_k, float c_log2, hipStream_t stream) {
-  hipLaunchKernelGGL((vt_kernel<D, BK>), dim3((uint32_t)((int64_t)bh * nb)), dim3(kVtThreads), 0,
+  hipLaunchKernelGGL((vt_kernel<D, PR ? 32 : BK>), dim3((uint32_t)((int64_t)bh * nb)), dim3(kVtThreads), 0,
                      stream, (const __bf16*)v, vt, nb, npad_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint32_t grid = 0;
-  e = attn_grid<D, BK>(w.items, &grid);
+  e = attn_grid<D, BK, PR>(w.items, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_kernel<D, BK>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<D, BK, PR>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
                      count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2);
   return hipGetLastError();
@@ -907,15 +1008,15 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
 
   const float c_log2 = scale * 1.4426950408889634f;
   if (head_dim == 128 && w.sub == 64)
-    return launch_attn<128, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+    return launch_attn<128, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
                                 w.nbs_q, npad_q, npad_k, c_log2, stream);
   if (head_dim == 64 && w.sub == 64)
-    return launch_attn<64, 64>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+    return launch_attn<64, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
                                w.nbs_q, npad_q, npad_k, c_log2, stream);
   if (head_dim == 128 && w.sub == 32)
-    return launch_attn<128, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
+    return launch_attn<128, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
                                 w.nbs_q, npad_q, npad_k, c_log2, stream);
-  return launch_attn<64, 32>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
+  return launch_attn<64, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
                              npad_q, npad_k, c_log2, stream);
 }
 }  // namespace

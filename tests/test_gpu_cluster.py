@@ -512,15 +512,17 @@ def test_kmeans_assignment_full_size_sampled():
     assert tolerated <= 6
 
 
-def test_cluster_mask_and_attention_full_size_sampled():
+@pytest.mark.parametrize("align", [64, 32])
+def test_cluster_mask_and_attention_full_size_sampled(align):
     """Wan-720p shape with 400 query / 1000 key clusters (seeded labels, ten
-    empty key clusters), align 64: GPU means and cluster mask against the
-    oracle's over all rows, attention with the oracle's mask on 12 sampled
-    query clusters per head, and tail merging of the oracle's mask."""
+    empty key clusters), align 64 or 32 (32: 32-token schedule entries streamed
+    two per 64-key tile): GPU means and cluster mask against the oracle's over
+    all rows, attention with the oracle's mask on 12 sampled query clusters per
+    head, and tail merging of the oracle's mask."""
     m = _m()
     q, k, v = _wan720_heads()
     B, H, N, D = q.shape
-    nq, nk, align = 400, 1000, 64
+    nq, nk = 400, 1000
     qlab = cluster_labels(N, nq, B, H, seed=31, stream=1)
     klab = cluster_labels(N, nk, B, H, seed=31, stream=2, empty=10)
     f64 = dict(dtype=torch.float64, device="cuda")
