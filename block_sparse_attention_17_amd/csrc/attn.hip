@@ -90,6 +90,8 @@ __device__ __forceinline__ int32_t clamp_valid(int32_t v, int32_t sub) {
 }
 
 struct GeomSched {
+  // 3D-padded layouts hold sub-blocks of padding only inside a kept block
+  static constexpr bool kSkipEmpty = true;
   Geom g;
   int32_t ratio, sub;
   __device__ int32_t ncols() const { return g.nb; }
@@ -117,6 +119,9 @@ __device__ __forceinline__ int32_t owner_of(const int32_t* start, int32_t n, int
 }
 
 struct TableSched {
+  // clusters start on sub-block boundaries, so every sub-block of a kept key
+  // cluster's range holds some of its keys (an empty cluster has no range)
+  static constexpr bool kSkipEmpty = false;
   const int32_t *q_start, *q_size, *k_start, *k_size;
   int32_t nq, nk, sub;
   __device__ int32_t ncols() const { return nk; }
@@ -171,7 +176,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
       int32_t j0, j1;
       sc.keys(bh, jb, &j0, &j1);
       for (int32_t j = j0; j < j1; ++j)
-        if (j < nb && sc.kvalid(bh, j) > 0) atomicOr(&mask[j], 1u << m);
+        if (j < nb && (!Sched::kSkipEmpty || sc.kvalid(bh, j) > 0)) atomicOr(&mask[j], 1u << m);
     }
   }
   __syncthreads();
