@@ -377,6 +377,59 @@ def test_attention_edge_cases_custom_csr():
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
+@pytest.mark.parametrize("pad3d", [False, True])
+def test_attention_96_token_blocks_d128(pad3d):
+    """Blocks of 96 tokens (three 32-token sub-blocks: the kernel streams the
+    schedule two entries per 64-key tile, so tiles straddle blocks) at head_dim
+    128, packed (partial tail block) and 3D-padded (partial tiles, sub-blocks
+    of padding only): every valid row against the oracle on random kept sets."""
+    import block_sparse_attention_17_amd as m
+    from svsa_synth.gen import f32_to_bf16_bits
+    grid, tile, H, D = (5, 7, 10), (3, 4, 8), 3, 128
+    N, Bk = grid[0] * grid[1] * grid[2], tile[0] * tile[1] * tile[2]
+    slots, counts = orc.block_layout(grid, tile, pad3d)
+    nb = len(counts)
+    rng = np.random.default_rng(41 + int(pad3d))
+    nat = {n: f32_to_bf16_bits(rng.standard_normal((1, H, N, D)).astype(np.float32))
+           for n in "qkv"}
+    valid = slots >= 0
+    tiled = {}
+    for n in "qkv":
+        t = np.zeros((1, H, nb * Bk, D), np.uint16)
+        t[:, :, valid] = nat[n][:, :, slots[valid]]
+        tiled[n] = t
+    lists = []
+    for h in range(H):
+        for i in range(nb):
+            keep = set(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+            lists.append(sorted(keep | {i}))
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    ci = np.array([c for cs in lists for c in cs], np.int32)
+    geom = m.Geometry(*grid, *tile, pad3d=pad3d)
+    out = torch.empty((1, H, nb * Bk, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, geom), dtype=torch.uint8, device="cuda")
+    gc.log(f"96-token blocks, D 128, pad3d={pad3d}: {nb} blocks, {int(rp[-1])} kept pairs")
+    m.svsa_block_sparse_attn(*(gc.bits_to_dev(tiled[n]) for n in "qkv"), out, geom,
+                             1 / np.sqrt(D), torch.from_numpy(rp.astype(np.int32)).cuda(),
+                             torch.from_numpy(ci).cuda(), ws)
+    torch.cuda.synchronize()
+    got = gc.dev_to_bits(out)
+    ref = orc.attention(tiled["q"], tiled["k"], tiled["v"], rp, ci, N, Bk, 1 / np.sqrt(D),
+                        counts=counts)
+    g_all, r_all = [], []
+    for h in range(H):
+        for i in range(nb):
+            rows = slice(i * Bk, i * Bk + int(counts[i]))
+            g_all.append(orc.widen(got[0, h, rows]).ravel())
+            r_all.append(ref[0, h, rows].ravel())
+    g, r = np.concatenate(g_all), np.concatenate(r_all)
+    max_abs = float(np.max(np.abs(g - r)))
+    rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    gc.log(f"  max_abs {max_abs:.3e} rel_l2 {rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
 def test_tail_keys_masked_wan720():
     """The 16-token tail block of the Wan-720p shape: padded keys are excluded."""
     cfg = get_config("wan720")
