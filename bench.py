@@ -71,11 +71,39 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan720_hbm_traffic.txt"
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_17_amd", "csrc", "attn.hip")
 
 
+def code_digest(path):
+    """sha256 of a C / HIP source with its comments removed and whitespace runs
+    collapsed (string and character literals kept): it changes when the code
+    changes, not when only comments or layout do."""
+    import hashlib
+    import re
+    src = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return hashlib.sha256(re.sub(r"\s+", " ", "".join(out)).strip().encode()).hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per attention launch from the committed counter summary, or None
-    when the summary is missing, covers another workload, or was taken on an
-    attention source other than the one in the tree."""
-    import hashlib
+    when the summary is missing, covers another workload, or was taken on
+    attention code other than the tree's (comments aside)."""
     if workload != "wan720" or not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -84,9 +112,7 @@ def measured_traffic(workload):
             if ":" in line and not line.startswith((" ", "#", "\t")):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    with open(ATTN_SOURCE, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
-    if fields.get("attn_source_sha256") != sha:
+    if fields.get("attn_code_sha256") != code_digest(ATTN_SOURCE):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])

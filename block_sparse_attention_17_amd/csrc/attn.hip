@@ -680,7 +680,8 @@ struct Ring {
 //  * phase ph = t - G: even -> M phase of block ph / 2, odd -> V phase;
 //  * odd t: wait for this wave's copies of block (t + 1) / 2 before the
 //    barrier, so the block is complete when group 0 reads it at t + 1.
-// ent[x] is list entry t0 / 2 - 1 + x.
+// ent[x] is the list data of key tile t0 / 2 - 1 + x (one list entry, or two
+// in paired mode).
 template <int D, int BK, bool PR, int G, int I>
 __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, const Ring<D, BK>& rg,
                                          int32_t t0, const TileEnt (&ent)[kEnt], int32_t wave_off) {
