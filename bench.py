@@ -51,7 +51,8 @@ def parse():
                     help="variable-size blocks: query/key k-means, cluster mask and attention")
     ap.add_argument("--q-clusters", type=int, default=400)
     ap.add_argument("--k-clusters", type=int, default=1000)
-    ap.add_argument("--align", type=int, default=64, choices=[32, 64])
+    ap.add_argument("--align", type=int, default=32, choices=[32, 64],
+                    help="cluster padding granularity (32: less padding for clusters of tens of tokens)")
     ap.add_argument("--iters", type=int, default=2, help="Lloyd iterations per side per step")
     ap.add_argument("--tail-merge", action="store_true",
                     help="tail merging of the query clusters before the attention")

@@ -85,8 +85,11 @@ class ClusteredAttention:
     cluster attention -> token order.  Centroids persist between calls (warm
     start across denoising steps); initial centroids are the caller's."""
 
-    def __init__(self, batch, heads, head_dim, n, q_clusters, k_clusters, align=64,
+    def __init__(self, batch, heads, head_dim, n, q_clusters, k_clusters, align=32,
                  q_iters=2, k_iters=2, tail_merge=False, tail_rounds=2, device="cuda"):
+        # align: cluster padding granularity, 32 or 64 tokens.  Clusters of a
+        # few dozen to a few hundred tokens waste less at 32, and the attention
+        # kernel then streams two 32-token entries per 64-key tile.
         self.batch, self.heads, self.head_dim, self.n = batch, heads, head_dim, n
         self.nq, self.nk, self.align = q_clusters, k_clusters, align
         self.q_iters, self.k_iters = q_iters, k_iters
