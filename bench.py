@@ -324,31 +324,28 @@ def main():
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    stage_names = ["permute_qkv", "pool", "mask", "attention", "permute_out"]
+    # Q and K are reordered and pooled in one pass; V is only reordered
+    stage_names = ["permute_pool_qk_permute_v", "mask", "attention", "permute_out"]
 
     stripe = stripe_params(cfg.heads, seed=args.seed) if args.stripe else None
 
     def step(record=None):
-        marks = [ev() for _ in range(6)] if record is not None else None
+        marks = [ev() for _ in range(5)] if record is not None else None
         if marks: marks[0].record(stream)
         bsa.permute_in(q, k, v)
         if marks: marks[1].record(stream)
-        if stripe is None:
-            m.svsa_pool(bsa.qt, bsa.qbar, geom)
-            m.svsa_pool(bsa.kt, bsa.kbar, geom)
-        if marks: marks[2].record(stream)
         if stripe is None:
             m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
                               bsa.col_idx, bsa.mask_ws, top_p=tp, keep_frac=kf,
                               band_width=cfg.band)
         else:
             bsa.build_stripe_mask(stripe, band_width=cfg.band)
-        if marks: marks[3].record(stream)
+        if marks: marks[2].record(stream)
         bsa.attend()
-        if marks: marks[4].record(stream)
+        if marks: marks[3].record(stream)
         bsa.permute_out()
         if marks:
-            marks[5].record(stream)
+            marks[4].record(stream)
             record.append(marks)
 
     for _ in range(args.warmup):
@@ -366,7 +363,7 @@ def main():
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     stage_ms = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]))
                 for i, n in enumerate(stage_names)}
-    step_ms = float(np.mean([r[0].elapsed_time(r[5]) for r in recs]))
+    step_ms = float(np.mean([r[0].elapsed_time(r[4]) for r in recs]))
     print(f"[bench] timed {args.steps} steps: {wall_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     rp = bsa.row_ptr.cpu().numpy().astype(np.int64)
@@ -382,10 +379,7 @@ def main():
 
     dense = None
     if not args.no_dense:
-        # same kernel with every block kept, same inputs
-        if stripe is not None:   # the stripe steps never pooled
-            m.svsa_pool(bsa.qt, bsa.qbar, geom)
-            m.svsa_pool(bsa.kt, bsa.kbar, geom)
+        # same kernel with every block kept, same inputs (permute_in left the block means)
         m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
                           bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
         bsa.attend()
@@ -416,8 +410,6 @@ def main():
             a, b = ev(), ev()
             a.record(stream)
             bsa.permute_in(q, k, v)
-            m.svsa_pool(bsa.qt, bsa.qbar, geom)
-            m.svsa_pool(bsa.kt, bsa.kbar, geom)
             m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
                               bsa.col_idx, bsa.mask_ws,
                               top_p=np.full(cfg.heads, p_k, np.float32), band_width=cfg.band)

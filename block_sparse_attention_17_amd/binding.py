@@ -98,6 +98,7 @@ def _load():
     sig = {
         "svsa_tile_permute": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, gp, i32, vp]),
         "svsa_pool": (ctypes.c_int, [vp, i32, vp, i32, i32, i32, gp, vp]),
+        "svsa_tile_permute_pool": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, gp, vp]),
         "svsa_block_mask_workspace_bytes": (sz, [i32, i32, i32]),
         "svsa_block_mask": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, dbl, fp, fp, i32, vp, vp,
                                            i64, vp, sz, vp]),
@@ -143,8 +144,8 @@ def _load():
 
 _lib = _load()
 
-EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_block_mask_workspace_bytes",
-            "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
+EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_tile_permute_pool",
+            "svsa_block_mask_workspace_bytes", "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
             "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_snr_top_p",
             "svsa_kmeans_workspace_bytes", "svsa_kmeans", "svsa_cluster_metric",
             "svsa_cluster_means_workspace_bytes", "svsa_cluster_means",
@@ -229,6 +230,17 @@ def svsa_pool(x_tiled, out, geom, stream=None):
         _ptr(x_tiled, "x_tiled", (torch.bfloat16, torch.float32)), _dtype_code(x_tiled),
         _ptr(out, "out", (torch.float64,)), B, Hh, D, ctypes.byref(geom.c()), _stream(stream)))
     return out
+
+
+def svsa_tile_permute_pool(src, dst, means, geom, stream=None):
+    """dst <- tile-ordered src and means (float64 [B, Hh, nb, D]) <- its block means, one pass."""
+    import torch
+    B, Hh, _, D = src.shape
+    _check("svsa_tile_permute_pool", _lib.svsa_tile_permute_pool(
+        _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
+        _ptr(means, "means", (torch.float64,)), _dtype_code(src), B, Hh, D,
+        ctypes.byref(geom.c()), _stream(stream)))
+    return dst
 
 
 def svsa_snr_top_p(sigmas, first_sparse, p_min, tau):

@@ -302,6 +302,31 @@ int svsa_pool(const void* x_tiled, int32_t dtype, double* out, int32_t batch, in
                                     static_cast<hipStream_t>(stream)));
 }
 
+int svsa_tile_permute_pool(const void* src, void* dst, double* means, int32_t dtype,
+                           int32_t batch, int32_t heads, int32_t head_dim, const svsa_geom* gin,
+                           void* stream) {
+  if (!(al(src, 16) && al(dst, 16) && al(means, 8))) return SVSA_E_INVALID;
+  Geom g;
+  if (!src || !dst || !means || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
+    return SVSA_E_INVALID;
+  const int eb = elt_bytes(dtype);
+  if (!eb) return SVSA_E_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)head_dim * eb;
+  if (row_bytes % 16 != 0 || row_bytes / 16 > 256 || 256 % (row_bytes / 16) != 0 ||
+      (256 / (row_bytes / 16)) * head_dim * 8 > 64 * 1024)
+    return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * g.nb > 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  const size_t src_bytes = (size_t)bh * g.N * row_bytes;
+  const size_t dst_bytes = (size_t)bh * g.Npad * row_bytes;
+  const size_t means_bytes = (size_t)bh * g.nb * head_dim * sizeof(double);
+  if (overlaps(src, src_bytes, dst, dst_bytes) || overlaps(means, means_bytes, src, src_bytes) ||
+      overlaps(means, means_bytes, dst, dst_bytes))
+    return SVSA_E_INVALID;
+  return from_hip(svsa::launch_tile_permute_pool(src, dst, means, dtype == SVSA_BF16, (int32_t)bh,
+                                                 head_dim, g, static_cast<hipStream_t>(stream)));
+}
+
 size_t svsa_block_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nb) {
   if (batch < 1 || heads < 1 || nb < 1) return 0;
   return svsa::mask_ws_layout((int64_t)batch * heads * nb, nb).total;

@@ -88,7 +88,127 @@ tile_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int3
   }
 }
 
+// Forward reorder fused with the block means (stages 1 and 2 in one pass).
+// One workgroup per (b, h, block): the block's tiled slots are filled from
+// their natural rows and the valid rows are summed in float64 on the way, so
+// the tiled tensor is not read back for pooling.  Blocks are walked in the
+// tiled order rather than by tile because in the packed layout a block can
+// span several partial tiles.  The natural row of tiled slot p inverts the
+// tile walk: the slab of tile rows along t (every earlier slab is full), then
+// the row of tiles along h inside it (every earlier row is full), then the
+// tile along w, then (t, h, w) inside the tile.  kElt: 2 (bf16) or 4 (f32).
+constexpr int kMapRows = 1024;  // natural-row map entries held in LDS at once
+
+__device__ __forceinline__ int32_t natural_row(const Geom& g, int32_t blk, int32_t slot) {
+  int32_t a, b, c, o;
+  if (g.pad3d) {
+    a = blk / (g.nH * g.nW);
+    b = (blk / g.nW) % g.nH;
+    c = blk % g.nW;
+    o = slot;
+  } else {
+    const int32_t p = blk * g.Bk + slot;
+    const int32_t slab = g.tt * g.H * g.W;
+    a = p / slab;
+    int32_t r = p - a * slab;
+    const int32_t sa = min(g.tt, g.T - a * g.tt);
+    const int32_t row = sa * g.th * g.W;
+    b = r / row;
+    r -= b * row;
+    const int32_t tsz = sa * min(g.th, g.H - b * g.th) * g.tw;
+    c = r / tsz;
+    o = r - c * tsz;
+  }
+  const int32_t sb = min(g.th, g.H - b * g.th);
+  const int32_t sc = min(g.tw, g.W - c * g.tw);
+  const int32_t lt = o / (sb * sc);
+  const int32_t rem = o - lt * sb * sc;
+  const int32_t lh = rem / sc;
+  const int32_t lw = rem - lh * sc;
+  return ((a * g.tt + lt) * g.H + b * g.th + lh) * g.W + c * g.tw + lw;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int kElt>
+__global__ void __launch_bounds__(kThreads)
+tile_permute_pool_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                         double* __restrict__ means, int32_t head_dim, Geom g) {
+  constexpr int kPer = 16 / kElt;
+  __shared__ int32_t nat_map[kMapRows];
+  extern __shared__ double red[];  // [groups][head_dim]
+  const int32_t nb = g.nb;
+  const int64_t bh = blockIdx.x / nb;
+  const int32_t blk = blockIdx.x % nb;
+  const int32_t n_valid = block_valid(g, blk);
+  const int32_t chunks = head_dim / kPer;
+  const int32_t groups = kThreads / chunks;
+  const int32_t ch = threadIdx.x % chunks;
+  const int32_t rg = threadIdx.x / chunks;
+  const uint4* sbase = src + bh * g.N * chunks;
+  uint4* dbase = dst + (bh * g.Npad + (int64_t)blk * g.Bk) * chunks;
+
+  double acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.0;
+  for (int32_t r0 = 0; r0 < g.Bk; r0 += kMapRows) {
+    const int32_t rows = min(kMapRows, g.Bk - r0);
+    const int32_t valid = max(0, min(rows, n_valid - r0));
+    if (r0 > 0) __syncthreads();  // the previous chunk's map is no longer read
+    for (int32_t t = threadIdx.x; t < valid; t += kThreads) nat_map[t] = natural_row(g, blk, r0 + t);
+    __syncthreads();
+    for (int32_t r = rg; r < rows; r += groups) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (r < valid) {
+        u = sbase[(int64_t)nat_map[r] * chunks + ch];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        if (kElt == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)bf16_lo(w[e]);
+            acc[2 * e + 1] += (double)bf16_hi(w[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(w[e]);
+        }
+      }
+      dbase[(int64_t)(r0 + r) * chunks + ch] = u;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) red[rg * head_dim + ch * kPer + e] = acc[e];
+  __syncthreads();
+  const double n = (double)n_valid;
+  for (int32_t d = threadIdx.x; d < head_dim; d += kThreads) {
+    double s = 0.0;
+    for (int32_t r = 0; r < groups; ++r) s += red[r * head_dim + d];
+    means[(bh * nb + blk) * head_dim + d] = s / n;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile_permute_pool(const void* src, void* dst, double* means, bool is_bf16,
+                                    int32_t bh, int32_t head_dim, const Geom& g,
+                                    hipStream_t stream) {
+  const int elt = is_bf16 ? 2 : 4;
+  const int32_t chunks = head_dim * elt / 16;
+  if (chunks <= 0 || chunks > kThreads || kThreads % chunks != 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(kThreads / chunks) * head_dim * sizeof(double);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)bh * g.nb;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (is_bf16) {
+    hipLaunchKernelGGL(tile_permute_pool_kernel<2>, dim3((uint32_t)blocks), dim3(kThreads), lds,
+                       stream, (const uint4*)src, (uint4*)dst, means, head_dim, g);
+  } else {
+    hipLaunchKernelGGL(tile_permute_pool_kernel<4>, dim3((uint32_t)blocks), dim3(kThreads), lds,
+                       stream, (const uint4*)src, (uint4*)dst, means, head_dim, g);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
                                int32_t head_dim, const Geom& g, bool inverse,

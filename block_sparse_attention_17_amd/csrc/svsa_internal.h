@@ -30,6 +30,9 @@ __host__ __device__ inline int32_t block_valid(const Geom& g, int32_t b) {
 hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
                                int32_t head_dim, const Geom& g, bool inverse,
                                hipStream_t stream);
+hipError_t launch_tile_permute_pool(const void* src, void* dst, double* means, bool is_bf16,
+                                    int32_t bh, int32_t head_dim, const Geom& g,
+                                    hipStream_t stream);
 hipError_t launch_pool(const void* x, bool is_bf16, double* out, int32_t bh,
                        int32_t head_dim, const Geom& g, hipStream_t stream);
 

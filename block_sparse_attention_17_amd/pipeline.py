@@ -35,13 +35,13 @@ class BlockSparseAttention:
                                    dtype=torch.uint8, device=dev)
 
     def permute_in(self, q, k, v, stream=None):
-        B.svsa_tile_permute(q, self.qt, self.geom, stream=stream)
-        B.svsa_tile_permute(k, self.kt, self.geom, stream=stream)
+        """Tile reorder of Q, K, V; Q and K are pooled into qbar / kbar in the same pass."""
+        B.svsa_tile_permute_pool(q, self.qt, self.qbar, self.geom, stream=stream)
+        B.svsa_tile_permute_pool(k, self.kt, self.kbar, self.geom, stream=stream)
         B.svsa_tile_permute(v, self.vt, self.geom, stream=stream)
 
     def build_mask(self, top_p=None, keep_frac=None, band_width=1, stream=None):
-        B.svsa_pool(self.qt, self.qbar, self.geom, stream=stream)
-        B.svsa_pool(self.kt, self.kbar, self.geom, stream=stream)
+        """Block mask from the block means that permute_in wrote."""
         B.svsa_block_mask(self.qbar, self.kbar, 1.0 / sqrt(self.head_dim), self.row_ptr,
                           self.col_idx, self.mask_ws, top_p=top_p, keep_frac=keep_frac,
                           band_width=band_width, stream=stream)

@@ -6,6 +6,7 @@
  *
  *   1. svsa_tile_permute  reorder (T,H,W) tokens into contiguous tiles
  *   2. svsa_pool          mean-pool Q and K per block (block summaries)
+ *      (svsa_tile_permute_pool does stages 1 and 2 for Q and K in one pass)
  *   3. svsa_block_mask    softmax(Qbar Kbar^T * scale) per query block, keep the
  *                         top-p (or a fixed fraction of) key blocks plus a
  *                         diagonal band, emitted as CSR index lists
@@ -121,6 +122,21 @@ SVSA_API int svsa_tile_permute(const void* src, void* dst, int32_t dtype, int32_
  */
 SVSA_API int svsa_pool(const void* x_tiled, int32_t dtype, double* out, int32_t batch,
               int32_t heads, int32_t head_dim, const svsa_geom* g, void* stream);
+
+/*
+ * Stages 1 and 2 in one pass, for Q and K: dst <- the forward tile reorder of
+ * src (exactly what svsa_tile_permute with inverse == 0 writes, padding rows
+ * zeroed) and means <- the block means of dst (exactly what svsa_pool writes
+ * for it), without reading dst back.  [PSA] Sec. 3.2 (the reorder) and
+ * [SPADE] abstract (the block summary) define the two results.
+ *
+ * src: [batch,heads,N,D] natural; dst: [batch,heads,N_pad,D] tiled; both of
+ * dtype SVSA_BF16 or SVSA_F32.  means: float64 [batch,heads,nb,D].  The head
+ * dimension limits of svsa_pool apply.  src, dst and means must not overlap.
+ */
+SVSA_API int svsa_tile_permute_pool(const void* src, void* dst, double* means, int32_t dtype,
+                                    int32_t batch, int32_t heads, int32_t head_dim,
+                                    const svsa_geom* g, void* stream);
 
 /*
  * Workspace (device bytes) needed by svsa_block_mask for these sizes.

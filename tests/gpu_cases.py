@@ -58,12 +58,9 @@ class GpuRun:
         self.geom = geometry(cfg)
         self.m = m
         self.bsa = m.BlockSparseAttention(cfg.batch, cfg.heads, cfg.head_dim, self.geom)
-        log(f"{name}: permute Q,K,V on the GPU")
+        log(f"{name}: permute Q,K,V and pool Q,K on the GPU (svsa_tile_permute_pool for Q, K)")
         self.q_dev, self.k_dev, self.v_dev = (bits_to_dev(x) for x in (inp.q, inp.k, inp.v))
         self.bsa.permute_in(self.q_dev, self.k_dev, self.v_dev)
-        log(f"{name}: pool Q,K on the GPU")
-        m.svsa_pool(self.bsa.qt, self.bsa.qbar, self.geom)
-        m.svsa_pool(self.bsa.kt, self.bsa.kbar, self.geom)
         torch.cuda.synchronize()
         self.qt_bits = dev_to_bits(self.bsa.qt)
         self.kt_bits = dev_to_bits(self.bsa.kt)

@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -58,6 +58,24 @@ def test_permute_argument_errors(mod):
     bad = mod.Geometry(4, 8, 8, 2, 4, 4).c()
     bad.pad3d = 2                                                                  # not 0/1
     assert lib.svsa_tile_permute(FAKE, FAKE2, 0, 1, 1, 64, ctypes.byref(bad), 0, None) == E_INV
+
+
+def test_fused_permute_pool_argument_errors(mod):
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)
+    M = ctypes.c_void_p(0x4000000)
+    E_INV, E_UNS = -1, -2
+    f = lib.svsa_tile_permute_pool
+    assert f(None, FAKE2, M, 0, 1, 1, 64, g, None) == E_INV
+    assert f(FAKE, None, M, 0, 1, 1, 64, g, None) == E_INV
+    assert f(FAKE, FAKE2, None, 0, 1, 1, 64, g, None) == E_INV
+    assert f(FAKE, FAKE2, M, 0, 1, 0, 64, g, None) == E_INV                      # heads
+    assert f(FAKE, FAKE2, M, 5, 1, 1, 64, g, None) == E_UNS                      # dtype
+    assert f(FAKE, FAKE2, M, 0, 1, 1, 12, g, None) == E_UNS                      # 24-byte rows
+    assert f(FAKE, FAKE2, M, 0, 1, 1, 64, None, None) == E_INV
+    assert f(FAKE, FAKE, M, 0, 1, 1, 64, g, None) == E_INV                       # src == dst
+    assert f(FAKE, FAKE2, FAKE2, 0, 1, 1, 64, g, None) == E_INV                  # means in dst
+    assert f(FAKE, FAKE2, ctypes.c_void_p(0x4000004), 0, 1, 1, 64, g, None) == E_INV  # 8-byte
 
 
 def test_pad3d_geometry_counts(mod):

@@ -91,6 +91,47 @@ def test_pool_f32_partial_tail():
     np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-15, atol=1e-15)
 
 
+@pytest.mark.parametrize("grid,tile,D", [((3, 5, 6), (2, 2, 4), 64), ((5, 7, 3), (4, 4, 4), 128),
+                                         ((21, 30, 52), (4, 4, 4), 128), ((1, 1, 1), (2, 2, 2), 64),
+                                         ((9, 21, 35), (3, 8, 16), 128),
+                                         ((5, 20, 40), (4, 16, 32), 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("pad3d", [False, True])
+def test_fused_permute_pool(grid, tile, D, dtype, pad3d):
+    """svsa_tile_permute_pool equals svsa_tile_permute followed by svsa_pool
+    bitwise, and the oracle's reorder and block means (exactly for bf16
+    inputs, to 1e-15 for float32 ones).  Partial tiles on every axis, blocks
+    straddling partial tiles (packed layout), padding-only block slots (3D
+    padding), and a 2048-token block (more rows than one pass of the kernel's
+    row map holds)."""
+    import block_sparse_attention_17_amd as m
+    G = m.Geometry(*grid, *tile, pad3d=pad3d)
+    gc.log(f"fused permute+pool grid {grid} tile {tile} D={D} {dtype} pad3d={pad3d}")
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(rng.standard_normal((2, 3, G.N, D)).astype(np.float32)).cuda()
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    x64 = x.float().cpu().numpy().astype(np.float64)
+    fused = torch.full((2, 3, G.N_pad, D), 7, dtype=x.dtype, device="cuda")
+    means = torch.full((2, 3, G.nb, D), 7.0, dtype=torch.float64, device="cuda")
+    m.svsa_tile_permute_pool(x, fused, means, G)
+    two = torch.full_like(fused, 5)
+    means2 = torch.full_like(means, 5.0)
+    m.svsa_tile_permute(x, two, G)
+    m.svsa_pool(two, means2, G)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.cpu(), two.cpu())
+    assert torch.equal(means.cpu(), means2.cpu())
+    ref_t = orc.permute_fwd(x64, grid, tile, pad3d)
+    assert np.array_equal(fused.float().cpu().numpy().astype(np.float64), ref_t)
+    _, counts = orc.block_layout(grid, tile, pad3d)
+    ref_m = orc.pool(ref_t, G.N, G.Bk, counts)
+    if dtype == "bf16":
+        assert np.array_equal(means.cpu().numpy(), ref_m)
+    else:
+        np.testing.assert_allclose(means.cpu().numpy(), ref_m, rtol=1e-15, atol=1e-15)
+
+
 # ---------------------------------------------------------------- stage 3
 MASK_CASES = [("tiny", 0.9, None), ("small", 0.9, None), ("wan480", 0.9, None),
               ("wan720", 0.9, None), ("wan720", 0.8, None), ("wan720", 0.95, None),
