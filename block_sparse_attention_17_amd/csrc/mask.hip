@@ -50,8 +50,14 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
               int32_t nk, int32_t D, double scale, int32_t tiles_q, int32_t tiles_k) {
   __shared__ double As[kTile * kLdsStride];
   __shared__ double Bs[kTile * kLdsStride];
-  const int64_t bh = blockIdx.x / (tiles_q * tiles_k);
-  const int32_t t2 = blockIdx.x % (tiles_q * tiles_k);
+  // Workgroups go to the chip's 8 XCDs in turn (workgroup w to XCD w % 8).
+  // Numbering the tiles XCD-major hands each XCD a contiguous run of them, so
+  // the tiles of one (b, h) share one L2 instead of every XCD fetching that
+  // head's Qbar and Kbar.  XCD x takes q + (x < r) tiles, q = G / 8, r = G % 8.
+  const uint32_t G = gridDim.x, q8 = G / 8, r8 = G % 8, x8 = blockIdx.x % 8;
+  const uint32_t wg = x8 * q8 + min(x8, r8) + blockIdx.x / 8;
+  const int64_t bh = wg / (tiles_q * tiles_k);
+  const int32_t t2 = wg % (tiles_q * tiles_k);
   const int32_t i0 = (t2 / tiles_k) * kTile, j0 = (t2 % tiles_k) * kTile;
   const double* qb = qbar + bh * nq * D;
   const double* kb = kbar + bh * nk * D;
@@ -65,7 +71,7 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
     for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   for (int32_t dc = 0; dc < D; dc += kDc) {
-    // stage rows i0 .. i0 + 63 and j0 .. j0 + 63, dims dc .. dc + kDc - 1
+    // stage rows i0 .. i0 + kTile - 1 and j0 .. j0 + kTile - 1, dims dc .. dc + kDc - 1
     for (int32_t e = threadIdx.x; e < kTile * kDc; e += kLThreads) {
       const int32_t r = e / kDc, d = e % kDc;
       const bool dok = dc + d < D;
