@@ -70,15 +70,33 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int32_t dc = 0; dc < D; dc += kDc) {
-    // stage rows i0 .. i0 + kTile - 1 and j0 .. j0 + kTile - 1, dims dc .. dc + kDc - 1
-    for (int32_t e = threadIdx.x; e < kTile * kDc; e += kLThreads) {
+  // Operand chunks (rows i0 .. i0 + kTile - 1 and j0 .. j0 + kTile - 1, kDc
+  // dims) are loaded into registers one chunk ahead, so the global loads of
+  // chunk c + 1 are in flight while the MFMAs of chunk c run.
+  constexpr int kPerThread = kTile * kDc / kLThreads;
+  static_assert(kTile * kDc % kLThreads == 0, "whole staging rounds");
+  double pa[kPerThread], pb[kPerThread];
+  auto load_chunk = [&](int32_t dc) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int32_t e = threadIdx.x + u * kLThreads;
       const int32_t r = e / kDc, d = e % kDc;
       const bool dok = dc + d < D;
-      As[r * kLdsStride + d] = (i0 + r < nq && dok) ? qb[(int64_t)(i0 + r) * D + dc + d] : 0.0;
-      Bs[r * kLdsStride + d] = (j0 + r < nk && dok) ? kb[(int64_t)(j0 + r) * D + dc + d] : 0.0;
+      pa[u] = (i0 + r < nq && dok) ? qb[(int64_t)(i0 + r) * D + dc + d] : 0.0;
+      pb[u] = (j0 + r < nk && dok) ? kb[(int64_t)(j0 + r) * D + dc + d] : 0.0;
+    }
+  };
+  load_chunk(0);
+  for (int32_t dc = 0; dc < D; dc += kDc) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int32_t e = threadIdx.x + u * kLThreads;
+      const int32_t r = e / kDc, d = e % kDc;
+      As[r * kLdsStride + d] = pa[u];
+      Bs[r * kLdsStride + d] = pb[u];
     }
     __syncthreads();
+    if (dc + kDc < D) load_chunk(dc + kDc);
 #pragma unroll
     for (int ks = 0; ks < kDc / 4; ++ks) {
       const int32_t d = 4 * ks + lk;
