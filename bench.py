@@ -324,8 +324,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    # Q and K are reordered and pooled in one pass; V is only reordered
-    stage_names = ["permute_pool_qk_permute_v", "mask", "attention", "permute_out"]
+    # Q and K are reordered and pooled in one pass each; V is reordered straight
+    # into the attention workspace's V^T
+    stage_names = ["permute_pool_qk_stage_v", "mask", "attention", "permute_out"]
 
     stripe = stripe_params(cfg.heads, seed=args.seed) if args.stripe else None
 
@@ -481,8 +482,8 @@ def main():
         "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
         "dense": dense,
         "roofline": {
-            "kernel": "svsa_block_sparse_attn (union_kernel + queue_kernel + vt_kernel + "
-                      "attn_kernel; attn_kernel is >99% of it)",
+            "kernel": "svsa_block_sparse_attn on V staged by svsa_attn_stage_v (union_kernel + "
+                      "queue_kernel + attn_kernel; attn_kernel is >99% of it)",
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": BF16_PEAK_TFLOPS,

@@ -108,6 +108,7 @@ def _load():
         "svsa_attn_workspace_bytes": (sz, [i32, i32, gp]),
         "svsa_block_sparse_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp, vp,
                                                   vp, sz, vp]),
+        "svsa_attn_stage_v": (ctypes.c_int, [vp, i32, i32, i32, gp, vp, sz, vp]),
         "svsa_snr_top_p": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), i32, i32, flt, flt,
                                           fp]),
         "svsa_kmeans_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -146,7 +147,8 @@ _lib = _load()
 
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_tile_permute_pool",
             "svsa_block_mask_workspace_bytes", "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
-            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_snr_top_p",
+            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_attn_stage_v",
+            "svsa_snr_top_p",
             "svsa_kmeans_workspace_bytes", "svsa_kmeans", "svsa_cluster_metric",
             "svsa_cluster_means_workspace_bytes", "svsa_cluster_means",
             "svsa_cluster_capacity", "svsa_cluster_layout_workspace_bytes",
@@ -306,7 +308,8 @@ def svsa_attn_workspace_bytes(batch, heads, geom):
 
 def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, workspace,
                            stream=None):
-    """out (bf16, tile order) <- block-sparse attention of q, k, v over the CSR lists."""
+    """out (bf16, tile order) <- block-sparse attention of q, k, v over the CSR lists.
+    v=None: V as staged into `workspace` by svsa_attn_stage_v."""
     import torch
     B, Hh, _, D = q.shape
     bf = (torch.bfloat16,)
@@ -316,6 +319,16 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
         _ptr(col_idx, "col_idx", (torch.int32,)), _ptr(workspace, "workspace", (torch.uint8,)),
         workspace.numel(), _stream(stream)))
     return out
+
+
+def svsa_attn_stage_v(v, workspace, geom, stream=None):
+    """Natural-order V (bf16 [B, Hh, N, D]) -> the attention workspace's V^T, tile order."""
+    import torch
+    B, Hh, _, D = v.shape
+    _check("svsa_attn_stage_v", _lib.svsa_attn_stage_v(
+        _ptr(v, "v", (torch.bfloat16,)), B, Hh, D, ctypes.byref(geom.c()),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+    return workspace
 
 
 # ---------------------------------------------------------------------------

@@ -430,7 +430,8 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
         al(workspace, 256)))
     return SVSA_E_INVALID;
   Geom g;
-  if (!q || !k || !v || !out || !row_ptr || !col_idx || batch < 1 || heads < 1 ||
+  // v == NULL: V^T was staged into the workspace by svsa_attn_stage_v
+  if (!q || !k || !out || !row_ptr || !col_idx || batch < 1 || heads < 1 ||
       head_dim < 1 || !make_geom(gin, &g) || !isfinite(softmax_scale))
     return SVSA_E_INVALID;
   if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
@@ -444,13 +445,35 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
   if (bh * nbs * nbs >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
   const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;
   if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
-      overlaps(out, tbytes, v, tbytes))
+      (v && overlaps(out, tbytes, v, tbytes)))
     return SVSA_E_INVALID;
   if (!workspace || ws_bytes < svsa_attn_workspace_bytes(batch, heads, gin))
     return SVSA_E_WORKSPACE;
+  if (overlaps(out, tbytes, workspace, ws_bytes)) return SVSA_E_INVALID;
   return from_hip(svsa::launch_block_sparse_attn(q, k, v, out, (int32_t)bh, head_dim, g,
                                                  softmax_scale, row_ptr, col_idx, workspace,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int svsa_attn_stage_v(const void* v, int32_t batch, int32_t heads, int32_t head_dim,
+                      const svsa_geom* gin, void* workspace, size_t ws_bytes, void* stream) {
+  if (!(al(v, 16) && al(workspace, 256))) return SVSA_E_INVALID;
+  Geom g;
+  if (!v || batch < 1 || heads < 1 || head_dim < 1 || !make_geom(gin, &g))
+    return SVSA_E_INVALID;
+  if (head_dim != 64 && head_dim != 128) return SVSA_E_UNSUPPORTED;
+  if (g.Bk % 32 != 0 || g.nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int32_t sub = g.Bk % 64 == 0 ? 64 : 32;
+  const int64_t nbs = g.pad3d ? (int64_t)g.nb * (g.Bk / sub) : ((int64_t)g.N + sub - 1) / sub;
+  if (nbs > kMaxNb) return SVSA_E_UNSUPPORTED;
+  if ((int64_t)g.Npad * head_dim * 2 >= (1ll << 31)) return SVSA_E_UNSUPPORTED;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh * nbs * nbs >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (!workspace || ws_bytes < svsa_attn_workspace_bytes(batch, heads, gin))
+    return SVSA_E_WORKSPACE;
+  if (overlaps(v, (size_t)bh * g.N * head_dim * 2, workspace, ws_bytes)) return SVSA_E_INVALID;
+  return from_hip(svsa::launch_attn_stage_v(v, (int32_t)bh, head_dim, g, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t svsa_cluster_attn_workspace_bytes(int32_t batch, int32_t heads, int32_t n_q, int32_t nq,

@@ -25,8 +25,10 @@
 //    per XCD, a whole (b, h) per queue, so that the workgroups of one XCD
 //    share the head's key blocks in its L2; a persistent kernel drains its
 //    own XCD's queue first, then the others.
-//  * V is transposed once per call (vt_kernel), so both MFMA A operands (K
-//    rows for S^T, V^T rows for O^T) are plain 16-byte LDS reads.
+//  * V is transposed once per call (vt_kernel), or once per step straight
+//    from natural-order V (stage_v_kernel, svsa_attn_stage_v), so both MFMA
+//    A operands (K rows for S^T, V^T rows for O^T) are plain 16-byte LDS
+//    reads.
 //  * Key blocks reach LDS through a 4-slot ring filled by MUBUF buffer loads
 //    with the LDS destination (no VGPR staging), issued two blocks ahead and
 //    waited for with explicit vmcnt counts.  Tiles are XOR-swizzled by row so
@@ -294,6 +296,19 @@ __device__ __forceinline__ int vt_pos(int kv) {
 
 constexpr int kVtThreads = 256;
 
+// Second half of the transpose: the key block staged row-major in LDS goes
+// out as D rows of BK keys in vt_pos order; output word i holds positions
+// 2p, 2p+1 of row d.
+template <int D, int BK>
+__device__ __forceinline__ void vt_store(const uint16_t (*tile)[D + 2], uint16_t* dst) {
+  for (int i = threadIdx.x; i < BK * D / 2; i += kVtThreads) {
+    const int d = (2 * i) / BK, p = (2 * i) % BK;
+    // positions p, p+1 hold keys vt_pos^-1(p), vt_pos^-1(p+1) (vt_pos is an involution)
+    const uint32_t lo = tile[vt_pos(p)][d], hi = tile[vt_pos(p + 1)][d];
+    reinterpret_cast<uint32_t*>(dst)[i] = lo | (hi << 16);
+  }
+}
+
 template <int D, int BK>
 __global__ void __launch_bounds__(kVtThreads)
 vt_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt, int32_t nb, int32_t Npad) {
@@ -309,13 +324,43 @@ vt_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt, int32_t nb, int
     tile[kv][d + 1] = (uint16_t)(w >> 16);
   }
   __syncthreads();
-  // output word i holds positions 2p, 2p+1 of row d
-  for (int i = threadIdx.x; i < BK * D / 2; i += kVtThreads) {
-    const int d = (2 * i) / BK, p = (2 * i) % BK;
-    // positions p, p+1 hold keys vt_pos^-1(p), vt_pos^-1(p+1) (vt_pos is an involution)
-    const uint32_t lo = tile[vt_pos(p)][d], hi = tile[vt_pos(p + 1)][d];
-    reinterpret_cast<uint32_t*>(dst)[i] = lo | (hi << 16);
+  vt_store<D, BK>(tile, dst);
+}
+
+// The same V^T from natural-order V: the rows of key sub-block j are gathered
+// from their natural positions (the tile reorder of [PSA] Sec. 3.2, inverted
+// per row) and padding slots become zeros, so the result equals vt_kernel run
+// on the reordered V without that tensor ever being written.  nbs sub-blocks
+// of BK rows per (b, h).
+template <int D, int BK>
+__global__ void __launch_bounds__(kVtThreads)
+stage_v_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt, int32_t nbs, Geom g) {
+  static_assert(BK <= kVtThreads, "one thread per row for the row map");
+  __shared__ __align__(16) uint16_t tile[BK][D + 2];
+  __shared__ int32_t nat[BK];
+  const int64_t bh = blockIdx.x / nbs;
+  const int32_t j = blockIdx.x % nbs;
+  if (threadIdx.x < BK) {
+    const int32_t p = j * BK + (int32_t)threadIdx.x;  // tiled row
+    const int32_t blk = p / g.Bk, slot = p - blk * g.Bk;
+    nat[threadIdx.x] =
+        (blk < g.nb && slot < block_valid(g, blk)) ? natural_row(g, blk, slot) : -1;
   }
+  __syncthreads();
+  constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  const uint4* src = reinterpret_cast<const uint4*>(v) + bh * g.N * kChunks;
+  for (int i = threadIdx.x; i < BK * kChunks; i += kVtThreads) {
+    const int kv = i / kChunks, c = i % kChunks;
+    const int32_t n = nat[kv];
+    const uint4 u = n >= 0 ? src[(int64_t)n * kChunks + c] : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t* row = reinterpret_cast<uint32_t*>(&tile[kv][8 * c]);  // rows are 4-byte aligned
+    row[0] = u.x;
+    row[1] = u.y;
+    row[2] = u.z;
+    row[3] = u.w;
+  }
+  __syncthreads();
+  vt_store<D, BK>(tile, reinterpret_cast<uint16_t*>(vt) + (bh * g.Npad + (int64_t)j * BK) * D);
 }
 
 // ---------------------------------------------------------------------------
@@ -949,10 +994,13 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
                        int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
                        int32_t npad_k, float c_log2, hipStream_t stream) {
-  hipLaunchKernelGGL((vt_kernel<D, PR ? 32 : BK>), dim3((uint32_t)((int64_t)bh * nb)), dim3(kVtThreads), 0,
-                     stream, (const __bf16*)v, vt, nb, npad_k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (v) {  // else V^T is already in the workspace (launch_attn_stage_v)
+    hipLaunchKernelGGL((vt_kernel<D, PR ? 32 : BK>), dim3((uint32_t)((int64_t)bh * nb)),
+                       dim3(kVtThreads), 0, stream, (const __bf16*)v, vt, nb, npad_k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   uint32_t grid = 0;
   e = attn_grid<D, BK, PR>(w.items, &grid);
   if (e != hipSuccess) return e;
@@ -1052,6 +1100,27 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
   const GeomSched sc{g, w.ratio, w.sub};
   return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
                        ws, stream);
+}
+
+hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
+                               void* ws, hipStream_t stream) {
+  if (g.Bk % 32 != 0) return hipErrorInvalidValue;
+  if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
+  const AttnWs w = attn_ws_layout(bh, g);
+  const int64_t blocks = (int64_t)bh * w.nbs;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  __bf16* vt = reinterpret_cast<__bf16*>(static_cast<char*>(ws) + w.vt_off);
+  const dim3 grid((uint32_t)blocks), blk(kVtThreads);
+  // the sub-block size and V^T layout that launch_block_sparse_attn's kernels read
+  if (head_dim == 128 && w.sub == 64)
+    hipLaunchKernelGGL((stage_v_kernel<128, 64>), grid, blk, 0, stream, (const __bf16*)v, vt, w.nbs, g);
+  else if (head_dim == 64 && w.sub == 64)
+    hipLaunchKernelGGL((stage_v_kernel<64, 64>), grid, blk, 0, stream, (const __bf16*)v, vt, w.nbs, g);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((stage_v_kernel<128, 32>), grid, blk, 0, stream, (const __bf16*)v, vt, w.nbs, g);
+  else
+    hipLaunchKernelGGL((stage_v_kernel<64, 32>), grid, blk, 0, stream, (const __bf16*)v, vt, w.nbs, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void* out,

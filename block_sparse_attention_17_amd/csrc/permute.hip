@@ -99,35 +99,6 @@ tile_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int3
 // tile along w, then (t, h, w) inside the tile.  kElt: 2 (bf16) or 4 (f32).
 constexpr int kMapRows = 1024;  // natural-row map entries held in LDS at once
 
-__device__ __forceinline__ int32_t natural_row(const Geom& g, int32_t blk, int32_t slot) {
-  int32_t a, b, c, o;
-  if (g.pad3d) {
-    a = blk / (g.nH * g.nW);
-    b = (blk / g.nW) % g.nH;
-    c = blk % g.nW;
-    o = slot;
-  } else {
-    const int32_t p = blk * g.Bk + slot;
-    const int32_t slab = g.tt * g.H * g.W;
-    a = p / slab;
-    int32_t r = p - a * slab;
-    const int32_t sa = min(g.tt, g.T - a * g.tt);
-    const int32_t row = sa * g.th * g.W;
-    b = r / row;
-    r -= b * row;
-    const int32_t tsz = sa * min(g.th, g.H - b * g.th) * g.tw;
-    c = r / tsz;
-    o = r - c * tsz;
-  }
-  const int32_t sb = min(g.th, g.H - b * g.th);
-  const int32_t sc = min(g.tw, g.W - c * g.tw);
-  const int32_t lt = o / (sb * sc);
-  const int32_t rem = o - lt * sb * sc;
-  const int32_t lh = rem / sc;
-  const int32_t lw = rem - lh * sc;
-  return ((a * g.tt + lt) * g.H + b * g.th + lh) * g.W + c * g.tw + lw;
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -26,10 +26,49 @@ __host__ __device__ inline int32_t block_valid(const Geom& g, int32_t b) {
   return sa * sb * sc;
 }
 
+// Natural row (t*H*W + h*W + w) of slot `slot` of block `blk` in the tiled
+// sequence; the slot must be valid (slot < block_valid(g, blk)).  It inverts
+// the tile walk: the slab of tile rows along t (every earlier slab is full),
+// then the row of tiles along h inside it (every earlier row is full), then
+// the tile along w, then (t, h, w) inside the tile; in the 3D-padded layout
+// the block is the tile.
+__device__ inline int32_t natural_row(const Geom& g, int32_t blk, int32_t slot) {
+  int32_t a, b, c, o;
+  if (g.pad3d) {
+    a = blk / (g.nH * g.nW);
+    b = (blk / g.nW) % g.nH;
+    c = blk % g.nW;
+    o = slot;
+  } else {
+    const int32_t p = blk * g.Bk + slot;
+    const int32_t slab = g.tt * g.H * g.W;
+    a = p / slab;
+    int32_t r = p - a * slab;
+    const int32_t sa = min(g.tt, g.T - a * g.tt);
+    const int32_t row = sa * g.th * g.W;
+    b = r / row;
+    r -= b * row;
+    const int32_t tsz = sa * min(g.th, g.H - b * g.th) * g.tw;
+    c = r / tsz;
+    o = r - c * tsz;
+  }
+  const int32_t sb = min(g.th, g.H - b * g.th);
+  const int32_t sc = min(g.tw, g.W - c * g.tw);
+  const int32_t lt = o / (sb * sc);
+  const int32_t rem = o - lt * sb * sc;
+  const int32_t lh = rem / sc;
+  const int32_t lw = rem - lh * sc;
+  return ((a * g.tt + lt) * g.H + b * g.th + lh) * g.W + c * g.tw + lw;
+}
+
 // Launchers: enqueue on `stream`, return the launch status.
 hipError_t launch_tile_permute(const void* src, void* dst, int elt_bytes, int32_t bh,
                                int32_t head_dim, const Geom& g, bool inverse,
                                hipStream_t stream);
+// V^T for the attention kernel straight from natural-order V (into the
+// attention workspace laid out by attn_ws_layout).
+hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
+                               void* ws, hipStream_t stream);
 hipError_t launch_tile_permute_pool(const void* src, void* dst, double* means, bool is_bf16,
                                     int32_t bh, int32_t head_dim, const Geom& g,
                                     hipStream_t stream);

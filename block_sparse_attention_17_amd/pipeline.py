@@ -21,8 +21,7 @@ class BlockSparseAttention:
         shp_t = (batch, heads, g.N_pad, head_dim)
         self.qt = torch.empty(shp_t, **bf)
         self.kt = torch.empty(shp_t, **bf)
-        self.vt = torch.empty(shp_t, **bf)
-        self.ot = torch.empty(shp_t, **bf)
+        self.ot = torch.empty(shp_t, **bf)   # V goes straight into attn_ws (no tiled copy)
         self.out = torch.empty((batch, heads, g.N, head_dim), **bf)
         self.qbar = torch.empty((batch, heads, g.nb, head_dim), dtype=torch.float64, device=dev)
         self.kbar = torch.empty_like(self.qbar)
@@ -35,10 +34,11 @@ class BlockSparseAttention:
                                    dtype=torch.uint8, device=dev)
 
     def permute_in(self, q, k, v, stream=None):
-        """Tile reorder of Q, K, V; Q and K are pooled into qbar / kbar in the same pass."""
+        """Tile reorder of Q and K with their block means (qbar / kbar) in the same
+        pass; V is reordered straight into the attention workspace's V^T."""
         B.svsa_tile_permute_pool(q, self.qt, self.qbar, self.geom, stream=stream)
         B.svsa_tile_permute_pool(k, self.kt, self.kbar, self.geom, stream=stream)
-        B.svsa_tile_permute(v, self.vt, self.geom, stream=stream)
+        B.svsa_attn_stage_v(v, self.attn_ws, self.geom, stream=stream)
 
     def build_mask(self, top_p=None, keep_frac=None, band_width=1, stream=None):
         """Block mask from the block means that permute_in wrote."""
@@ -58,7 +58,7 @@ class BlockSparseAttention:
 
     def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None):
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
-        B.svsa_block_sparse_attn(self.qt, self.kt, self.vt, self.ot, self.geom, scale,
+        B.svsa_block_sparse_attn(self.qt, self.kt, None, self.ot, self.geom, scale,
                                  self.row_ptr if row_ptr is None else row_ptr,
                                  self.col_idx if col_idx is None else col_idx,
                                  self.attn_ws, stream=stream)

@@ -6,7 +6,8 @@
  *
  *   1. svsa_tile_permute  reorder (T,H,W) tokens into contiguous tiles
  *   2. svsa_pool          mean-pool Q and K per block (block summaries)
- *      (svsa_tile_permute_pool does stages 1 and 2 for Q and K in one pass)
+ *      (svsa_tile_permute_pool does stages 1 and 2 for Q and K in one pass;
+ *      svsa_attn_stage_v does stage 1 for V straight into stage 4's workspace)
  *   3. svsa_block_mask    softmax(Qbar Kbar^T * scale) per query block, keep the
  *                         top-p (or a fixed fraction of) key blocks plus a
  *                         diagonal band, emitted as CSR index lists
@@ -230,8 +231,14 @@ SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const sv
  *   t over the valid keys (index < N) of the blocks listed for q's block.
  *
  * q, k, v, out: bf16 [batch,heads,N_pad,D] in tile order.  Output rows of
- *   padded query positions (>= N) are written but unspecified.  out must not
- *   overlap q, k or v.  A query block with an empty list gets zeros.
+ *   padding slots (positions >= N in the packed layout, a block's slots past
+ *   its valid tokens in the 3D-padded one) are unspecified: they may be
+ *   written with any value or left untouched.  out must not
+ *   overlap q, k, v or the workspace.  A query block with an empty list gets
+ *   zeros.  v may be NULL when svsa_attn_stage_v has written V into this
+ *   workspace for the same batch, heads, head_dim and geometry, and nothing
+ *   has written the workspace since (other svsa_block_sparse_attn calls with
+ *   v == NULL leave it intact).
  * row_ptr / col_idx: CSR as produced by svsa_block_mask (rows (b,h,i); each
  *   column in [0, nb)).  Columns outside [0, nb) are ignored.
  * head_dim: 64 or 128; tile volume Bk: any multiple of 32 (blocks are run as
@@ -248,6 +255,22 @@ SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v,
                            const svsa_geom* g, float softmax_scale,
                            const int32_t* row_ptr, const int32_t* col_idx,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 1 for V fused with the layout change the attention kernel needs:
+ * natural-order V ([batch,heads,N,D], bf16) is written into `workspace` as
+ * the transposed key blocks svsa_block_sparse_attn reads, in tile order
+ * ([PSA] Sec. 3.2), with zeros in padding slots.  The result is what
+ * svsa_block_sparse_attn would build from svsa_tile_permute's tiled V, so a
+ * following svsa_block_sparse_attn(..., v = NULL, ..., workspace) gives the
+ * same output bitwise, and no tiled V has to be stored.
+ *
+ * head_dim, geometry and the workspace size: as for svsa_block_sparse_attn.
+ * v must not overlap the workspace.
+ */
+SVSA_API int svsa_attn_stage_v(const void* v, int32_t batch, int32_t heads, int32_t head_dim,
+                               const svsa_geom* g, void* workspace, size_t ws_bytes,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * Variable-size blocks: query / key clustering ([iCATS] Sec. 3.1 and 4.1,

@@ -64,7 +64,13 @@ class GpuRun:
         torch.cuda.synchronize()
         self.qt_bits = dev_to_bits(self.bsa.qt)
         self.kt_bits = dev_to_bits(self.bsa.kt)
-        self.vt_bits = dev_to_bits(self.bsa.vt)
+        # the pipeline stages V straight into the attention workspace; the tiled V
+        # that svsa_tile_permute writes is checked on its own
+        vt = torch.empty_like(self.bsa.qt)
+        m.svsa_tile_permute(self.v_dev, vt, self.geom)
+        torch.cuda.synchronize()
+        self.vt_bits = dev_to_bits(vt)
+        del vt
         self.qbar = self.bsa.qbar.cpu().numpy()
         self.kbar = self.bsa.kbar.cpu().numpy()
 

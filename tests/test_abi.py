@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -76,6 +76,24 @@ def test_fused_permute_pool_argument_errors(mod):
     assert f(FAKE, FAKE, M, 0, 1, 1, 64, g, None) == E_INV                       # src == dst
     assert f(FAKE, FAKE2, FAKE2, 0, 1, 1, 64, g, None) == E_INV                  # means in dst
     assert f(FAKE, FAKE2, ctypes.c_void_p(0x4000004), 0, 1, 1, 64, g, None) == E_INV  # 8-byte
+
+
+def test_attn_stage_v_argument_errors(mod):
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)                      # Bk = 32
+    ws = ctypes.c_void_p(0x4000000)
+    need = lib.svsa_attn_workspace_bytes(1, 1, g)
+    assert need > 0
+    E_INV, E_UNS, E_WS = -1, -2, -3
+    f = lib.svsa_attn_stage_v
+    assert f(None, 1, 1, 64, g, ws, need, None) == E_INV
+    assert f(FAKE, 0, 1, 64, g, ws, need, None) == E_INV                          # batch
+    assert f(FAKE, 1, 1, 96, g, ws, need, None) == E_UNS                          # head_dim
+    assert f(FAKE, 1, 1, 64, _g(mod, 4, 8, 8, 1, 4, 4), ws, need, None) == E_UNS  # Bk 16
+    assert f(FAKE, 1, 1, 64, g, None, need, None) == E_WS
+    assert f(FAKE, 1, 1, 64, g, ws, need - 1, None) == E_WS
+    assert f(FAKE, 1, 1, 64, g, ctypes.c_void_p(0x4000080), need, None) == E_INV  # not 256-aligned
+    assert f(ws, 1, 1, 64, g, ws, need, None) == E_INV                            # v inside ws
 
 
 def test_pad3d_geometry_counts(mod):

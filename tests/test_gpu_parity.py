@@ -418,6 +418,53 @@ def test_attention_edge_cases_custom_csr():
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
+@pytest.mark.parametrize("grid,tile,D,pad3d", [((5, 9, 14), (4, 4, 4), 128, False),
+                                               ((5, 9, 14), (4, 4, 4), 64, True),
+                                               ((7, 20, 35), (3, 4, 8), 128, False),
+                                               ((7, 20, 35), (3, 4, 8), 64, True),
+                                               ((9, 21, 35), (3, 8, 16), 128, False),
+                                               ((9, 21, 35), (3, 8, 16), 128, True)])
+def test_staged_v_equals_tiled_v(grid, tile, D, pad3d):
+    """svsa_attn_stage_v from natural-order V, then svsa_block_sparse_attn with
+    v = NULL, gives the output of svsa_block_sparse_attn on svsa_tile_permute's
+    tiled V bitwise (64- and 32-token sub-blocks, partial tiles, both layouts,
+    random kept sets); a second call on the same workspace gives it again."""
+    import block_sparse_attention_17_amd as m
+    G = m.Geometry(*grid, *tile, pad3d=pad3d)
+    H, nb = 2, G.nb
+    gc.log(f"staged V: grid {grid} tile {tile} D={D} pad3d={pad3d}, {nb} blocks")
+    rng = np.random.default_rng(59)
+    nat = [torch.from_numpy(rng.standard_normal((1, H, G.N, D)).astype(np.float32)).cuda()
+           .to(torch.bfloat16) for _ in range(3)]
+    tiled = [torch.empty((1, H, G.N_pad, D), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    for x, t in zip(nat, tiled):
+        m.svsa_tile_permute(x, t, G)
+    lists = [sorted(set(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+                    | {i}) for _ in range(H) for i in range(nb)]
+    rp = np.zeros(H * nb + 1, np.int32)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    rp_d = torch.from_numpy(rp).cuda()
+    ci_d = torch.from_numpy(np.array([c for cs in lists for c in cs], np.int32)).cuda()
+    wsb = m.svsa_attn_workspace_bytes(1, H, G)
+    ws1 = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws2 = torch.full((wsb,), 0x5A, dtype=torch.uint8, device="cuda")
+    ref = torch.empty_like(tiled[0])
+    got = torch.full_like(tiled[0], 3.0)
+    got2 = torch.full_like(tiled[0], 5.0)
+    m.svsa_block_sparse_attn(tiled[0], tiled[1], tiled[2], ref, G, 1 / np.sqrt(D), rp_d, ci_d, ws1)
+    m.svsa_attn_stage_v(nat[2], ws2, G)
+    m.svsa_block_sparse_attn(tiled[0], tiled[1], None, got, G, 1 / np.sqrt(D), rp_d, ci_d, ws2)
+    m.svsa_block_sparse_attn(tiled[0], tiled[1], None, got2, G, 1 / np.sqrt(D), rp_d, ci_d, ws2)
+    torch.cuda.synchronize()
+    # padding slots of the output are unspecified (the packed layout's tail past
+    # the last sub-block is not written at all): compare the valid rows
+    slots, _ = orc.block_layout(grid, tile, pad3d)
+    valid = torch.from_numpy(slots >= 0)
+    r = ref.view(torch.int16).cpu()[:, :, valid]
+    assert torch.equal(r, got.view(torch.int16).cpu()[:, :, valid])
+    assert torch.equal(r, got2.view(torch.int16).cpu()[:, :, valid])
+
+
 @pytest.mark.parametrize("pad3d", [False, True])
 def test_attention_96_token_blocks_d128(pad3d):
     """Blocks of 96 tokens (three 32-token sub-blocks: the kernel streams the
