@@ -325,13 +325,13 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     # Q and K are reordered and pooled in one pass each; V is reordered straight
-    # into the attention workspace's V^T
-    stage_names = ["permute_pool_qk_stage_v", "mask", "attention", "permute_out"]
+    # into the attention workspace's V^T; attention writes O in natural order
+    stage_names = ["permute_pool_qk_stage_v", "mask", "attention_natural_out"]
 
     stripe = stripe_params(cfg.heads, seed=args.seed) if args.stripe else None
 
     def step(record=None):
-        marks = [ev() for _ in range(5)] if record is not None else None
+        marks = [ev() for _ in range(4)] if record is not None else None
         if marks: marks[0].record(stream)
         bsa.permute_in(q, k, v)
         if marks: marks[1].record(stream)
@@ -342,11 +342,9 @@ def main():
         else:
             bsa.build_stripe_mask(stripe, band_width=cfg.band)
         if marks: marks[2].record(stream)
-        bsa.attend()
-        if marks: marks[3].record(stream)
-        bsa.permute_out()
+        bsa.attend(natural_out=True)
         if marks:
-            marks[4].record(stream)
+            marks[3].record(stream)
             record.append(marks)
 
     for _ in range(args.warmup):
@@ -364,7 +362,7 @@ def main():
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     stage_ms = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in recs]))
                 for i, n in enumerate(stage_names)}
-    step_ms = float(np.mean([r[0].elapsed_time(r[4]) for r in recs]))
+    step_ms = float(np.mean([r[0].elapsed_time(r[3]) for r in recs]))
     print(f"[bench] timed {args.steps} steps: {wall_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     rp = bsa.row_ptr.cpu().numpy().astype(np.int64)
@@ -375,7 +373,7 @@ def main():
     counts = np.diff(rp).reshape(cfg.batch * cfg.heads, cfg.nb)
     sparsity_per_head = 1 - counts.sum(1) / cfg.nb ** 2
 
-    attn_ms = stage_ms["attention"]
+    attn_ms = stage_ms["attention_natural_out"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
 
     dense = None
@@ -383,13 +381,13 @@ def main():
         # same kernel with every block kept, same inputs (permute_in left the block means)
         m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
                           bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
-        bsa.attend()
+        bsa.attend(natural_out=True)
         torch.cuda.synchronize()
         reps = max(2, min(5, args.steps))
         d_ev = [(ev(), ev()) for _ in range(reps)]
         for a, b in d_ev:
             a.record(stream)
-            bsa.attend()
+            bsa.attend(natural_out=True)
             b.record(stream)
         torch.cuda.synchronize()
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in d_ev]))
@@ -414,8 +412,7 @@ def main():
             m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
                               bsa.col_idx, bsa.mask_ws,
                               top_p=np.full(cfg.heads, p_k, np.float32), band_width=cfg.band)
-            bsa.attend()
-            bsa.permute_out()
+            bsa.attend(natural_out=True)
             b.record(stream)
             torch.cuda.synchronize()
             s_ms.append(a.elapsed_time(b))
@@ -482,8 +479,9 @@ def main():
         "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
         "dense": dense,
         "roofline": {
-            "kernel": "svsa_block_sparse_attn on V staged by svsa_attn_stage_v (union_kernel + "
-                      "queue_kernel + attn_kernel; attn_kernel is >99% of it)",
+            "kernel": "svsa_block_sparse_attn_ex (natural-order output) on V staged by "
+                      "svsa_attn_stage_v (union_kernel + queue_kernel + attn_kernel; attn_kernel "
+                      "is >99% of it)",
             "bound": "mfma",
             "achieved": attn_tflops,
             "peak": BF16_PEAK_TFLOPS,

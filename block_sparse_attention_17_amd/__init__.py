@@ -15,7 +15,8 @@ from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, librar
                       svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
                       svsa_snr_top_p, svsa_status_string, svsa_stripe_mask,
                       svsa_stripe_mask_workspace_bytes, svsa_tile_permute, svsa_tile_permute_pool,
-                      svsa_attn_stage_v, svsa_version)
+                      svsa_attn_stage_v, svsa_block_sparse_attn_ex,
+                      SVSA_ATTN_OUT_NATURAL, svsa_version)
 from .pipeline import BlockSparseAttention, ClusteredAttention
 
 __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
@@ -23,7 +24,8 @@ __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "librar
            "svsa_block_mask_workspace_bytes", "svsa_block_sparse_attn", "svsa_pool",
            "svsa_snr_top_p", "svsa_status_string", "svsa_stripe_mask",
            "svsa_stripe_mask_workspace_bytes", "svsa_tile_permute", "svsa_tile_permute_pool",
-           "svsa_attn_stage_v", "svsa_version",
+           "svsa_attn_stage_v", "svsa_block_sparse_attn_ex", "SVSA_ATTN_OUT_NATURAL",
+           "svsa_version",
            "BlockSparseAttention", "ClusteredAttention", "svsa_cluster_attn",
            "svsa_cluster_attn_workspace_bytes", "svsa_cluster_capacity", "svsa_cluster_layout",
            "svsa_cluster_mask", "svsa_cluster_mask_workspace_bytes", "svsa_cluster_metric",

@@ -109,6 +109,8 @@ def _load():
         "svsa_block_sparse_attn": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp, vp,
                                                   vp, sz, vp]),
         "svsa_attn_stage_v": (ctypes.c_int, [vp, i32, i32, i32, gp, vp, sz, vp]),
+        "svsa_block_sparse_attn_ex": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, gp, flt, vp,
+                                                     vp, i32, vp, sz, vp]),
         "svsa_snr_top_p": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), i32, i32, flt, flt,
                                           fp]),
         "svsa_kmeans_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
@@ -147,7 +149,8 @@ _lib = _load()
 
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_tile_permute_pool",
             "svsa_block_mask_workspace_bytes", "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
-            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_attn_stage_v",
+            "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_block_sparse_attn_ex",
+            "svsa_attn_stage_v",
             "svsa_snr_top_p",
             "svsa_kmeans_workspace_bytes", "svsa_kmeans", "svsa_cluster_metric",
             "svsa_cluster_means_workspace_bytes", "svsa_cluster_means",
@@ -318,6 +321,24 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
         ctypes.byref(geom.c()), float(softmax_scale), _ptr(row_ptr, "row_ptr", (torch.int32,)),
         _ptr(col_idx, "col_idx", (torch.int32,)), _ptr(workspace, "workspace", (torch.uint8,)),
         workspace.numel(), _stream(stream)))
+    return out
+
+
+SVSA_ATTN_OUT_NATURAL = 1
+
+
+def svsa_block_sparse_attn_ex(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, workspace,
+                              flags=0, stream=None):
+    """svsa_block_sparse_attn with flags; SVSA_ATTN_OUT_NATURAL: out is bf16
+    [B, Hh, N, D] in natural order (the inverse reorder done by the kernel)."""
+    import torch
+    B, Hh, _, D = q.shape
+    bf = (torch.bfloat16,)
+    _check("svsa_block_sparse_attn_ex", _lib.svsa_block_sparse_attn_ex(
+        _ptr(q, "q", bf), _ptr(k, "k", bf), _ptr(v, "v", bf), _ptr(out, "out", bf), B, Hh, D,
+        ctypes.byref(geom.c()), float(softmax_scale), _ptr(row_ptr, "row_ptr", (torch.int32,)),
+        _ptr(col_idx, "col_idx", (torch.int32,)), int(flags),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
     return out
 
 

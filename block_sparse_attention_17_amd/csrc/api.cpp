@@ -422,10 +422,13 @@ size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* 
   return svsa::attn_ws_layout(batch * heads, g).total;
 }
 
-int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
-                           int32_t heads, int32_t head_dim, const svsa_geom* gin,
-                           float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
-                           void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int attn_impl(const void* q, const void* k, const void* v, void* out, int32_t batch,
+              int32_t heads, int32_t head_dim, const svsa_geom* gin, float softmax_scale,
+              const int32_t* row_ptr, const int32_t* col_idx, int32_t flags, void* workspace,
+              size_t ws_bytes, void* stream) {
+  if (flags & ~SVSA_ATTN_OUT_NATURAL) return SVSA_E_INVALID;
+  const bool natural = (flags & SVSA_ATTN_OUT_NATURAL) != 0;
   if (!(al(q, 16) && al(k, 16) && al(v, 16) && al(out, 16) && al(row_ptr, 4) && al(col_idx, 4) &&
         al(workspace, 256)))
     return SVSA_E_INVALID;
@@ -444,15 +447,34 @@ int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* ou
   const int64_t bh = (int64_t)batch * heads;
   if (bh * nbs * nbs >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
   const size_t tbytes = (size_t)bh * g.Npad * head_dim * 2;
-  if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
-      (v && overlaps(out, tbytes, v, tbytes)))
+  const size_t obytes = natural ? (size_t)bh * g.N * head_dim * 2 : tbytes;
+  if (overlaps(out, obytes, q, tbytes) || overlaps(out, obytes, k, tbytes) ||
+      (v && overlaps(out, obytes, v, tbytes)))
     return SVSA_E_INVALID;
   if (!workspace || ws_bytes < svsa_attn_workspace_bytes(batch, heads, gin))
     return SVSA_E_WORKSPACE;
-  if (overlaps(out, tbytes, workspace, ws_bytes)) return SVSA_E_INVALID;
+  if (overlaps(out, obytes, workspace, ws_bytes)) return SVSA_E_INVALID;
   return from_hip(svsa::launch_block_sparse_attn(q, k, v, out, (int32_t)bh, head_dim, g,
                                                  softmax_scale, row_ptr, col_idx, workspace,
-                                                 static_cast<hipStream_t>(stream)));
+                                                 natural, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out, int32_t batch,
+                           int32_t heads, int32_t head_dim, const svsa_geom* g,
+                           float softmax_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  return attn_impl(q, k, v, out, batch, heads, head_dim, g, softmax_scale, row_ptr, col_idx, 0,
+                   workspace, ws_bytes, stream);
+}
+
+int svsa_block_sparse_attn_ex(const void* q, const void* k, const void* v, void* out,
+                              int32_t batch, int32_t heads, int32_t head_dim, const svsa_geom* g,
+                              float softmax_scale, const int32_t* row_ptr,
+                              const int32_t* col_idx, int32_t flags, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return attn_impl(q, k, v, out, batch, heads, head_dim, g, softmax_scale, row_ptr, col_idx,
+                   flags, workspace, ws_bytes, stream);
 }
 
 int svsa_attn_stage_v(const void* v, int32_t batch, int32_t heads, int32_t head_dim,

@@ -428,6 +428,14 @@ struct WaveState {
   bool o_rescale;
 };
 
+// Where the epilogue writes O: tile order (natural == 0; the cluster path
+// always), or the natural (t, h, w) order of the fixed-block geometry g
+// (natural == 1), where padding slots have no row and are not written.
+struct OutMap {
+  Geom g;
+  int32_t natural;
+};
+
 struct Ctx {
   __amdgpu_buffer_rsrc_t k_rsrc;   // K of this (b, h)
   __amdgpu_buffer_rsrc_t vt_rsrc;  // V^T blocks of this (b, h)
@@ -820,7 +828,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const int32_t* __restrict__ count, int64_t item,
                                          int32_t groups, int32_t nb, int32_t nq,
                                          int32_t npad_q, int32_t npad_k, float c_log2,
-                                         const Ring<D, BK>& rg) {
+                                         const OutMap& om, const Ring<D, BK>& rg) {
   using C = Cfg<D, BK>;
   constexpr int kS = D / 16, kDT = D / 32;
 
@@ -908,6 +916,11 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   const float l_tot = st.l_run + swap_halves(st.l_run, cx.lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   __bf16* orow = oh + (int64_t)qrow * D;
+  if (om.natural) {  // natural (t, h, w) order; padding slots have no row there
+    const int32_t blk = qrow / om.g.Bk, slot = qrow - blk * om.g.Bk;
+    if (blk >= om.g.nb || slot >= block_valid(om.g, blk)) return;
+    orow = out + (bh * (int64_t)om.g.N + natural_row(om.g, blk, slot)) * D;
+  }
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -929,7 +942,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
             const int32_t* __restrict__ list, const int32_t* __restrict__ count,
             const int32_t* __restrict__ queue, int32_t* __restrict__ meta, int32_t groups,
-            int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2) {
+            int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2, OutMap om) {
   using C = Cfg<D, BK>;
   __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
       k2[C::kTileBytes], k3[C::kTileBytes];
@@ -958,7 +971,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
     if (item < 0) break;
     run_item<D, BK, PR>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
-                    rg);
+                        om, rg);
   }
 }
 
@@ -993,7 +1006,7 @@ template <int D, int BK, bool PR>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
                        int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
-                       int32_t npad_k, float c_log2, hipStream_t stream) {
+                       int32_t npad_k, float c_log2, const OutMap& om, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (v) {  // else V^T is already in the workspace (launch_attn_stage_v)
     hipLaunchKernelGGL((vt_kernel<D, PR ? 32 : BK>), dim3((uint32_t)((int64_t)bh * nb)),
@@ -1006,7 +1019,7 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<D, BK, PR>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
-                     count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2);
+                     count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2, om);
   return hipGetLastError();
 }
 
@@ -1041,7 +1054,8 @@ template <typename Sched>
 hipError_t run_attention(const void* q, const void* k, const void* v, void* out, int32_t bh,
                          int32_t head_dim, const AttnWs& w, const Sched& sc, int32_t npad_q,
                          int32_t npad_k, float scale, const int32_t* row_ptr,
-                         const int32_t* col_idx, void* ws, hipStream_t stream) {
+                         const int32_t* col_idx, void* ws, const OutMap& om,
+                         hipStream_t stream) {
   if (w.items > 0x7fffffff) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
@@ -1063,15 +1077,15 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   const float c_log2 = scale * 1.4426950408889634f;
   if (head_dim == 128 && w.sub == 64)
     return launch_attn<128, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, stream);
+                                w.nbs_q, npad_q, npad_k, c_log2, om, stream);
   if (head_dim == 64 && w.sub == 64)
     return launch_attn<64, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                               w.nbs_q, npad_q, npad_k, c_log2, stream);
+                               w.nbs_q, npad_q, npad_k, c_log2, om, stream);
   if (head_dim == 128 && w.sub == 32)
     return launch_attn<128, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, stream);
+                                w.nbs_q, npad_q, npad_k, c_log2, om, stream);
   return launch_attn<64, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
-                             npad_q, npad_k, c_log2, stream);
+                             npad_q, npad_k, c_log2, om, stream);
 }
 }  // namespace
 
@@ -1093,13 +1107,14 @@ AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t n
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    hipStream_t stream) {
+                                    bool natural_out, hipStream_t stream) {
   if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = attn_ws_layout(bh, g);
   const GeomSched sc{g, w.ratio, w.sub};
+  const OutMap om{g, natural_out ? 1 : 0};
   return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
-                       ws, stream);
+                       ws, om, stream);
 }
 
 hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
@@ -1133,8 +1148,9 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = cluster_attn_ws_layout(bh, sub, npad_q, npad_k);
   const TableSched sc{q_start, q_size, k_start, k_size, nq, nk, sub};
+  const OutMap om{};  // tile (cluster) order
   return run_attention(q, k, v, out, bh, head_dim, w, sc, (int32_t)npad_q, (int32_t)npad_k, scale,
-                       row_ptr, col_idx, ws, stream);
+                       row_ptr, col_idx, ws, om, stream);
 }
 
 }  // namespace svsa

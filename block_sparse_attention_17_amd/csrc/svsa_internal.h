@@ -132,7 +132,7 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    hipStream_t stream);
+                                    bool natural_out, hipStream_t stream);
 
 // Clustering (variable-size blocks).
 int64_t cluster_lcap(int32_t N, int32_t C, int32_t align);   // padded layout capacity

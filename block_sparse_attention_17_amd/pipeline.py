@@ -56,12 +56,18 @@ class BlockSparseAttention:
         B.svsa_stripe_mask(self.geom, self.batch, params, self.row_ptr, self.col_idx,
                            self.stripe_ws, band_width=band_width, stream=stream)
 
-    def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None):
+    def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None, natural_out=False):
+        """Attention over the CSR lists into ot (tile order), or straight into out
+        (natural order, natural_out=True: the kernel does the inverse reorder)."""
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
-        B.svsa_block_sparse_attn(self.qt, self.kt, None, self.ot, self.geom, scale,
-                                 self.row_ptr if row_ptr is None else row_ptr,
-                                 self.col_idx if col_idx is None else col_idx,
-                                 self.attn_ws, stream=stream)
+        B.svsa_block_sparse_attn_ex(self.qt, self.kt, None, self.out if natural_out else self.ot,
+                                    self.geom, scale,
+                                    self.row_ptr if row_ptr is None else row_ptr,
+                                    self.col_idx if col_idx is None else col_idx,
+                                    self.attn_ws,
+                                    flags=B.SVSA_ATTN_OUT_NATURAL if natural_out else 0,
+                                    stream=stream)
+        return self.out if natural_out else self.ot
 
     def permute_out(self, stream=None):
         B.svsa_tile_permute(self.ot, self.out, self.geom, inverse=True, stream=stream)
@@ -71,8 +77,7 @@ class BlockSparseAttention:
         """One pass of the whole path; returns the natural-order bf16 output."""
         self.permute_in(q, k, v, stream)
         self.build_mask(top_p, keep_frac, band_width, stream)
-        self.attend(stream=stream)
-        return self.permute_out(stream)
+        return self.attend(stream=stream, natural_out=True)
 
 
 class ClusteredAttention:

@@ -256,6 +256,24 @@ SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v,
                            const int32_t* row_ptr, const int32_t* col_idx,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* Flags of svsa_block_sparse_attn_ex. */
+enum { SVSA_ATTN_OUT_NATURAL = 1 };
+
+/*
+ * svsa_block_sparse_attn with flags.  flags = 0: the same call.
+ * SVSA_ATTN_OUT_NATURAL: out is [batch,heads,N,D] in natural (t,h,w) order,
+ * each valid query row written at its natural position (the inverse tile
+ * reorder of [PSA] Sec. 3.2 done by the attention kernel's stores), so the
+ * result equals svsa_tile_permute(inverse = 1) applied to the tile-order
+ * output, bitwise.  Other bits: SVSA_E_INVALID.  Everything else as above.
+ */
+SVSA_API int svsa_block_sparse_attn_ex(const void* q, const void* k, const void* v, void* out,
+                                       int32_t batch, int32_t heads, int32_t head_dim,
+                                       const svsa_geom* g, float softmax_scale,
+                                       const int32_t* row_ptr, const int32_t* col_idx,
+                                       int32_t flags, void* workspace, size_t ws_bytes,
+                                       void* stream);
+
 /*
  * Stage 1 for V fused with the layout change the attention kernel needs:
  * natural-order V ([batch,heads,N,D], bf16) is written into `workspace` as

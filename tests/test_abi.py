@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -94,6 +94,20 @@ def test_attn_stage_v_argument_errors(mod):
     assert f(FAKE, 1, 1, 64, g, ws, need - 1, None) == E_WS
     assert f(FAKE, 1, 1, 64, g, ctypes.c_void_p(0x4000080), need, None) == E_INV  # not 256-aligned
     assert f(ws, 1, 1, 64, g, ws, need, None) == E_INV                            # v inside ws
+
+
+def test_attn_ex_rejects_unknown_flags(mod):
+    lib = mod.library()
+    g = _g(mod, 4, 8, 8, 2, 4, 4)
+    ws = ctypes.c_void_p(0x4000000)
+    need = lib.svsa_attn_workspace_bytes(1, 1, g)
+    Q, K, O = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
+    R, C = ctypes.c_void_p(0x5000000), ctypes.c_void_p(0x6000000)
+    f = lib.svsa_block_sparse_attn_ex
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 2, ws, need, None) == -1
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, -1, ws, need, None) == -1
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 1, ws, need - 1, None) == -3
+    assert f(Q, K, None, ws, 1, 1, 64, g, 0.125, R, C, 1, ws, need, None) == -1   # out in ws
 
 
 def test_pad3d_geometry_counts(mod):

@@ -428,7 +428,9 @@ def test_staged_v_equals_tiled_v(grid, tile, D, pad3d):
     """svsa_attn_stage_v from natural-order V, then svsa_block_sparse_attn with
     v = NULL, gives the output of svsa_block_sparse_attn on svsa_tile_permute's
     tiled V bitwise (64- and 32-token sub-blocks, partial tiles, both layouts,
-    random kept sets); a second call on the same workspace gives it again."""
+    random kept sets); a second call on the same workspace gives it again, and
+    the natural-order output (SVSA_ATTN_OUT_NATURAL) equals the inverse reorder
+    of the tile-order one."""
     import block_sparse_attention_17_amd as m
     G = m.Geometry(*grid, *tile, pad3d=pad3d)
     H, nb = 2, G.nb
@@ -455,7 +457,14 @@ def test_staged_v_equals_tiled_v(grid, tile, D, pad3d):
     m.svsa_attn_stage_v(nat[2], ws2, G)
     m.svsa_block_sparse_attn(tiled[0], tiled[1], None, got, G, 1 / np.sqrt(D), rp_d, ci_d, ws2)
     m.svsa_block_sparse_attn(tiled[0], tiled[1], None, got2, G, 1 / np.sqrt(D), rp_d, ci_d, ws2)
+    nat_out = torch.full((1, H, G.N, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    m.svsa_block_sparse_attn_ex(tiled[0], tiled[1], None, nat_out, G, 1 / np.sqrt(D), rp_d, ci_d,
+                                ws2, flags=m.SVSA_ATTN_OUT_NATURAL)
+    ref_nat = torch.empty_like(nat_out)
+    m.svsa_tile_permute(ref, ref_nat, G, inverse=True)
     torch.cuda.synchronize()
+    # natural-order output from the kernel = inverse reorder of the tile-order output
+    assert torch.equal(ref_nat.view(torch.int16).cpu(), nat_out.view(torch.int16).cpu())
     # padding slots of the output are unspecified (the packed layout's tail past
     # the last sub-block is not written at all): compare the valid rows
     slots, _ = orc.block_layout(grid, tile, pad3d)
