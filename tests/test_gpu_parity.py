@@ -43,6 +43,23 @@ def test_inverse_permute_round_trip(name):
     assert torch.equal(back.view(torch.int16), run.q_dev.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["wan720", "wan720_psa3d"])
+def test_natural_output_full_size(name):
+    """Full size, in the launch configuration bench.py times (V staged into the
+    attention workspace, top-p 0.9): the natural-order output of
+    svsa_block_sparse_attn_ex equals the inverse reorder of the tile-order
+    output bitwise on every token."""
+    import block_sparse_attention_17_amd as m
+    run = gc.gpu_run(name)
+    run.mask(top_p=np.full(run.cfg.heads, 0.9, np.float32), band=run.cfg.band)
+    tile_out = run.bsa.attend()
+    nat = run.bsa.attend(natural_out=True)
+    back = torch.empty_like(nat)
+    m.svsa_tile_permute(tile_out, back, run.geom, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), nat.view(torch.int16))
+
+
 @pytest.mark.parametrize("grid,tile,D", [((3, 5, 6), (2, 2, 4), 64), ((5, 7, 3), (4, 4, 4), 128),
                                          ((21, 30, 52), (4, 4, 4), 64), ((1, 1, 1), (2, 2, 2), 64),
                                          ((4, 6, 9), (2, 4, 4), 64), ((3, 1, 5), (2, 4, 4), 128)])
