@@ -208,6 +208,44 @@ def _ptr(t, name, dtypes=None, device=True):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _tensor(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+
+
+def _shape(t, name, shape):
+    """Refuse a tensor whose shape is not exactly `shape` (the C ABI sees no sizes)."""
+    if t is None:
+        return
+    _tensor(t, name)
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _at_least(t, name, n):
+    """Refuse a 1-D index array with fewer than n entries."""
+    if t is None:
+        return
+    _tensor(t, name)
+    if t.dim() != 1 or t.numel() < int(n):
+        raise ValueError(f"{name} must be 1-D with at least {int(n)} entries, "
+                         f"got shape {tuple(t.shape)}")
+
+
+def _ndim(t, name, n):
+    _tensor(t, name)
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _same_device(**tensors):
+    """Every given device tensor must live on one device."""
+    devs = {n: t.device for n, t in tensors.items() if t is not None and hasattr(t, "device")}
+    if len(set(devs.values())) > 1:
+        raise ValueError(f"tensors on different devices: {devs}")
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.bfloat16:
@@ -220,7 +258,12 @@ def _dtype_code(t):
 def svsa_tile_permute(src, dst, geom, inverse=False, stream=None):
     """dst <- tile-ordered src (inverse=False) or natural-ordered src (inverse=True)."""
     import torch
+    _ndim(src, "src", 4)
     B, Hh, _, D = src.shape
+    n_src, n_dst = (geom.N_pad, geom.N) if inverse else (geom.N, geom.N_pad)
+    _shape(src, "src", (B, Hh, n_src, D))
+    _shape(dst, "dst", (B, Hh, n_dst, D))
+    _same_device(src=src, dst=dst)
     _check("svsa_tile_permute", _lib.svsa_tile_permute(
         _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
         _dtype_code(src), B, Hh, D, ctypes.byref(geom.c()), int(bool(inverse)), _stream(stream)))
@@ -230,7 +273,11 @@ def svsa_tile_permute(src, dst, geom, inverse=False, stream=None):
 def svsa_pool(x_tiled, out, geom, stream=None):
     """out (float64 [B, Hh, nb, D]) <- per-block means of the valid rows of x_tiled."""
     import torch
+    _ndim(x_tiled, "x_tiled", 4)
     B, Hh, _, D = x_tiled.shape
+    _shape(x_tiled, "x_tiled", (B, Hh, geom.N_pad, D))
+    _shape(out, "out", (B, Hh, geom.nb, D))
+    _same_device(x_tiled=x_tiled, out=out)
     _check("svsa_pool", _lib.svsa_pool(
         _ptr(x_tiled, "x_tiled", (torch.bfloat16, torch.float32)), _dtype_code(x_tiled),
         _ptr(out, "out", (torch.float64,)), B, Hh, D, ctypes.byref(geom.c()), _stream(stream)))
@@ -240,7 +287,12 @@ def svsa_pool(x_tiled, out, geom, stream=None):
 def svsa_tile_permute_pool(src, dst, means, geom, stream=None):
     """dst <- tile-ordered src and means (float64 [B, Hh, nb, D]) <- its block means, one pass."""
     import torch
+    _ndim(src, "src", 4)
     B, Hh, _, D = src.shape
+    _shape(src, "src", (B, Hh, geom.N, D))
+    _shape(dst, "dst", (B, Hh, geom.N_pad, D))
+    _shape(means, "means", (B, Hh, geom.nb, D))
+    _same_device(src=src, dst=dst, means=means)
     _check("svsa_tile_permute_pool", _lib.svsa_tile_permute_pool(
         _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
         _ptr(means, "means", (torch.float64,)), _dtype_code(src), B, Hh, D,
@@ -273,7 +325,12 @@ def svsa_block_mask(qbar, kbar, softmax_scale, row_ptr, col_idx, workspace, top_
                     keep_frac=None, band_width=1, stream=None):
     """CSR (row_ptr, col_idx) of kept key blocks from float64 block summaries."""
     import torch
+    _ndim(qbar, "qbar", 4)
     B, Hh, nb, D = qbar.shape
+    _shape(kbar, "kbar", (B, Hh, nb, D))
+    _at_least(row_ptr, "row_ptr", B * Hh * nb + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(qbar=qbar, kbar=kbar, row_ptr=row_ptr, col_idx=col_idx, workspace=workspace)
     tp_arr, tp = _host_f32(top_p, Hh, "top_p")
     kf_arr, kf = _host_f32(keep_frac, Hh, "keep_frac")
     _check("svsa_block_mask", _lib.svsa_block_mask(
@@ -295,6 +352,9 @@ def svsa_stripe_mask(geom, batch, params, row_ptr, col_idx, workspace, band_widt
     import torch
     arr = np.ascontiguousarray(np.asarray(params, dtype=np.int32).reshape(-1, 6))
     heads = arr.shape[0]
+    _at_least(row_ptr, "row_ptr", int(batch) * heads * geom.nb + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(row_ptr=row_ptr, col_idx=col_idx, workspace=workspace)
     _check("svsa_stripe_mask", _lib.svsa_stripe_mask(
         ctypes.byref(geom.c()), int(batch), int(heads),
         arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(band_width),
@@ -314,6 +374,7 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
     """out (bf16, tile order) <- block-sparse attention of q, k, v over the CSR lists.
     v=None: V as staged into `workspace` by svsa_attn_stage_v."""
     import torch
+    _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace, natural=False)
     B, Hh, _, D = q.shape
     bf = (torch.bfloat16,)
     _check("svsa_block_sparse_attn", _lib.svsa_block_sparse_attn(
@@ -327,11 +388,27 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
 SVSA_ATTN_OUT_NATURAL = 1
 
 
+def _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace, natural):
+    """q, k, v (if given) tiled [B, Hh, N_pad, D]; out tiled, or natural
+    [B, Hh, N, D] with SVSA_ATTN_OUT_NATURAL; row_ptr >= B*Hh*nb + 1 entries."""
+    _ndim(q, "q", 4)
+    B, Hh, _, D = q.shape
+    _shape(q, "q", (B, Hh, geom.N_pad, D))
+    _shape(k, "k", (B, Hh, geom.N_pad, D))
+    _shape(v, "v", (B, Hh, geom.N_pad, D))
+    _shape(out, "out", (B, Hh, geom.N if natural else geom.N_pad, D))
+    _at_least(row_ptr, "row_ptr", B * Hh * geom.nb + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(q=q, k=k, v=v, out=out, row_ptr=row_ptr, col_idx=col_idx, workspace=workspace)
+
+
 def svsa_block_sparse_attn_ex(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, workspace,
                               flags=0, stream=None):
     """svsa_block_sparse_attn with flags; SVSA_ATTN_OUT_NATURAL: out is bf16
     [B, Hh, N, D] in natural order (the inverse reorder done by the kernel)."""
     import torch
+    _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace,
+                 natural=bool(int(flags) & SVSA_ATTN_OUT_NATURAL))
     B, Hh, _, D = q.shape
     bf = (torch.bfloat16,)
     _check("svsa_block_sparse_attn_ex", _lib.svsa_block_sparse_attn_ex(
@@ -345,7 +422,10 @@ def svsa_block_sparse_attn_ex(q, k, v, out, geom, softmax_scale, row_ptr, col_id
 def svsa_attn_stage_v(v, workspace, geom, stream=None):
     """Natural-order V (bf16 [B, Hh, N, D]) -> the attention workspace's V^T, tile order."""
     import torch
+    _ndim(v, "v", 4)
     B, Hh, _, D = v.shape
+    _shape(v, "v", (B, Hh, geom.N, D))
+    _same_device(v=v, workspace=workspace)
     _check("svsa_attn_stage_v", _lib.svsa_attn_stage_v(
         _ptr(v, "v", (torch.bfloat16,)), B, Hh, D, ctypes.byref(geom.c()),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
@@ -363,8 +443,16 @@ def svsa_kmeans(x, centroids, labels, sizes, workspace, iters, metric=None, stre
     """Lloyd iterations under the quadratic form `metric` (None: identity);
     centroids float64 [B, Hh, C, D] are updated in place."""
     import torch
+    _ndim(x, "x", 4)
     B_, Hh, N, D = x.shape
+    _ndim(centroids, "centroids", 4)
     C = centroids.shape[2]
+    _shape(centroids, "centroids", (B_, Hh, C, D))
+    _shape(metric, "metric", (B_, Hh, D, D))
+    _shape(labels, "labels", (B_, Hh, N))
+    _shape(sizes, "sizes", (B_, Hh, C))
+    _same_device(x=x, metric=metric, centroids=centroids, labels=labels, sizes=sizes,
+                 workspace=workspace)
     _check("svsa_kmeans", _lib.svsa_kmeans(
         _ptr(x, "x", (torch.bfloat16,)), B_, Hh, N, D,
         _ptr(metric, "metric", (torch.float64,)), _ptr(centroids, "centroids", (torch.float64,)),
@@ -381,8 +469,14 @@ def svsa_cluster_means_workspace_bytes(batch, heads, n, clusters):
 def svsa_cluster_means(x, labels, centroids, sizes, workspace, stream=None):
     """centroids (float64 [B, Hh, C, D]) <- means of the tokens of each label."""
     import torch
+    _ndim(x, "x", 4)
     B_, Hh, N, D = x.shape
+    _ndim(centroids, "centroids", 4)
     C = centroids.shape[2]
+    _shape(labels, "labels", (B_, Hh, N))
+    _shape(centroids, "centroids", (B_, Hh, C, D))
+    _shape(sizes, "sizes", (B_, Hh, C))
+    _same_device(x=x, labels=labels, centroids=centroids, sizes=sizes, workspace=workspace)
     _check("svsa_cluster_means", _lib.svsa_cluster_means(
         _ptr(x, "x", (torch.bfloat16,)), _ptr(labels, "labels", (torch.int32,)), B_, Hh, N, D, C,
         _ptr(centroids, "centroids", (torch.float64,)), _ptr(sizes, "sizes", (torch.int32,)),
@@ -392,7 +486,11 @@ def svsa_cluster_means(x, labels, centroids, sizes, workspace, stream=None):
 
 def svsa_cluster_metric(centroids, sizes, metric, stream=None):
     import torch
+    _ndim(centroids, "centroids", 4)
     B_, Hh, C, D = centroids.shape
+    _shape(sizes, "sizes", (B_, Hh, C))
+    _shape(metric, "metric", (B_, Hh, D, D))
+    _same_device(centroids=centroids, sizes=sizes, metric=metric)
     _check("svsa_cluster_metric", _lib.svsa_cluster_metric(
         _ptr(centroids, "centroids", (torch.float64,)), _ptr(sizes, "sizes", (torch.int32,)),
         B_, Hh, C, D, _ptr(metric, "metric", (torch.float64,)), _stream(stream)))
@@ -410,7 +508,14 @@ def svsa_cluster_layout_workspace_bytes(batch, heads, n, clusters):
 def svsa_cluster_layout(labels, clusters, align, start, sizes, slot, token, workspace,
                         stream=None):
     import torch
+    _ndim(labels, "labels", 3)
     B_, Hh, N = labels.shape
+    _shape(start, "start", (B_, Hh, int(clusters) + 1))
+    _shape(sizes, "sizes", (B_, Hh, int(clusters)))
+    _shape(slot, "slot", (B_, Hh, N))
+    _shape(token, "token", (B_, Hh, svsa_cluster_capacity(N, clusters, align)))
+    _same_device(labels=labels, start=start, sizes=sizes, slot=slot, token=token,
+                 workspace=workspace)
     i32 = (torch.int32,)
     _check("svsa_cluster_layout", _lib.svsa_cluster_layout(
         _ptr(labels, "labels", i32), B_, Hh, N, int(clusters), int(align),
@@ -422,7 +527,15 @@ def svsa_cluster_layout(labels, clusters, align, start, sizes, slot, token, work
 
 def svsa_cluster_permute(src, dst, n, clusters, align, map_, start, inverse=False, stream=None):
     import torch
+    _ndim(src, "src", 4)
     B_, Hh, _, D = src.shape
+    cap = svsa_cluster_capacity(n, clusters, align)
+    n_src, n_dst = (cap, n) if inverse else (n, cap)
+    _shape(src, "src", (B_, Hh, n_src, D))
+    _shape(dst, "dst", (B_, Hh, n_dst, D))
+    _shape(map_, "map", (B_, Hh, n if inverse else cap))
+    _shape(start, "start", (B_, Hh, int(clusters) + 1))
+    _same_device(src=src, dst=dst, map=map_, start=start)
     _check("svsa_cluster_permute", _lib.svsa_cluster_permute(
         _ptr(src, "src", (torch.bfloat16, torch.float32)), _ptr(dst, "dst", (src.dtype,)),
         _dtype_code(src), B_, Hh, int(n), D, int(clusters), int(align),
@@ -438,8 +551,16 @@ def svsa_cluster_mask_workspace_bytes(batch, heads, nq, nk):
 def svsa_cluster_mask(qbar, kbar, ksizes, softmax_scale, row_ptr, col_idx, workspace,
                       top_p=None, keep_frac=None, stream=None):
     import torch
+    _ndim(qbar, "qbar", 4)
     B_, Hh, nq, D = qbar.shape
+    _ndim(kbar, "kbar", 4)
     nk = kbar.shape[2]
+    _shape(kbar, "kbar", (B_, Hh, nk, D))
+    _shape(ksizes, "ksizes", (B_, Hh, nk))
+    _at_least(row_ptr, "row_ptr", B_ * Hh * nq + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(qbar=qbar, kbar=kbar, ksizes=ksizes, row_ptr=row_ptr, col_idx=col_idx,
+                 workspace=workspace)
     tp_arr, tp = _host_f32(top_p, Hh, "top_p")
     kf_arr, kf = _host_f32(keep_frac, Hh, "keep_frac")
     _check("svsa_cluster_mask", _lib.svsa_cluster_mask(
@@ -460,9 +581,24 @@ def svsa_cluster_attn(q, k, v, out, n_q, q_start, q_size, n_k, k_start, k_size, 
                       softmax_scale, row_ptr, col_idx, workspace, stream=None):
     """out (bf16, query cluster layout) <- attention over the kept key clusters."""
     import torch
+    _ndim(q, "q", 4)
     B_, Hh, _, D = q.shape
     bf, i32 = (torch.bfloat16,), (torch.int32,)
     nq, nk = q_size.shape[-1], k_size.shape[-1]
+    cap_q = svsa_cluster_capacity(n_q, nq, align)
+    cap_k = svsa_cluster_capacity(n_k, nk, align)
+    _shape(q, "q", (B_, Hh, cap_q, D))
+    _shape(k, "k", (B_, Hh, cap_k, D))
+    _shape(v, "v", (B_, Hh, cap_k, D))
+    _shape(out, "out", (B_, Hh, cap_q, D))
+    _shape(q_start, "q_start", (B_, Hh, nq + 1))
+    _shape(q_size, "q_size", (B_, Hh, nq))
+    _shape(k_start, "k_start", (B_, Hh, nk + 1))
+    _shape(k_size, "k_size", (B_, Hh, nk))
+    _at_least(row_ptr, "row_ptr", B_ * Hh * nq + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(q=q, k=k, v=v, out=out, q_start=q_start, q_size=q_size, k_start=k_start,
+                 k_size=k_size, row_ptr=row_ptr, col_idx=col_idx, workspace=workspace)
     _check("svsa_cluster_attn", _lib.svsa_cluster_attn(
         _ptr(q, "q", bf), _ptr(k, "k", bf), _ptr(v, "v", bf), _ptr(out, "out", bf), B_, Hh, D,
         int(n_q), int(nq), _ptr(q_start, "q_start", i32), _ptr(q_size, "q_size", i32), int(n_k),
@@ -480,7 +616,14 @@ def svsa_tail_merge(labels, nq, nk, block, row_ptr, col_idx, row_ptr_out, col_id
                     workspace, rounds=2, stream=None):
     """Query labels (in place) and the cluster mask after tail merging."""
     import torch
+    _ndim(labels, "labels", 3)
     B_, Hh, N = labels.shape
+    _at_least(row_ptr, "row_ptr", B_ * Hh * int(nq) + 1)
+    _at_least(row_ptr_out, "row_ptr_out", B_ * Hh * int(nq) + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _ndim(col_idx_out, "col_idx_out", 1)
+    _same_device(labels=labels, row_ptr=row_ptr, col_idx=col_idx, row_ptr_out=row_ptr_out,
+                 col_idx_out=col_idx_out, workspace=workspace)
     i32 = (torch.int32,)
     _check("svsa_tail_merge", _lib.svsa_tail_merge(
         _ptr(labels, "labels", i32), B_, Hh, N, int(nq), int(nk), int(block), int(rounds),

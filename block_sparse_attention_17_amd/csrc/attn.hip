@@ -854,8 +854,8 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   cx.n_list = count[item];
   cx.n_u = PR ? (cx.n_list + 1) / 2 : cx.n_list;            // key tiles streamed
   // intervals 0 .. 2 n_u + 1 carry work; the count is rounded up to whole
-  // rounds of 8 (the extra intervals do nothing); an empty union runs none
-  cx.T = cx.n_u > 0 ? (2 * cx.n_u + 2 + 7) & ~7 : 0;
+  // rounds of 8 (the extra intervals do nothing)
+  cx.T = (2 * cx.n_u + 2 + 7) & ~7;
   cx.nb = nb;
   cx.c_log2 = c_log2;
   cx.lst = list + item * nb;
@@ -909,8 +909,14 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   wg_barrier();
 
-  if (grp == 0) run_group<D, BK, PR, 0>(st, cx, rg);
-  else run_group<D, BK, PR, 1>(st, cx, rg);
+  // An item whose union list is empty (every row of its group is empty, or
+  // the group holds padding only) streams nothing: its output rows are zeros.
+  // The count is uniform over the workgroup, so every wave skips the loop and
+  // its barriers together; the loop's list reads need n_list >= 1.
+  if (cx.n_u > 0) {
+    if (grp == 0) run_group<D, BK, PR, 0>(st, cx, rg);
+    else run_group<D, BK, PR, 1>(st, cx, rg);
+  }
 
   if (!cx.has_rows) return;
   const float l_tot = st.l_run + swap_halves(st.l_run, cx.lane);
@@ -975,25 +981,19 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 }
 
-// Workgroups of the persistent attention kernel: every CU slot of the device
-// (CU count x resident workgroups per CU), at most one per item.
+// Workgroups of the persistent attention kernel: every CU slot of the current
+// device (CU count x resident workgroups per CU), at most one per item.  Both
+// figures are queried on every call: the library keeps no state between calls.
 template <int D, int BK, bool PR>
 hipError_t attn_grid(int64_t items, uint32_t* grid) {
-  static int cached[64] = {0};  // per device: CU count x resident workgroups per CU
-  int dev = 0;
+  int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int slots = (dev >= 0 && dev < 64) ? cached[dev] : 0;
-  if (slots <= 0) {
-    int cus = 0, per_cu = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK, PR>, kThreads, 0);
-    if (e != hipSuccess) return e;
-    slots = cus * (per_cu > 0 ? per_cu : 1);
-    if (slots <= 0) slots = 1;
-    if (dev >= 0 && dev < 64) cached[dev] = slots;
-  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK, PR>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  int64_t slots = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   *grid = (uint32_t)(items < slots ? items : slots);
   return hipSuccess;
 }

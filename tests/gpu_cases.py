@@ -124,7 +124,23 @@ class OracleRun:
         log(f"{self.cfg.name}: oracle mask")
         return orc.block_mask(self.S, band, top_p=top_p, keep_frac=keep_frac)
 
-    def attention_blocks(self, rp, ci, rows):
+    def attention_blocks(self, rp, ci, rows, threads=None):
+        """Oracle output rows of the listed query blocks.  threads > 1 spreads
+        the blocks over a thread pool (one BLAS thread each); every block is
+        still one call of the oracle's attention_rows."""
+        if threads is None:
+            threads = _oracle_threads() if len(rows) > 64 else 1
+        if threads > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            from threadpoolctl import threadpool_limits
+            rows = list(rows)
+            parts = [rows[k::threads] for k in range(threads)]
+            with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+                done = list(ex.map(lambda part: self.attention_blocks(rp, ci, part, 1), parts))
+            res = {}
+            for d in done:
+                res.update(d)
+            return {r: res[r] for r in rows}
         cfg = self.cfg
         scale = 1 / sqrt(cfg.head_dim)
         res = {}
@@ -134,6 +150,15 @@ class OracleRun:
             res[(b, h, i)] = orc.attention_rows(self.qt_bits, self.kt_bits, self.vt_bits, b, h, i,
                                                 cols, cfg.N, cfg.Bk, scale, self.counts)
         return res
+
+
+def _oracle_threads():
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 @lru_cache(maxsize=8)

@@ -316,3 +316,62 @@ def test_misaligned_pointers_are_refused(mod):
                                       0.125, FAKE, FAKE2, ws_off, ws, None) == -1
     assert lib.svsa_block_sparse_attn(off8, P[1], P[2], P[3], 1, 2, 64, ctypes.byref(G.c()),
                                       0.125, FAKE, FAKE2, FAKE, ws, None) == -1
+
+
+def test_binding_checks_shapes_against_the_geometry(mod):
+    """The C ABI sees pointers only, so the binding refuses tensors whose shape
+    does not match the geometry, each other or the row count (before any
+    device check: these are host tensors)."""
+    import torch
+    g = mod.Geometry(3, 5, 6, 2, 2, 4)            # N 90, Bk 16, nb 6, N_pad 96
+    bf = dict(dtype=torch.bfloat16)
+    nat = torch.zeros((1, 2, g.N, 64), **bf)
+    til = torch.zeros((1, 2, g.N_pad + 16, 64), **bf)          # one block too many
+    means = torch.zeros((1, 2, g.nb, 64), dtype=torch.float64)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_tile_permute(nat, til, g)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_tile_permute(til, nat, g, inverse=True)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_tile_permute_pool(nat, til, means, g)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_pool(torch.zeros((1, 2, g.N_pad, 64), **bf),
+                      torch.zeros((1, 2, g.nb + 1, 64), dtype=torch.float64), g)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_attn_stage_v(torch.zeros((1, 2, g.N + 1, 64), **bf),
+                              torch.zeros(16, dtype=torch.uint8), g)
+    # attention: k must match q; out natural vs tiled; row_ptr entries
+    q = torch.zeros((1, 2, g.N_pad, 64), **bf)
+    rp = torch.zeros(2 * g.nb + 1, dtype=torch.int32)
+    ci = torch.zeros(4, dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_block_sparse_attn(q, torch.zeros((1, 3, g.N_pad, 64), **bf), None, q, g, 0.1,
+                                   rp, ci, ws)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_block_sparse_attn_ex(q, q, None, q, g, 0.1, rp, ci, ws,
+                                      flags=mod.SVSA_ATTN_OUT_NATURAL)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_block_sparse_attn_ex(q, q, None, nat, g, 0.1, rp, ci, ws)
+    with pytest.raises(ValueError, match="entries"):
+        mod.svsa_block_sparse_attn(q, q, None, q, g, 0.1, rp[:-1], ci, ws)
+    with pytest.raises(ValueError, match="entries"):
+        mod.svsa_block_mask(means, means, 0.1, rp[:5], ci, ws, top_p=0.9)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_block_mask(means, means[:, :1], 0.1, rp, ci, ws, top_p=0.9)
+    # clusters
+    lab = torch.zeros((1, 2, g.N), dtype=torch.int32)
+    cents = torch.zeros((1, 2, 5, 64), dtype=torch.float64)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_cluster_means(nat, lab, cents, torch.zeros((1, 2, 4), dtype=torch.int32), ws)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_kmeans(nat, cents, lab[:, :, 1:], torch.zeros((1, 2, 5), dtype=torch.int32),
+                        ws, 1)
+    cap = mod.svsa_cluster_capacity(g.N, 5, 32)
+    with pytest.raises(ValueError, match="shape"):
+        mod.svsa_cluster_permute(nat, torch.zeros((1, 2, cap - 32, 64), **bf), g.N, 5, 32,
+                                 torch.zeros((1, 2, cap), dtype=torch.int32),
+                                 torch.zeros((1, 2, 6), dtype=torch.int32))
+    # tensors must be torch tensors
+    with pytest.raises(TypeError):
+        mod.svsa_tile_permute([1, 2], til, g)

@@ -96,8 +96,24 @@ def test_kmeans_one_iteration_matches_oracle(name, C, use_metric):
                 c_o, s_o, _ = orc.kmeans(xw[b, h], cents0[b, h], 1, Gh)
                 assert np.array_equal(sizes[b, h], s_o)
                 np.testing.assert_allclose(cents[b, h], c_o, rtol=1e-13, atol=1e-15)
+            # every head (also one with tolerated near-tie labels): the update
+            # step on the GPU's own labels
+            _check_update(x[b:b + 1, h:h + 1], labels[b, h], cents0[b, h], cents[b, h],
+                          sizes[b, h])
     gc.log(f"{name}: {tolerated} near-tie labels of {B * H * N}")
     assert tolerated <= max(2, B * H * N // 1000)
+
+
+def _check_update(x_bits, labels, cents0, cents, sizes):
+    """The means step of one head against the oracle on the GPU's labels:
+    sizes are the label counts, a non-empty cluster's centroid is the float64
+    mean of its members, an empty cluster keeps its initial centroid."""
+    C = cents0.shape[0]
+    m_o, s_o = orc.cluster_means(x_bits, labels[None, None], C)
+    assert np.array_equal(sizes, s_o[0, 0])
+    ne = s_o[0, 0] > 0
+    np.testing.assert_allclose(cents[ne], m_o[0, 0][ne], rtol=1e-13, atol=1e-15)
+    assert np.array_equal(cents[~ne], cents0[~ne])
 
 
 def _blobs(heads, n, C, D, seed):
@@ -290,11 +306,13 @@ class _ClusterCase:
         rph = rp.cpu().numpy().astype(np.int64)
         return rph, ci[: int(rph[-1])].cpu().numpy()
 
-    def gpu_attention(self, rp, ci):
+    def gpu_attention(self, rp, ci, fill=None):
         m = _m()
         ws = torch.empty(m.svsa_cluster_attn_workspace_bytes(self.B, self.H, self.N, self.nq,
                                                              self.N, self.nk, self.align),
                          dtype=torch.uint8, device="cuda")
+        if fill is not None:       # stale workspace contents must not matter
+            ws.fill_(fill)
         gc.log(f"{self.cfg.name}: cluster attention on {int(rp[-1])} kept cluster pairs")
         m.svsa_cluster_attn(self.qp, self.kp, self.vp, self.op, self.N, self.q_start, self.qs,
                             self.N, self.k_start, self.ks, self.align, 1 / np.sqrt(self.D),
@@ -368,18 +386,34 @@ def test_cluster_attention_matches_oracle(name, nq, nk, align):
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
-def test_cluster_attention_empty_rows_give_zeros():
-    c = _ClusterCase("small", 24, 40, 64)
+@pytest.mark.parametrize("align", [64, 32])
+def test_cluster_attention_empty_rows_give_zeros(align):
+    """Empty rows give zeros and the other rows match the oracle, with every
+    workspace byte 0xFF before the call (the padded tail of each head's query
+    layout is a group with an empty union list)."""
+    c = _ClusterCase("small", 24, 40, align)
     nq, H = c.nq, c.H
     cols = [[] if (i % 5 == 0) else [i % c.nk, (3 * i) % c.nk] for _ in range(H) for i in range(nq)]
     rp = np.zeros(H * nq + 1, np.int64)
     rp[1:] = np.cumsum([len(x) for x in cols])
     ci = np.array([j for x in cols for j in x], np.int32)
-    out = c.gpu_attention(rp, ci)
+    out = c.gpu_attention(rp, ci, fill=0xFF)
+    g_all, r_all = [], []
     for h in range(H):
-        for i in range(0, nq, 5):
+        for i in range(nq):
             toks = np.nonzero(c.qlab[0, h] == i)[0]
-            assert np.all(orc.widen(out[0, h, toks]) == 0)
+            if i % 5 == 0:
+                assert np.all(orc.widen(out[0, h, toks]) == 0)
+                continue
+            r = h * nq + i
+            toks, ref = orc.cluster_attention_rows(c.inp.q[0, h], c.inp.k[0, h], c.inp.v[0, h],
+                                                   c.qlab[0, h], c.klab[0, h], i,
+                                                   ci[rp[r]: rp[r + 1]], 1 / np.sqrt(c.D))
+            g_all.append(orc.widen(out[0, h, toks]).ravel())
+            r_all.append(ref.ravel())
+    g, r = np.concatenate(g_all), np.concatenate(r_all)
+    assert np.abs(g - r).max() <= gc.MAX_ABS
+    assert np.linalg.norm(g - r) / np.linalg.norm(r) <= gc.REL_L2
 
 
 def test_clustered_attention_all_kept_equals_dense():
@@ -494,8 +528,11 @@ def test_kmeans_assignment_full_size_sampled():
     xw = orc.widen(k)
     cents0 = np.stack([np.stack([xw[b, h, seeds[b, h]] for h in range(H)]) for b in range(B)])
     G = _metric(H, D, 8)
-    _, labels, sizes = _gpu_kmeans(k, cents0, 1, G)
+    cents, labels, sizes = _gpu_kmeans(k, cents0, 1, G)
     assert sizes.sum() == B * H * N
+    for h in range(H):
+        gc.log(f"wan720 k-means: means of head {h} on the GPU labels")
+        _check_update(k[:, h:h + 1], labels[0, h], cents0[0, h], cents[0, h], sizes[0, h])
     rng = np.random.default_rng(14)
     tolerated = 0
     for h in range(H):

@@ -265,15 +265,16 @@ def test_block_mask_over_snr_schedule():
 
 
 # ---------------------------------------------------------------- stage 4
-ATTN_CASES = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
+_ATTN_BASE = [("tiny", None), ("small", None), ("wan480", 6), ("wan720", 3), ("hv720", 2),
               ("small_b2", None), ("small_pad3d", None), ("tiny_pad3d", None), ("maxnb", 12)]
+# every top-p each config sweeps (Wan-720p: 0.8, 0.9 and 0.95)
+ATTN_CASES = [(name, per_head, p) for name, per_head in _ATTN_BASE for p in get_config(name).top_p]
 
 
-@pytest.mark.parametrize("name,per_head", ATTN_CASES)
-def test_attention_matches_oracle(name, per_head):
+@pytest.mark.parametrize("name,per_head,p", ATTN_CASES)
+def test_attention_matches_oracle(name, per_head, p):
     cfg = get_config(name)
     run, orun = gc.gpu_run(name), gc.oracle_run(name)
-    p = cfg.top_p[0]
     o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, p, np.float32), band=cfg.band)
     out_bits = run.attention(o_rp, o_ci)
     if per_head is None:
@@ -282,7 +283,34 @@ def test_attention_matches_oracle(name, per_head):
         rows = gc.sample_rows(cfg, o_rp, per_head)
     ref = orun.attention_blocks(o_rp, o_ci, rows)
     max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
-    gc.log(f"{name}: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    gc.log(f"{name} p={p}: {len(rows)} q-blocks, max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+@pytest.mark.parametrize("name,mode,which", [("wan720", 0.8, "heaviest"),
+                                             ("wan720", 0.95, "heaviest"),
+                                             ("hv720", 0.9, "heaviest"),
+                                             ("hv720", "fixed", "median")])
+def test_attention_whole_head(name, mode, which):
+    """Full size, every query block of one whole head against the oracle with
+    the oracle's mask: the heaviest head (most kept blocks) at the swept top-p
+    values not covered whole elsewhere, and a median head in the fixed-fraction
+    mode."""
+    cfg = get_config(name)
+    run, orun = gc.gpu_run(name), gc.oracle_run(name)
+    if mode == "fixed":
+        o_rp, o_ci = orun.mask(keep_frac=run.inp.keep_frac, band=cfg.band)
+    else:
+        o_rp, o_ci = orun.mask(top_p=np.full(cfg.heads, mode, np.float32), band=cfg.band)
+    out_bits = run.attention(o_rp, o_ci)
+    kept = np.diff(o_rp).reshape(cfg.heads, cfg.nb).sum(1)
+    order = np.argsort(kept, kind="stable")
+    h = int(order[-1]) if which == "heaviest" else int(order[len(order) // 2])
+    rows = [(0, h, i) for i in range(cfg.nb)]
+    gc.log(f"{name} {mode}: oracle attention of head {h} ({kept[h]} kept blocks)")
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(o_rp, o_ci, rows), cfg)
+    gc.log(f"{name} {mode} head {h} ({kept[h] / cfg.nb ** 2:.3f} kept), all {cfg.nb} q-blocks: "
+           f"max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
@@ -432,6 +460,69 @@ def test_attention_edge_cases_custom_csr():
             if (h, i) != (0, 5) and not (h == 2 and 8 <= i < 12)]
     ref = orun.attention_blocks(rp2, ci2, rows)
     max_abs, rel = gc.attn_errors(out_bits, ref, cfg)
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_empty_groups_with_stale_workspace():
+    """Work items whose union list is empty stream nothing and write zeros,
+    whatever the attention workspace held: every workspace byte is 0xFF before
+    V is staged.  Cases: a whole 4-block query group of empty rows, and PSA's
+    3D-padded 3x8x16 tiles on a 9x21x35 grid, whose last tile row holds sub-blocks
+    of padding only (their groups keep nothing)."""
+    import block_sparse_attention_17_amd as m
+    # (a) a whole query group of empty rows
+    cfg = get_config("small")
+    run, orun = gc.gpu_run("small"), gc.oracle_run("small")
+    nb, H = cfg.nb, cfg.heads
+    cols = [[] if (h == 3 and 4 <= i < 8) or (h == 0 and i < 4) else
+            sorted({i, (i * 7 + h) % nb, (i + 5) % nb}) for h in range(H) for i in range(nb)]
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in cols])
+    ci = np.array([c for cs in cols for c in cs], np.int32)
+    run.bsa.attn_ws.fill_(0xFF)
+    m.svsa_attn_stage_v(run.v_dev, run.bsa.attn_ws, run.geom)
+    out_bits = run.attention(rp, ci)
+    assert np.all(orc.widen(out_bits[0, 3, 4 * 64: 8 * 64]) == 0)
+    assert np.all(orc.widen(out_bits[0, 0, : 4 * 64]) == 0)
+    rows = [(0, h, i) for h in range(H) for i in range(nb) if cols[h * nb + i]]
+    max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
+    assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+    # (b) 3D-padded tiles with padding-only sub-blocks, every valid row
+    grid, tile, D, Hh = (9, 21, 35), (3, 8, 16), 128, 2
+    G = m.Geometry(*grid, *tile, pad3d=True)
+    rng = np.random.default_rng(61)
+    from svsa_synth import f32_to_bf16_bits
+    bits = [f32_to_bf16_bits(rng.standard_normal((1, Hh, G.N, D)).astype(np.float32))
+            for _ in range(3)]
+    nat = [gc.bits_to_dev(b) for b in bits]
+    tiled = [torch.empty((1, Hh, G.N_pad, D), dtype=torch.bfloat16, device="cuda")
+             for _ in range(2)]
+    for x, t in zip(nat, tiled):
+        m.svsa_tile_permute(x, t, G)
+    lists = [sorted(set(rng.choice(G.nb, size=int(rng.integers(1, G.nb + 1)),
+                                   replace=False).tolist()) | {i})
+             for _ in range(Hh) for i in range(G.nb)]
+    rp = np.zeros(Hh * G.nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    ci = np.array([c for cs in lists for c in cs], np.int32)
+    rp_d = torch.from_numpy(rp.astype(np.int32)).cuda()
+    ci_d = torch.from_numpy(ci).cuda()
+    ws = torch.full((m.svsa_attn_workspace_bytes(1, Hh, G),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    m.svsa_attn_stage_v(nat[2], ws, G)
+    out = torch.full((1, Hh, G.N, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    m.svsa_block_sparse_attn_ex(tiled[0], tiled[1], None, out, G, 1 / np.sqrt(D), rp_d, ci_d, ws,
+                                flags=m.SVSA_ATTN_OUT_NATURAL)
+    torch.cuda.synchronize()
+    got = orc.widen(gc.dev_to_bits(out))
+    slots, counts = orc.block_layout(grid, tile, True)
+    assert (counts % 64 != 0).any() and (counts <= G.Bk - 64).any()   # padding-only sub-blocks
+    qt, kt, vt = (orc.permute_fwd(b, grid, tile, True) for b in bits)
+    ref_t = orc.attention(qt, kt, vt, rp, ci, G.N, G.Bk, 1 / np.sqrt(D), counts=counts)
+    ref = orc.permute_inv(ref_t, grid, tile, True)
+    max_abs = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    gc.log(f"stale workspace, 3D-padded 3x8x16: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
