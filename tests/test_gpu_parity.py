@@ -526,6 +526,45 @@ def test_empty_groups_with_stale_workspace():
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_large_logit_range(D):
+    """Rows whose later kept key block scores ~80 nats above the blocks they
+    keep first: the online softmax has to move its running offset by far more
+    than its lazy threshold and rescale what it accumulated; the result still
+    matches the oracle.  Other rows of the same call keep ordinary logits."""
+    import block_sparse_attention_17_amd as m
+    from svsa_synth import f32_to_bf16_bits
+    G = m.Geometry(4, 8, 16, 4, 4, 4)            # 512 tokens, 8 blocks of 64
+    H, nb = 2, G.nb
+    rng = np.random.default_rng(71)
+    q = rng.standard_normal((1, H, G.N_pad, D)).astype(np.float32)
+    k = rng.standard_normal((1, H, G.N_pad, D)).astype(np.float32)
+    v = rng.standard_normal((1, H, G.N_pad, D)).astype(np.float32)
+    u = np.zeros(D, np.float32)
+    u[3] = 1.0
+    q[0, 0, :128] = 30.0 * u + 0.01 * q[0, 0, :128]     # query blocks 0, 1 of head 0
+    k[0, 0, 5 * 64: 6 * 64] = 30.0 * u                    # key block 5 of head 0
+    bits = [f32_to_bf16_bits(x) for x in (q, k, v)]
+    lists = [sorted({i, 5, (i + 3) % nb}) for _ in range(H) for i in range(nb)]
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    ci = np.array([c for cs in lists for c in cs], np.int32)
+    dev = [gc.bits_to_dev(b) for b in bits]
+    out = torch.empty_like(dev[0])
+    ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, G), dtype=torch.uint8, device="cuda")
+    m.svsa_block_sparse_attn(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D),
+                             torch.from_numpy(rp.astype(np.int32)).cuda(),
+                             torch.from_numpy(ci).cuda(), ws)
+    torch.cuda.synchronize()
+    got = orc.widen(gc.dev_to_bits(out))
+    ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    gc.log(f"large logit range D={D}: max_abs={err.max():.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
 @pytest.mark.parametrize("grid,tile,D,pad3d", [((5, 9, 14), (4, 4, 4), 128, False),
                                                ((5, 9, 14), (4, 4, 4), 64, True),
                                                ((7, 20, 35), (3, 4, 8), 128, False),
