@@ -12,7 +12,8 @@ from .binding import (svsa_cluster_attn, svsa_cluster_attn_workspace_bytes,
                       svsa_tail_merge_workspace_bytes)
 from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, library, library_path,
                       status_string, svsa_attn_workspace_bytes, svsa_block_mask,
-                      svsa_block_mask_workspace_bytes, svsa_block_sparse_attn, svsa_pool,
+                      svsa_block_mask_workspace_bytes, svsa_block_mask_noalloc,
+                      svsa_block_sparse_attn, svsa_pool,
                       svsa_snr_top_p, svsa_status_string, svsa_stripe_mask,
                       svsa_stripe_mask_workspace_bytes, svsa_tile_permute, svsa_tile_permute_pool,
                       svsa_attn_stage_v, svsa_block_sparse_attn_ex,
@@ -21,7 +22,8 @@ from .pipeline import BlockSparseAttention, ClusteredAttention
 
 __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
            "library_path", "status_string", "svsa_attn_workspace_bytes", "svsa_block_mask",
-           "svsa_block_mask_workspace_bytes", "svsa_block_sparse_attn", "svsa_pool",
+           "svsa_block_mask_workspace_bytes", "svsa_block_mask_noalloc", "svsa_block_sparse_attn",
+           "svsa_pool",
            "svsa_snr_top_p", "svsa_status_string", "svsa_stripe_mask",
            "svsa_stripe_mask_workspace_bytes", "svsa_tile_permute", "svsa_tile_permute_pool",
            "svsa_attn_stage_v", "svsa_block_sparse_attn_ex", "SVSA_ATTN_OUT_NATURAL",

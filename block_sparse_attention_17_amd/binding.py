@@ -102,6 +102,8 @@ def _load():
         "svsa_block_mask_workspace_bytes": (sz, [i32, i32, i32]),
         "svsa_block_mask": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, dbl, fp, fp, i32, vp, vp,
                                            i64, vp, sz, vp]),
+        "svsa_block_mask_noalloc": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, dbl, fp, fp, i32,
+                                                   vp, vp, i64, vp]),
         "svsa_stripe_mask_workspace_bytes": (sz, [i32, i32, gp]),
         "svsa_stripe_mask": (ctypes.c_int, [gp, i32, i32, ctypes.POINTER(ctypes.c_int32), i32, vp,
                                             vp, i64, vp, sz, vp]),
@@ -148,7 +150,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("svsa_tile_permute", "svsa_pool", "svsa_tile_permute_pool",
-            "svsa_block_mask_workspace_bytes", "svsa_block_mask", "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
+            "svsa_block_mask_workspace_bytes", "svsa_block_mask", "svsa_block_mask_noalloc",
+            "svsa_stripe_mask_workspace_bytes", "svsa_stripe_mask",
             "svsa_attn_workspace_bytes", "svsa_block_sparse_attn", "svsa_block_sparse_attn_ex",
             "svsa_attn_stage_v",
             "svsa_snr_top_p",
@@ -338,6 +341,27 @@ def svsa_block_mask(qbar, kbar, softmax_scale, row_ptr, col_idx, workspace, top_
         float(softmax_scale), tp, kf, int(band_width), _ptr(row_ptr, "row_ptr", (torch.int32,)),
         _ptr(col_idx, "col_idx", (torch.int32,)), col_idx.numel(),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(stream)))
+    del tp_arr, kf_arr
+    return row_ptr, col_idx
+
+
+def svsa_block_mask_noalloc(qbar, kbar, softmax_scale, row_ptr, col_idx, top_p=None,
+                            keep_frac=None, band_width=1, stream=None):
+    """svsa_block_mask with the library's own device scratch (no workspace, no
+    allocation); calls overlapping in time on one device race."""
+    import torch
+    _ndim(qbar, "qbar", 4)
+    B, Hh, nb, D = qbar.shape
+    _shape(kbar, "kbar", (B, Hh, nb, D))
+    _at_least(row_ptr, "row_ptr", B * Hh * nb + 1)
+    _ndim(col_idx, "col_idx", 1)
+    _same_device(qbar=qbar, kbar=kbar, row_ptr=row_ptr, col_idx=col_idx)
+    tp_arr, tp = _host_f32(top_p, Hh, "top_p")
+    kf_arr, kf = _host_f32(keep_frac, Hh, "keep_frac")
+    _check("svsa_block_mask_noalloc", _lib.svsa_block_mask_noalloc(
+        _ptr(qbar, "qbar", (torch.float64,)), _ptr(kbar, "kbar", (torch.float64,)), B, Hh, nb, D,
+        float(softmax_scale), tp, kf, int(band_width), _ptr(row_ptr, "row_ptr", (torch.int32,)),
+        _ptr(col_idx, "col_idx", (torch.int32,)), col_idx.numel(), _stream(stream)))
     del tp_arr, kf_arr
     return row_ptr, col_idx
 

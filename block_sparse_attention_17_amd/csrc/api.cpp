@@ -357,6 +357,30 @@ int svsa_block_mask(const double* qbar, const double* kbar, int32_t batch, int32
                                           col_idx, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int svsa_block_mask_noalloc(const double* qbar, const double* kbar, int32_t batch, int32_t heads,
+                            int32_t nb, int32_t head_dim, double softmax_scale,
+                            const float* top_p, const float* keep_frac, int32_t band_width,
+                            int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                            void* stream) {
+  if (!(al(qbar, 8) && al(kbar, 8) && al(row_ptr, 4) && al(col_idx, 4))) return SVSA_E_INVALID;
+  if (!qbar || !kbar || !row_ptr || !col_idx || batch < 1 || heads < 1 || nb < 1 ||
+      head_dim < 1 || band_width < 1 || !isfinite(softmax_scale))
+    return SVSA_E_INVALID;
+  if ((top_p == nullptr) == (keep_frac == nullptr)) return SVSA_E_INVALID;
+  const float* par = top_p ? top_p : keep_frac;
+  for (int32_t h = 0; h < heads && h < kMaxHeadsMask; ++h)
+    if (!(par[h] > 0.f && par[h] <= 1.f)) return SVSA_E_INVALID;
+  if (heads > kMaxHeadsMask || nb > kMaxNb) return SVSA_E_UNSUPPORTED;
+  const int64_t worst = (int64_t)batch * heads * nb * nb;
+  if (worst >= 0x7fffffff) return SVSA_E_UNSUPPORTED;
+  if (col_capacity < worst) return SVSA_E_CAPACITY;
+  if (!svsa::block_mask_fits_scratch((int64_t)batch * heads, nb)) return SVSA_E_WORKSPACE;
+  return from_hip(svsa::launch_block_mask_noalloc(qbar, kbar, batch * heads, heads, nb, head_dim,
+                                                  softmax_scale, top_p, keep_frac, band_width,
+                                                  row_ptr, col_idx,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 size_t svsa_cluster_mask_workspace_bytes(int32_t batch, int32_t heads, int32_t nq, int32_t nk) {
   if (batch < 1 || heads < 1 || nq < 1 || nk < 1) return 0;
   return svsa::mask_ws_layout((int64_t)batch * heads * nq, nk).total;

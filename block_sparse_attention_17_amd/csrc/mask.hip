@@ -17,6 +17,8 @@
 //                   histograms, kept bitmap, row count
 //   scan_kernel     exclusive scan of row counts -> row_ptr
 //   compact_kernel  one wavefront per row: bitmap -> ascending col_idx
+#include <mutex>
+
 #include "svsa_internal.h"
 
 namespace svsa {
@@ -179,11 +181,13 @@ struct RadixStep {
 
 // mode: 0 = top-p, 1 = fixed fraction.  PER = elements per thread (nb <= 256 * PER).
 // Rows r = (bh, i) with nq rows per head; nb columns (key blocks or clusters).
+// L holds the logits of rows row0 .. row0 + gridDim.x - 1 (row r at L[(r - row0) * nb]);
+// bits and counts are indexed by the global row r.
 template <int PER>
 __global__ void __launch_bounds__(kSThreads)
 select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
               int32_t* __restrict__ counts, int32_t nq, int32_t nb, int32_t heads,
-              int32_t words, int32_t band, int32_t mode, HeadParams hp) {
+              int32_t words, int32_t band, int32_t mode, HeadParams hp, int64_t row0) {
   __shared__ uint32_t hcnt[256];
   __shared__ unsigned long long hmass[256];
   __shared__ double red[4];   // one partial value per wavefront
@@ -191,10 +195,10 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
   __shared__ uint32_t tie[kMaxNb / 32];
   __shared__ RadixStep res;
 
-  const int64_t r = blockIdx.x;
+  const int64_t r = row0 + blockIdx.x;
   const int32_t i = (int32_t)(r % nq);
   const int32_t h = (int32_t)((r / nq) % heads);
-  const double* Lr = L + r * nb;
+  const double* Lr = L + (int64_t)blockIdx.x * nb;
   const int t = threadIdx.x, lane = t & 63;
 
   // 1. softmax of the row, elements j = t + 256 k held in registers
@@ -520,6 +524,52 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                              keep_frac, band, row_ptr, col_idx, ws, stream);
 }
 
+namespace {
+// Logits and selection for the (b, h) pairs b0 .. b0 + cb - 1 (rows b0 * nq ..):
+// the logits go to L (cb * nq * nb doubles), the kept bitmaps and counts to
+// the global rows of bits / counts.
+hipError_t mask_rows(const double* qbar, const double* kbar, const int32_t* ksizes, int64_t b0,
+                     int64_t cb, int32_t heads, int32_t nq, int32_t nb, int32_t head_dim,
+                     double scale, const HeadParams& hp, int mode, int32_t band, int32_t words,
+                     double* L, uint32_t* bits, int32_t* counts, hipStream_t stream) {
+  const int32_t tiles_q = (nq + kTile - 1) / kTile, tiles_k = (nb + kTile - 1) / kTile;
+  const int64_t lblocks = cb * tiles_q * tiles_k;
+  const int64_t rows = cb * nq;
+  if (lblocks > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(logits_kernel, dim3((uint32_t)lblocks), dim3(kLThreads), 0, stream,
+                     qbar + b0 * nq * head_dim, kbar + b0 * nb * head_dim,
+                     ksizes ? ksizes + b0 * nb : nullptr, L, nq, nb, head_dim, scale, tiles_q,
+                     tiles_k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((uint32_t)rows), blk(kSThreads);
+  const int64_t row0 = b0 * nq;
+  if (nb <= kSThreads)
+    hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
+                       words, band, mode, hp, row0);
+  else if (nb <= 2 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<2>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
+                       words, band, mode, hp, row0);
+  else if (nb <= 4 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<4>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
+                       words, band, mode, hp, row0);
+  else if (nb <= 8 * kSThreads)
+    hipLaunchKernelGGL(select_kernel<8>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
+                       words, band, mode, hp, row0);
+  else
+    hipLaunchKernelGGL(select_kernel<16>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
+                       words, band, mode, hp, row0);
+  return hipGetLastError();
+}
+
+HeadParams head_params(int32_t heads, const float* top_p, const float* keep_frac) {
+  HeadParams hp{};
+  const float* src = top_p ? top_p : keep_frac;
+  for (int32_t h = 0; h < heads; ++h) hp.v[h] = src[h];
+  return hp;
+}
+}  // namespace
+
 hipError_t launch_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,
                                int32_t bh, int32_t heads, int32_t nq, int32_t nb,
                                int32_t head_dim, double scale, const float* top_p,
@@ -532,38 +582,81 @@ hipError_t launch_cluster_mask(const double* qbar, const double* kbar, const int
   double* L = reinterpret_cast<double*>(w + m.logits_off);
   uint32_t* bits = reinterpret_cast<uint32_t*>(w + m.bits_off);
   int32_t* counts = reinterpret_cast<int32_t*>(w + m.counts_off);
-
-  const int32_t tiles_q = (nq + kTile - 1) / kTile, tiles_k = (nb + kTile - 1) / kTile;
-  const int64_t lblocks = (int64_t)bh * tiles_q * tiles_k;
-  if (lblocks > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(logits_kernel, dim3((uint32_t)lblocks), dim3(kLThreads), 0, stream, qbar,
-                     kbar, ksizes, L, nq, nb, head_dim, scale, tiles_q, tiles_k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  HeadParams hp{};
-  const float* src = top_p ? top_p : keep_frac;
-  for (int32_t h = 0; h < heads; ++h) hp.v[h] = src[h];
-  const int mode = top_p ? 0 : 1;
-  const dim3 grid((uint32_t)rows), blk(kSThreads);
-  if (nb <= kSThreads)
-    hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
-                       m.words, band, mode, hp);
-  else if (nb <= 2 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<2>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
-                       m.words, band, mode, hp);
-  else if (nb <= 4 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<4>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
-                       m.words, band, mode, hp);
-  else if (nb <= 8 * kSThreads)
-    hipLaunchKernelGGL(select_kernel<8>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
-                       m.words, band, mode, hp);
-  else
-    hipLaunchKernelGGL(select_kernel<16>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
-                       m.words, band, mode, hp);
-  e = hipGetLastError();
+  const HeadParams hp = head_params(heads, top_p, keep_frac);
+  hipError_t e = mask_rows(qbar, kbar, ksizes, 0, bh, heads, nq, nb, head_dim, scale, hp,
+                           top_p ? 0 : 1, band, m.words, L, bits, counts, stream);
   if (e != hipSuccess) return e;
   return launch_csr_from_bits(bits, counts, row_ptr, col_idx, rows, m.words, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The block mask without a caller workspace: its scratch is a file-scope device
+// array of kScratchBytes (held on each device the library runs on until the
+// process ends).  The logits of a chunk of whole (b, h) pairs go to its first
+// kScratchLogits bytes, one chunk after the other; the kept bitmaps and row
+// counts of every row to the rest.  Each device's copy of the array has its
+// own address, looked up once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchLogits = (size_t)64 << 20;
+constexpr size_t kScratchBits = (size_t)16 << 20;
+constexpr size_t kScratchBytes = kScratchLogits + kScratchBits;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// This device's address of `scratch` (nullptr and an error on failure).
+hipError_t device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = scratch_ptr[dev];
+  return scratch_err[dev];
+}
+}  // namespace
+
+bool block_mask_fits_scratch(int64_t bh, int32_t nb) {
+  const int64_t words = (nb + 31) / 32;
+  const uint64_t per_head = (uint64_t)nb * nb * sizeof(double);
+  const uint64_t rows = (uint64_t)bh * nb;
+  return per_head <= kScratchLogits &&
+         align_up(rows * words * sizeof(uint32_t), 256) + rows * sizeof(int32_t) <= kScratchBits;
+}
+
+hipError_t launch_block_mask_noalloc(const double* qbar, const double* kbar, int32_t bh,
+                                     int32_t heads, int32_t nb, int32_t head_dim, double scale,
+                                     const float* top_p, const float* keep_frac, int32_t band,
+                                     int32_t* row_ptr, int32_t* col_idx, hipStream_t stream) {
+  if (heads > kMaxHeads || nb > kMaxNb || !block_mask_fits_scratch(bh, nb))
+    return hipErrorInvalidValue;
+  void* base = nullptr;
+  hipError_t e = device_scratch(&base);
+  if (e != hipSuccess) return e;
+  char* w = static_cast<char*>(base);
+  double* L = reinterpret_cast<double*>(w);
+  const int64_t rows = (int64_t)bh * nb;
+  const int32_t words = (nb + 31) / 32;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(w + kScratchLogits);
+  int32_t* counts = reinterpret_cast<int32_t*>(
+      w + kScratchLogits + align_up((size_t)rows * words * sizeof(uint32_t), 256));
+  const HeadParams hp = head_params(heads, top_p, keep_frac);
+  const int64_t chunk = (int64_t)(kScratchLogits / ((size_t)nb * nb * sizeof(double)));
+  for (int64_t b0 = 0; b0 < bh; b0 += chunk) {
+    const int64_t cb = bh - b0 < chunk ? bh - b0 : chunk;
+    e = mask_rows(qbar, kbar, nullptr, b0, cb, heads, nb, nb, head_dim, scale, hp,
+                  top_p ? 0 : 1, band, words, L, bits, counts, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_csr_from_bits(bits, counts, row_ptr, col_idx, rows, words, stream);
 }
 
 }  // namespace svsa

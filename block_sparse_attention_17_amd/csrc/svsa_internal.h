@@ -86,6 +86,14 @@ hipError_t launch_block_mask(const double* qbar, const double* kbar, int32_t bh,
                              const float* keep_frac, int32_t band, int32_t* row_ptr,
                              int32_t* col_idx, void* ws, hipStream_t stream);
 
+// The block mask with its scratch in a file-scope device array (no workspace
+// argument): whether the sizes fit, and the launch.
+bool block_mask_fits_scratch(int64_t bh, int32_t nb);
+hipError_t launch_block_mask_noalloc(const double* qbar, const double* kbar, int32_t bh,
+                                     int32_t heads, int32_t nb, int32_t head_dim, double scale,
+                                     const float* top_p, const float* keep_frac, int32_t band,
+                                     int32_t* row_ptr, int32_t* col_idx, hipStream_t stream);
+
 // Rectangular variant: nq query rows per head against nb key clusters, with
 // + ln n_j on every logit of key cluster j when ksizes is given.
 hipError_t launch_cluster_mask(const double* qbar, const double* kbar, const int32_t* ksizes,

@@ -27,7 +27,9 @@
  *
  * Conventions shared by every call
  *   - Tensor pointers are DEVICE pointers allocated and owned by the caller.
- *     The calls never allocate or free memory and keep no state between calls.
+ *     The calls never allocate or free memory and keep no state between calls
+ *     (the one exception: svsa_block_mask_noalloc's scratch array and the
+ *     per-device address of it that the library looks up once).
  *   - Per-head parameter arrays (top_p, keep_frac) are HOST pointers, read
  *     during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -177,6 +179,30 @@ SVSA_API int svsa_block_mask(const double* qbar, const double* kbar, int32_t bat
                     const float* keep_frac, int32_t band_width,
                     int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * svsa_block_mask without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, rule, outputs and
+ * checks as svsa_block_mask; it allocates and frees nothing.  Its scratch is
+ * a fixed device array inside the library (80 MiB: 64 MiB for the float64
+ * logits of a chunk of whole (batch, head) pairs, processed one chunk after
+ * the other, and 16 MiB for the kept bitmaps and counts of all rows), which
+ * every device the library runs on holds until the process ends.
+ * Limits beyond svsa_block_mask's: nb * nb * 8 <= 64 MiB (nb <= 2896), and
+ * batch*heads*nb * (4 * ceil(nb / 32) + 4) bytes (rounded up to 256 for the
+ * bitmaps) <= 16 MiB; otherwise SVSA_E_WORKSPACE, before any launch.
+ * Every call on a device uses that device's one array: calls that overlap in
+ * time on one device (other streams, other host threads) race and must be
+ * ordered by the caller.  The array keeps the last call's contents; every
+ * call writes all of it that it reads.
+ */
+SVSA_API int svsa_block_mask_noalloc(const double* qbar, const double* kbar, int32_t batch,
+                                     int32_t heads, int32_t nb, int32_t head_dim,
+                                     double softmax_scale, const float* top_p,
+                                     const float* keep_frac, int32_t band_width,
+                                     int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                     void* stream);
 
 /*
  * Workspace (device bytes) needed by svsa_stripe_mask.  Returns 0 if the

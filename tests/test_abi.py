@@ -22,7 +22,7 @@ def mod():
 
 def test_every_declared_symbol_is_exported(mod):
     names = _declared()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     lib = ctypes.CDLL(mod.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -375,3 +375,26 @@ def test_binding_checks_shapes_against_the_geometry(mod):
     # tensors must be torch tensors
     with pytest.raises(TypeError):
         mod.svsa_tile_permute([1, 2], til, g)
+
+
+def test_block_mask_noalloc_argument_errors(mod):
+    """The no-allocation block mask refuses what svsa_block_mask refuses, and
+    sizes beyond its fixed scratch (SVSA_E_WORKSPACE), before any launch."""
+    lib = mod.library()
+    E_INV, E_UNS, E_WS, E_CAP = -1, -2, -3, -4
+    tp = (ctypes.c_float * 256)(*([0.9] * 256))
+    bad = (ctypes.c_float * 256)(*([1.5] * 256))
+    f = lib.svsa_block_mask_noalloc
+    assert f(None, FAKE2, 1, 1, 8, 64, 0.1, tp, None, 1, FAKE, FAKE2, 64, None) == E_INV
+    assert f(FAKE, FAKE2, 1, 1, 8, 64, 0.1, None, None, 1, FAKE, FAKE2, 64, None) == E_INV
+    assert f(FAKE, FAKE2, 1, 1, 8, 64, 0.1, tp, tp, 1, FAKE, FAKE2, 64, None) == E_INV
+    assert f(FAKE, FAKE2, 1, 1, 8, 64, 0.1, bad, None, 1, FAKE, FAKE2, 64, None) == E_INV
+    assert f(FAKE, FAKE2, 1, 1, 8, 64, 0.1, tp, None, 0, FAKE, FAKE2, 64, None) == E_INV
+    assert f(FAKE, FAKE2, 1, 1, 8, 64, 0.1, tp, None, 1, FAKE, FAKE2, 63, None) == E_CAP
+    assert f(FAKE, FAKE2, 1, 1, 5000, 64, 0.1, tp, None, 1, FAKE, FAKE2, 1 << 30, None) == E_UNS
+    # one head's logits beyond the 64 MiB chunk (nb = 2897)
+    assert f(FAKE, FAKE2, 1, 1, 2897, 64, 0.1, tp, None, 1, FAKE, FAKE2, 2897 * 2897,
+             None) == E_WS
+    # bitmaps and counts beyond 16 MiB: 200 heads of 1182 blocks
+    assert f(FAKE, FAKE2, 1, 200, 1182, 64, 0.1, tp, None, 1, FAKE, FAKE2, 200 * 1182 * 1182,
+             None) == E_WS
