@@ -142,51 +142,110 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(cfg, inp_head, top_p, budget_s, heads_total, total_flops):
-    """The oracle on a bounded sample: the full mask stages of one head plus the
-    attention of seeded query blocks of that head, extrapolated to a whole step."""
-    from oracle import svsa_oracle as orc
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        blas_threads = None
+        return None
+
+
+def _sample_blocks(counts_row, nb, k, rng):
+    """Query blocks of one head in the order they are checked: the tail block,
+    block 0, the heaviest and the lightest row, then seeded random ones."""
+    first = [nb - 1, 0, int(np.argmax(counts_row)), int(np.argmin(counts_row))]
+    order = list(dict.fromkeys(first))
+    rest = [int(x) for x in rng.permutation(nb) if int(x) not in order]
+    return order + rest[: max(0, k - len(order))]
+
+
+def oracle_leg(cfg, inp, top_p, keep_frac, g_rp, g_ci, g_out, budget_s, total_flops,
+               blocks_per_head=16):
+    """The fp64 oracle on the timed workload, checked against the last timed
+    step and timed as the CPU baseline.
+
+    Every (batch, head): the oracle's tile reorder of Q, K, V, block means,
+    block scores and mask ([iCATS] Sec. 3.2), compared list by list with the
+    GPU's CSR under the near-threshold rule; then up to ``blocks_per_head``
+    seeded query blocks of that head (the per-head share of ``budget_s``, at
+    least the first four) through the oracle's attention, compared with the
+    GPU's natural-order output.  CPU time: the mask stages are measured on
+    every head; attention is extrapolated to the whole step at the measured
+    oracle FLOP rate."""
+    from oracle import parity
+    from oracle import svsa_oracle as orc
     N, Bk, nb, D = cfg.N, cfg.Bk, cfg.nb, cfg.head_dim
+    H = cfg.heads
     scale = 1 / sqrt(D)
-    t0 = time.perf_counter()
-    _, n = orc.block_layout(cfg.grid, cfg.tile, cfg.pad3d)
-    qp = orc.permute_fwd(inp_head.q, cfg.grid, cfg.tile, cfg.pad3d)
-    kp = orc.permute_fwd(inp_head.k, cfg.grid, cfg.tile, cfg.pad3d)
-    vp = orc.permute_fwd(inp_head.v, cfg.grid, cfg.tile, cfg.pad3d)
-    S = orc.block_scores(orc.pool(qp, N, Bk, n), orc.pool(kp, N, Bk, n), scale)
-    rp, ci = orc.block_mask(S, cfg.band, top_p=np.array([top_p], np.float32))
-    t_mask = time.perf_counter() - t0
+    slots, n = orc.block_layout(cfg.grid, cfg.tile, cfg.pad3d)
     rng = np.random.default_rng(11)
-    order = rng.permutation(nb)
-    t1 = time.perf_counter()
-    done, flops = 0, 0
-    for i in order:
-        cols = ci[rp[i]: rp[i + 1]]
-        orc.attention_rows(qp, kp, vp, 0, 0, int(i), cols, N, Bk, scale, n)
-        flops += 4 * D * int(n[i]) * int(n[cols].sum())
-        done += 1
-        if time.perf_counter() - t1 > budget_s:
-            break
-    t_attn = time.perf_counter() - t1
-    # extrapolate: mask stages per head x heads, attention at the measured FLOP rate
-    step_s = t_mask * heads_total + total_flops / (flops / t_attn)
-    return {
+    per_head_s = budget_s / (cfg.batch * H)
+    acc = parity.ErrorAccumulator()
+    t_mask = t_attn = 0.0
+    flops_done = blocks_done = 0
+    rows_same = rows_tol = 0
+    failing = []
+    for b in range(cfg.batch):
+        for h in range(H):
+            t0 = time.perf_counter()
+            one = lambda x: orc.permute_fwd(x[b:b + 1, h:h + 1], cfg.grid, cfg.tile, cfg.pad3d)
+            qp, kp, vp = one(inp.q), one(inp.k), one(inp.v)
+            S = orc.block_scores(orc.pool(qp, N, Bk, n), orc.pool(kp, N, Bk, n), scale)
+            tp = None if top_p is None else np.array([top_p[h]], np.float32)
+            kf = None if keep_frac is None else np.array([keep_frac[h]], np.float32)
+            o_rp, o_ci = orc.block_mask(S, cfg.band, top_p=tp, keep_frac=kf)
+            t_mask += time.perf_counter() - t0
+            r0 = (b * H + h) * nb
+            h_rp = g_rp[r0: r0 + nb + 1] - g_rp[r0]
+            h_ci = g_ci[g_rp[r0]: g_rp[r0 + nb]]
+            tol, bad = parity.mask_mismatch(S, 1, h_rp, h_ci, o_rp, o_ci, top_p=tp,
+                                            keep_frac=kf, band=cfg.band)
+            rows_tol += len(tol)
+            rows_same += nb - len(tol) - len(bad)
+            failing += [(b, h, i) for i in bad]
+            # attention of sampled query blocks on the oracle's own mask
+            t1 = time.perf_counter()
+            picks = _sample_blocks(np.diff(o_rp), nb, blocks_per_head, rng)
+            for c, i in enumerate(picks):
+                if c >= 4 and time.perf_counter() - t1 > per_head_s:
+                    break
+                cols = o_ci[o_rp[i]: o_rp[i + 1]]
+                ref = orc.attention_rows(qp, kp, vp, 0, 0, i, cols, N, Bk, scale, n)
+                ni = int(n[i])
+                acc.add(g_out[b, h, slots[i * Bk: i * Bk + ni]], ref, key=(b, h))
+                flops_done += 4 * D * ni * int(n[cols].sum())
+                blocks_done += 1
+            t_attn += time.perf_counter() - t1
+    step_s = t_mask + total_flops / (flops_done / t_attn)
+    per_head = acc.rel_l2_per_key()
+    cores = _blas_threads()
+    cpu = {
         "value": total_flops / step_s / 1e12,
         "unit": "TFLOP/s",
-        "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+        "cores": cores if cores else len(os.sched_getaffinity(0)),
         "host_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: permute+pool+scores+top-p mask of 1 head "
-                   f"({t_mask:.2f} s) and attention of {done}/{nb} seeded query blocks of that "
-                   f"head ({t_attn:.2f} s, {flops / t_attn / 1e9:.2f} GFLOP/s); whole-step time "
-                   f"extrapolated to {heads_total} heads = {step_s:.1f} s"),
+        "sample": (f"fp64 NumPy oracle: reorder+means+scores+mask of all {cfg.batch * H} heads "
+                   f"({t_mask:.2f} s, measured) and attention of {blocks_done} seeded query "
+                   f"blocks spread over every head ({t_attn:.2f} s, "
+                   f"{flops_done / t_attn / 1e9:.2f} GFLOP/s); whole-step time with attention "
+                   f"extrapolated at that rate = {step_s:.1f} s"),
     }
+    report = {
+        "mask": {"rows": cfg.batch * H * nb, "identical": rows_same,
+                 "tolerated_near_threshold": rows_tol, "failing": len(failing),
+                 "failing_rows": failing[:8], "heads": cfg.batch * H},
+        "attention": {"query_blocks": blocks_done, "rows": acc.rows,
+                      "max_abs": acc.max_abs, "rel_l2": acc.rel_l2,
+                      "rel_l2_worst_head": max(per_head.values()) if per_head else None,
+                      "tolerance": {"max_abs": parity.MAX_ABS, "rel_l2": parity.REL_L2},
+                      "on": "natural-order output of the last timed step; oracle rows on the "
+                            "oracle's own mask"},
+    }
+    report["pass"] = (len(failing) == 0 and acc.max_abs <= parity.MAX_ABS
+                      and acc.rel_l2 <= parity.REL_L2)
+    return cpu, report
 
 
 def cluster_bench(args, cfg, m, inp, torch):
@@ -372,6 +431,14 @@ def main():
     kept_frac = flops / dense_flops
     counts = np.diff(rp).reshape(cfg.batch * cfg.heads, cfg.nb)
     sparsity_per_head = 1 - counts.sum(1) / cfg.nb ** 2
+    # natural-order output of the last timed step, for the oracle's check
+    out_bits = bsa.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    # algorithmic bytes of the first stage: Q, K, V read once in natural order;
+    # tiled Q, K and the staged V^T written once; the float64 block means of Q, K
+    bh = cfg.batch * cfg.heads
+    n_pad = cfg.nb * cfg.Bk
+    perm_bytes = bh * cfg.head_dim * (3 * cfg.N * 2 + 3 * n_pad * 2 + 2 * cfg.nb * 8)
+    perm_gbs = perm_bytes / (stage_ms["permute_pool_qk_stage_v"] * 1e-3) / 1e9
 
     attn_ms = stage_ms["attention_natural_out"]
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
@@ -434,13 +501,13 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline and not args.stripe:
-        head = 0
-        inp1 = make_inputs(cfg, seed=args.seed, heads=[head])
-        cpu = cpu_baseline(cfg, inp1, top_p if not args.fixed else 0.9, args.cpu_budget_s,
-                           cfg.heads * cfg.batch, flops)
-        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s", file=sys.stderr, flush=True)
+        print("[bench] oracle: every head's mask and sampled attention rows", file=sys.stderr,
+              flush=True)
+        cpu, parity = oracle_leg(cfg, inp, tp, kf, rp, ci, out_bits, args.cpu_budget_s, flops)
+        print(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s; parity pass={parity['pass']}",
+              file=sys.stderr, flush=True)
 
     out = {
         "metric": "kept-block attention TFLOP/s and % bf16 MFMA peak; speedup vs dense, 1 GPU",
@@ -473,7 +540,14 @@ def main():
         "kept_fraction": kept_frac,
         "sparsity_per_head": {"min": float(sparsity_per_head.min()),
                               "mean": float(sparsity_per_head.mean()),
-                              "max": float(sparsity_per_head.max())},
+                              "max": float(sparsity_per_head.max()),
+                              "histogram_10pct": np.histogram(
+                                  sparsity_per_head, bins=10, range=(0, 1))[0].tolist()},
+        "kept_blocks_per_row": {"min": int(counts.min()), "median": float(np.median(counts)),
+                                "max": int(counts.max())},
+        "permute_pool_stage": {"ms": stage_ms["permute_pool_qk_stage_v"],
+                               "algorithmic_bytes": perm_bytes, "gbs": perm_gbs,
+                               "frac_hbm_peak": perm_gbs / HBM_PEAK_GBS},
         "stage_ms": stage_ms,
         "attention_tflops": attn_tflops,
         "attention_frac_peak": attn_tflops / BF16_PEAK_TFLOPS,
@@ -491,6 +565,7 @@ def main():
             else measured_traffic(args.workload),
         },
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
     }
     if snr is not None:
         out["snr_schedule"] = snr

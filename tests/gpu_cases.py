@@ -16,12 +16,10 @@ from math import sqrt
 import numpy as np
 import torch
 
+from oracle import parity
 from oracle import svsa_oracle as orc
+from oracle.parity import MASK_REL, MAX_ABS, REL_L2  # noqa: F401
 from svsa_synth import get_config, make_inputs
-
-MAX_ABS = 2e-2
-REL_L2 = 5e-3
-MASK_REL = 1e-4
 
 
 def log(msg):
@@ -167,46 +165,10 @@ def oracle_run(name, seed=0):
 
 
 def mask_mismatch(cfg, S, g_rp, g_ci, o_rp, o_ci, top_p=None, keep_frac=None, band=1):
-    """Rows where GPU and oracle lists differ, split into (tolerated, failing).
-
-    A row is tolerated when either
-      (a) every differing block j is outside the band and its score is within
-          1e-4 relative of tau, the smallest score the oracle selected by
-          top-p / top-k in that row, or
-      (b) the GPU set lies between the oracle's sets at p(1-1e-4) and p(1+1e-4)
-          (top-p mode; the cumulative mass sits within 1e-4 of p).
-    """
-    nb = cfg.nb
-    tolerated, failing = [], []
-    rows = len(o_rp) - 1
-    for r in range(rows):
-        G = g_ci[g_rp[r]: g_rp[r + 1]]
-        R = o_ci[o_rp[r]: o_rp[r + 1]]
-        if G.size == R.size and np.array_equal(G, R):
-            continue
-        b_h, i = divmod(r, nb)
-        b, h = divmod(b_h, cfg.heads)
-        s = S[b, h, i]
-        Gs, Rs = set(G.tolist()), set(R.tolist())
-        band_set = {j for j in range(max(0, i - band + 1), min(nb, i + band))}
-        # selected-by-rule set of the oracle (band-only additions excluded)
-        order = np.argsort(-s, kind="stable")
-        if keep_frac is not None:
-            k = min(max(int(np.ceil(float(np.float32(keep_frac[h])) * nb)), 1), nb)
-        else:
-            p = float(np.float32(top_p[h]))
-            cs = np.cumsum(s[order])
-            hit = np.nonzero(cs >= p)[0]
-            k = nb if p >= 1 else (int(hit[0]) + 1 if hit.size else nb)
-        tau = s[order[k - 1]]
-        ok_a = all((j not in band_set) and abs(s[j] - tau) <= MASK_REL * tau for j in Gs ^ Rs)
-        ok_b = False
-        if top_p is not None:
-            lo = set(orc.select_row(s, i, band, top_p=np.float32(top_p[h] * (1 - MASK_REL))).tolist())
-            hi = set(orc.select_row(s, i, band, top_p=np.float32(min(1.0, top_p[h] * (1 + MASK_REL)))).tolist())
-            ok_b = lo <= Gs <= hi
-        (tolerated if (ok_a or ok_b) else failing).append(r)
-    return tolerated, failing
+    """Rows where GPU and oracle lists differ, split into (tolerated, failing)
+    under the near-threshold rule of ``oracle.parity.mask_mismatch``."""
+    return parity.mask_mismatch(S, cfg.heads, g_rp, g_ci, o_rp, o_ci, top_p=top_p,
+                                keep_frac=keep_frac, band=band)
 
 
 def attn_errors(gpu_tiled_bits, ref_blocks, cfg):
