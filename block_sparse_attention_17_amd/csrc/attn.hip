@@ -578,7 +578,7 @@ __device__ __forceinline__ bf16x8 k_operand(const Ctx& cx, const char* kt, int j
 // the first kPre P V jobs were read at the end of the previous phase.
 template <int D, int BK, bool PV, bool QK, bool PR>
 __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx, const char* vprev,
-                                            const char* kcur, bool ha, bool hb) {
+                                            const char* kcur) {
   using C = Cfg<D, BK>;
   constexpr int kNpv = PV ? (D / 32) * C::kPSteps : 0;
   constexpr int kNqk = QK ? (D / 16) * C::kSTiles : 0;
@@ -598,19 +598,18 @@ __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx,
   for (int i = 0; i < kN; ++i) {
     const bf16x8 a = win[i % kWin];
     if (i + kWin < kN) win[i % kWin] = rd(i + kWin);
-    // paired mode: ha / hb say whether the wave keeps the tile's first / second
-    // 32 keys (P V steps 0-1 / 2-3, S^T tile 0 / 1); a skipped half is masked
-    // in the softmax and contributes nothing
+    // paired mode: a half of the tile the wave does not keep is not skipped
+    // on the matrix cores: its scores are masked in the softmax, so its P is
+    // zero and its P V MFMAs add nothing, and a branch per MFMA would cost
+    // registers that the paired variant does not have
     if (i < kNpv) {
       const int s = i / (D / 32), dt = i % (D / 32);
-      if (!PR || ((s >> 1) ? hb : ha))
-        st.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pk[s], st.oacc[dt], 0, 0, 0);
+      st.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.pk[s], st.oacc[dt], 0, 0, 0);
     } else {
       const int j = i - kNpv;
       const int s = j / C::kSTiles, c = j % C::kSTiles;
       const f32x16 acc = s == 0 ? f32x16{} : st.sacc[c];  // S^T starts at 0
-      if (!PR || (c ? hb : ha))
-        st.sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[s], acc, 0, 0, 0);
+      st.sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[s], acc, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -630,10 +629,8 @@ __device__ __forceinline__ void m_phase(WaveState<D, BK>& st, const Ctx& cx, int
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) st.oacc[dt] = st.oacc[dt] * st.o_alpha;
   }
-  if (pv)
-    mfma_stream<D, BK, true, false, PR>(st, cx, vprev, kcur, keeps(cx, ent_prev.a),
-                                        keeps(cx, ent_prev.b));
-  if (qk) mfma_stream<D, BK, false, true, PR>(st, cx, vprev, kcur, keeps(cx, ent.a), keeps(cx, ent.b));
+  if (pv) mfma_stream<D, BK, true, false, PR>(st, cx, vprev, kcur);
+  if (qk) mfma_stream<D, BK, false, true, PR>(st, cx, vprev, kcur);
   __builtin_amdgcn_s_setprio(0);
 }
 
