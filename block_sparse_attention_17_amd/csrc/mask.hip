@@ -14,7 +14,9 @@
 //                   tile per workgroup
 //   select_kernel   one workgroup per row: softmax, radix select of the
 //                   boundary block over the score bits with fixed-point mass
-//                   histograms, kept bitmap, row count
+//                   histograms, kept bitmap, row count (rows of more than
+//                   2048 columns)
+//   select_wave_kernel  the same, one wavefront per row (up to 2048 columns)
 //   scan_kernel     exclusive scan of row counts -> row_ptr
 //   compact_kernel  one wavefront per row: bitmap -> ascending col_idx
 #include <mutex>
@@ -406,6 +408,246 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
 }
 
 // ---------------------------------------------------------------------------
+// The same selection with one wavefront per row (nb <= 64 * PER <= 2048):
+// every reduction, the histograms and the search for the crossing bin stay
+// inside the wavefront, so a row needs no workgroup barrier, and four rows
+// share a workgroup.  Each lane holds the score keys of columns
+// j = lane + 64 k; a key's fixed-point mass is recomputed from it when a pass
+// needs it.  The softmax sums in another order than select_kernel's (lanes,
+// then a butterfly), so Z, and with it a score's last bits, can differ from
+// that kernel's; every step after Z is the same.
+// ---------------------------------------------------------------------------
+constexpr int kWRows = 4;          // rows (wavefronts) per workgroup
+constexpr int kWMaxWords = 64;     // bitmap words of a row: nb <= 2048
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  // butterfly: every lane ends with the same value (the operations commute)
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) v = op(v, __shfl_xor(v, s, 64));
+  return v;
+}
+
+// LDS accesses of one wavefront stay in program order; this keeps the
+// compiler from moving them across the points where other lanes' results
+// are read.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int PER>
+__global__ void __launch_bounds__(64 * kWRows)
+select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
+                   int32_t* __restrict__ counts, int32_t nq, int32_t nb, int32_t heads,
+                   int32_t words, int32_t band, int32_t mode, HeadParams hp, int64_t row0,
+                   int64_t nrows) {
+  __shared__ uint32_t hcnt_s[kWRows][256];
+  __shared__ unsigned long long hmass_s[kWRows][256];
+  __shared__ uint32_t flag_s[kWRows][kWMaxWords];
+  __shared__ uint32_t tie_s[kWRows][kWMaxWords];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rl = (int64_t)blockIdx.x * kWRows + wv;  // row of this launch
+  if (rl >= nrows) return;                               // whole wavefront
+  uint32_t* hcnt = hcnt_s[wv];
+  unsigned long long* hmass = hmass_s[wv];
+  uint32_t* flag = flag_s[wv];
+  uint32_t* tie = tie_s[wv];
+  const int64_t r = row0 + rl;
+  const int32_t i = (int32_t)(r % nq);
+  const int32_t h = (int32_t)((r / nq) % heads);
+  const double* Lr = L + rl * nb;
+
+  // 1. softmax of the row
+  double x[PER];
+  double mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = lane + 64 * k;
+    x[k] = j < nb ? Lr[j] : -INFINITY;
+    mx = fmax(mx, x[k]);
+  }
+  mx = wave_reduce(mx, [](double a, double b) { return fmax(a, b); });
+  double part = 0.0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = lane + 64 * k;
+    x[k] = j < nb ? exp(x[k] - mx) : 0.0;
+    part += x[k];
+  }
+  const double Z = wave_reduce(part, [](double a, double b) { return a + b; });
+  uint64_t key[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) key[k] = (uint64_t)__double_as_longlong(x[k] / Z);
+
+  // 2. targets
+  const double pval = (double)hp.v[h];
+  uint64_t P = 0;
+  int32_t K = nb;
+  bool keep_all;
+  if (mode == 1) {
+    K = max(1, min((int32_t)ceil(pval * (double)nb), nb));
+    keep_all = K >= nb;
+  } else {
+    keep_all = pval >= 1.0;
+    P = (uint64_t)ceil(pval * 9223372036854775808.0);
+  }
+
+  // 3. radix select of the boundary element (as in select_kernel)
+  unsigned long long kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (lane + 64 * k < nb) {
+      kmin = key[k] < kmin ? key[k] : kmin;
+      kmax = key[k] > kmax ? key[k] : kmax;
+    }
+  }
+  kmin = wave_reduce(kmin, [](unsigned long long a, unsigned long long b) { return a < b ? a : b; });
+  kmax = wave_reduce(kmax, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+  int shift = kmin == kmax ? 0 : 64 - __clzll((long long)(kmin ^ kmax));
+  uint64_t prefix = kmax >> shift, A = 0;
+  uint32_t C = 0;
+  bool resolved = false;
+  uint32_t last_cnt = (uint32_t)nb;
+  while (!keep_all && shift > 0) {
+    const int w = shift < 8 ? shift : 8;   // digit width
+    shift -= w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hcnt[4 * lane + q] = 0u;
+      hmass[4 * lane + q] = 0ull;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (lane + 64 * k < nb && (key[k] >> (shift + w)) == prefix) {
+        const uint32_t b = (uint32_t)(key[k] >> shift) & ((1u << w) - 1u);
+        atomicAdd(&hcnt[b], 1u);
+        atomicAdd(&hmass[b], (unsigned long long)to_fixed(__longlong_as_double((long long)key[k])));
+      }
+    }
+    wave_lds_sync();
+    // lane holds positions 4 lane .. 4 lane + 3 of the descending bin order
+    uint64_t ms[4], im[4];
+    uint32_t cs[4], ic[4];
+    uint64_t lm = 0;
+    uint32_t lc = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = 255 - (4 * lane + q);
+      ms[q] = hmass[b];
+      cs[q] = hcnt[b];
+      lm += ms[q];
+      lc += cs[q];
+      im[q] = lm;
+      ic[q] = lc;
+    }
+    uint64_t pm = lm;
+    uint32_t pc = lc;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const uint64_t om = __shfl_up(pm, s, 64);
+      const uint32_t oc = __shfl_up(pc, s, 64);
+      if (lane >= s) {
+        pm += om;
+        pc += oc;
+      }
+    }
+    pm -= lm;  // exclusive over lanes
+    pc -= lc;
+    int first = -1;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      const bool cross = mode == 1 ? (C + pc + ic[q] >= (uint32_t)K) : (A + pm + im[q] >= P);
+      if (cross) first = q;
+    }
+    const unsigned long long bal = __ballot(first >= 0);
+    if (bal == 0ull) {  // total mass below p (rounding): every block is kept
+      keep_all = true;
+      break;
+    }
+    const int src = __ffsll((long long)bal) - 1;
+    const int fq = first < 0 ? 0 : first;
+    const int32_t my_bin = 255 - (4 * lane + fq);
+    const uint32_t my_cnt = cs[fq];
+    const uint32_t my_above_cnt = C + pc + ic[fq] - cs[fq];
+    const uint64_t my_above_mass = A + pm + im[fq] - ms[fq];
+    const int32_t bin = __shfl(my_bin, src, 64);
+    const uint32_t bin_cnt = __shfl(my_cnt, src, 64);
+    C = __shfl(my_above_cnt, src, 64);
+    A = __shfl(my_above_mass, src, 64);
+    prefix = (prefix << w) | (uint64_t)bin;
+    last_cnt = bin_cnt;
+    wave_lds_sync();   // the next pass clears the bins read above
+    if (bin_cnt == 1u) {
+      resolved = true;
+      break;
+    }
+  }
+
+  // 4. kept flags
+  if (lane < words) {
+    flag[lane] = 0u;
+    tie[lane] = 0u;
+  }
+  wave_lds_sync();
+  uint32_t k_tie = 0;
+  if (!keep_all && !resolved) {  // exact ties at tau: lowest indices first
+    if (mode == 1) {
+      k_tie = (uint32_t)K - C;
+    } else {
+      const uint64_t m_tau = to_fixed(__longlong_as_double((long long)prefix));
+      const uint64_t need = P - A;
+      k_tie = (uint32_t)((need + m_tau - 1) / m_tau);
+    }
+    k_tie = max(1u, min(k_tie, last_cnt));
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t j = lane + 64 * k;
+    if (j >= nb) continue;
+    bool kept;
+    if (keep_all) {
+      kept = true;
+    } else {
+      const uint64_t hi = key[k] >> shift;
+      kept = hi > prefix || (hi == prefix && resolved);
+      if (hi == prefix && !resolved) atomicOr(&tie[j >> 5], 1u << (j & 31));
+    }
+    if (kept) atomicOr(&flag[j >> 5], 1u << (j & 31));
+  }
+  // diagonal band |i - j| <= band - 1
+  for (int32_t d = lane - (band - 1); d <= band - 1; d += 64) {
+    const int32_t j = i + d;
+    if (j >= 0 && j < nb) atomicOr(&flag[j >> 5], 1u << (j & 31));
+  }
+  wave_lds_sync();
+  if (k_tie > 0 && lane == 0) {
+    uint32_t taken = 0;
+    for (int32_t w = 0; w < words && taken < k_tie; ++w) {
+      uint32_t f = tie[w];
+      while (f && taken < k_tie) {
+        const uint32_t lowbit = f & (~f + 1u);
+        flag[w] |= lowbit;
+        f ^= lowbit;
+        ++taken;
+      }
+    }
+  }
+  wave_lds_sync();
+
+  // 5. bitmap out + count
+  int32_t c = 0;
+  if (lane < words) {
+    const uint32_t f = flag[lane];
+    bits[r * words + lane] = f;
+    c = __popc(f);
+  }
+  c = wave_reduce(c, [](int32_t a, int32_t b) { return a + b; });
+  if (lane == 0) counts[r] = c;
+}
+
+// ---------------------------------------------------------------------------
 // row_ptr = exclusive scan of counts (one workgroup; rows fit comfortably)
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
@@ -542,8 +784,25 @@ hipError_t mask_rows(const double* qbar, const double* kbar, const int32_t* ksiz
                      tiles_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((uint32_t)rows), blk(kSThreads);
   const int64_t row0 = b0 * nq;
+  if (nb <= 64 * 32) {
+    const dim3 wgrid((uint32_t)((rows + kWRows - 1) / kWRows)), wblk(64 * kWRows);
+    const int per = (nb + 63) / 64;
+#define SVSA_SELECT_WAVE(PER_)                                                                  \
+  hipLaunchKernelGGL(select_wave_kernel<PER_>, wgrid, wblk, 0, stream, L, bits, counts, nq, nb, \
+                     heads, words, band, mode, hp, row0, rows)
+    if (per <= 4) SVSA_SELECT_WAVE(4);
+    else if (per <= 8) SVSA_SELECT_WAVE(8);
+    else if (per <= 12) SVSA_SELECT_WAVE(12);
+    else if (per <= 16) SVSA_SELECT_WAVE(16);
+    else if (per <= 20) SVSA_SELECT_WAVE(20);
+    else if (per <= 24) SVSA_SELECT_WAVE(24);
+    else if (per <= 28) SVSA_SELECT_WAVE(28);
+    else SVSA_SELECT_WAVE(32);
+#undef SVSA_SELECT_WAVE
+    return hipGetLastError();
+  }
+  const dim3 grid((uint32_t)rows), blk(kSThreads);
   if (nb <= kSThreads)
     hipLaunchKernelGGL(select_kernel<1>, grid, blk, 0, stream, L, bits, counts, nq, nb, heads,
                        words, band, mode, hp, row0);
