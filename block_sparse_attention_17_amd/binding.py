@@ -410,6 +410,7 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
 
 
 SVSA_ATTN_OUT_NATURAL = 1
+SVSA_ATTN_POSITIONAL_GROUPS = 2
 
 
 def _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace, natural):
@@ -429,7 +430,8 @@ def _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace, natural):
 def svsa_block_sparse_attn_ex(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, workspace,
                               flags=0, stream=None):
     """svsa_block_sparse_attn with flags; SVSA_ATTN_OUT_NATURAL: out is bf16
-    [B, Hh, N, D] in natural order (the inverse reorder done by the kernel)."""
+    [B, Hh, N, D] in natural order (the inverse reorder done by the kernel);
+    SVSA_ATTN_POSITIONAL_GROUPS: query blocks grouped by position only."""
     import torch
     _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace,
                  natural=bool(int(flags) & SVSA_ATTN_OUT_NATURAL))

@@ -156,7 +156,7 @@ template <typename Sched>
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t nq,
-             int32_t groups, int32_t group_size, Sched sc) {
+             int32_t groups, int32_t group_size, Sched sc, const int32_t* __restrict__ perm) {
   const int32_t ncols = sc.ncols();
   extern __shared__ uint32_t mask[];  // [nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
@@ -166,9 +166,12 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   const int t = threadIdx.x;
   for (int32_t j = t; j < nb; j += kSchedThreads) mask[j] = 0u;
   __syncthreads();
+  // the group's query sub-blocks: consecutive, or as regrouped (perm, with
+  // -1 for empty slots)
+  const int32_t* gp = perm ? perm + item * group_size : nullptr;
   for (int m = 0; m < group_size; ++m) {
-    const int32_t i = g * group_size + m;   // query sub-block
-    if (i >= nq) break;
+    const int32_t i = gp ? gp[m] : g * group_size + m;   // query sub-block
+    if (i < 0 || i >= nq) continue;
     if (sc.qvalid(bh, i) == 0) continue;     // padding only: nothing to compute
     const int64_t row = sc.row(bh, i);
     const int32_t e0 = row_ptr[row], e1 = row_ptr[row + 1];
@@ -187,7 +190,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   const int lane = t & 63, wv = t >> 6;
   // the list starts at the group's own diagonal key sub-block and wraps
   // around, so neighbouring query groups walk the same keys at the same time
-  int32_t j0 = sc.rotation(g * group_size);
+  int32_t j0 = sc.rotation(gp ? max(gp[0], 0) : g * group_size);
   j0 = j0 < nb ? j0 : 0;
   for (int32_t base = 0; base < nb; base += kSchedThreads) {
     const int32_t jj = base + t;
@@ -208,6 +211,145 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     __syncthreads();
   }
   if (t == 0) count[item] = off;
+}
+
+// ---------------------------------------------------------------------------
+// Regrouping of query blocks (fixed-size blocks of one 64-token sub-block):
+// the workgroup of an item streams the union of its four query blocks'
+// lists, and a union entry costs the whole workgroup a key block whether one
+// or four of the blocks keep it, so grouping blocks whose lists overlap
+// shortens the unions.  Per window of kGWin consecutive query blocks of a
+// head, greedily: the lowest block not yet taken anchors a group, then three
+// times the free block of the window that maximises 3 |L n U| - |L| (U: the
+// union of the group so far, L: the candidate's list; ties to the lower
+// block) joins it.  perm[(bh * groups + g) * 4 + m] = the m-th block of group
+// g (-1 for the empty slots of the last group), the groups of a window in
+// anchor order, so that neighbouring items still work on neighbouring blocks.
+// One workgroup per window; thread t holds block t's list as a bitmap in
+// registers, the group's union in registers too.
+// ---------------------------------------------------------------------------
+constexpr int kGWin = 256;   // query blocks per window = threads per workgroup
+
+// Maximum of an unsigned value over the wavefront, returned to every lane:
+// running maxima within each row of 16 lanes (DPP row shifts), then across
+// rows (row broadcasts of lanes 15 and 31); lane 63 holds the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int WORDS>
+__global__ void __launch_bounds__(kGWin)
+group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+             int32_t* __restrict__ perm, int32_t nq, int32_t groups, int32_t windows) {
+  constexpr int kStride = WORDS | 1;   // odd row stride: the row reads hit distinct banks
+  static_assert(WORDS <= 64, "scores must fit 14 bits");
+  __shared__ uint32_t bs[kGWin * kStride];
+  __shared__ uint32_t red[2][kGWin / 64];
+  const int64_t bh = blockIdx.x / windows;
+  const int32_t w0 = (int32_t)(blockIdx.x % windows) * kGWin;
+  const int32_t nrow = min(kGWin, nq - w0);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // the window's bitmaps: thread t builds row t's in its own LDS row.  Loads
+  // go sixteen at a time (independent, so their latencies overlap); bits
+  // collect in a register while the columns stay in one 32-block word (CSR
+  // columns come ascending from the mask stage) and are OR-ed into the row
+  // when the word changes, so unsorted lists are handled too, only slower.
+  for (int w = 0; w < WORDS; ++w) bs[t * kStride + w] = 0u;
+  if (t < nrow) {
+    const int64_t r = bh * nq + w0 + t;
+    const int32_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+    int32_t cur = -1;
+    uint32_t acc = 0u;
+    for (int32_t e = e0; e < e1; e += 16) {
+      int32_t jj[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) jj[u] = e + u < e1 ? col_idx[e + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int32_t j = jj[u];
+        if (j < 0 || j >= 32 * WORDS) continue;
+        if ((j >> 5) != cur) {
+          if (cur >= 0) bs[t * kStride + cur] |= acc;
+          cur = j >> 5;
+          acc = 0u;
+        }
+        acc |= 1u << (j & 31);
+      }
+    }
+    if (cur >= 0) bs[t * kStride + cur] |= acc;
+  }
+  __syncthreads();
+  uint32_t mine[WORDS], un[WORDS];
+  int32_t cnt = 0;
+#pragma unroll
+  for (int w = 0; w < WORDS; ++w) {
+    mine[w] = bs[t * kStride + w];
+    cnt += __popc(mine[w]);
+  }
+  // blocks taken so far, as a 256-bit mask that every thread keeps alike
+  // (every winner is known to all threads), so the anchor scan needs no
+  // barrier; bits past nrow start set
+  static_assert(kGWin == 256, "four 64-bit mask words");
+  auto init_word = [](int32_t n, int32_t lo) {
+    return n >= lo + 64 ? 0ull : (n <= lo ? ~0ull : ~((1ull << (n - lo)) - 1ull));
+  };
+  uint64_t tk0 = init_word(nrow, 0), tk1 = init_word(nrow, 64), tk2 = init_word(nrow, 128),
+           tk3 = init_word(nrow, 192);
+#define SVSA_TAKE(b)                                   \
+  do {                                                 \
+    const uint64_t bit_ = 1ull << ((b) & 63);          \
+    const int32_t x_ = (b) >> 6;                       \
+    tk0 |= x_ == 0 ? bit_ : 0ull;                      \
+    tk1 |= x_ == 1 ? bit_ : 0ull;                      \
+    tk2 |= x_ == 2 ? bit_ : 0ull;                      \
+    tk3 |= x_ == 3 ? bit_ : 0ull;                      \
+  } while (0)
+#define SVSA_TAKEN(b)                                                                     \
+  (((((b) >> 6) == 0 ? tk0 : ((b) >> 6) == 1 ? tk1 : ((b) >> 6) == 2 ? tk2 : tk3) >>     \
+    ((b) & 63)) & 1ull)
+  int32_t* out = perm + (bh * groups + w0 / 4) * 4;   // this window's groups
+  int32_t g = 0;
+  int buf = 0;
+  for (int32_t a = 0; a < nrow; ++a) {
+    if (SVSA_TAKEN(a)) continue;   // uniform: the masks agree
+    SVSA_TAKE(a);
+    if (t == 0) out[4 * g] = w0 + a;
+#pragma unroll
+    for (int w = 0; w < WORDS; ++w) un[w] = bs[a * kStride + w];
+    for (int m = 1; m < 4; ++m) {
+      uint32_t key = 0u;
+      if (!SVSA_TAKEN(t)) {
+        int32_t inter = 0;
+#pragma unroll
+        for (int w = 0; w < WORDS; ++w) inter += __popc(mine[w] & un[w]);
+        // 3 |L n U| - |L| made positive (< 2^14), ties to the lower t
+        const uint32_t score = (uint32_t)(3 * inter - cnt + 32 * WORDS + 1);
+        key = (score << 8) | (uint32_t)(kGWin - 1 - t);
+      }
+      key = wave_max_u32(key);
+      if (lane == 0) red[buf][wave] = key;
+      __syncthreads();
+      uint32_t best = red[buf][0];
+#pragma unroll
+      for (int x = 1; x < kGWin / 64; ++x) best = max(best, red[buf][x]);
+      buf ^= 1;                  // red[buf] is rewritten only after the next barrier
+      const int32_t win = best == 0u ? -1 : (int32_t)(kGWin - 1 - (best & 255u));
+      if (t == 0) out[4 * g + m] = win < 0 ? -1 : w0 + win;
+      if (win < 0) continue;     // uniform: no free block left (the slot stays -1)
+      SVSA_TAKE(win);
+#pragma unroll
+      for (int w = 0; w < WORDS; ++w) un[w] |= bs[win * kStride + w];
+    }
+    ++g;
+  }
+#undef SVSA_TAKE
+#undef SVSA_TAKEN
 }
 
 // Work queues.  The items of one (b, h) all go to one of kQueues queues (one
@@ -825,7 +967,8 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const int32_t* __restrict__ count, int64_t item,
                                          int32_t groups, int32_t nb, int32_t nq,
                                          int32_t npad_q, int32_t npad_k, float c_log2,
-                                         const OutMap& om, const Ring<D, BK>& rg) {
+                                         const OutMap& om, const int32_t* __restrict__ perm,
+                                         const Ring<D, BK>& rg) {
   using C = Cfg<D, BK>;
   constexpr int kS = D / 16, kDT = D / 32;
 
@@ -846,8 +989,10 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
 
   const int64_t bh = item / groups;
   const int32_t gi = (int32_t)(item % groups);
-  const int32_t iq = gi * kQGroup + cx.qb;
-  cx.has_rows = iq < nq;
+  // the wave's query block: consecutive in the group, or as regrouped by
+  // group_kernel (-1: an empty slot of the head's last group)
+  const int32_t iq = perm ? perm[item * kQGroup + cx.qb] : gi * kQGroup + cx.qb;
+  cx.has_rows = iq >= 0 && iq < nq;
   cx.n_list = count[item];
   cx.n_u = PR ? (cx.n_list + 1) / 2 : cx.n_list;            // key tiles streamed
   // intervals 0 .. 2 n_u + 1 carry work; the count is rounded up to whole
@@ -945,7 +1090,8 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
             const int32_t* __restrict__ list, const int32_t* __restrict__ count,
             const int32_t* __restrict__ queue, int32_t* __restrict__ meta, int32_t groups,
-            int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2, OutMap om) {
+            int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2, OutMap om,
+            const int32_t* __restrict__ perm) {
   using C = Cfg<D, BK>;
   __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
       k2[C::kTileBytes], k3[C::kTileBytes];
@@ -974,7 +1120,7 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
     if (item < 0) break;
     run_item<D, BK, PR>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
-                        om, rg);
+                        om, perm, rg);
   }
 }
 
@@ -1003,7 +1149,8 @@ template <int D, int BK, bool PR>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
                        int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
-                       int32_t npad_k, float c_log2, const OutMap& om, hipStream_t stream) {
+                       int32_t npad_k, float c_log2, const OutMap& om, const int32_t* perm,
+                       hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (v) {  // else V^T is already in the workspace (launch_attn_stage_v)
     hipLaunchKernelGGL((vt_kernel<D, PR ? 32 : BK>), dim3((uint32_t)((int64_t)bh * nb)),
@@ -1016,15 +1163,17 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<D, BK, PR>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
-                     count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2, om);
+                     count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2, om, perm);
   return hipGetLastError();
 }
 
 }  // namespace
 
 namespace {
-AttnWs ws_common(int32_t bh, int32_t sub, int32_t nbs_q, int32_t nbs_k, int64_t npad_k) {
+AttnWs ws_common(int32_t bh, int32_t sub, int32_t nbs_q, int32_t nbs_k, int64_t npad_k,
+                 bool groupable) {
   AttnWs w{};
+  w.groupable = groupable;
   w.sub = sub;
   w.nbs = nbs_k;
   w.nbs_q = nbs_q;
@@ -1042,6 +1191,8 @@ AttnWs ws_common(int32_t bh, int32_t sub, int32_t nbs_q, int32_t nbs_k, int64_t 
   off = align_up(off + 3 * kQueues * sizeof(int32_t), 256);
   w.vt_off = off;
   off = align_up(off + (size_t)bh * npad_k * kMaxHeadDim * 2, 256);  // V^T (bf16)
+  w.perm_off = off;
+  if (groupable) off = align_up(off + (size_t)w.items * w.group_size * sizeof(int32_t), 256);
   w.total = off;
   return w;
 }
@@ -1051,7 +1202,7 @@ template <typename Sched>
 hipError_t run_attention(const void* q, const void* k, const void* v, void* out, int32_t bh,
                          int32_t head_dim, const AttnWs& w, const Sched& sc, int32_t npad_q,
                          int32_t npad_k, float scale, const int32_t* row_ptr,
-                         const int32_t* col_idx, void* ws, const OutMap& om,
+                         const int32_t* col_idx, void* ws, const OutMap& om, bool regroup,
                          hipStream_t stream) {
   if (w.items > 0x7fffffff) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -1060,11 +1211,32 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   int32_t* queue = reinterpret_cast<int32_t*>(base + w.queue_off);
   int32_t* meta = reinterpret_cast<int32_t*>(base + w.meta_off);
   __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
+  int32_t* perm = nullptr;
+  hipError_t e = hipSuccess;
+  if (regroup && w.groupable) {
+    perm = reinterpret_cast<int32_t*>(base + w.perm_off);
+    const int32_t windows = (w.nbs_q + kGWin - 1) / kGWin;
+    const dim3 ggrid((uint32_t)((int64_t)bh * windows)), gblk(kGWin);
+    if (w.nbs <= 512)
+      hipLaunchKernelGGL(group_kernel<16>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+                         w.nbs_q, w.groups, windows);
+    else if (w.nbs <= 1024)
+      hipLaunchKernelGGL(group_kernel<32>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+                         w.nbs_q, w.groups, windows);
+    else if (w.nbs <= 1536)
+      hipLaunchKernelGGL(group_kernel<48>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+                         w.nbs_q, w.groups, windows);
+    else
+      hipLaunchKernelGGL(group_kernel<64>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+                         w.nbs_q, w.groups, windows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   hipLaunchKernelGGL(union_kernel<Sched>, dim3((uint32_t)w.items), dim3(kSchedThreads),
                      (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
-                     w.nbs, w.nbs_q, w.groups, w.group_size, sc);
-  hipError_t e = hipGetLastError();
+                     w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
                      w.groups);
@@ -1074,15 +1246,15 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   const float c_log2 = scale * 1.4426950408889634f;
   if (head_dim == 128 && w.sub == 64)
     return launch_attn<128, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, om, stream);
+                                w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
   if (head_dim == 64 && w.sub == 64)
     return launch_attn<64, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                               w.nbs_q, npad_q, npad_k, c_log2, om, stream);
+                               w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
   if (head_dim == 128 && w.sub == 32)
     return launch_attn<128, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, om, stream);
+                                w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
   return launch_attn<64, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
-                             npad_q, npad_k, c_log2, om, stream);
+                             npad_q, npad_k, c_log2, om, perm, stream);
 }
 }  // namespace
 
@@ -1090,13 +1262,16 @@ AttnWs attn_ws_layout(int32_t bh, const Geom& g) {
   const int32_t sub = g.Bk % 64 == 0 ? 64 : 32;
   const int32_t ratio = g.Bk / sub;
   const int32_t nbs = g.pad3d ? g.nb * ratio : (g.N + sub - 1) / sub;
-  AttnWs w = ws_common(bh, sub, nbs, nbs, g.Npad);
+  // query blocks can be regrouped when a block is one 64-token sub-block and
+  // a list fits group_kernel's bitmaps (2048 blocks)
+  const bool groupable = sub == 64 && ratio == 1 && nbs <= 2048;
+  AttnWs w = ws_common(bh, sub, nbs, nbs, g.Npad, groupable);
   w.ratio = ratio;
   return w;
 }
 
 AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t npad_k) {
-  AttnWs w = ws_common(bh, sub, (int32_t)(npad_q / sub), (int32_t)(npad_k / sub), npad_k);
+  AttnWs w = ws_common(bh, sub, (int32_t)(npad_q / sub), (int32_t)(npad_k / sub), npad_k, false);
   w.ratio = 1;
   return w;
 }
@@ -1104,14 +1279,15 @@ AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t n
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    bool natural_out, hipStream_t stream) {
+                                    bool natural_out, bool positional_groups,
+                                    hipStream_t stream) {
   if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = attn_ws_layout(bh, g);
   const GeomSched sc{g, w.ratio, w.sub};
   const OutMap om{g, natural_out ? 1 : 0};
   return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
-                       ws, om, stream);
+                       ws, om, !positional_groups, stream);
 }
 
 hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
@@ -1147,7 +1323,7 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
   const TableSched sc{q_start, q_size, k_start, k_size, nq, nk, sub};
   const OutMap om{};  // tile (cluster) order
   return run_attention(q, k, v, out, bh, head_dim, w, sc, (int32_t)npad_q, (int32_t)npad_k, scale,
-                       row_ptr, col_idx, ws, om, stream);
+                       row_ptr, col_idx, ws, om, false, stream);
 }
 
 }  // namespace svsa

@@ -120,7 +120,8 @@ hipError_t launch_stripe_mask(const Geom& g, int32_t bh, int32_t heads, const in
 
 // Attention workspace layout.
 struct AttnWs {
-  size_t list_off, count_off, queue_off, meta_off, vt_off, total;
+  size_t list_off, count_off, queue_off, meta_off, vt_off, perm_off, total;
+  bool groupable;      // query blocks may be regrouped by list (perm_off holds the groups)
   int64_t items;
   int32_t groups;      // query sub-block groups per (b, h)
   int32_t group_size;  // query sub-blocks per group (256 query rows per group)
@@ -140,7 +141,7 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    bool natural_out, hipStream_t stream);
+                                    bool natural_out, bool positional_groups, hipStream_t stream);
 
 // Clustering (variable-size blocks).
 int64_t cluster_lcap(int32_t N, int32_t C, int32_t align);   // padded layout capacity

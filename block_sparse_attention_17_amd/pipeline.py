@@ -56,17 +56,19 @@ class BlockSparseAttention:
         B.svsa_stripe_mask(self.geom, self.batch, params, self.row_ptr, self.col_idx,
                            self.stripe_ws, band_width=band_width, stream=stream)
 
-    def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None, natural_out=False):
+    def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None, natural_out=False,
+               positional_groups=False):
         """Attention over the CSR lists into ot (tile order), or straight into out
-        (natural order, natural_out=True: the kernel does the inverse reorder)."""
+        (natural order, natural_out=True: the kernel does the inverse reorder).
+        positional_groups=True: query blocks grouped by position only."""
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
+        flags = (B.SVSA_ATTN_OUT_NATURAL if natural_out else 0) | \
+            (B.SVSA_ATTN_POSITIONAL_GROUPS if positional_groups else 0)
         B.svsa_block_sparse_attn_ex(self.qt, self.kt, None, self.out if natural_out else self.ot,
                                     self.geom, scale,
                                     self.row_ptr if row_ptr is None else row_ptr,
                                     self.col_idx if col_idx is None else col_idx,
-                                    self.attn_ws,
-                                    flags=B.SVSA_ATTN_OUT_NATURAL if natural_out else 0,
-                                    stream=stream)
+                                    self.attn_ws, flags=flags, stream=stream)
         return self.out if natural_out else self.ot
 
     def permute_out(self, stream=None):

@@ -782,3 +782,53 @@ def test_tail_keys_masked_wan720():
     rows = [(0, h, i) for h in (0, 1) for i in (0, 1, 500, nb - 2, nb - 1)]
     max_abs, rel = gc.attn_errors(out_bits, orun.attention_blocks(rp, ci, rows), cfg)
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
+
+
+def test_regrouped_query_blocks_cover_every_row():
+    """Query blocks regrouped by their lists (64-token blocks, 270 per head: two
+    windows of the grouping, a last group with two empty slots).  Each row keeps
+    one of five seeded key-block templates plus its diagonal, so rows with equal
+    lists lie far apart and the groups are not consecutive.  The output is
+    prefilled with NaN: every valid row must be written and match the oracle; the
+    positional grouping (SVSA_ATTN_POSITIONAL_GROUPS) agrees to rounding but not
+    bitwise (the regrouped path ran), and a repeated call is bitwise the same."""
+    import block_sparse_attention_17_amd as m
+    from svsa_synth import f32_to_bf16_bits
+    G = m.Geometry(10, 36, 48, 4, 4, 4)          # 17280 tokens, 270 blocks of 64
+    H, D, nb = 2, 128, G.nb
+    assert nb == 270 and nb % 4 == 2
+    rng = np.random.default_rng(83)
+    q, k, v = (rng.standard_normal((1, H, G.N_pad, D)).astype(np.float32) for _ in range(3))
+    bits = [f32_to_bf16_bits(x) for x in (q, k, v)]
+    templates = [sorted(rng.choice(nb, size=24, replace=False).tolist()) for _ in range(5)]
+    which = rng.integers(0, 5, size=(H, nb))
+    lists = [sorted(set(templates[which[h, i]]) | {i}) for h in range(H) for i in range(nb)]
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    ci = np.array([c for cs in lists for c in cs], np.int32)
+    dev = [gc.bits_to_dev(b) for b in bits]
+    rpd = torch.from_numpy(rp.astype(np.int32)).cuda()
+    cid = torch.from_numpy(ci).cuda()
+    ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, G), dtype=torch.uint8, device="cuda")
+
+    def run(flags):
+        out = torch.full_like(dev[0], float("nan"))
+        m.svsa_block_sparse_attn_ex(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D), rpd, cid, ws,
+                                    flags=flags)
+        torch.cuda.synchronize()
+        return gc.dev_to_bits(out)
+
+    gc.log("regrouped attention: 2 heads x 270 blocks")
+    grouped, again = run(0), run(0)
+    positional = run(m.SVSA_ATTN_POSITIONAL_GROUPS)
+    assert np.array_equal(grouped, again)
+    ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))
+    for name, o in (("regrouped", grouped), ("positional", positional)):
+        got = orc.widen(o[:, :, :G.N])
+        assert np.all(np.isfinite(got)), name
+        err = got - ref[:, :, :G.N]
+        max_abs = float(np.abs(err).max())
+        rel = float(np.linalg.norm(err) / np.linalg.norm(ref[:, :, :G.N]))
+        gc.log(f"{name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2, name
+    assert not np.array_equal(grouped[:, :, :G.N], positional[:, :, :G.N])
