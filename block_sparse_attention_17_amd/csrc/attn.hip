@@ -255,6 +255,17 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
   const int32_t w0 = (int32_t)(blockIdx.x % windows) * kGWin;
   const int32_t nrow = min(kGWin, nq - w0);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t* out = perm + (bh * groups + w0 / 4) * 4;   // this window's groups
+  // every row keeps every key block: no grouping changes a union, so the
+  // groups stay positional (the all-kept launch pays no search)
+  {
+    const int64_t r0 = bh * nq + w0;
+    const int64_t kept = (int64_t)row_ptr[r0 + nrow] - row_ptr[r0];
+    if (kept == (int64_t)nrow * nq) {
+      for (int32_t x = t; x < 4 * ((nrow + 3) / 4); x += kGWin) out[x] = x < nrow ? w0 + x : -1;
+      return;
+    }
+  }
   // the window's bitmaps: thread t builds row t's in its own LDS row.  Loads
   // go sixteen at a time (independent, so their latencies overlap); bits
   // collect in a register while the columns stay in one 32-block word (CSR
@@ -313,7 +324,6 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
 #define SVSA_TAKEN(b)                                                                     \
   (((((b) >> 6) == 0 ? tk0 : ((b) >> 6) == 1 ? tk1 : ((b) >> 6) == 2 ? tk2 : tk3) >>     \
     ((b) & 63)) & 1ull)
-  int32_t* out = perm + (bh * groups + w0 / 4) * 4;   // this window's groups
   int32_t g = 0;
   int buf = 0;
   for (int32_t a = 0; a < nrow; ++a) {

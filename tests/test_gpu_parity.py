@@ -832,3 +832,37 @@ def test_regrouped_query_blocks_cover_every_row():
         gc.log(f"{name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
         assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2, name
     assert not np.array_equal(grouped[:, :, :G.N], positional[:, :, :G.N])
+
+
+def test_all_kept_lists_keep_positional_groups():
+    """Every row keeps every key block (the dense launch): the regrouping keeps
+    the positional groups, and the output matches both the oracle and the call
+    with SVSA_ATTN_POSITIONAL_GROUPS bitwise."""
+    import block_sparse_attention_17_amd as m
+    from svsa_synth import f32_to_bf16_bits
+    G = m.Geometry(6, 12, 20, 4, 4, 4)           # 1440 tokens, 23 blocks (partial tail)
+    H, D, nb = 2, 128, G.nb
+    rng = np.random.default_rng(89)
+    bits = [f32_to_bf16_bits(rng.standard_normal((1, H, G.N_pad, D)).astype(np.float32))
+            for _ in range(3)]
+    lists = [list(range(nb)) for _ in range(H * nb)]
+    rp = np.zeros(H * nb + 1, np.int64)
+    rp[1:] = np.cumsum([len(c) for c in lists])
+    ci = np.array([c for cs in lists for c in cs], np.int32)
+    dev = [gc.bits_to_dev(b) for b in bits]
+    rpd = torch.from_numpy(rp.astype(np.int32)).cuda()
+    cid = torch.from_numpy(ci).cuda()
+    ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, G), dtype=torch.uint8, device="cuda")
+    outs = []
+    for flags in (0, m.SVSA_ATTN_POSITIONAL_GROUPS):
+        out = torch.full_like(dev[0], float("nan"))
+        m.svsa_block_sparse_attn_ex(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D), rpd, cid, ws,
+                                    flags=flags)
+        torch.cuda.synchronize()
+        outs.append(gc.dev_to_bits(out)[:, :, :G.N])
+    assert np.array_equal(outs[0], outs[1])
+    ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))[:, :, :G.N]
+    got = orc.widen(outs[0])
+    err = got - ref
+    assert np.abs(err).max() <= gc.MAX_ABS
+    assert np.linalg.norm(err) / np.linalg.norm(ref) <= gc.REL_L2
