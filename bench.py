@@ -61,8 +61,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--positional-groups", action="store_true",
-                    help="query blocks grouped by position only (no regrouping by list)")
+    ap.add_argument("--groups", choices=("auto", "list", "positional"), default="auto",
+                    help="how the attention groups query blocks: by their lists when the "
+                         "work is large enough (auto), always by list, or by position only")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed region, copy 1 GiB device to device once (the "
@@ -403,7 +404,7 @@ def main():
         else:
             bsa.build_stripe_mask(stripe, band_width=cfg.band)
         if marks: marks[2].record(stream)
-        bsa.attend(natural_out=True, positional_groups=args.positional_groups)
+        bsa.attend(natural_out=True, groups=args.groups)
         if marks:
             marks[3].record(stream)
             record.append(marks)
@@ -450,13 +451,13 @@ def main():
         # same kernel with every block kept, same inputs (permute_in left the block means)
         m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
                           bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
-        bsa.attend(natural_out=True, positional_groups=args.positional_groups)
+        bsa.attend(natural_out=True, groups=args.groups)
         torch.cuda.synchronize()
         reps = max(2, min(5, args.steps))
         d_ev = [(ev(), ev()) for _ in range(reps)]
         for a, b in d_ev:
             a.record(stream)
-            bsa.attend(natural_out=True, positional_groups=args.positional_groups)
+            bsa.attend(natural_out=True, groups=args.groups)
             b.record(stream)
         torch.cuda.synchronize()
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in d_ev]))
@@ -481,7 +482,7 @@ def main():
             m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
                               bsa.col_idx, bsa.mask_ws,
                               top_p=np.full(cfg.heads, p_k, np.float32), band_width=cfg.band)
-            bsa.attend(natural_out=True, positional_groups=args.positional_groups)
+            bsa.attend(natural_out=True, groups=args.groups)
             b.record(stream)
             torch.cuda.synchronize()
             s_ms.append(a.elapsed_time(b))

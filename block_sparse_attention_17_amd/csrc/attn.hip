@@ -1212,7 +1212,7 @@ template <typename Sched>
 hipError_t run_attention(const void* q, const void* k, const void* v, void* out, int32_t bh,
                          int32_t head_dim, const AttnWs& w, const Sched& sc, int32_t npad_q,
                          int32_t npad_k, float scale, const int32_t* row_ptr,
-                         const int32_t* col_idx, void* ws, const OutMap& om, bool regroup,
+                         const int32_t* col_idx, void* ws, const OutMap& om, int regroup,
                          hipStream_t stream) {
   if (w.items > 0x7fffffff) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -1223,7 +1223,11 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   __bf16* vt = reinterpret_cast<__bf16*>(base + w.vt_off);
   int32_t* perm = nullptr;
   hipError_t e = hipSuccess;
-  if (regroup && w.groupable) {
+  // regroup: 0 never, 2 always (when groupable), 1 when the work is large
+  // enough to pay for the search (~0.3 ms, against ~1.5% of the attention
+  // time): batch * heads * nb^2 * head_dim >= 2^32 (Wan-720p: 1.7 * 2^32)
+  const bool big = (double)bh * w.nbs * w.nbs * head_dim >= 4294967296.0;
+  if (w.groupable && (regroup == 2 || (regroup == 1 && big))) {
     perm = reinterpret_cast<int32_t*>(base + w.perm_off);
     const int32_t windows = (w.nbs_q + kGWin - 1) / kGWin;
     const dim3 ggrid((uint32_t)((int64_t)bh * windows)), gblk(kGWin);
@@ -1289,15 +1293,14 @@ AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t n
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    bool natural_out, bool positional_groups,
-                                    hipStream_t stream) {
+                                    bool natural_out, int regroup, hipStream_t stream) {
   if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = attn_ws_layout(bh, g);
   const GeomSched sc{g, w.ratio, w.sub};
   const OutMap om{g, natural_out ? 1 : 0};
   return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
-                       ws, om, !positional_groups, stream);
+                       ws, om, regroup, stream);
 }
 
 hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
@@ -1333,7 +1336,7 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
   const TableSched sc{q_start, q_size, k_start, k_size, nq, nk, sub};
   const OutMap om{};  // tile (cluster) order
   return run_attention(q, k, v, out, bh, head_dim, w, sc, (int32_t)npad_q, (int32_t)npad_k, scale,
-                       row_ptr, col_idx, ws, om, false, stream);
+                       row_ptr, col_idx, ws, om, 0, stream);
 }
 
 }  // namespace svsa

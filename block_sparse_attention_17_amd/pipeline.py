@@ -57,13 +57,15 @@ class BlockSparseAttention:
                            self.stripe_ws, band_width=band_width, stream=stream)
 
     def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None, natural_out=False,
-               positional_groups=False):
+               groups="auto"):
         """Attention over the CSR lists into ot (tile order), or straight into out
         (natural order, natural_out=True: the kernel does the inverse reorder).
-        positional_groups=True: query blocks grouped by position only."""
+        groups: "auto" (query blocks grouped by their lists when the work is
+        large enough), "list" (always when the blocks allow it) or "positional"."""
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
-        flags = (B.SVSA_ATTN_OUT_NATURAL if natural_out else 0) | \
-            (B.SVSA_ATTN_POSITIONAL_GROUPS if positional_groups else 0)
+        gflag = {"auto": 0, "list": B.SVSA_ATTN_GROUPS_BY_LIST,
+                 "positional": B.SVSA_ATTN_POSITIONAL_GROUPS}[groups]
+        flags = (B.SVSA_ATTN_OUT_NATURAL if natural_out else 0) | gflag
         B.svsa_block_sparse_attn_ex(self.qt, self.kt, None, self.out if natural_out else self.ot,
                                     self.geom, scale,
                                     self.row_ptr if row_ptr is None else row_ptr,

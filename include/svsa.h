@@ -276,12 +276,13 @@ SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const sv
  *   float32.
  * Scheduling (no effect on what is computed): query blocks are processed in
  *   groups of four that stream the union of their lists.  With 64-token
- *   blocks (Bk = 64) and nb <= 2048 the groups are formed from each head's
- *   lists, per window of 256 consecutive blocks (a greedy choice of blocks
- *   whose lists overlap), so a key block's products are summed in another
- *   order than with positional groups: results agree with those to float32
- *   rounding, not bitwise (SVSA_ATTN_POSITIONAL_GROUPS keeps consecutive
- *   groups).  Either way a call is bitwise reproducible.
+ *   blocks (Bk = 64), nb <= 2048 and batch * heads * nb^2 * head_dim >= 2^32
+ *   (work large enough to pay for the ~0.3 ms search) the groups are formed
+ *   from each head's lists, per window of 256 consecutive blocks (a greedy
+ *   choice of blocks whose lists overlap), so a key block's products are
+ *   summed in another order than with positional groups: results agree with
+ *   those to float32 rounding, not bitwise.  svsa_block_sparse_attn_ex can
+ *   force either grouping.  Either way a call is bitwise reproducible.
  * workspace: at least svsa_attn_workspace_bytes(batch, heads, g) bytes.
  */
 SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
@@ -291,7 +292,11 @@ SVSA_API int svsa_block_sparse_attn(const void* q, const void* k, const void* v,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* Flags of svsa_block_sparse_attn_ex. */
-enum { SVSA_ATTN_OUT_NATURAL = 1, SVSA_ATTN_POSITIONAL_GROUPS = 2 };
+enum {
+  SVSA_ATTN_OUT_NATURAL = 1,
+  SVSA_ATTN_POSITIONAL_GROUPS = 2,
+  SVSA_ATTN_GROUPS_BY_LIST = 4
+};
 
 /*
  * svsa_block_sparse_attn with flags.  flags = 0: the same call.
@@ -300,8 +305,10 @@ enum { SVSA_ATTN_OUT_NATURAL = 1, SVSA_ATTN_POSITIONAL_GROUPS = 2 };
  * reorder of [PSA] Sec. 3.2 done by the attention kernel's stores), so the
  * result equals svsa_tile_permute(inverse = 1) applied to the tile-order
  * output, bitwise.  SVSA_ATTN_POSITIONAL_GROUPS: query blocks grouped four
- * consecutive ones at a time, never by their lists (see "Scheduling" above).
- * Other bits: SVSA_E_INVALID.  Everything else as above.
+ * consecutive ones at a time, never by their lists; SVSA_ATTN_GROUPS_BY_LIST:
+ * grouped by their lists whenever the blocks allow it (64-token blocks,
+ * nb <= 2048), whatever the size of the work (see "Scheduling" above); both
+ * together, or other bits: SVSA_E_INVALID.  Everything else as above.
  */
 SVSA_API int svsa_block_sparse_attn_ex(const void* q, const void* k, const void* v, void* out,
                                        int32_t batch, int32_t heads, int32_t head_dim,

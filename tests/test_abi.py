@@ -104,11 +104,14 @@ def test_attn_ex_rejects_unknown_flags(mod):
     Q, K, O = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
     R, C = ctypes.c_void_p(0x5000000), ctypes.c_void_p(0x6000000)
     f = lib.svsa_block_sparse_attn_ex
-    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 4, ws, need, None) == -1
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 8, ws, need, None) == -1
     assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, -1, ws, need, None) == -1
-    # both defined flags together pass the flag check (then the workspace size fails)
-    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 3, ws, need - 1, None) == -3
-    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 1, ws, need - 1, None) == -3
+    # positional and by-list grouping together contradict each other
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 6, ws, need, None) == -1
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 7, ws, need, None) == -1
+    # valid combinations pass the flag check (then the workspace size fails)
+    for fl in (1, 2, 3, 4, 5):
+        assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, fl, ws, need - 1, None) == -3
     assert f(Q, K, None, ws, 1, 1, 64, g, 0.125, R, C, 1, ws, need, None) == -1   # out in ws
 
 

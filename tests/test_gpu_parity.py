@@ -785,7 +785,8 @@ def test_tail_keys_masked_wan720():
 
 
 def test_regrouped_query_blocks_cover_every_row():
-    """Query blocks regrouped by their lists (64-token blocks, 270 per head: two
+    """Query blocks regrouped by their lists (SVSA_ATTN_GROUPS_BY_LIST: the shape
+    is below the size where the default regroups; 64-token blocks, 270 per head: two
     windows of the grouping, a last group with two empty slots).  Each row keeps
     one of five seeded key-block templates plus its diagonal, so rows with equal
     lists lie far apart and the groups are not consecutive.  The output is
@@ -819,7 +820,7 @@ def test_regrouped_query_blocks_cover_every_row():
         return gc.dev_to_bits(out)
 
     gc.log("regrouped attention: 2 heads x 270 blocks")
-    grouped, again = run(0), run(0)
+    grouped, again = run(m.SVSA_ATTN_GROUPS_BY_LIST), run(m.SVSA_ATTN_GROUPS_BY_LIST)
     positional = run(m.SVSA_ATTN_POSITIONAL_GROUPS)
     assert np.array_equal(grouped, again)
     ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))
@@ -854,13 +855,13 @@ def test_all_kept_lists_keep_positional_groups():
     cid = torch.from_numpy(ci).cuda()
     ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, G), dtype=torch.uint8, device="cuda")
     outs = []
-    for flags in (0, m.SVSA_ATTN_POSITIONAL_GROUPS):
+    for flags in (m.SVSA_ATTN_GROUPS_BY_LIST, m.SVSA_ATTN_POSITIONAL_GROUPS, 0):
         out = torch.full_like(dev[0], float("nan"))
         m.svsa_block_sparse_attn_ex(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D), rpd, cid, ws,
                                     flags=flags)
         torch.cuda.synchronize()
         outs.append(gc.dev_to_bits(out)[:, :, :G.N])
-    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))[:, :, :G.N]
     got = orc.widen(outs[0])
     err = got - ref
