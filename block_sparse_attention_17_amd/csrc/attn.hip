@@ -218,7 +218,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
 // the workgroup of an item streams the union of its four query blocks'
 // lists, and a union entry costs the whole workgroup a key block whether one
 // or four of the blocks keep it, so grouping blocks whose lists overlap
-// shortens the unions.  Per window of kGWin consecutive query blocks of a
+// shortens the unions.  Per window of WIN consecutive query blocks of a
 // head, greedily: the lowest block not yet taken anchors a group, then three
 // times the free block of the window that maximises 3 |L n U| - |L| (U: the
 // union of the group so far, L: the candidate's list; ties to the lower
@@ -226,7 +226,10 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
 // g (-1 for the empty slots of the last group), the groups of a window in
 // anchor order, so that neighbouring items still work on neighbouring blocks.
 // One workgroup per window; thread t holds block t's list as a bitmap in
-// registers, the group's union in registers too.
+// registers, the group's union in registers too.  Windows of 512 blocks
+// shorten the unions of fixed-fraction masks by a further 2.4% (top-p masks:
+// 0.2-0.4%), but each pick then costs ~3x as long (twice the candidates per
+// SIMD), 0.57 instead of 0.25 ms at HunyuanVideo 720p: 256 is the default.
 // ---------------------------------------------------------------------------
 constexpr int kGWin = 256;   // query blocks per window = threads per workgroup
 
@@ -243,17 +246,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-template <int WORDS>
-__global__ void __launch_bounds__(kGWin)
+template <int WORDS, int WIN>
+__global__ void __launch_bounds__(WIN)
 group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ perm, int32_t nq, int32_t groups, int32_t windows) {
-  constexpr int kStride = WORDS | 1;   // odd row stride: the row reads hit distinct banks
-  static_assert(WORDS <= 64, "scores must fit 14 bits");
-  __shared__ uint32_t bs[kGWin * kStride];
-  __shared__ uint32_t red[2][kGWin / 64];
+  // row stride: a whole number of 16-byte units (the union update reads the
+  // winner's row four words at a time, the same address in every lane)
+  constexpr int kStride = WORDS + 4;
+  static_assert(WORDS <= 64 && WORDS % 4 == 0, "scores must fit 14 bits");
+  constexpr int kNW = WIN / 64;          // 64-bit words of the taken mask
+  constexpr int kTB = WIN == 512 ? 9 : 8; // bits of the thread index in a key
+  static_assert(WIN == 256 || WIN == 512, "window of 256 or 512 blocks");
+  __shared__ __align__(16) uint32_t bs[WIN * kStride];
+  __shared__ uint32_t red[2][kNW];
   const int64_t bh = blockIdx.x / windows;
-  const int32_t w0 = (int32_t)(blockIdx.x % windows) * kGWin;
-  const int32_t nrow = min(kGWin, nq - w0);
+  const int32_t w0 = (int32_t)(blockIdx.x % windows) * WIN;
+  const int32_t nrow = min(WIN, nq - w0);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int32_t* out = perm + (bh * groups + w0 / 4) * 4;   // this window's groups
   // every row keeps every key block: no grouping changes a union, so the
@@ -262,38 +270,50 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     const int64_t r0 = bh * nq + w0;
     const int64_t kept = (int64_t)row_ptr[r0 + nrow] - row_ptr[r0];
     if (kept == (int64_t)nrow * nq) {
-      for (int32_t x = t; x < 4 * ((nrow + 3) / 4); x += kGWin) out[x] = x < nrow ? w0 + x : -1;
+      for (int32_t x = t; x < 4 * ((nrow + 3) / 4); x += WIN) out[x] = x < nrow ? w0 + x : -1;
       return;
     }
   }
-  // the window's bitmaps: thread t builds row t's in its own LDS row.  Loads
-  // go sixteen at a time (independent, so their latencies overlap); bits
-  // collect in a register while the columns stay in one 32-block word (CSR
-  // columns come ascending from the mask stage) and are OR-ed into the row
-  // when the word changes, so unsorted lists are handled too, only slower.
-  for (int w = 0; w < WORDS; ++w) bs[t * kStride + w] = 0u;
+  // the window's bitmaps: thread t builds row t's in its own LDS row.  The
+  // row's column indices are read as 16-byte vectors from the 16-byte aligned
+  // address at or below its first entry, sixteen vectors (64 entries) at a
+  // time so that their latencies overlap; a vector that would start before
+  // the array or pass the row's end is read as single words.  Every entry's
+  // bit is OR-ed into the row with an LDS atomic that returns nothing (no
+  // wait; any column order works); entries outside the row OR zero into the
+  // row's padding word.
+  for (int w = 0; w < kStride; ++w) bs[t * kStride + w] = 0u;
   if (t < nrow) {
     const int64_t r = bh * nq + w0 + t;
     const int32_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
-    int32_t cur = -1;
-    uint32_t acc = 0u;
-    for (int32_t e = e0; e < e1; e += 16) {
-      int32_t jj[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) jj[u] = e + u < e1 ? col_idx[e + u] : -1;
+    uint32_t* row = bs + t * kStride;
+    // col_idx + x is 16-byte aligned when (x + mis) % 4 == 0
+    const int32_t mis = (int32_t)((reinterpret_cast<uintptr_t>(col_idx) >> 2) & 3);
+    for (int32_t e = ((e0 + mis) & ~3) - mis; e < e1; e += 64) {
+      int4 v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int32_t j = jj[u];
-        if (j < 0 || j >= 32 * WORDS) continue;
-        if ((j >> 5) != cur) {
-          if (cur >= 0) bs[t * kStride + cur] |= acc;
-          cur = j >> 5;
-          acc = 0u;
+        const int32_t x = e + 4 * u;
+        if (x >= 0 && x + 3 < e1) {
+          v[u] = *reinterpret_cast<const int4*>(col_idx + x);
+        } else {
+          v[u].x = x >= e0 && x < e1 ? col_idx[x] : -1;
+          v[u].y = x + 1 >= e0 && x + 1 < e1 ? col_idx[x + 1] : -1;
+          v[u].z = x + 2 >= e0 && x + 2 < e1 ? col_idx[x + 2] : -1;
+          v[u].w = x + 3 >= e0 && x + 3 < e1 ? col_idx[x + 3] : -1;
         }
-        acc |= 1u << (j & 31);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int32_t x = e + 4 * u + c;
+          const int32_t j = c == 0 ? v[u].x : c == 1 ? v[u].y : c == 2 ? v[u].z : v[u].w;
+          const bool ok = x >= e0 && j >= 0 && j < 32 * WORDS;
+          atomicOr(row + (ok ? (j >> 5) : WORDS), ok ? 1u << (j & 31) : 0u);
+        }
       }
     }
-    if (cur >= 0) bs[t * kStride + cur] |= acc;
   }
   __syncthreads();
   uint32_t mine[WORDS], un[WORDS];
@@ -303,27 +323,29 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     mine[w] = bs[t * kStride + w];
     cnt += __popc(mine[w]);
   }
-  // blocks taken so far, as a 256-bit mask that every thread keeps alike
+  // blocks taken so far, as a WIN-bit mask that every thread keeps alike
   // (every winner is known to all threads), so the anchor scan needs no
-  // barrier; bits past nrow start set
-  static_assert(kGWin == 256, "four 64-bit mask words");
-  auto init_word = [](int32_t n, int32_t lo) {
-    return n >= lo + 64 ? 0ull : (n <= lo ? ~0ull : ~((1ull << (n - lo)) - 1ull));
-  };
-  uint64_t tk0 = init_word(nrow, 0), tk1 = init_word(nrow, 64), tk2 = init_word(nrow, 128),
-           tk3 = init_word(nrow, 192);
+  // barrier; bits past nrow start set.  Indexed only with compile-time word
+  // numbers (selects), so the mask stays in registers.
+  uint64_t tk[kNW];
+#pragma unroll
+  for (int x = 0; x < kNW; ++x) {
+    const int32_t lo = 64 * x;
+    tk[x] = nrow >= lo + 64 ? 0ull : (nrow <= lo ? ~0ull : ~((1ull << (nrow - lo)) - 1ull));
+  }
 #define SVSA_TAKE(b)                                   \
   do {                                                 \
     const uint64_t bit_ = 1ull << ((b) & 63);          \
     const int32_t x_ = (b) >> 6;                       \
-    tk0 |= x_ == 0 ? bit_ : 0ull;                      \
-    tk1 |= x_ == 1 ? bit_ : 0ull;                      \
-    tk2 |= x_ == 2 ? bit_ : 0ull;                      \
-    tk3 |= x_ == 3 ? bit_ : 0ull;                      \
+    _Pragma("unroll") for (int x = 0; x < kNW; ++x) tk[x] |= x_ == x ? bit_ : 0ull; \
   } while (0)
-#define SVSA_TAKEN(b)                                                                     \
-  (((((b) >> 6) == 0 ? tk0 : ((b) >> 6) == 1 ? tk1 : ((b) >> 6) == 2 ? tk2 : tk3) >>     \
-    ((b) & 63)) & 1ull)
+#define SVSA_TAKEN(b)                                                            \
+  ({                                                                             \
+    const int32_t b_ = (b);                                                      \
+    uint64_t w_ = 0ull;                                                          \
+    _Pragma("unroll") for (int x = 0; x < kNW; ++x) w_ = (b_ >> 6) == x ? tk[x] : w_; \
+    (w_ >> (b_ & 63)) & 1ull;                                                    \
+  })
   int32_t g = 0;
   int buf = 0;
   for (int32_t a = 0; a < nrow; ++a) {
@@ -331,30 +353,45 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     SVSA_TAKE(a);
     if (t == 0) out[4 * g] = w0 + a;
 #pragma unroll
-    for (int w = 0; w < WORDS; ++w) un[w] = bs[a * kStride + w];
+    for (int w = 0; w < WORDS; w += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(&bs[a * kStride + w]);
+      un[w] = q.x;
+      un[w + 1] = q.y;
+      un[w + 2] = q.z;
+      un[w + 3] = q.w;
+    }
     for (int m = 1; m < 4; ++m) {
       uint32_t key = 0u;
       if (!SVSA_TAKEN(t)) {
         int32_t inter = 0;
+        // four independent sums (a single chain of dependent adds is latency bound)
+        int32_t i4[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int w = 0; w < WORDS; ++w) inter += __popc(mine[w] & un[w]);
+        for (int w = 0; w < WORDS; ++w) i4[w & 3] += __popc(mine[w] & un[w]);
+        inter = (i4[0] + i4[1]) + (i4[2] + i4[3]);
         // 3 |L n U| - |L| made positive (< 2^14), ties to the lower t
         const uint32_t score = (uint32_t)(3 * inter - cnt + 32 * WORDS + 1);
-        key = (score << 8) | (uint32_t)(kGWin - 1 - t);
+        key = (score << kTB) | (uint32_t)(WIN - 1 - t);
       }
       key = wave_max_u32(key);
       if (lane == 0) red[buf][wave] = key;
       __syncthreads();
       uint32_t best = red[buf][0];
 #pragma unroll
-      for (int x = 1; x < kGWin / 64; ++x) best = max(best, red[buf][x]);
+      for (int x = 1; x < kNW; ++x) best = max(best, red[buf][x]);
       buf ^= 1;                  // red[buf] is rewritten only after the next barrier
-      const int32_t win = best == 0u ? -1 : (int32_t)(kGWin - 1 - (best & 255u));
+      const int32_t win = best == 0u ? -1 : (int32_t)(WIN - 1 - (best & ((1u << kTB) - 1u)));
       if (t == 0) out[4 * g + m] = win < 0 ? -1 : w0 + win;
       if (win < 0) continue;     // uniform: no free block left (the slot stays -1)
       SVSA_TAKE(win);
 #pragma unroll
-      for (int w = 0; w < WORDS; ++w) un[w] |= bs[win * kStride + w];
+      for (int w = 0; w < WORDS; w += 4) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&bs[win * kStride + w]);
+        un[w] |= q.x;
+        un[w + 1] |= q.y;
+        un[w + 2] |= q.z;
+        un[w + 3] |= q.w;
+      }
     }
     ++g;
   }
@@ -1232,16 +1269,16 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
     const int32_t windows = (w.nbs_q + kGWin - 1) / kGWin;
     const dim3 ggrid((uint32_t)((int64_t)bh * windows)), gblk(kGWin);
     if (w.nbs <= 512)
-      hipLaunchKernelGGL(group_kernel<16>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+      hipLaunchKernelGGL((group_kernel<16, kGWin>), ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
                          w.nbs_q, w.groups, windows);
     else if (w.nbs <= 1024)
-      hipLaunchKernelGGL(group_kernel<32>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+      hipLaunchKernelGGL((group_kernel<32, kGWin>), ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
                          w.nbs_q, w.groups, windows);
     else if (w.nbs <= 1536)
-      hipLaunchKernelGGL(group_kernel<48>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+      hipLaunchKernelGGL((group_kernel<48, kGWin>), ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
                          w.nbs_q, w.groups, windows);
     else
-      hipLaunchKernelGGL(group_kernel<64>, ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
+      hipLaunchKernelGGL((group_kernel<64, kGWin>), ggrid, gblk, 0, stream, row_ptr, col_idx, perm,
                          w.nbs_q, w.groups, windows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -696,16 +696,23 @@ scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, i
 }
 
 // ---------------------------------------------------------------------------
-// bitmap -> ascending column indices, one wavefront per row
+// bitmap -> ascending column indices, one wavefront per row.  Per chunk of 64
+// bitmap words (2048 columns) each lane writes the columns of its word into
+// the wavefront's LDS buffer at their place in the row (a scan of the word
+// counts gives it), then the wavefront copies the chunk's indices to col_idx
+// with consecutive lanes on consecutive entries (whole-line stores).
 // ---------------------------------------------------------------------------
 constexpr int kCThreads = 256;
+constexpr int kCChunk = 64 * 32;   // columns per chunk: 64 words of 32
 
 __global__ void __launch_bounds__(kCThreads)
 compact_kernel(const uint32_t* __restrict__ bits, const int32_t* __restrict__ row_ptr,
                int32_t* __restrict__ col_idx, int64_t rows, int32_t words) {
+  __shared__ int32_t stage_s[kCThreads / 64][kCChunk];
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * (kCThreads / 64) + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  if (r >= rows) return;   // whole wavefront
+  int32_t* st = stage_s[threadIdx.x >> 6];
   int32_t out = row_ptr[r];
   const uint32_t* br = bits + r * words;
   for (int32_t w0 = 0; w0 < words; w0 += 64) {
@@ -719,13 +726,17 @@ compact_kernel(const uint32_t* __restrict__ bits, const int32_t* __restrict__ ro
       const int32_t o = __shfl_up(inc, s, 64);
       if (lane >= s) inc += o;
     }
-    int32_t pos = out + inc - c;
+    int32_t pos = inc - c;
     while (f) {
       const int b = __ffs(f) - 1;
-      col_idx[pos++] = w * 32 + b;
+      st[pos++] = w * 32 + b;
       f &= f - 1;
     }
-    out += __shfl(inc, 63, 64);
+    const int32_t tot = __shfl(inc, 63, 64);
+    wave_lds_sync();
+    for (int32_t k = lane; k < tot; k += 64) col_idx[out + k] = st[k];
+    out += tot;
+    wave_lds_sync();   // the next chunk rewrites the buffer
   }
 }
 

@@ -812,9 +812,9 @@ def test_regrouped_query_blocks_cover_every_row():
     cid = torch.from_numpy(ci).cuda()
     ws = torch.empty(m.svsa_attn_workspace_bytes(1, H, G), dtype=torch.uint8, device="cuda")
 
-    def run(flags):
+    def run(flags, c=cid):
         out = torch.full_like(dev[0], float("nan"))
-        m.svsa_block_sparse_attn_ex(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D), rpd, cid, ws,
+        m.svsa_block_sparse_attn_ex(dev[0], dev[1], dev[2], out, G, 1 / np.sqrt(D), rpd, c, ws,
                                     flags=flags)
         torch.cuda.synchronize()
         return gc.dev_to_bits(out)
@@ -823,6 +823,15 @@ def test_regrouped_query_blocks_cover_every_row():
     grouped, again = run(m.SVSA_ATTN_GROUPS_BY_LIST), run(m.SVSA_ATTN_GROUPS_BY_LIST)
     positional = run(m.SVSA_ATTN_POSITIONAL_GROUPS)
     assert np.array_equal(grouped, again)
+    # the grouping reads the lists in 16-byte vectors from aligned addresses:
+    # col_idx 4, 8 and 12 bytes past a 16-byte boundary (neighbours hold
+    # out-of-range values) gives the same output bitwise
+    for shift in (1, 2, 3):
+        big = torch.full((ci.size + 4,), -7, dtype=torch.int32, device="cuda")
+        big[shift: shift + ci.size] = cid
+        view = big[shift: shift + ci.size]
+        assert view.data_ptr() % 16 == 4 * shift
+        assert np.array_equal(run(m.SVSA_ATTN_GROUPS_BY_LIST, view), grouped), shift
     ref = orc.attention(bits[0], bits[1], bits[2], rp, ci, G.N, G.Bk, 1 / np.sqrt(D))
     for name, o in (("regrouped", grouped), ("positional", positional)):
         got = orc.widen(o[:, :, :G.N])
