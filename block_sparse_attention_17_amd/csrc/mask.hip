@@ -48,7 +48,11 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // With ksizes (cluster mode) every logit of key cluster j gets + ln n_j, and
 // empty key clusters get -inf.
-__global__ void __launch_bounds__(kLThreads)
+// At most 128 VGPRs (4 waves per SIMD), so two workgroups share a CU and one's
+// first loads and last stores overlap the other's MFMAs: 0.38 -> 0.33 ms at
+// Wan2.1 720p.  The 16-dim chunk is walked one 4-dim step at a time (not
+// unrolled) to stay within that budget without spills.
+__global__ void __launch_bounds__(kLThreads, 4)
 logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
               const int32_t* __restrict__ ksizes, double* __restrict__ L, int32_t nq,
               int32_t nk, int32_t D, double scale, int32_t tiles_q, int32_t tiles_k) {
@@ -101,7 +105,7 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
     }
     __syncthreads();
     if (dc + kDc < D) load_chunk(dc + kDc);
-#pragma unroll
+#pragma unroll 1
     for (int ks = 0; ks < kDc / 4; ++ks) {
       const int32_t d = 4 * ks + lk;
       double av[2], bv[4];
