@@ -589,12 +589,10 @@ select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
     }
   }
 
-  // 4. kept flags
-  if (lane < words) {
-    flag[lane] = 0u;
-    tie[lane] = 0u;
-  }
-  wave_lds_sync();
+  // 4. kept flags.  A ballot over step k holds columns 64 k .. 64 k + 63,
+  // i.e. bitmap words 2 k (lanes 0-31) and 2 k + 1 (lanes 32-63), so the
+  // words are written whole (2 PER <= kWMaxWords; words past the row's last
+  // hold zeros), with no atomics on shared words.
   uint32_t k_tie = 0;
   if (!keep_all && !resolved) {  // exact ties at tau: lowest indices first
     if (mode == 1) {
@@ -608,18 +606,19 @@ select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int32_t j = lane + 64 * k;
-    if (j >= nb) continue;
-    bool kept;
-    if (keep_all) {
-      kept = true;
-    } else {
-      const uint64_t hi = key[k] >> shift;
-      kept = hi > prefix || (hi == prefix && resolved);
-      if (hi == prefix && !resolved) atomicOr(&tie[j >> 5], 1u << (j & 31));
+    const bool valid = lane + 64 * k < nb;
+    const uint64_t hi = key[k] >> shift;
+    const bool kept = valid && (keep_all || hi > prefix || (hi == prefix && resolved));
+    const bool at_tau = valid && !keep_all && hi == prefix && !resolved;
+    const uint64_t kb = __ballot(kept), tb = __ballot(at_tau);
+    if (lane == 0) {
+      flag[2 * k] = (uint32_t)kb;
+      flag[2 * k + 1] = (uint32_t)(kb >> 32);
+      tie[2 * k] = (uint32_t)tb;
+      tie[2 * k + 1] = (uint32_t)(tb >> 32);
     }
-    if (kept) atomicOr(&flag[j >> 5], 1u << (j & 31));
   }
+  wave_lds_sync();
   // diagonal band |i - j| <= band - 1
   for (int32_t d = lane - (band - 1); d <= band - 1; d += 64) {
     const int32_t j = i + d;
@@ -660,7 +659,9 @@ __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, int64_t rows) {
   __shared__ int32_t wsum[kScanThreads / 64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  constexpr int kPer = 4;
+  // 16 counts per thread per round: a round costs about one global load
+  // latency and two barriers, so fewer, larger rounds (3 at 47,280 rows)
+  constexpr int kPer = 16;
   constexpr int kChunk = kScanThreads * kPer;
   int32_t carry = 0;
   for (int64_t base = 0; base < rows; base += kChunk) {
