@@ -416,7 +416,7 @@ constexpr int kItemCost = 4;        // fixed cost of one item, in key blocks
 __global__ void __launch_bounds__(kQueueThreads)
 queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
              int32_t* __restrict__ meta, int32_t bh_count, int32_t groups) {
-  __shared__ int64_t work[kQueueMaxBh];
+  __shared__ unsigned long long work[kQueueMaxBh];
   __shared__ int32_t qof[kQueueMaxBh];   // queue of each (b, h)
   __shared__ int32_t off[kQueueMaxBh];   // its first position inside that queue
   __shared__ int32_t by_rank[kQueueMaxBh];  // (b, h) pairs, heaviest first
@@ -424,11 +424,13 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   const int t = threadIdx.x;
   const bool by_work = bh_count <= kQueueMaxBh;
   if (by_work) {
-    for (int32_t b = t; b < bh_count; b += kQueueThreads) {
-      int64_t w = 0;
-      for (int32_t g = 0; g < groups; ++g) w += count[(int64_t)b * groups + g] + kItemCost;
-      work[b] = w;
-    }
+    // work per (b, h): every thread adds a strided share of all items (loads
+    // independent and coalesced), integer sums so the order does not matter
+    for (int32_t b = t; b < bh_count; b += kQueueThreads) work[b] = 0ull;
+    __syncthreads();
+    const int64_t n_items = (int64_t)bh_count * groups;
+    for (int64_t it = t; it < n_items; it += kQueueThreads)
+      atomicAdd(&work[it / groups], (unsigned long long)(count[it] + kItemCost));
     __syncthreads();
     for (int32_t b = t; b < bh_count; b += kQueueThreads) {
       int32_t rank = 0;
@@ -439,7 +441,7 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   }
   __syncthreads();
   if (t == 0) {
-    int64_t load[kQueues];
+    unsigned long long load[kQueues];
     for (int x = 0; x < kQueues; ++x) { load[x] = 0; len[x] = 0; }
     for (int32_t k = 0; k < (by_work ? bh_count : 0); ++k) {
       const int32_t b = by_rank[k];

@@ -657,20 +657,31 @@ constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, int64_t rows) {
-  __shared__ int32_t wsum[kScanThreads / 64];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   // 16 counts per thread per round: a round costs about one global load
-  // latency and two barriers, so fewer, larger rounds (3 at 47,280 rows)
+  // latency and a few barriers, so fewer, larger rounds (3 at 47,280 rows).
+  // Counts come in and offsets go out with consecutive threads on consecutive
+  // rows (whole-line accesses), through an LDS buffer in which thread t's 16
+  // consecutive rows are a contiguous run; runs are 17 words apart, so the
+  // run reads and writes of a wavefront hit distinct banks.
   constexpr int kPer = 16;
   constexpr int kChunk = kScanThreads * kPer;
+  __shared__ int32_t buf[kScanThreads * (kPer + 1)];
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  auto at = [](int e) { return (e / kPer) * (kPer + 1) + e % kPer; };   // row e of the chunk
   int32_t carry = 0;
   for (int64_t base = 0; base < rows; base += kChunk) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = q * kScanThreads + t;
+      buf[at(e)] = base + e < rows ? counts[base + e] : 0;
+    }
+    __syncthreads();
     int32_t v[kPer];
     int32_t local = 0;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int64_t r = base + (int64_t)t * kPer + q;
-      v[q] = r < rows ? counts[r] : 0;
+      v[q] = buf[t * (kPer + 1) + q];
       local += v[q];
     }
     int32_t inc = local;
@@ -690,12 +701,17 @@ scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, i
     int32_t run = carry + wbase + inc - local;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int64_t r = base + (int64_t)t * kPer + q;
-      if (r < rows) row_ptr[r] = run;
+      buf[t * (kPer + 1) + q] = run;
       run += v[q];
     }
     carry += total;
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int e = q * kScanThreads + t;
+      if (base + e < rows) row_ptr[base + e] = buf[at(e)];
+    }
+    __syncthreads();   // buf and wsum are rewritten by the next round
   }
   if (t == 0) row_ptr[rows] = carry;
 }
