@@ -22,9 +22,10 @@
 //    wavefront whose block keeps the current key block computes on it.
 //  * The schedule kernel merges the group's CSR rows into that union list,
 //    with a "who keeps it" bit mask per entry.  Items go to one work queue
-//    per XCD, a whole (b, h) per queue, so that the workgroups of one XCD
-//    share the head's key blocks in its L2; a persistent kernel drains its
-//    own XCD's queue first, then the others.
+//    per XCD, a quarter of a (b, h)'s consecutive query groups per queue
+//    entry, so that the workgroups of one XCD share the head's key blocks in
+//    its L2; a persistent kernel drains its own XCD's queue first, then the
+//    others.
 //  * V is transposed once per call (vt_kernel), or once per step straight
 //    from natural-order V (stage_v_kernel, svsa_attn_stage_v), so both MFMA
 //    A operands (K rows for S^T, V^T rows for O^T) are plain 16-byte LDS
@@ -399,58 +400,75 @@ group_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
 #undef SVSA_TAKEN
 }
 
-// Work queues.  The items of one (b, h) all go to one of kQueues queues (one
-// per XCD of the chip) and, inside it, stay in query group order, so the
-// workgroups running on one XCD at a time work on neighbouring query groups of
-// the same head and share its key blocks in that XCD's L2.  (b, h) pairs are
-// taken heaviest first (work = union lengths plus a per-item constant) and
-// each goes to the queue with the least work so far, so every queue ends with
-// its lightest heads and the last items of the launch are short.
+// Work queues.  The query groups of one (b, h) are cut into kHeadParts runs
+// of consecutive groups (units); the items of a unit all go to one of kQueues
+// queues (one per XCD of the chip) and, inside it, stay in query group order,
+// so the workgroups running on one XCD at a time work on neighbouring query
+// groups of the same head and share its key blocks in that XCD's L2.  Units
+// are taken heaviest first (work = union lengths plus a per-item constant)
+// and each goes to the queue with the least work so far, so every queue ends
+// with its lightest units and the last items of the launch are short.  Four
+// parts per head beat whole heads per queue by 3-4% at Wan2.1 and
+// HunyuanVideo 720p (A/B on one box; 3 to 8 parts, or units of 64 groups,
+// within 0.5% of each other): the parts of a head run at the same time on
+// several XCDs, which then share its K / V^T in the Infinity Cache, and the
+// finer units balance the queues' ends.
 // meta = {base[8], len[8], take[8]}; take[] is zeroed here, before every
 // attention launch.
 constexpr int kQueues = 8;
 constexpr int kQueueThreads = 1024;
-constexpr int kQueueMaxBh = 2048;   // (b, h) pairs placed by work; beyond, by bh % 8
+constexpr int kQueueMaxBh = 2048;   // units placed by work; beyond, whole heads by bh % 8
 constexpr int kItemCost = 4;        // fixed cost of one item, in key blocks
+constexpr int kHeadParts = 4;       // units one (b, h) is cut into
 
 __global__ void __launch_bounds__(kQueueThreads)
 queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
-             int32_t* __restrict__ meta, int32_t bh_count, int32_t groups) {
+             int32_t* __restrict__ meta, int32_t bh_count, int32_t groups, int32_t parts) {
+  // units: each (b, h) split into `parts` runs of consecutive query groups
+  // (gpu groups each, the last one shorter), placed like whole heads
   __shared__ unsigned long long work[kQueueMaxBh];
-  __shared__ int32_t qof[kQueueMaxBh];   // queue of each (b, h)
+  __shared__ int32_t qof[kQueueMaxBh];   // queue of each unit
   __shared__ int32_t off[kQueueMaxBh];   // its first position inside that queue
-  __shared__ int32_t by_rank[kQueueMaxBh];  // (b, h) pairs, heaviest first
+  __shared__ int32_t by_rank[kQueueMaxBh];  // units, heaviest first
   __shared__ int32_t len[kQueues], base[kQueues];
   const int t = threadIdx.x;
-  const bool by_work = bh_count <= kQueueMaxBh;
+  parts = max(1, min(parts, groups));
+  const int32_t gpu = (groups + parts - 1) / parts;   // query groups per unit
+  parts = (groups + gpu - 1) / gpu;                    // no empty unit
+  const int32_t units = bh_count * parts;
+  const bool by_work = units <= kQueueMaxBh;
   if (by_work) {
-    // work per (b, h): every thread adds a strided share of all items (loads
+    // work per unit: every thread adds a strided share of all items (loads
     // independent and coalesced), integer sums so the order does not matter
-    for (int32_t b = t; b < bh_count; b += kQueueThreads) work[b] = 0ull;
+    for (int32_t u = t; u < units; u += kQueueThreads) work[u] = 0ull;
     __syncthreads();
     const int64_t n_items = (int64_t)bh_count * groups;
-    for (int64_t it = t; it < n_items; it += kQueueThreads)
-      atomicAdd(&work[it / groups], (unsigned long long)(count[it] + kItemCost));
+    for (int64_t it = t; it < n_items; it += kQueueThreads) {
+      const int32_t u = (int32_t)(it / groups) * parts + (int32_t)(it % groups) / gpu;
+      atomicAdd(&work[u], (unsigned long long)(count[it] + kItemCost));
+    }
     __syncthreads();
-    for (int32_t b = t; b < bh_count; b += kQueueThreads) {
+    for (int32_t u = t; u < units; u += kQueueThreads) {
       int32_t rank = 0;
-      for (int32_t o = 0; o < bh_count; ++o)
-        rank += (work[o] > work[b]) || (work[o] == work[b] && o < b);
-      by_rank[rank] = b;
+      for (int32_t o = 0; o < units; ++o)
+        rank += (work[o] > work[u]) || (work[o] == work[u] && o < u);
+      by_rank[rank] = u;
     }
   }
   __syncthreads();
   if (t == 0) {
     unsigned long long load[kQueues];
     for (int x = 0; x < kQueues; ++x) { load[x] = 0; len[x] = 0; }
-    for (int32_t k = 0; k < (by_work ? bh_count : 0); ++k) {
-      const int32_t b = by_rank[k];
+    for (int32_t k = 0; k < (by_work ? units : 0); ++k) {
+      const int32_t u = by_rank[k];
+      const int32_t part = u % parts;
+      const int32_t n = min(groups, (part + 1) * gpu) - part * gpu;
       int best = 0;
       for (int x = 1; x < kQueues; ++x) if (load[x] < load[best]) best = x;
-      qof[b] = best;
-      off[b] = len[best];
-      len[best] += groups;
-      load[best] += work[b];
+      qof[u] = best;
+      off[u] = len[best];
+      len[best] += n;
+      load[best] += work[u];
     }
     if (!by_work)
       for (int x = 0; x < kQueues; ++x)
@@ -467,9 +485,12 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   const int64_t items = (int64_t)bh_count * groups;
   for (int64_t it = t; it < items; it += kQueueThreads) {
     const int32_t b = (int32_t)(it / groups), g = (int32_t)(it % groups);
-    const int x = by_work ? qof[b] : b % kQueues;
-    const int32_t o = by_work ? off[b] : (b / kQueues) * groups;
-    queue[base[x] + o + g] = (int32_t)it;
+    if (by_work) {
+      const int32_t u = b * parts + g / gpu;
+      queue[base[qof[u]] + off[u] + (g - (g / gpu) * gpu)] = (int32_t)it;
+    } else {
+      queue[base[b % kQueues] + (b / kQueues) * groups + g] = (int32_t)it;
+    }
   }
 }
 
@@ -1292,7 +1313,7 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
-                     w.groups);
+                     w.groups, kHeadParts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
