@@ -433,8 +433,8 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   __shared__ int32_t len[kQueues], base[kQueues];
   const int t = threadIdx.x;
   parts = max(1, min(parts, groups));
-  const int32_t gpu = (groups + parts - 1) / parts;   // query groups per unit
-  parts = (groups + gpu - 1) / gpu;                    // no empty unit
+  const int32_t gpu = max(1, (groups + parts - 1) / parts);   // query groups per unit
+  parts = max(1, (groups + gpu - 1) / gpu);                    // no empty unit
   const int32_t units = bh_count * parts;
   const bool by_work = units <= kQueueMaxBh;
   if (by_work) {
