@@ -49,6 +49,8 @@
 //  * Online softmax in base 2 with lazy rescaling: the running max only moves
 //    (and O, l are only rescaled) when a tile raises it by more than 2^8, so
 //    probabilities stay <= 256 and the O rescale is skipped on most tiles.
+#include <algorithm>
+
 #include "svsa_internal.h"
 
 namespace svsa {
@@ -1312,8 +1314,11 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
                      w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // fewer runs per head when there are many heads, so that every unit is still
+  // placed by its work (kQueueMaxBh units at most)
+  const int32_t parts = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kHeadParts, kQueueMaxBh / bh));
   hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQueueThreads), 0, stream, count, queue, meta, bh,
-                     w.groups, kHeadParts);
+                     w.groups, parts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
