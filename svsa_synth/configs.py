@@ -83,6 +83,9 @@ CONFIGS = {
     # more (batch, head) pairs than the work queues place by measured work
     # (2100 > 2048): a tiny grid, batch 2100, one head
     "manybh": Config("manybh", 12, 2100, 1, 64, (4, 8, 8), (4, 4, 4), "bf16", (0.9,)),
+    # 700 (batch, head) pairs of two query groups each: the work queues cut each
+    # pair into fewer runs (2048 / 700 = 2) so that all 1,400 runs are placed by work
+    "midbh": Config("midbh", 13, 700, 1, 64, (4, 8, 16), (4, 4, 4), "bf16", (0.9,)),
     # two independent samples of the small shape in one call (batch > 1)
     "small_b2": Config("small_b2", 6, 2, 8, 64, (8, 16, 16), (4, 4, 4), "bf16", (0.9,),
                        pe_freq="per_head"),
