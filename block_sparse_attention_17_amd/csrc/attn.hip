@@ -459,22 +459,45 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
   }
   __syncthreads();
   if (t == 0) {
+    // one thread places the units in rank order (each choice depends on the
+    // ones before); queue loads and lengths stay in registers (compile-time
+    // indices only) and the units' ids and work are read eight at a time, so
+    // the loop does not wait on an LDS read per unit
     unsigned long long load[kQueues];
-    for (int x = 0; x < kQueues; ++x) { load[x] = 0; len[x] = 0; }
-    for (int32_t k = 0; k < (by_work ? units : 0); ++k) {
-      const int32_t u = by_rank[k];
-      const int32_t part = u % parts;
-      const int32_t n = min(groups, (part + 1) * gpu) - part * gpu;
-      int best = 0;
-      for (int x = 1; x < kQueues; ++x) if (load[x] < load[best]) best = x;
-      qof[u] = best;
-      off[u] = len[best];
-      len[best] += n;
-      load[best] += work[u];
+    int32_t lenr[kQueues];
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x) { load[x] = 0ull; lenr[x] = 0; }
+    constexpr int kBatch = 8;
+    const int32_t n_place = by_work ? units : 0;
+    for (int32_t k0 = 0; k0 < n_place; k0 += kBatch) {
+      int32_t ub[kBatch];
+      unsigned long long wb[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) ub[j] = k0 + j < n_place ? by_rank[k0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) wb[j] = ub[j] >= 0 ? work[ub[j]] : 0ull;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int32_t u = ub[j];
+        if (u < 0) break;
+        const int32_t part = u % parts;
+        const int32_t n = min(groups, (part + 1) * gpu) - part * gpu;
+        int best = 0;
+        unsigned long long best_load = load[0];
+        int32_t best_len = lenr[0];
+#pragma unroll
+        for (int x = 1; x < kQueues; ++x)
+          if (load[x] < best_load) { best = x; best_load = load[x]; best_len = lenr[x]; }
+        qof[u] = best;
+        off[u] = best_len;
+#pragma unroll
+        for (int x = 0; x < kQueues; ++x)
+          if (x == best) { lenr[x] += n; load[x] += wb[j]; }
+      }
     }
-    if (!by_work)
-      for (int x = 0; x < kQueues; ++x)
-        len[x] = ((bh_count - x + kQueues - 1) / kQueues) * groups;
+#pragma unroll
+    for (int x = 0; x < kQueues; ++x)
+      len[x] = by_work ? lenr[x] : ((bh_count - x + kQueues - 1) / kQueues) * groups;
     int32_t acc = 0;
     for (int x = 0; x < kQueues; ++x) { base[x] = acc; acc += len[x]; }
     for (int x = 0; x < kQueues; ++x) {
