@@ -458,28 +458,28 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
     }
   }
   __syncthreads();
-  if (t == 0) {
-    // one thread places the units in rank order (each choice depends on the
-    // ones before); queue loads and lengths stay in registers (compile-time
-    // indices only) and the units' ids and work are read eight at a time, so
-    // the loop does not wait on an LDS read per unit
+  if (t < 64) {
+    // wavefront 0 places the units in rank order (each choice depends on the
+    // ones before).  Lane j loads unit k0 + j of a batch of 64 (one LDS read
+    // for the batch); the loop takes each unit's values with readlane, so
+    // they, the queue loads and the choice are wave-uniform (scalar unit)
+    // and no step waits on LDS.
+    const int lane = t;
     unsigned long long load[kQueues];
     int32_t lenr[kQueues];
 #pragma unroll
     for (int x = 0; x < kQueues; ++x) { load[x] = 0ull; lenr[x] = 0; }
-    constexpr int kBatch = 8;
     const int32_t n_place = by_work ? units : 0;
-    for (int32_t k0 = 0; k0 < n_place; k0 += kBatch) {
-      int32_t ub[kBatch];
-      unsigned long long wb[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) ub[j] = k0 + j < n_place ? by_rank[k0 + j] : -1;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) wb[j] = ub[j] >= 0 ? work[ub[j]] : 0ull;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int32_t u = ub[j];
-        if (u < 0) break;
+    for (int32_t k0 = 0; k0 < n_place; k0 += 64) {
+      const int32_t kj = k0 + lane;
+      const int32_t uj = kj < n_place ? by_rank[kj] : 0;
+      const unsigned long long wj = kj < n_place ? work[uj] : 0ull;
+      const int32_t cnt = min(64, n_place - k0);
+      for (int32_t j = 0; j < cnt; ++j) {
+        const int32_t u = __builtin_amdgcn_readlane(uj, j);
+        const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)wj, j);
+        const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(wj >> 32), j);
+        const unsigned long long w = ((unsigned long long)whi << 32) | wlo;
         const int32_t part = u % parts;
         const int32_t n = min(groups, (part + 1) * gpu) - part * gpu;
         int best = 0;
@@ -488,16 +488,22 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
 #pragma unroll
         for (int x = 1; x < kQueues; ++x)
           if (load[x] < best_load) { best = x; best_load = load[x]; best_len = lenr[x]; }
-        qof[u] = best;
-        off[u] = best_len;
+        if (lane == 0) {
+          qof[u] = best;
+          off[u] = best_len;
+        }
 #pragma unroll
         for (int x = 0; x < kQueues; ++x)
-          if (x == best) { lenr[x] += n; load[x] += wb[j]; }
+          if (x == best) { lenr[x] += n; load[x] += w; }
       }
     }
+    if (lane == 0) {
 #pragma unroll
-    for (int x = 0; x < kQueues; ++x)
-      len[x] = by_work ? lenr[x] : ((bh_count - x + kQueues - 1) / kQueues) * groups;
+      for (int x = 0; x < kQueues; ++x)
+        len[x] = by_work ? lenr[x] : ((bh_count - x + kQueues - 1) / kQueues) * groups;
+    }
+  }
+  if (t == 0) {
     int32_t acc = 0;
     for (int x = 0; x < kQueues; ++x) { base[x] = acc; acc += len[x]; }
     for (int x = 0; x < kQueues; ++x) {
