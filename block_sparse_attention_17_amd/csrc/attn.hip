@@ -444,10 +444,25 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
     // independent and coalesced), integer sums so the order does not matter
     for (int32_t u = t; u < units; u += kQueueThreads) work[u] = 0ull;
     __syncthreads();
+    // each thread sums a contiguous run of items (one division to find where
+    // it starts, then (b, g, part) advance by one), adding to a unit's work
+    // once per unit it touches
     const int64_t n_items = (int64_t)bh_count * groups;
-    for (int64_t it = t; it < n_items; it += kQueueThreads) {
-      const int32_t u = (int32_t)(it / groups) * parts + (int32_t)(it % groups) / gpu;
-      atomicAdd(&work[u], (unsigned long long)(count[it] + kItemCost));
+    const int64_t per = (n_items + kQueueThreads - 1) / kQueueThreads;
+    const int64_t it0 = min(n_items, (int64_t)t * per), it1 = min(n_items, it0 + per);
+    if (it0 < it1) {
+      int32_t b = (int32_t)(it0 / groups), g = (int32_t)(it0 % groups);
+      int32_t part = g / gpu, next = min(groups, (part + 1) * gpu);
+      unsigned long long acc = 0ull;
+      for (int64_t it = it0; it < it1; ++it) {
+        acc += (unsigned long long)(count[it] + kItemCost);
+        if (++g == next || it + 1 == it1) {   // the unit ends here (or the run does)
+          atomicAdd(&work[b * parts + part], acc);
+          acc = 0ull;
+          if (g == groups) { g = 0; ++b; part = 0; } else { ++part; }
+          next = min(groups, (part + 1) * gpu);
+        }
+      }
     }
     __syncthreads();
     for (int32_t u = t; u < units; u += kQueueThreads) {
@@ -513,14 +528,23 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
     }
   }
   __syncthreads();
+  // every item into its unit's place: contiguous runs per thread again, with
+  // (b, g, part) advanced by one per item
   const int64_t items = (int64_t)bh_count * groups;
-  for (int64_t it = t; it < items; it += kQueueThreads) {
-    const int32_t b = (int32_t)(it / groups), g = (int32_t)(it % groups);
-    if (by_work) {
-      const int32_t u = b * parts + g / gpu;
-      queue[base[qof[u]] + off[u] + (g - (g / gpu) * gpu)] = (int32_t)it;
-    } else {
-      queue[base[b % kQueues] + (b / kQueues) * groups + g] = (int32_t)it;
+  const int64_t per_t = (items + kQueueThreads - 1) / kQueueThreads;
+  const int64_t i0 = min(items, (int64_t)t * per_t), i1 = min(items, i0 + per_t);
+  if (i0 < i1) {
+    int32_t b = (int32_t)(i0 / groups), g = (int32_t)(i0 % groups);
+    int32_t part = g / gpu;
+    for (int64_t it = i0; it < i1; ++it) {
+      if (by_work) {
+        const int32_t u = b * parts + part;
+        queue[base[qof[u]] + off[u] + (g - part * gpu)] = (int32_t)it;
+      } else {
+        queue[base[b % kQueues] + (b / kQueues) * groups + g] = (int32_t)it;
+      }
+      if (++g == groups) { g = 0; ++b; part = 0; }
+      else if (g == (part + 1) * gpu) { ++part; }
     }
   }
 }
