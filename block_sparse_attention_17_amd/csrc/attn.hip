@@ -454,21 +454,33 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
       int32_t b = (int32_t)(it0 / groups), g = (int32_t)(it0 % groups);
       int32_t part = g / gpu, next = min(groups, (part + 1) * gpu);
       unsigned long long acc = 0ull;
-      for (int64_t it = it0; it < it1; ++it) {
-        acc += (unsigned long long)(count[it] + kItemCost);
-        if (++g == next || it + 1 == it1) {   // the unit ends here (or the run does)
-          atomicAdd(&work[b * parts + part], acc);
-          acc = 0ull;
-          if (g == groups) { g = 0; ++b; part = 0; } else { ++part; }
-          next = min(groups, (part + 1) * gpu);
+      for (int64_t c0 = it0; c0 < it1; c0 += 16) {
+        int32_t cb[16];   // sixteen counts in flight at a time
+#pragma unroll
+        for (int j = 0; j < 16; ++j) cb[j] = c0 + j < it1 ? count[c0 + j] : 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t it = c0 + j;
+          if (it >= it1) break;
+          acc += (unsigned long long)(cb[j] + kItemCost);
+          if (++g == next || it + 1 == it1) {   // the unit ends here (or the run does)
+            atomicAdd(&work[b * parts + part], acc);
+            acc = 0ull;
+            if (g == groups) { g = 0; ++b; part = 0; } else { ++part; }
+            next = min(groups, (part + 1) * gpu);
+          }
         }
       }
     }
     __syncthreads();
     for (int32_t u = t; u < units; u += kQueueThreads) {
+      const unsigned long long wu = work[u];
       int32_t rank = 0;
-      for (int32_t o = 0; o < units; ++o)
-        rank += (work[o] > work[u]) || (work[o] == work[u] && o < u);
+#pragma unroll 8
+      for (int32_t o = 0; o < units; ++o) {
+        const unsigned long long wo = work[o];   // same address in every lane
+        rank += (wo > wu) || (wo == wu && o < u);
+      }
       by_rank[rank] = u;
     }
   }
@@ -489,14 +501,15 @@ queue_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ queue,
       const int32_t kj = k0 + lane;
       const int32_t uj = kj < n_place ? by_rank[kj] : 0;
       const unsigned long long wj = kj < n_place ? work[uj] : 0ull;
+      const int32_t pj = uj % parts;                                   // the unit's part
+      const int32_t nj = min(groups, (pj + 1) * gpu) - pj * gpu;       // and its groups
       const int32_t cnt = min(64, n_place - k0);
       for (int32_t j = 0; j < cnt; ++j) {
         const int32_t u = __builtin_amdgcn_readlane(uj, j);
         const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)wj, j);
         const uint32_t whi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(wj >> 32), j);
         const unsigned long long w = ((unsigned long long)whi << 32) | wlo;
-        const int32_t part = u % parts;
-        const int32_t n = min(groups, (part + 1) * gpu) - part * gpu;
+        const int32_t n = __builtin_amdgcn_readlane(nj, j);
         int best = 0;
         unsigned long long best_load = load[0];
         int32_t best_len = lenr[0];
