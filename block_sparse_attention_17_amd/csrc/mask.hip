@@ -10,7 +10,7 @@
 // inside a band of width w when d <= w - 1.
 //
 // Kernels (all float64 arithmetic, all deterministic):
-//   logits_kernel   L = scale * Qbar Kbar^T on the float64 MFMA, 64x64 output
+//   logits_kernel   L = scale * Qbar Kbar^T on the float64 MFMA, 128x128 output
 //                   tile per workgroup
 //   select_kernel   one workgroup per row: softmax, radix select of the
 //                   boundary block over the score bits with fixed-point mass
@@ -69,9 +69,16 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
   const int32_t i0 = (t2 / tiles_k) * kTile, j0 = (t2 % tiles_k) * kTile;
   const double* qb = qbar + bh * nq * D;
   const double* kb = kbar + bh * nk * D;
-  const int32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int32_t wr = 32 * (wave / 2), wc = 64 * (wave % 2);
   const int32_t lr = lane % 16, lk = lane / 16;
+  // 16 x 16 result tiles of this wave that hold any row < nq and column < nk
+  // (a prefix of a and of b): in the last tile row / column of a head the
+  // others are skipped on the matrix cores.  The tiles that run keep the
+  // accumulation order of a full tile, so every stored logit is unchanged.
+  const int32_t na = min(2, max(0, (nq - i0 - wr + 15) / 16));
+  const int32_t nbt = min(4, max(0, (nk - j0 - wc + 15) / 16));
+  const bool full = na == 2 && nbt == 4;
   f64x4 acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -105,19 +112,22 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
     }
     __syncthreads();
     if (dc + kDc < D) load_chunk(dc + kDc);
+    if (na > 0 && nbt > 0) {
 #pragma unroll 1
-    for (int ks = 0; ks < kDc / 4; ++ks) {
-      const int32_t d = 4 * ks + lk;
-      double av[2], bv[4];
+      for (int ks = 0; ks < kDc / 4; ++ks) {
+        const int32_t d = 4 * ks + lk;
+        double av[2], bv[4];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = As[(wr + 16 * a + lr) * kLdsStride + d];
+        for (int a = 0; a < 2; ++a) av[a] = As[(wr + 16 * a + lr) * kLdsStride + d];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[(wc + 16 * b + lr) * kLdsStride + d];
+        for (int b = 0; b < 4; ++b) bv[b] = Bs[(wc + 16 * b + lr) * kLdsStride + d];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+          for (int b = 0; b < 4; ++b)
+            if (full || (a < na && b < nbt))  // wave-uniform
+              acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
