@@ -168,20 +168,174 @@ logits_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar,
 // ---------------------------------------------------------------------------
 constexpr int kSThreads = 256;
 
+// ---------------------------------------------------------------------------
+// Wavefront-wide combines in registers, without LDS: DPP moves within rows of
+// 16 lanes and gfx950's lane-swap permutes across rows and halves.
+//
+// xchg<S>: the value of a partner lane, step S of a butterfly: lane ^ 1 and
+// lane ^ 2 (DPP quad permutes), the mirror lane within 8 and within 16 lanes
+// (DPP row half-mirror and mirror: after the earlier steps every lane of a
+// quad, then of 8 lanes, holds the same partial, so the mirror pairs whole
+// groups as an xor would), lane ^ 16 and lane ^ 32 (permlane swaps).
+// ---------------------------------------------------------------------------
+template <int S>
+__device__ __forceinline__ uint32_t xchg32(uint32_t x, int lane) {
+  if constexpr (S == 0) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  } else if constexpr (S == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  } else if constexpr (S == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  } else if constexpr (S == 3) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);  // row_mirror
+  } else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return lane < 32 ? r[1] : r[0];
+  }
+}
+template <int S, typename T>
+__device__ __forceinline__ T xchg(T v, int lane) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, xchg32<S>(__builtin_bit_cast(uint32_t, v), lane));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = xchg32<S>((uint32_t)u, lane), hi = xchg32<S>((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+// op over the 64 lanes, every lane ends with the result (op commutative and
+// associative on the values combined; a float sum follows this fixed tree).
+// The whole wavefront must be active.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  const int lane = (int)(threadIdx.x & 63);
+  v = op(v, xchg<0>(v, lane));
+  v = op(v, xchg<1>(v, lane));
+  v = op(v, xchg<2>(v, lane));
+  v = op(v, xchg<3>(v, lane));
+  v = op(v, xchg<4>(v, lane));
+  v = op(v, xchg<5>(v, lane));
+  return v;
+}
+// inclusive prefix sum over the 64 lanes (integers): shifts by 1, 2, 4, 8
+// within each row of 16 (DPP row_shr; lanes without a source add 0), then
+// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the
+// total of rows 0-1 into rows 2-3 (row_bcast:31).  The whole wavefront must
+// be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask, typename T>
+__device__ __forceinline__ T dpp_or_zero_t(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_or_zero<kCtrl, kRowMask>(__builtin_bit_cast(uint32_t, v)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_or_zero<kCtrl, kRowMask>((uint32_t)u);
+    const uint32_t hi = dpp_or_zero<kCtrl, kRowMask>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_sum(T v) {
+  v += dpp_or_zero_t<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or_zero_t<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or_zero_t<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or_zero_t<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or_zero_t<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero_t<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// the value of lane src (wave-uniform), read into a scalar register
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int src) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+
 // Fixed-order reduction over the kSThreads (= 4 wavefronts) partial values: a
-// butterfly inside each wavefront (every lane ends with the same value, as
-// the operations are commutative), then the four wavefront results in index
-// order.
+// fixed tree inside each wavefront (wave_reduce; every lane ends with the same
+// value), then the four wavefront results in index order.
 static_assert(kSThreads == 256, "block_reduce combines four wavefronts");
 template <typename T, typename Op>
 __device__ T block_reduce(T v, T* scratch, Op op) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v = op(v, __shfl_xor(v, s, 64));
+  v = wave_reduce(v, op);
   if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
   const T r = op(op(scratch[0], scratch[1]), op(scratch[2], scratch[3]));
   __syncthreads();
   return r;
+}
+
+// e^t for t <= 0 (or -inf), to about one ulp.  Cody and Waite's argument
+// reduction: t = n ln2 + r with n = rint(t / ln2), ln2 split into a high part
+// of 32 significant bits (so n times it is exact for |n| < 2^21) and the
+// remainder, leaving |r| <= ln2 / 2 (about).  e^r is the Taylor series to
+// degree 13 (remainder below 6e-18, 0.05 ulp) by Horner's rule with fused
+// multiply-adds, and e^t = 2^n e^r by ldexp, which rounds once when the result
+// lands among the subnormals.  Arguments below -1100 are clamped there (e^-1100
+// underflows to +0, as does e^-inf).  It needs none of the general exp's
+// overflow and special-case code.  The constants live in scalar registers,
+// set up once per thread (ExpConst), so each Horner step is one instruction.
+struct ExpConst {
+  double c[17];  // 1 / ln 2, ln 2 high part, ln 2 remainder, then 1 / k! for k = 13 .. 0
+  __device__ __forceinline__ ExpConst() {
+    constexpr double kInit[17] = {
+        1.4426950408889634, 0.6931471806019545, -4.2009150726810846e-11,
+        1.0 / 6227020800.0, 1.0 / 479001600.0, 1.0 / 39916800.0, 1.0 / 3628800.0,
+        1.0 / 362880.0, 1.0 / 40320.0, 1.0 / 5040.0, 1.0 / 720.0, 1.0 / 120.0, 1.0 / 24.0,
+        1.0 / 6.0, 0.5, 1.0, 1.0};
+#pragma unroll
+    for (int k = 0; k < 17; ++k) {
+      c[k] = kInit[k];
+      // opaque scalar: keeps the value in an SGPR pair as the fma's addend
+      // instead of re-materialising it into VGPRs at every use
+      asm volatile("" : "+s"(c[k]));
+    }
+  }
+};
+
+__device__ __forceinline__ double exp_nonpos(double t, const ExpConst& e) {
+  t = fmax(t, -1100.0);
+  const double n = rint(t * e.c[0]);
+  double r = fma(-n, e.c[1], t);
+  r = fma(-n, e.c[2], r);
+  double p = e.c[3];
+#pragma unroll
+  for (int k = 4; k < 17; ++k) p = fma(p, r, e.c[k]);
+  return ldexp(p, (int)n);
+}
+
+// x / z for 0 <= x <= z (z >= 1: the softmax denominator), with 1 / z shared
+// by every element of a row: q0 = x r with r = 1 / z correctly rounded, then
+// one correction by the remainder x - q0 z (exact in a fused multiply-add),
+// q = q0 + (x - q0 z) r.  By Markstein's division theorem (r within half an
+// ulp of 1 / z, q0 within one ulp of x / z) q is the correctly rounded
+// quotient, i.e. the same double as x / z, whenever that is a normal number:
+// three instructions per element instead of a dozen.  A nonzero x whose
+// quotient falls below 2^-1000, where the remainder may not be exact, is
+// flagged by div_needs_plain and its caller divides it plainly.
+struct SharedDivisor {
+  double z, r;
+  __device__ __forceinline__ explicit SharedDivisor(double zz) : z(zz), r(1.0 / zz) {}
+};
+__device__ __forceinline__ double div_shared(double x, const SharedDivisor& d) {
+  const double q0 = x * d.r;
+  return fma(fma(-q0, d.z, x), d.r, q0);
+}
+__device__ __forceinline__ bool div_needs_plain(double x, double q) {
+  return x > 0.0 && q < 0x1p-1000;
 }
 
 __device__ __forceinline__ uint64_t to_fixed(double s) {
@@ -227,18 +381,36 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
     mx = fmax(mx, x[k]);
   }
   mx = block_reduce(mx, red, [](double a, double b) { return fmax(a, b); });
+  const ExpConst ec;
   double part = 0.0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int32_t j = t + k * kSThreads;
-    x[k] = j < nb ? exp(x[k] - mx) : 0.0;
+    x[k] = j < nb ? exp_nonpos(x[k] - mx, ec) : 0.0;
     part += x[k];
   }
   const double Z = block_reduce(part, red, [](double a, double b) { return a + b; });
   uint64_t key[PER], mass[PER];
+  const SharedDivisor dz(Z);
+  bool plain = false;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const double sc = x[k] / Z;
+    const double q = div_shared(x[k], dz);
+    plain |= div_needs_plain(x[k], q);
+    x[k] = q;
+  }
+  if (__builtin_amdgcn_ballot_w64(plain) != 0) {
+    // rare (a quotient among the subnormals): those elements again, by plain division
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int32_t j = t + k * kSThreads;
+      const double e = j < nb ? exp_nonpos(Lr[j] - mx, ec) : 0.0;
+      if (div_needs_plain(e, x[k])) x[k] = e / Z;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const double sc = x[k];
     key[k] = (uint64_t)__double_as_longlong(sc);
     mass[k] = to_fixed(sc);
   }
@@ -313,17 +485,8 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
         im[q] = lm;
         ic[q] = lc;
       }
-      uint64_t pm = lm;
-      uint32_t pc = lc;
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) {
-        const uint64_t om = __shfl_up(pm, s, 64);
-        const uint32_t oc = __shfl_up(pc, s, 64);
-        if (lane >= s) {
-          pm += om;
-          pc += oc;
-        }
-      }
+      uint64_t pm = wave_inclusive_sum(lm);   // wavefront 0 only, whole
+      uint32_t pc = wave_inclusive_sum(lc);
       pm -= lm;  // exclusive over lanes
       pc -= lc;
       int first = -1;
@@ -428,19 +591,12 @@ select_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
 // share a workgroup.  Each lane holds the score keys of columns
 // j = lane + 64 k; a key's fixed-point mass is recomputed from it when a pass
 // needs it.  The softmax sums in another order than select_kernel's (lanes,
-// then a butterfly), so Z, and with it a score's last bits, can differ from
+// then one wavefront's fixed tree, against four wavefronts' trees and their
+// results in order), so Z, and with it a score's last bits, can differ from
 // that kernel's; every step after Z is the same.
 // ---------------------------------------------------------------------------
 constexpr int kWRows = 4;          // rows (wavefronts) per workgroup
 constexpr int kWMaxWords = 64;     // bitmap words of a row: nb <= 2048
-
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_reduce(T v, Op op) {
-  // butterfly: every lane ends with the same value (the operations commute)
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) v = op(v, __shfl_xor(v, s, 64));
-  return v;
-}
 
 // LDS accesses of one wavefront stay in program order; this keeps the
 // compiler from moving them across the points where other lanes' results
@@ -451,7 +607,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 template <int PER>
-__global__ void __launch_bounds__(64 * kWRows)
+__global__ void __launch_bounds__(64 * kWRows) __attribute__((amdgpu_waves_per_eu(PER <= 20 ? 3 : 1)))
 select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
                    int32_t* __restrict__ counts, int32_t nq, int32_t nb, int32_t heads,
                    int32_t words, int32_t band, int32_t mode, HeadParams hp, int64_t row0,
@@ -482,17 +638,35 @@ select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
     mx = fmax(mx, x[k]);
   }
   mx = wave_reduce(mx, [](double a, double b) { return fmax(a, b); });
+  const ExpConst ec;
   double part = 0.0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int32_t j = lane + 64 * k;
-    x[k] = j < nb ? exp(x[k] - mx) : 0.0;
+    x[k] = j < nb ? exp_nonpos(x[k] - mx, ec) : 0.0;
     part += x[k];
   }
   const double Z = wave_reduce(part, [](double a, double b) { return a + b; });
   uint64_t key[PER];
+  const SharedDivisor dz(Z);
+  bool plain = false;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) key[k] = (uint64_t)__double_as_longlong(x[k] / Z);
+  for (int k = 0; k < PER; ++k) {
+    const double q = div_shared(x[k], dz);
+    plain |= div_needs_plain(x[k], q);
+    x[k] = q;
+  }
+  if (__builtin_amdgcn_ballot_w64(plain) != 0) {
+    // rare (a quotient among the subnormals): those elements again, by plain division
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int32_t j = lane + 64 * k;
+      const double e = j < nb ? exp_nonpos(Lr[j] - mx, ec) : 0.0;
+      if (div_needs_plain(e, x[k])) x[k] = e / Z;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) key[k] = (uint64_t)__double_as_longlong(x[k]);
 
   // 2. targets
   const double pval = (double)hp.v[h];
@@ -556,17 +730,8 @@ select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
       im[q] = lm;
       ic[q] = lc;
     }
-    uint64_t pm = lm;
-    uint32_t pc = lc;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const uint64_t om = __shfl_up(pm, s, 64);
-      const uint32_t oc = __shfl_up(pc, s, 64);
-      if (lane >= s) {
-        pm += om;
-        pc += oc;
-      }
-    }
+    uint64_t pm = wave_inclusive_sum(lm);
+    uint32_t pc = wave_inclusive_sum(lc);
     pm -= lm;  // exclusive over lanes
     pc -= lc;
     int first = -1;
@@ -586,10 +751,10 @@ select_wave_kernel(const double* __restrict__ L, uint32_t* __restrict__ bits,
     const uint32_t my_cnt = cs[fq];
     const uint32_t my_above_cnt = C + pc + ic[fq] - cs[fq];
     const uint64_t my_above_mass = A + pm + im[fq] - ms[fq];
-    const int32_t bin = __shfl(my_bin, src, 64);
-    const uint32_t bin_cnt = __shfl(my_cnt, src, 64);
-    C = __shfl(my_above_cnt, src, 64);
-    A = __shfl(my_above_mass, src, 64);
+    const int32_t bin = lane_value(my_bin, src);
+    const uint32_t bin_cnt = lane_value(my_cnt, src);
+    C = lane_value(my_above_cnt, src);
+    A = lane_value(my_above_mass, src);
     prefix = (prefix << w) | (uint64_t)bin;
     last_cnt = bin_cnt;
     wave_lds_sync();   // the next pass clears the bins read above
@@ -694,12 +859,7 @@ scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr, i
       v[q] = buf[t * (kPer + 1) + q];
       local += v[q];
     }
-    int32_t inc = local;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const int32_t o = __shfl_up(inc, s, 64);
-      if (lane >= s) inc += o;
-    }
+    const int32_t inc = wave_inclusive_sum(local);
     if (lane == 63) wsum[wv] = inc;
     __syncthreads();
     int32_t wbase = 0, total = 0;
@@ -750,20 +910,14 @@ compact_kernel(const uint32_t* __restrict__ bits, const int32_t* __restrict__ ro
     const int32_t w = w0 + lane;
     uint32_t f = w < words ? br[w] : 0u;
     const int32_t c = __popc(f);
-    // inclusive wave scan of c
-    int32_t inc = c;
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const int32_t o = __shfl_up(inc, s, 64);
-      if (lane >= s) inc += o;
-    }
+    const int32_t inc = wave_inclusive_sum(c);
     int32_t pos = inc - c;
     while (f) {
       const int b = __ffs(f) - 1;
       st[pos++] = w * 32 + b;
       f &= f - 1;
     }
-    const int32_t tot = __shfl(inc, 63, 64);
+    const int32_t tot = lane_value(inc, 63);
     wave_lds_sync();
     for (int32_t k = lane; k < tot; k += 64) col_idx[out + k] = st[k];
     out += tot;

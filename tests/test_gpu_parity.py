@@ -197,12 +197,14 @@ def test_block_mask_equal_and_few_distinct_scores(nb):
     """Crafted block summaries whose rows hold exactly equal scores (no radix
     pass; the tie rule alone decides), two or three distinct values (long
     common key prefixes, ties at the boundary), scores that underflow to zero,
-    and many ties at row-dependent scales: the lists equal the oracle's up to
-    the near-threshold rule, in top-p and fixed-fraction modes."""
+    many ties at row-dependent scales, and rows whose probabilities past the
+    first ten blocks are subnormal (the normalisation's plain-division path,
+    and a fixed-fraction boundary among subnormal keys): the lists equal the
+    oracle's up to the near-threshold rule, in top-p and fixed-fraction modes."""
     import types
     import torch
     from block_sparse_attention_17_amd import binding as B
-    H, D = 5, 16
+    H, D = 6, 16
     scale = 1.0 / np.sqrt(D)
     j = np.arange(nb)
     logit = np.zeros((H, nb))
@@ -210,6 +212,7 @@ def test_block_mask_equal_and_few_distinct_scores(nb):
     logit[2] = np.where(j % 5 == 0, 3.0, np.where(j % 7 == 0, 1.5, 0.0))
     logit[3] = np.where(j < 40, 0.0, -1000.0)          # exp underflows to 0.0
     logit[4] = np.round(np.random.default_rng(11).normal(size=nb) * 2) / 2
+    logit[5] = np.where(j < 10, 0.0, -712.0 - 30.0 * j / nb)   # e^-712 .. e^-742: subnormal
     qbar = np.zeros((1, H, nb, D))
     kbar = np.zeros((1, H, nb, D))
     qbar[0, :, :, 0] = 1.0 / scale
