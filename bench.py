@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--step-pairs", choices=("auto", "on", "off"), default="auto",
+                    help="union lists walked in steps of one or two key blocks with disjoint "
+                         "keepers (auto: in fixed keep-fraction mode)")
     ap.add_argument("--groups", choices=("auto", "list", "positional"), default="auto",
                     help="how the attention groups query blocks: by their lists when the "
                          "work is large enough (auto), always by list, or by position only")
@@ -384,6 +387,7 @@ def main():
     tp = None if args.fixed else np.full(cfg.heads, top_p, np.float32)
     kf = inp.keep_frac if args.fixed else None
     stream = torch.cuda.current_stream()
+    step_pairs = args.step_pairs == "on" or (args.step_pairs == "auto" and args.fixed)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     # Q and K are reordered and pooled in one pass each; V is reordered straight
@@ -404,7 +408,7 @@ def main():
         else:
             bsa.build_stripe_mask(stripe, band_width=cfg.band)
         if marks: marks[2].record(stream)
-        bsa.attend(natural_out=True, groups=args.groups)
+        bsa.attend(natural_out=True, groups=args.groups, step_pairs=step_pairs)
         if marks:
             marks[3].record(stream)
             record.append(marks)
@@ -451,13 +455,13 @@ def main():
         # same kernel with every block kept, same inputs (permute_in left the block means)
         m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr, bsa.col_idx,
                           bsa.mask_ws, top_p=np.ones(cfg.heads, np.float32), band_width=1)
-        bsa.attend(natural_out=True, groups=args.groups)
+        bsa.attend(natural_out=True, groups=args.groups, step_pairs=step_pairs)
         torch.cuda.synchronize()
         reps = max(2, min(5, args.steps))
         d_ev = [(ev(), ev()) for _ in range(reps)]
         for a, b in d_ev:
             a.record(stream)
-            bsa.attend(natural_out=True, groups=args.groups)
+            bsa.attend(natural_out=True, groups=args.groups, step_pairs=step_pairs)
             b.record(stream)
         torch.cuda.synchronize()
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in d_ev]))
@@ -482,7 +486,7 @@ def main():
             m.svsa_block_mask(bsa.qbar, bsa.kbar, 1 / sqrt(cfg.head_dim), bsa.row_ptr,
                               bsa.col_idx, bsa.mask_ws,
                               top_p=np.full(cfg.heads, p_k, np.float32), band_width=cfg.band)
-            bsa.attend(natural_out=True, groups=args.groups)
+            bsa.attend(natural_out=True, groups=args.groups, step_pairs=step_pairs)
             b.record(stream)
             torch.cuda.synchronize()
             s_ms.append(a.elapsed_time(b))
@@ -533,7 +537,8 @@ def main():
                          f"{cfg.batch}, " + ("PSA stripe masks (seeded per-head parameters "
                                              "from PSA's Wan 2.1 search ranges)" if args.stripe
                                              else "fixed keep-fraction mode" if args.fixed
-                                             else f"top-p {top_p}") + f", band {cfg.band}"),
+                                             else f"top-p {top_p}") + f", band {cfg.band}"
+                         + (", union lists in step pairs" if step_pairs else "")),
             "global_batch": cfg.batch,
             "seq_len": cfg.N,
             "parallelism": "single GPU",

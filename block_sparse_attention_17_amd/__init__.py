@@ -18,7 +18,7 @@ from .binding import (EXPORTED, Geometry, SvsaError, SVSA_BF16, SVSA_F32, librar
                       svsa_stripe_mask_workspace_bytes, svsa_tile_permute, svsa_tile_permute_pool,
                       svsa_attn_stage_v, svsa_block_sparse_attn_ex,
                       SVSA_ATTN_OUT_NATURAL, SVSA_ATTN_POSITIONAL_GROUPS,
-                      SVSA_ATTN_GROUPS_BY_LIST, svsa_version)
+                      SVSA_ATTN_GROUPS_BY_LIST, SVSA_ATTN_STEP_PAIRS, svsa_version)
 from .pipeline import BlockSparseAttention, ClusteredAttention
 
 __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "library",
@@ -28,7 +28,7 @@ __all__ = ["EXPORTED", "Geometry", "SvsaError", "SVSA_BF16", "SVSA_F32", "librar
            "svsa_snr_top_p", "svsa_status_string", "svsa_stripe_mask",
            "svsa_stripe_mask_workspace_bytes", "svsa_tile_permute", "svsa_tile_permute_pool",
            "svsa_attn_stage_v", "svsa_block_sparse_attn_ex", "SVSA_ATTN_OUT_NATURAL",
-           "SVSA_ATTN_POSITIONAL_GROUPS", "SVSA_ATTN_GROUPS_BY_LIST",
+           "SVSA_ATTN_POSITIONAL_GROUPS", "SVSA_ATTN_GROUPS_BY_LIST", "SVSA_ATTN_STEP_PAIRS",
            "svsa_version",
            "BlockSparseAttention", "ClusteredAttention", "svsa_cluster_attn",
            "svsa_cluster_attn_workspace_bytes", "svsa_cluster_capacity", "svsa_cluster_layout",

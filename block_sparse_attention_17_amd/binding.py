@@ -412,6 +412,7 @@ def svsa_block_sparse_attn(q, k, v, out, geom, softmax_scale, row_ptr, col_idx, 
 SVSA_ATTN_OUT_NATURAL = 1
 SVSA_ATTN_POSITIONAL_GROUPS = 2
 SVSA_ATTN_GROUPS_BY_LIST = 4
+SVSA_ATTN_STEP_PAIRS = 8
 
 
 def _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace, natural):
@@ -433,7 +434,9 @@ def svsa_block_sparse_attn_ex(q, k, v, out, geom, softmax_scale, row_ptr, col_id
     """svsa_block_sparse_attn with flags; SVSA_ATTN_OUT_NATURAL: out is bf16
     [B, Hh, N, D] in natural order (the inverse reorder done by the kernel);
     SVSA_ATTN_POSITIONAL_GROUPS: query blocks grouped by position only;
-    SVSA_ATTN_GROUPS_BY_LIST: grouped by their lists whatever the size."""
+    SVSA_ATTN_GROUPS_BY_LIST: grouped by their lists whatever the size;
+    SVSA_ATTN_STEP_PAIRS: the union list walked in steps of one or two key
+    blocks with disjoint keepers (64-token blocks)."""
     import torch
     _attn_shapes(q, k, v, out, geom, row_ptr, col_idx, workspace,
                  natural=bool(int(flags) & SVSA_ATTN_OUT_NATURAL))

@@ -451,11 +451,13 @@ int attn_impl(const void* q, const void* k, const void* v, void* out, int32_t ba
               int32_t heads, int32_t head_dim, const svsa_geom* gin, float softmax_scale,
               const int32_t* row_ptr, const int32_t* col_idx, int32_t flags, void* workspace,
               size_t ws_bytes, void* stream) {
-  if (flags & ~(SVSA_ATTN_OUT_NATURAL | SVSA_ATTN_POSITIONAL_GROUPS | SVSA_ATTN_GROUPS_BY_LIST))
+  if (flags & ~(SVSA_ATTN_OUT_NATURAL | SVSA_ATTN_POSITIONAL_GROUPS | SVSA_ATTN_GROUPS_BY_LIST |
+                SVSA_ATTN_STEP_PAIRS))
     return SVSA_E_INVALID;
   if ((flags & SVSA_ATTN_POSITIONAL_GROUPS) && (flags & SVSA_ATTN_GROUPS_BY_LIST))
     return SVSA_E_INVALID;
   const bool natural = (flags & SVSA_ATTN_OUT_NATURAL) != 0;
+  const bool steps = (flags & SVSA_ATTN_STEP_PAIRS) != 0;
   const int regroup = (flags & SVSA_ATTN_POSITIONAL_GROUPS) ? 0
                       : (flags & SVSA_ATTN_GROUPS_BY_LIST) ? 2 : 1;
   if (!(al(q, 16) && al(k, 16) && al(v, 16) && al(out, 16) && al(row_ptr, 4) && al(col_idx, 4) &&
@@ -485,7 +487,8 @@ int attn_impl(const void* q, const void* k, const void* v, void* out, int32_t ba
   if (overlaps(out, obytes, workspace, ws_bytes)) return SVSA_E_INVALID;
   return from_hip(svsa::launch_block_sparse_attn(q, k, v, out, (int32_t)bh, head_dim, g,
                                                  softmax_scale, row_ptr, col_idx, workspace,
-                                                 natural, regroup, static_cast<hipStream_t>(stream)));
+                                                 natural, regroup, steps,
+                                                 static_cast<hipStream_t>(stream)));
 }
 }  // namespace
 

@@ -155,14 +155,44 @@ struct TableSched {
   __device__ int32_t rotation(int32_t) const { return 0; }
 };
 
+// Step lists.  With groups of four 64-token query sub-blocks (one per SIMD)
+// the attention kernel walks STEPS of two list entries (a, b): a step costs
+// one key block's time, and each wavefront works on the entry its sub-block
+// keeps.  Two entries share a step when their keep masks are disjoint, so a
+// union entry that only some sub-blocks keep no longer leaves the other
+// SIMDs idle for a whole key block.  On the oracle's masks this takes the
+// steps of a Wan2.1-720p top-p 0.9 head group to 0.89 of its union entries
+// (kept pairs per step and sub-block 0.86 -> 0.97), and in HunyuanVideo-720p
+// fixed-fraction mode to 0.68 (0.61 -> 0.91).
+//
+// Pairing: entries are bucketed by mask (1..15) and ranked in list order;
+// the rules below, in order, pair the k-th free entry of the first bucket
+// with the k-th free entry of the second: three keepers with the other one,
+// two with the other two, two with one of the other two, one with one.  The
+// first entry of a pair heads the step and keeps its place in the list order;
+// the second leaves the list.  Ranks follow the list order, so the pairing is
+// deterministic.
+constexpr int kPairRules = 25;
+constexpr int8_t kPairRule[kPairRules][2] = {
+    {7, 8},  {11, 4}, {13, 2}, {14, 1},                                     // 3 + 1
+    {3, 12}, {5, 10}, {6, 9},                                               // 2 + 2
+    {3, 4},  {3, 8},  {5, 2},  {5, 8}, {6, 1}, {6, 8}, {9, 2}, {9, 4},      // 2 + 1
+    {10, 1}, {10, 4}, {12, 1}, {12, 2},
+    {1, 2},  {1, 4},  {1, 8},  {2, 4}, {2, 8}, {4, 8}};                     // 1 + 1
+constexpr int32_t kPairMaxNb = 4096;   // staging in LDS: 3 words per key sub-block
+
+// out_mode: 0 = one word per entry (paired 32-key tiles read entries two at a
+// time), 1 = steps {entry, 0}, 2 = steps paired as above (nb <= kPairMaxNb).
 template <typename Sched>
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t nq,
-             int32_t groups, int32_t group_size, Sched sc, const int32_t* __restrict__ perm) {
+             int32_t groups, int32_t group_size, Sched sc, const int32_t* __restrict__ perm,
+             int32_t out_mode) {
   const int32_t ncols = sc.ncols();
-  extern __shared__ uint32_t mask[];  // [nb]
+  extern __shared__ uint32_t mask[];  // [nb]; out_mode 2: then entw[nb], pos[nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
+  __shared__ int32_t s_base[16], s_rule[kPairRules][3];
   const int64_t item = blockIdx.x;
   const int64_t bh = item / groups;
   const int32_t g = (int32_t)(item % groups);
@@ -188,7 +218,8 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     }
   }
   __syncthreads();
-  int32_t* out = list + item * nb;
+  int32_t* out = list + item * (out_mode == 0 ? nb : 2 * nb);
+  uint32_t* entw = mask + nb;   // out_mode 2: the list in LDS
   int32_t off = 0;
   const int lane = t & 63, wv = t >> 6;
   // the list starts at the group's own diagonal key sub-block and wraps
@@ -208,12 +239,108 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
       if (k < wv) wbase += wave_tot[k];
       tot += wave_tot[k];
     }
-    if (m != 0u)
-      out[off + wbase + before] = j | (sc.kvalid(bh, j) << 13) | (int32_t)(m << 24);
+    if (m != 0u) {
+      const int32_t word = j | (sc.kvalid(bh, j) << 13) | (int32_t)(m << 24);
+      const int32_t at = off + wbase + before;
+      if (out_mode == 0) {
+        out[at] = word;
+      } else if (out_mode == 1) {
+        out[2 * at] = word;
+        out[2 * at + 1] = 0;
+      } else {
+        entw[at] = (uint32_t)word;
+      }
+    }
     off += tot;
     __syncthreads();
   }
-  if (t == 0) count[item] = off;
+  if (out_mode != 2) {
+    if (t == 0) count[item] = off;
+    return;
+  }
+
+  // ---- pairing (out_mode 2); mask[] is free from here on
+  const int32_t n = off;
+  uint32_t* key = mask;          // (bucket << 16) | rank in the bucket
+  uint32_t* pos = mask + 2 * nb; // entry index by (bucket start + rank)
+  if (wv == 0) {
+    int32_t cnt[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) cnt[b] = 0;
+    for (int32_t c0 = 0; c0 < n; c0 += 64) {
+      const int32_t e = c0 + lane;
+      const uint32_t m = e < n ? (entw[e] >> 24) & 15u : 0u;
+      int32_t rank = 0;
+#pragma unroll
+      for (int b = 1; b < 16; ++b) {
+        const unsigned long long bal = __ballot(m == (uint32_t)b);
+        if (m == (uint32_t)b) rank = cnt[b] + __popcll(bal & ((1ull << lane) - 1ull));
+        cnt[b] += __popcll(bal);
+      }
+      if (e < n) key[e] = (m << 16) | (uint32_t)rank;
+    }
+    if (lane == 0) {
+      int32_t rem[16], base = 0;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        s_base[b] = base;
+        base += cnt[b];
+        rem[b] = cnt[b];
+      }
+#pragma unroll
+      for (int r = 0; r < kPairRules; ++r) {
+        const int c1 = kPairRule[r][0], c2 = kPairRule[r][1];
+        const int32_t k = min(rem[c1], rem[c2]);
+        s_rule[r][0] = k;
+        s_rule[r][1] = cnt[c1] - rem[c1];
+        s_rule[r][2] = cnt[c2] - rem[c2];
+        rem[c1] -= k;
+        rem[c2] -= k;
+      }
+    }
+  }
+  __syncthreads();
+  for (int32_t e = t; e < n; e += kSchedThreads) {
+    const uint32_t k = key[e];
+    pos[s_base[k >> 16] + (int32_t)(k & 0xffffu)] = (uint32_t)e;
+  }
+  __syncthreads();
+  // steps: the heads in list order, each with its partner (or none)
+  int32_t soff = 0;
+  for (int32_t base = 0; base < n; base += kSchedThreads) {
+    const int32_t e = base + t;
+    bool head = e < n;
+    int32_t partner = -1;
+    if (e < n) {
+      const uint32_t k = key[e];
+      const int c = (int)(k >> 16);
+      const int32_t r = (int32_t)(k & 0xffffu);
+#pragma unroll
+      for (int ri = 0; ri < kPairRules; ++ri) {
+        const int c1 = kPairRule[ri][0], c2 = kPairRule[ri][1];
+        const int32_t kk = s_rule[ri][0], sa = s_rule[ri][1], sb = s_rule[ri][2];
+        if (c == c1 && r >= sa && r < sa + kk) partner = (int32_t)pos[s_base[c2] + sb + (r - sa)];
+        if (c == c2 && r >= sb && r < sb + kk) head = false;
+      }
+    }
+    const unsigned long long bal = __ballot(head);
+    const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wv] = __popcll(bal);
+    __syncthreads();
+    int32_t wbase = 0, tot = 0;
+    for (int k = 0; k < kSchedThreads / 64; ++k) {
+      if (k < wv) wbase += wave_tot[k];
+      tot += wave_tot[k];
+    }
+    if (head) {
+      const int32_t at = soff + wbase + before;
+      out[2 * at] = (int32_t)entw[e];
+      out[2 * at + 1] = partner >= 0 ? (int32_t)entw[partner] : 0;
+    }
+    soff += tot;
+    __syncthreads();
+  }
+  if (t == 0) count[item] = soff;
 }
 
 // ---------------------------------------------------------------------------
@@ -825,9 +952,10 @@ __device__ __forceinline__ bool keeps(const Ctx& cx, int32_t ent) {
   return ((((uint32_t)ent) >> 24) >> cx.qb) & 1u;
 }
 // ... any key of the tile (paired mode: either half)?
+// (step lists: the wave keeps at most one of a and b; b = 0 keeps nothing)
 template <bool PR>
 __device__ __forceinline__ bool active(const Ctx& cx, TileEnt te) {
-  return PR ? (keeps(cx, te.a) || keeps(cx, te.b)) : keeps(cx, te.a);
+  return keeps(cx, te.a) || keeps(cx, te.b);
 }
 
 // V^T A operand of P V job i (step s = i / (D / 32), d tile dt = i % (D / 32);
@@ -856,7 +984,7 @@ __device__ __forceinline__ bf16x8 k_operand(const Ctx& cx, const char* kt, int j
 // One stream of MFMA jobs: the P V jobs (if PV) followed by the S^T jobs (if
 // QK), with LDS operand reads kWin jobs ahead of their MFMA.  The operands of
 // the first kPre P V jobs were read at the end of the previous phase.
-template <int D, int BK, bool PV, bool QK, bool PR>
+template <int D, int BK, bool PV, bool QK, bool PR, int PRE>
 __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx, const char* vprev,
                                             const char* kcur) {
   using C = Cfg<D, BK>;
@@ -872,7 +1000,7 @@ __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx,
   bf16x8 win[kWin];
 #pragma unroll
   for (int i = 0; i < kWin; ++i)
-    if (i < kN) win[i] = (PV && i < kPre) ? st.pre[i] : rd(i);
+    if (i < kN) win[i] = (PV && i < PRE) ? st.pre[i] : rd(i);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kN; ++i) {
@@ -895,8 +1023,9 @@ __device__ __forceinline__ void mfma_stream(WaveState<D, BK>& st, const Ctx& cx,
   }
 }
 
-// M phase for key block e: O += P(e-1) V(e-1); S(e) = K(e) Q^T.
-template <int D, int BK, bool PR>
+// M phase for key block e: O += P(e-1) V(e-1); S(e) = K(e) Q^T.  The first
+// PRE operands of P V were read at the end of the wave's softmax phase.
+template <int D, int BK, bool PR, int PRE>
 __device__ __forceinline__ void m_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
                                         TileEnt ent_prev, TileEnt ent, const char* vprev,
                                         const char* kcur) {
@@ -909,13 +1038,13 @@ __device__ __forceinline__ void m_phase(WaveState<D, BK>& st, const Ctx& cx, int
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) st.oacc[dt] = st.oacc[dt] * st.o_alpha;
   }
-  if (pv) mfma_stream<D, BK, true, false, PR>(st, cx, vprev, kcur);
-  if (qk) mfma_stream<D, BK, false, true, PR>(st, cx, vprev, kcur);
+  if (pv) mfma_stream<D, BK, true, false, PR, PRE>(st, cx, vprev, kcur);
+  if (qk) mfma_stream<D, BK, false, true, PR, PRE>(st, cx, vprev, kcur);
   __builtin_amdgcn_s_setprio(0);
 }
 
 // V phase for key block e: online softmax of S(e) -> P(e).
-template <int D, int BK, bool PR>
+template <int D, int BK, bool PR, int PRE>
 __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int32_t e,
                                         TileEnt te, const char* vcur) {
   using C = Cfg<D, BK>;
@@ -937,7 +1066,8 @@ __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int
         }
     }
   }
-  const int32_t nvalid = PR ? BK : (te.a >> 13) & 127;   // valid keys: the first nvalid
+  // valid keys: the first nvalid (step lists: of the entry this wave keeps)
+  const int32_t nvalid = PR ? BK : ((keeps(cx, te.b) ? te.b : te.a) >> 13) & 127;
   if (!PR && nvalid < BK) {
     // lane-dependent limit, computed here (an opaque value keeps the 32
     // compares out of loop-invariant code motion, where they would pin 32
@@ -989,11 +1119,13 @@ __device__ __forceinline__ void v_phase(WaveState<D, BK>& st, const Ctx& cx, int
   for (int s = 0; s < C::kPSteps; ++s)
 #pragma unroll
     for (int x = 0; x < 8; ++x) st.pk[s][x] = (__bf16)st.sacc[s >> 1][8 * (s & 1) + x];
-  // The next phase of this wave is M(e + 1), whose P V reads V^T(e): block e
-  // is complete in LDS and its slot is not rewritten before interval 2 e + 4,
-  // so its first operands are read now, ahead of the barrier.
+  // The next phase of this wave is M(e + 1), whose P V reads V^T(e): where the
+  // schedule has V^T(e) complete in LDS by now (PRE > 0), its first operands
+  // are read ahead of the barrier.
+  if constexpr (PRE > 0) {
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) st.pre[i] = v_operand<D, BK>(cx, vcur, i);
+    for (int i = 0; i < PRE; ++i) st.pre[i] = v_operand<D, BK>(cx, vcur, i);
+  }
 }
 
 // LDS ring: key block e lives in slot e % 4 (separate LDS objects, so the
@@ -1031,10 +1163,10 @@ __device__ __forceinline__ void interval(WaveState<D, BK>& st, const Ctx& cx, co
     if constexpr (((I - G) & 1) == 0) {
       constexpr int sc = (((I - G) >> 1) + 4) & 3;
       constexpr int sp = (sc + 3) & 3;
-      m_phase<D, BK, PR>(st, cx, e, ent[x - 1], ent[x], rg.v[sp], rg.k[sc]);
+      m_phase<D, BK, PR, kPre>(st, cx, e, ent[x - 1], ent[x], rg.v[sp], rg.k[sc]);
     } else {
       constexpr int se = ((I - G) >> 1) & 3;  // ring slot of block e
-      v_phase<D, BK, PR>(st, cx, e, ent[x], rg.v[se]);
+      v_phase<D, BK, PR, kPre>(st, cx, e, ent[x], rg.v[se]);
     }
   }
   if (I & 1) {
@@ -1088,6 +1220,129 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Step schedule (64-token sub-blocks): the list holds steps {a, b} of one or
+// two entries with disjoint keep masks (union_kernel), and each wave works on
+// the entry its query sub-block keeps.  The ring holds two steps, each with an
+// a and a b tile of K and of V^T (8 x 16 KB at D = 128, as the 4-slot ring):
+// step s lives in slot s % 2, one LDS object per slot and operand with the b
+// tile after the a tile, so a wave picks its tile by an offset and the
+// compiler still tells the copies into one slot from the reads of the other
+// (a pointer chosen between two objects would make it wait for every copy in
+// flight before each read).  Copies run one step ahead: at even interval t
+// every wave issues its share of K(t / 2 + 1) and V^T(t / 2) (a tiles, and b
+// tiles where the step has a b entry), and before the barrier closing
+// interval t + 1 it waits for all of them.  Slot safety: K(s) is read in M(s) (intervals
+// 2 s, 2 s + 1), so its slot takes K(s + 2) from interval 2 s + 2 on; V^T(s)
+// is read in M(s + 1) (up to 2 s + 3), so its slot takes V^T(s + 2) from 2 s
+// + 4 on; both after the barrier closing the last read.
+// ---------------------------------------------------------------------------
+template <int D, int BK>
+struct PairRing {
+  char* k[2];   // 2 tiles each: a, then b
+  char* v[2];
+};
+
+// This wave's copies of the K (PART 0) or V^T (PART 1) tiles of step te into
+// slot dst: the a tile, then the b tile when the step has one (the count of
+// copies in flight may vary: they are waited for with vmcnt 0).
+template <int D, int BK, int PART>
+__device__ __forceinline__ void issue_step_copies(const Ctx& cx, TileEnt te, char* slot,
+                                                  int32_t wave_off) {
+  using C = Cfg<D, BK>;
+  char* const da = slot;
+  char* const db = slot + C::kTileBytes;
+  static_assert(C::kDmaPerTile % kWaves == 0, "copies of a tile split evenly over the waves");
+  constexpr int kPer = C::kDmaPerTile / kWaves;  // copies per wave per tile
+  const __amdgpu_buffer_rsrc_t rs = PART == 0 ? cx.k_rsrc : cx.vt_rsrc;
+  const int32_t oa = (te.a & 0x1fff) * C::kTileBytes;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(da + wave_off + u * kWaves * 1024), 16,
+        (int)cx.dma_off[PART * kPer + u], oa, 0, 0);
+  if (te.b != 0) {  // wave-uniform
+    const int32_t ob = (te.b & 0x1fff) * C::kTileBytes;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(db + wave_off + u * kWaves * 1024), 16,
+          (int)cx.dma_off[PART * kPer + u], ob, 0, 0);
+  }
+}
+
+// One interval t = t0 + I of group G in the step schedule (t0 a multiple of
+// 8, so every slot and ent[] index is a compile-time constant; ent[x] is step
+// t0 / 2 - 1 + x).
+template <int D, int BK, int G, int I>
+__device__ __forceinline__ void interval_step(WaveState<D, BK>& st, const Ctx& cx,
+                                              const PairRing<D, BK>& rg, int32_t t0,
+                                              const TileEnt (&ent)[kEnt], int32_t wave_off) {
+  const int32_t t = t0 + I;
+  if ((I & 1) == 0) {
+    constexpr int sk = (I / 2 + 1) & 1, sv = (I / 2) & 1;
+    issue_step_copies<D, BK, 0>(cx, ent[I / 2 + 2], rg.k[sk], wave_off);
+    issue_step_copies<D, BK, 1>(cx, ent[I / 2 + 1], rg.v[sv], wave_off);
+  }
+  const int32_t ph = t - G;
+  if (ph >= 0 && cx.has_rows) {
+    const int32_t e = ph >> 1;
+    constexpr int x = ((I - G) >> 1) + 1;  // ent[] index of step e
+    if constexpr (((I - G) & 1) == 0) {
+      constexpr int sc = ((I - G) >> 1) & 1;  // slot of step e; e - 1 in the other
+      const TileEnt ep = ent[x - 1], ec = ent[x];
+      constexpr int32_t kTB = Cfg<D, BK>::kTileBytes;
+      const char* vprev = rg.v[sc ^ 1] + (keeps(cx, ep.b) ? kTB : 0);
+      const char* kcur = rg.k[sc] + (keeps(cx, ec.b) ? kTB : 0);
+      m_phase<D, BK, false, G == 1 ? kPre : 0>(st, cx, e, ep, ec, vprev, kcur);
+    } else {
+      // Group 1's softmax of step e runs in interval 2 e + 2, after the
+      // barrier that completed V^T(e) (copied in 2 e): it reads the first
+      // operands of its next P V ahead.  Group 0's runs in 2 e + 1, while
+      // that copy may still be in flight.
+      constexpr int se = ((I - G) >> 1) & 1;  // slot of step e
+      const char* vcur = rg.v[se] + (keeps(cx, ent[x].b) ? Cfg<D, BK>::kTileBytes : 0);
+      v_phase<D, BK, false, G == 1 ? kPre : 0>(st, cx, e, ent[x], vcur);
+    }
+  }
+  if (I & 1) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    wg_barrier();
+  }
+}
+
+template <int D, int BK, int G>
+__device__ __forceinline__ void run_group_steps(WaveState<D, BK>& st, const Ctx& cx,
+                                                const PairRing<D, BK>& rg) {
+  // The first round (t0 = -8) only issues copies (of step 0 where the index
+  // is negative); its last even interval brings K(0).
+  for (int32_t t0 = -8; t0 < cx.T; t0 += 8) {
+    TileEnt ent[kEnt];   // the step schedule uses ent[0 .. 5]
+#pragma unroll
+    for (int x = 0; x < kEnt; ++x) {
+      if (x > 5) {
+        ent[x] = ent[5];
+        continue;
+      }
+      const int32_t step = min(max(t0 / 2 - 1 + x, 0), cx.n_u - 1);
+      ent[x].a = cx.lst[2 * step];
+      ent[x].b = cx.lst[2 * step + 1];
+    }
+#pragma unroll
+    for (int x = 0; x < 6; ++x) asm volatile("" : "+s"(ent[x].a), "+s"(ent[x].b));
+    int32_t wave_off = cx.wave * 1024;
+    asm volatile("" : "+s"(wave_off));
+    interval_step<D, BK, G, 0>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 1>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 2>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 3>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 4>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 5>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 6>(st, cx, rg, t0, ent, wave_off);
+    interval_step<D, BK, G, 7>(st, cx, rg, t0, ent, wave_off);
+  }
+}
+
 // Ping-pong schedule.  The 8 wavefronts form two groups (waves 0-3 and 4-7;
 // each SIMD holds one wave of each).  Per key block e a wave runs an MFMA
 // phase M(e) = { O += P(e-1) V(e-1) ; S(e) = K(e) Q^T } and a VALU phase
@@ -1097,7 +1352,7 @@ __device__ __forceinline__ void run_group(WaveState<D, BK>& st, const Ctx& cx,
 // softmax.  Key block e is copied HBM -> LDS at interval 2e - 4, two key
 // blocks ahead of its first use, and is read during intervals 2e .. 2e+3.
 // One work item: query group gi of head bh, whose union list is list[item].
-template <int D, int BK, bool PR>
+template <int D, int BK, bool PR, bool STEPS, typename RingT>
 __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ vt, __bf16* __restrict__ out,
@@ -1106,7 +1361,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
                                          int32_t groups, int32_t nb, int32_t nq,
                                          int32_t npad_q, int32_t npad_k, float c_log2,
                                          const OutMap& om, const int32_t* __restrict__ perm,
-                                         const Ring<D, BK>& rg) {
+                                         const RingT& rg) {
   using C = Cfg<D, BK>;
   constexpr int kS = D / 16, kDT = D / 32;
 
@@ -1138,7 +1393,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   cx.T = (2 * cx.n_u + 2 + 7) & ~7;
   cx.nb = nb;
   cx.c_log2 = c_log2;
-  cx.lst = list + item * nb;
+  cx.lst = list + item * (STEPS ? 2 * nb : nb);   // entries, or steps of two words
   // raw buffer resources over this head's K and V^T (byte range npad_k * D * 2,
   // below 2^31 by the host checks; dword 3 = 0x00020000: raw 32-bit data)
   const int32_t head_bytes = npad_k * D * 2;
@@ -1194,8 +1449,13 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
   // The count is uniform over the workgroup, so every wave skips the loop and
   // its barriers together; the loop's list reads need n_list >= 1.
   if (cx.n_u > 0) {
-    if (grp == 0) run_group<D, BK, PR, 0>(st, cx, rg);
-    else run_group<D, BK, PR, 1>(st, cx, rg);
+    if constexpr (STEPS) {
+      if (grp == 0) run_group_steps<D, BK, 0>(st, cx, rg);
+      else run_group_steps<D, BK, 1>(st, cx, rg);
+    } else {
+      if (grp == 0) run_group<D, BK, PR, 0>(st, cx, rg);
+      else run_group<D, BK, PR, 1>(st, cx, rg);
+    }
   }
 
   if (!cx.has_rows) return;
@@ -1222,7 +1482,7 @@ __device__ __forceinline__ void run_item(const __bf16* __restrict__ q,
 // Persistent kernel: one workgroup per CU slot takes items from the queue of
 // the XCD it runs on (hardware register XCC_ID), then from the other queues;
 // it exits once every queue is drained.
-template <int D, int BK, bool PR>
+template <int D, int BK, bool PR, bool STEPS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const __bf16* __restrict__ vt, __bf16* __restrict__ out,
@@ -1231,15 +1491,11 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             int32_t nb, int32_t nq, int32_t npad_q, int32_t npad_k, float c_log2, OutMap om,
             const int32_t* __restrict__ perm) {
   using C = Cfg<D, BK>;
-  __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
-      k2[C::kTileBytes], k3[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v0[C::kTileBytes], v1[C::kTileBytes],
-      v2[C::kTileBytes], v3[C::kTileBytes];
   __shared__ int32_t s_item;
-  const Ring<D, BK> rg{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
   const int home = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1);  // XCC_ID
   int probe = 0;  // thread 0: queues home, home + 1, ... found empty so far
-  for (;;) {
+  // thread 0 takes the next item (-1: every queue drained), broadcast via LDS
+  auto next_item = [&]() {
     if (threadIdx.x == 0) {
       int32_t it = -1;
       while (probe < kQueues) {
@@ -1256,23 +1512,42 @@ attn_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __syncthreads();
     const int32_t item = s_item;
     __syncthreads();
-    if (item < 0) break;
-    run_item<D, BK, PR>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k, c_log2,
-                        om, perm, rg);
+    return item;
+  };
+  if constexpr (!STEPS) {
+    // entries (paired 32-key tiles or 64-key blocks): 4-slot ring, one object per tile
+    __shared__ __attribute__((aligned(1024))) char k0[C::kTileBytes], k1[C::kTileBytes],
+        k2[C::kTileBytes], k3[C::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char v0[C::kTileBytes], v1[C::kTileBytes],
+        v2[C::kTileBytes], v3[C::kTileBytes];
+    const Ring<D, BK> rg{{k0, k1, k2, k3}, {v0, v1, v2, v3}};
+    for (int32_t item = next_item(); item >= 0; item = next_item())
+      run_item<D, BK, PR, STEPS>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k,
+                          c_log2, om, perm, rg);
+  } else {
+    static_assert(!PR, "step lists hold 64-key entries");
+    // steps: 2-step ring, one object per slot holding the a and b tiles
+    __shared__ __attribute__((aligned(1024))) char k0[2 * C::kTileBytes], k1[2 * C::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char v0[2 * C::kTileBytes], v1[2 * C::kTileBytes];
+    const PairRing<D, BK> rg{{k0, k1}, {v0, v1}};
+    for (int32_t item = next_item(); item >= 0; item = next_item())
+      run_item<D, BK, PR, STEPS>(q, k, vt, out, list, count, item, groups, nb, nq, npad_q, npad_k,
+                          c_log2, om, perm, rg);
   }
 }
 
 // Workgroups of the persistent attention kernel: every CU slot of the current
 // device (CU count x resident workgroups per CU), at most one per item.  Both
 // figures are queried on every call: the library keeps no state between calls.
-template <int D, int BK, bool PR>
+template <int D, int BK, bool PR, bool STEPS>
 hipError_t attn_grid(int64_t items, uint32_t* grid) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK, PR>, kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_kernel<D, BK, PR, STEPS>, kThreads,
+                                                   0);
   if (e != hipSuccess) return e;
   int64_t slots = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   *grid = (uint32_t)(items < slots ? items : slots);
@@ -1283,7 +1558,7 @@ hipError_t attn_grid(int64_t items, uint32_t* grid) {
 // npad_q / npad_k: rows per head of Q and O / of K and V.
 // PR: paired mode (32-key schedule entries streamed two per 64-key tile; V^T
 // is laid out per 32-key sub-block)
-template <int D, int BK, bool PR>
+template <int D, int BK, bool PR, bool STEPS>
 hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, const int32_t* list,
                        const int32_t* count, const int32_t* queue, int32_t* meta, __bf16* vt,
                        int32_t bh, const AttnWs& w, int32_t nb, int32_t nq, int32_t npad_q,
@@ -1297,9 +1572,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, void* out, c
     if (e != hipSuccess) return e;
   }
   uint32_t grid = 0;
-  e = attn_grid<D, BK, PR>(w.items, &grid);
+  e = attn_grid<D, BK, PR, STEPS>(w.items, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_kernel<D, BK, PR>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<D, BK, PR, STEPS>), dim3(grid), dim3(kThreads), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)vt, (__bf16*)out, list,
                      count, queue, meta, w.groups, nb, nq, npad_q, npad_k, c_log2, om, perm);
   return hipGetLastError();
@@ -1319,8 +1594,8 @@ AttnWs ws_common(int32_t bh, int32_t sub, int32_t nbs_q, int32_t nbs_k, int64_t 
   w.groups = (nbs_q + w.group_size - 1) / w.group_size;
   w.items = (int64_t)bh * w.groups;
   size_t off = 0;
-  w.list_off = off;
-  off = align_up(off + (size_t)w.items * w.nbs * sizeof(int32_t), 256);
+  w.list_off = off;   // per item: nbs entries, or nbs steps of two words
+  off = align_up(off + (size_t)w.items * w.nbs * 2 * sizeof(int32_t), 256);
   w.count_off = off;
   off = align_up(off + (size_t)w.items * sizeof(int32_t), 256);
   w.queue_off = off;
@@ -1341,7 +1616,7 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
                          int32_t head_dim, const AttnWs& w, const Sched& sc, int32_t npad_q,
                          int32_t npad_k, float scale, const int32_t* row_ptr,
                          const int32_t* col_idx, void* ws, const OutMap& om, int regroup,
-                         hipStream_t stream) {
+                         bool steps, hipStream_t stream) {
   if (w.items > 0x7fffffff) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   int32_t* list = reinterpret_cast<int32_t*>(base + w.list_off);
@@ -1375,9 +1650,14 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
     if (e != hipSuccess) return e;
   }
 
+  // step lists (64-token sub-blocks only), paired when the staging fits in
+  // LDS; otherwise one word per entry
+  steps = steps && w.sub == 64;
+  const int32_t out_mode = steps ? (w.nbs <= kPairMaxNb ? 2 : 1) : 0;
   hipLaunchKernelGGL(union_kernel<Sched>, dim3((uint32_t)w.items), dim3(kSchedThreads),
-                     (size_t)w.nbs * sizeof(uint32_t), stream, row_ptr, col_idx, list, count,
-                     w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
+                     (size_t)w.nbs * sizeof(uint32_t) * (out_mode == 2 ? 3 : 1), stream, row_ptr,
+                     col_idx, list, count, w.nbs, w.nbs_q, w.groups, w.group_size, sc,
+                     (const int32_t*)perm, out_mode);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // fewer runs per head when there are many heads, so that every unit is still
@@ -1389,17 +1669,20 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   if (e != hipSuccess) return e;
 
   const float c_log2 = scale * 1.4426950408889634f;
-  if (head_dim == 128 && w.sub == 64)
-    return launch_attn<128, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
-  if (head_dim == 64 && w.sub == 64)
-    return launch_attn<64, 64, false>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                               w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
-  if (head_dim == 128 && w.sub == 32)
-    return launch_attn<128, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,
-                                w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream);
-  return launch_attn<64, 64, true>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs, w.nbs_q,
-                             npad_q, npad_k, c_log2, om, perm, stream);
+#define SVSA_LAUNCH(DD, PR, ST)                                                                  \
+  return launch_attn<DD, 64, PR, ST>(q, k, v, out, list, count, queue, meta, vt, bh, w, w.nbs,  \
+                                     w.nbs_q, npad_q, npad_k, c_log2, om, perm, stream)
+  if (w.sub == 64) {
+    if (head_dim == 128) {
+      if (steps) SVSA_LAUNCH(128, false, true);
+      SVSA_LAUNCH(128, false, false);
+    }
+    if (steps) SVSA_LAUNCH(64, false, true);
+    SVSA_LAUNCH(64, false, false);
+  }
+  if (head_dim == 128) SVSA_LAUNCH(128, true, false);
+  SVSA_LAUNCH(64, true, false);
+#undef SVSA_LAUNCH
 }
 }  // namespace
 
@@ -1424,14 +1707,15 @@ AttnWs cluster_attn_ws_layout(int32_t bh, int32_t sub, int64_t npad_q, int64_t n
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, void* out,
                                     int32_t bh, int32_t head_dim, const Geom& g, float scale,
                                     const int32_t* row_ptr, const int32_t* col_idx, void* ws,
-                                    bool natural_out, int regroup, hipStream_t stream) {
+                                    bool natural_out, int regroup, bool steps,
+                                    hipStream_t stream) {
   if (g.Bk % 32 != 0) return hipErrorInvalidValue;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
   const AttnWs w = attn_ws_layout(bh, g);
   const GeomSched sc{g, w.ratio, w.sub};
   const OutMap om{g, natural_out ? 1 : 0};
   return run_attention(q, k, v, out, bh, head_dim, w, sc, g.Npad, g.Npad, scale, row_ptr, col_idx,
-                       ws, om, regroup, stream);
+                       ws, om, regroup, steps, stream);
 }
 
 hipError_t launch_attn_stage_v(const void* v, int32_t bh, int32_t head_dim, const Geom& g,
@@ -1467,7 +1751,7 @@ hipError_t launch_cluster_attn(const void* q, const void* k, const void* v, void
   const TableSched sc{q_start, q_size, k_start, k_size, nq, nk, sub};
   const OutMap om{};  // tile (cluster) order
   return run_attention(q, k, v, out, bh, head_dim, w, sc, (int32_t)npad_q, (int32_t)npad_k, scale,
-                       row_ptr, col_idx, ws, om, 0, stream);
+                       row_ptr, col_idx, ws, om, 0, false, stream);
 }
 
 }  // namespace svsa

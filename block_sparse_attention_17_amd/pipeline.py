@@ -57,15 +57,18 @@ class BlockSparseAttention:
                            self.stripe_ws, band_width=band_width, stream=stream)
 
     def attend(self, scale=None, stream=None, row_ptr=None, col_idx=None, natural_out=False,
-               groups="auto"):
+               groups="auto", step_pairs=False):
         """Attention over the CSR lists into ot (tile order), or straight into out
         (natural order, natural_out=True: the kernel does the inverse reorder).
         groups: "auto" (query blocks grouped by their lists when the work is
-        large enough), "list" (always when the blocks allow it) or "positional"."""
+        large enough), "list" (always when the blocks allow it) or "positional".
+        step_pairs: walk each union list in steps of one or two key blocks with
+        disjoint keepers (SVSA_ATTN_STEP_PAIRS; pays on fixed-fraction masks)."""
         scale = 1.0 / sqrt(self.head_dim) if scale is None else scale
         gflag = {"auto": 0, "list": B.SVSA_ATTN_GROUPS_BY_LIST,
                  "positional": B.SVSA_ATTN_POSITIONAL_GROUPS}[groups]
-        flags = (B.SVSA_ATTN_OUT_NATURAL if natural_out else 0) | gflag
+        flags = ((B.SVSA_ATTN_OUT_NATURAL if natural_out else 0) | gflag
+                 | (B.SVSA_ATTN_STEP_PAIRS if step_pairs else 0))
         B.svsa_block_sparse_attn_ex(self.qt, self.kt, None, self.out if natural_out else self.ot,
                                     self.geom, scale,
                                     self.row_ptr if row_ptr is None else row_ptr,
@@ -78,10 +81,11 @@ class BlockSparseAttention:
         return self.out
 
     def __call__(self, q, k, v, top_p=None, keep_frac=None, band_width=1, stream=None):
-        """One pass of the whole path; returns the natural-order bf16 output."""
+        """One pass of the whole path; returns the natural-order bf16 output.
+        Fixed-fraction masks (keep_frac) run with step pairs."""
         self.permute_in(q, k, v, stream)
         self.build_mask(top_p, keep_frac, band_width, stream)
-        return self.attend(stream=stream, natural_out=True)
+        return self.attend(stream=stream, natural_out=True, step_pairs=keep_frac is not None)
 
 
 class ClusteredAttention:

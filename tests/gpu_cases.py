@@ -80,12 +80,13 @@ class GpuRun:
         ci = self.bsa.col_idx[: int(rp[-1])].cpu().numpy()
         return rp, ci
 
-    def attention(self, rp, ci):
-        """Tiled bf16 output bits of the attention stage run on the given CSR."""
-        log(f"{self.cfg.name}: attention on {int(rp[-1])} kept blocks")
+    def attention(self, rp, ci, step_pairs=False):
+        """Tiled bf16 output bits of the attention stage run on the given CSR
+        (step_pairs: SVSA_ATTN_STEP_PAIRS)."""
+        log(f"{self.cfg.name}: attention on {int(rp[-1])} kept blocks, step_pairs={step_pairs}")
         rpd = torch.from_numpy(rp.astype(np.int32)).cuda()
         cid = torch.from_numpy(ci.astype(np.int32)).cuda()
-        self.bsa.attend(row_ptr=rpd, col_idx=cid)
+        self.bsa.attend(row_ptr=rpd, col_idx=cid, step_pairs=step_pairs)
         torch.cuda.synchronize()
         return dev_to_bits(self.bsa.ot)
 

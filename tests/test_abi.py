@@ -104,14 +104,15 @@ def test_attn_ex_rejects_unknown_flags(mod):
     Q, K, O = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
     R, C = ctypes.c_void_p(0x5000000), ctypes.c_void_p(0x6000000)
     f = lib.svsa_block_sparse_attn_ex
-    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 8, ws, need, None) == -1
+    assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 16, ws, need, None) == -1
     assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, -1, ws, need, None) == -1
     # positional and by-list grouping together contradict each other
     assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 6, ws, need, None) == -1
     assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, 7, ws, need, None) == -1
     # valid combinations pass the flag check (then the workspace size fails)
-    for fl in (1, 2, 3, 4, 5):
+    for fl in (1, 2, 3, 4, 5, 8, 9, 10, 13):
         assert f(Q, K, None, O, 1, 1, 64, g, 0.125, R, C, fl, ws, need - 1, None) == -3
+    assert mod.SVSA_ATTN_STEP_PAIRS == 8
     assert f(Q, K, None, ws, 1, 1, 64, g, 0.125, R, C, 1, ws, need, None) == -1   # out in ws
 
 

@@ -450,9 +450,11 @@ def test_whole_path_bitwise_deterministic():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
-def test_attention_edge_cases_custom_csr():
+@pytest.mark.parametrize("step_pairs", [False, True])
+def test_attention_edge_cases_custom_csr(step_pairs):
     """Empty row -> zeros (also a whole 4-block query group with nothing to
-    do); out-of-range columns ignored; one block per row is local attention."""
+    do); out-of-range columns ignored; one block per row is local attention.
+    Both list walks (entries, and step pairs)."""
     import block_sparse_attention_17_amd as m
     cfg = get_config("small")
     run, orun = gc.gpu_run("small"), gc.oracle_run("small")
@@ -469,7 +471,7 @@ def test_attention_edge_cases_custom_csr():
     rp = np.zeros(H * nb + 1, np.int64)
     rp[1:] = np.cumsum([len(c) for c in rows_cols])
     ci = np.array([c for cs in rows_cols for c in cs], np.int32)
-    out_bits = run.attention(rp, ci)
+    out_bits = run.attention(rp, ci, step_pairs=step_pairs)
     zero_blk = orc.widen(out_bits[0, 0, 5 * 64: 6 * 64])
     assert np.all(zero_blk == 0)
     assert np.all(orc.widen(out_bits[0, 2, 8 * 64: 12 * 64]) == 0)
@@ -484,12 +486,13 @@ def test_attention_edge_cases_custom_csr():
     assert max_abs <= gc.MAX_ABS and rel <= gc.REL_L2
 
 
-def test_empty_groups_with_stale_workspace():
+@pytest.mark.parametrize("step_pairs", [False, True])
+def test_empty_groups_with_stale_workspace(step_pairs):
     """Work items whose union list is empty stream nothing and write zeros,
     whatever the attention workspace held: every workspace byte is 0xFF before
     V is staged.  Cases: a whole 4-block query group of empty rows, and PSA's
     3D-padded 3x8x16 tiles on a 9x21x35 grid, whose last tile row holds sub-blocks
-    of padding only (their groups keep nothing)."""
+    of padding only (their groups keep nothing).  Both list walks."""
     import block_sparse_attention_17_amd as m
     # (a) a whole query group of empty rows
     cfg = get_config("small")
@@ -502,7 +505,7 @@ def test_empty_groups_with_stale_workspace():
     ci = np.array([c for cs in cols for c in cs], np.int32)
     run.bsa.attn_ws.fill_(0xFF)
     m.svsa_attn_stage_v(run.v_dev, run.bsa.attn_ws, run.geom)
-    out_bits = run.attention(rp, ci)
+    out_bits = run.attention(rp, ci, step_pairs=step_pairs)
     assert np.all(orc.widen(out_bits[0, 3, 4 * 64: 8 * 64]) == 0)
     assert np.all(orc.widen(out_bits[0, 0, : 4 * 64]) == 0)
     rows = [(0, h, i) for h in range(H) for i in range(nb) if cols[h * nb + i]]
@@ -533,7 +536,8 @@ def test_empty_groups_with_stale_workspace():
     m.svsa_attn_stage_v(nat[2], ws, G)
     out = torch.full((1, Hh, G.N, D), 7.0, dtype=torch.bfloat16, device="cuda")
     m.svsa_block_sparse_attn_ex(tiled[0], tiled[1], None, out, G, 1 / np.sqrt(D), rp_d, ci_d, ws,
-                                flags=m.SVSA_ATTN_OUT_NATURAL)
+                                flags=m.SVSA_ATTN_OUT_NATURAL
+                                | (m.SVSA_ATTN_STEP_PAIRS if step_pairs else 0))
     torch.cuda.synchronize()
     got = orc.widen(gc.dev_to_bits(out))
     slots, counts = orc.block_layout(grid, tile, True)
