@@ -160,10 +160,12 @@ struct TableSched {
 // one key block's time, and each wavefront works on the entry its sub-block
 // keeps.  Two entries share a step when their keep masks are disjoint, so a
 // union entry that only some sub-blocks keep no longer leaves the other
-// SIMDs idle for a whole key block.  On the oracle's masks this takes the
-// steps of a Wan2.1-720p top-p 0.9 head group to 0.89 of its union entries
-// (kept pairs per step and sub-block 0.86 -> 0.97), and in HunyuanVideo-720p
-// fixed-fraction mode to 0.68 (0.61 -> 0.91).
+// SIMDs idle for a whole key block.  Over all items of a call (query blocks
+// regrouped by their lists) this takes the steps to 0.886 of the union
+// entries at Wan2.1-720p top-p 0.9 (kept pairs per step and sub-block 0.856
+// -> 0.967) and to 0.759 in HunyuanVideo-720p fixed-fraction mode (0.721 ->
+// 0.950).  A step holding two blocks keeps its copy and ring cost; pairing
+// only within windows of 64 consecutive entries paired less and ran slower.
 //
 // Pairing: entries are bucketed by mask (1..15) and ranked in list order;
 // the rules below, in order, pair the k-th free entry of the first bucket
