@@ -183,14 +183,13 @@ constexpr int8_t kPairRule[kPairRules][2] = {
     {1, 2},  {1, 4},  {1, 8},  {2, 4}, {2, 8}, {4, 8}};                     // 1 + 1
 constexpr int32_t kPairMaxNb = 4096;   // staging in LDS: 3 words per key sub-block
 
-// out_mode: 0 = one word per entry (paired 32-key tiles read entries two at a
-// time), 1 = steps {entry, 0}, 2 = steps paired as above (nb <= kPairMaxNb).
-template <typename Sched>
+// out_mode: 0 = one word per entry (the entry walks), 1 = steps {entry, 0},
+// 2 = steps paired as above (nb <= kPairMaxNb).
+template <typename Sched, int out_mode>
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
              int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t nb, int32_t nq,
-             int32_t groups, int32_t group_size, Sched sc, const int32_t* __restrict__ perm,
-             int32_t out_mode) {
+             int32_t groups, int32_t group_size, Sched sc, const int32_t* __restrict__ perm) {
   const int32_t ncols = sc.ncols();
   extern __shared__ uint32_t mask[];  // [nb]; out_mode 2: then entw[nb], pos[nb]
   __shared__ int32_t wave_tot[kSchedThreads / 64];
@@ -244,9 +243,9 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     if (m != 0u) {
       const int32_t word = j | (sc.kvalid(bh, j) << 13) | (int32_t)(m << 24);
       const int32_t at = off + wbase + before;
-      if (out_mode == 0) {
+      if constexpr (out_mode == 0) {
         out[at] = word;
-      } else if (out_mode == 1) {
+      } else if constexpr (out_mode == 1) {
         out[2 * at] = word;
         out[2 * at + 1] = 0;
       } else {
@@ -256,7 +255,7 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     off += tot;
     __syncthreads();
   }
-  if (out_mode != 2) {
+  if constexpr (out_mode != 2) {
     if (t == 0) count[item] = off;
     return;
   }
@@ -1656,10 +1655,17 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
   // LDS; otherwise one word per entry
   steps = steps && w.sub == 64;
   const int32_t out_mode = steps ? (w.nbs <= kPairMaxNb ? 2 : 1) : 0;
-  hipLaunchKernelGGL(union_kernel<Sched>, dim3((uint32_t)w.items), dim3(kSchedThreads),
-                     (size_t)w.nbs * sizeof(uint32_t) * (out_mode == 2 ? 3 : 1), stream, row_ptr,
-                     col_idx, list, count, w.nbs, w.nbs_q, w.groups, w.group_size, sc,
-                     (const int32_t*)perm, out_mode);
+  const dim3 ugrid((uint32_t)w.items), ublk(kSchedThreads);
+  const size_t ushm = (size_t)w.nbs * sizeof(uint32_t) * (out_mode == 2 ? 3 : 1);
+  if (out_mode == 2)
+    hipLaunchKernelGGL((union_kernel<Sched, 2>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,
+                       count, w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
+  else if (out_mode == 1)
+    hipLaunchKernelGGL((union_kernel<Sched, 1>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,
+                       count, w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
+  else
+    hipLaunchKernelGGL((union_kernel<Sched, 0>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,
+                       count, w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // fewer runs per head when there are many heads, so that every unit is still
