@@ -183,8 +183,8 @@ constexpr int8_t kPairRule[kPairRules][2] = {
     {1, 2},  {1, 4},  {1, 8},  {2, 4}, {2, 8}, {4, 8}};                     // 1 + 1
 constexpr int32_t kPairMaxNb = 4096;   // staging in LDS: 3 words per key sub-block
 
-// out_mode: 0 = one word per entry (the entry walks), 1 = steps {entry, 0},
-// 2 = steps paired as above (nb <= kPairMaxNb).
+// out_mode: 0 = one word per entry (the entry walks), 2 = steps paired as
+// above (nb <= kPairMaxNb).
 template <typename Sched, int out_mode>
 __global__ void __launch_bounds__(kSchedThreads)
 union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
@@ -243,19 +243,13 @@ union_kernel(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ co
     if (m != 0u) {
       const int32_t word = j | (sc.kvalid(bh, j) << 13) | (int32_t)(m << 24);
       const int32_t at = off + wbase + before;
-      if constexpr (out_mode == 0) {
-        out[at] = word;
-      } else if constexpr (out_mode == 1) {
-        out[2 * at] = word;
-        out[2 * at + 1] = 0;
-      } else {
-        entw[at] = (uint32_t)word;
-      }
+      if constexpr (out_mode == 0) out[at] = word;
+      else entw[at] = (uint32_t)word;
     }
     off += tot;
     __syncthreads();
   }
-  if constexpr (out_mode != 2) {
+  if constexpr (out_mode == 0) {
     if (t == 0) count[item] = off;
     return;
   }
@@ -1651,17 +1645,14 @@ hipError_t run_attention(const void* q, const void* k, const void* v, void* out,
     if (e != hipSuccess) return e;
   }
 
-  // step lists (64-token sub-blocks only), paired when the staging fits in
-  // LDS; otherwise one word per entry
-  steps = steps && w.sub == 64;
-  const int32_t out_mode = steps ? (w.nbs <= kPairMaxNb ? 2 : 1) : 0;
+  // step lists: 64-token sub-blocks and a staging that fits in LDS; otherwise
+  // the entry walk (one word per entry)
+  steps = steps && w.sub == 64 && w.nbs <= kPairMaxNb;
+  const int32_t out_mode = steps ? 2 : 0;
   const dim3 ugrid((uint32_t)w.items), ublk(kSchedThreads);
   const size_t ushm = (size_t)w.nbs * sizeof(uint32_t) * (out_mode == 2 ? 3 : 1);
   if (out_mode == 2)
     hipLaunchKernelGGL((union_kernel<Sched, 2>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,
-                       count, w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
-  else if (out_mode == 1)
-    hipLaunchKernelGGL((union_kernel<Sched, 1>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,
                        count, w.nbs, w.nbs_q, w.groups, w.group_size, sc, (const int32_t*)perm);
   else
     hipLaunchKernelGGL((union_kernel<Sched, 0>), ugrid, ublk, ushm, stream, row_ptr, col_idx, list,

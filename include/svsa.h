@@ -310,7 +310,8 @@ enum {
  * grouped by their lists whenever the blocks allow it (64-token blocks,
  * nb <= 2048), whatever the size of the work (see "Scheduling" above); both
  * together, or other bits: SVSA_E_INVALID.  SVSA_ATTN_STEP_PAIRS (blocks that
- * are whole 64-token sub-blocks; ignored with 32-token ones): the four query
+ * are whole 64-token sub-blocks, at most 4096 of them per head; ignored
+ * otherwise): the four query
  * blocks of a workgroup walk their union list in steps of one or two key
  * blocks, two when the sets of query blocks keeping them are disjoint, each
  * query block computing on the one it keeps ([PSA] App. B, Alg. 2 per query
