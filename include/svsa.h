@@ -240,9 +240,10 @@ SVSA_API int svsa_stripe_mask(const svsa_geom* g, int32_t batch, int32_t heads,
 
 /*
  * Workspace (device bytes) needed by svsa_block_sparse_attn: the per-group
- * union lists and work queues, plus a transposed copy of V (sized for
- * head_dim 128, so the figure does not depend on head_dim).  Returns 0 if the
- * sizes are invalid.
+ * union lists (room for two words per key sub-block, as the step walk of
+ * SVSA_ATTN_STEP_PAIRS needs) and work queues, plus a transposed copy of V
+ * (sized for head_dim 128, so the figure does not depend on head_dim).
+ * Returns 0 if the sizes are invalid.
  */
 SVSA_API size_t svsa_attn_workspace_bytes(int32_t batch, int32_t heads, const svsa_geom* g);
 
