@@ -171,9 +171,9 @@ struct TableSched {
 // the rules below, in order, pair the k-th free entry of the first bucket
 // with the k-th free entry of the second: three keepers with the other one,
 // two with the other two, two with one of the other two, one with one.  The
-// first entry of a pair heads the step and keeps its place in the list order;
-// the second leaves the list.  Ranks follow the list order, so the pairing is
-// deterministic.
+// entry from a rule's first bucket heads the step and keeps its place in the
+// list order (wherever its partner stood); the partner leaves the list.  Ranks
+// follow the list order, so the pairing is deterministic.
 constexpr int kPairRules = 25;
 constexpr int8_t kPairRule[kPairRules][2] = {
     {7, 8},  {11, 4}, {13, 2}, {14, 1},                                     // 3 + 1
