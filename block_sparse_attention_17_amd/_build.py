@@ -30,7 +30,7 @@ def hipcc():
 
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
-            # keep the compiler from forming packed fp32 math (see DESIGN notes)
+            # keep the compiler from forming packed fp32 instructions from float code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fvisibility=hidden", "-Wall", "-Wno-unused-result", "-Wno-unused-variable"]
 
