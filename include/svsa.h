@@ -310,19 +310,18 @@ enum {
  * consecutive ones at a time, never by their lists; SVSA_ATTN_GROUPS_BY_LIST:
  * grouped by their lists whenever the blocks allow it (64-token blocks,
  * nb <= 2048), whatever the size of the work (see "Scheduling" above); both
- * together, or other bits: SVSA_E_INVALID.  SVSA_ATTN_STEP_PAIRS (blocks that
- * are whole 64-token sub-blocks, at most 4096 of them per head; ignored
- * otherwise): the four query
- * blocks of a workgroup walk their union list in steps of one or two key
- * blocks, two when the sets of query blocks keeping them are disjoint, each
- * query block computing on the one it keeps ([PSA] App. B, Alg. 2 per query
- * block; the steps only change which workgroup-wide interval a kept block is
- * processed in).  It pays where neighbouring query blocks keep different key
- * blocks (fixed-fraction masks) and costs a little where they keep mostly the
- * same ones (top-p masks), as its copy pipeline is one key block shallower.
- * The same kept pairs are computed, in another order: results agree to
- * float32 rounding, and a call is bitwise reproducible.  Everything else as
- * above.
+ * together, or other bits: SVSA_E_INVALID.  SVSA_ATTN_STEP_PAIRS (blocks
+ * that are whole 64-token sub-blocks, at most 4096 of them per head;
+ * ignored otherwise): the four query blocks of a workgroup walk their union
+ * list in steps of one or two key blocks, two when the sets of query blocks
+ * keeping them are disjoint, each query block computing on the one it keeps
+ * ([PSA] App. B, Alg. 2 per query block; the steps only change which
+ * workgroup-wide interval a kept block is processed in).  It pays where
+ * neighbouring query blocks keep different key blocks (fixed-fraction
+ * masks) and costs a little where they keep mostly the same ones (top-p
+ * masks), as its copy pipeline is one key block shallower. The same kept
+ * pairs are computed, in another order: results agree to float32 rounding,
+ * and a call is bitwise reproducible.  Everything else as above.
  */
 SVSA_API int svsa_block_sparse_attn_ex(const void* q, const void* k, const void* v, void* out,
                                        int32_t batch, int32_t heads, int32_t head_dim,
