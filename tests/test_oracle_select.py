@@ -129,3 +129,22 @@ def test_topp_reaching_p_exactly_is_inclusive():
     s = np.array([0.5, 0.25, 0.25])
     assert orc.select_row(s, 0, band=0, top_p=np.float32(0.75)).tolist() == [0, 1]
     assert orc.select_row(s, 0, band=0, top_p=np.float32(0.7500001)).tolist() == [0, 1, 2]
+
+
+def test_fixed_fraction_count_uses_the_float32_fraction():
+    # k = ceil(f * nb) with f the float32 value of the fraction, widened
+    # exactly: float32(0.3) = 0.300000011920928955..., so 10 blocks keep 4;
+    # 0.25 is exact in binary, so 8 blocks keep 2; a tiny fraction still
+    # keeps the top block, and the count never exceeds nb.
+    assert float(np.float32(0.3)) > 0.3
+    s = np.linspace(1.0, 2.0, 10)[::-1] / fsum(np.linspace(1.0, 2.0, 10))
+    assert orc.select_row(s, 9, band=0, keep_frac=np.float32(0.3)).tolist() == [0, 1, 2, 3]
+    s8 = np.array([0.05, 0.3, 0.1, 0.2, 0.05, 0.1, 0.15, 0.05])
+    assert orc.select_row(s8, 0, band=0, keep_frac=np.float32(0.25)).tolist() == [1, 3]
+    assert orc.select_row(s8, 0, band=0, keep_frac=np.float32(1e-6)).tolist() == [1]
+    assert orc.select_row(s8, 0, band=0, keep_frac=np.float32(1.0)).tolist() == list(range(8))
+    # the band is added after the count and does not count toward it
+    assert orc.select_row(s8, 5, band=2, keep_frac=np.float32(0.25)).tolist() == [1, 3, 4, 5, 6]
+    # equal scores at the cut go to the lower key index, as in top-p
+    s4 = np.array([0.1, 0.3, 0.3, 0.3])
+    assert orc.select_row(s4, 0, band=0, keep_frac=np.float32(0.5)).tolist() == [1, 2]
