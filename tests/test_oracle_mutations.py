@@ -67,6 +67,29 @@ def _select_strict(s_row, i, band, top_p=None, keep_frac=None):
     return np.nonzero(kept)[0]
 
 
+
+def _select_fixed_variant(count):
+    """Fixed-fraction selection with another block count rule."""
+    def select(s_row, i, band, top_p=None, keep_frac=None):
+        if keep_frac is None:
+            return _orig_select(s_row, i, band, top_p=top_p)
+        nb = s_row.size
+        k = min(max(count(np.float32(keep_frac), nb), 1), nb)
+        kept = np.zeros(nb, bool)
+        kept[np.argsort(-s_row, kind="stable")[:k]] = True
+        kept |= np.abs(np.arange(nb) - i) <= band - 1
+        return np.nonzero(kept)[0]
+    select.__name__ = f"_select_fixed_{count.__name__}"
+    return select
+
+
+def float32_product(f, nb):
+    return int(np.ceil(np.float32(f) * np.float32(nb)))
+
+
+def nearest(f, nb):
+    return int(round(float(f) * nb))
+
 def _attention_rows_with_pads(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
     n_i = min(Bk, N - i * Bk)
     q = orc.widen(qp[b, h, i * Bk: i * Bk + n_i])
@@ -269,6 +292,10 @@ MUTATIONS = [
     ("tile_order", _tile_order_swapped, tp.test_tile_order_worked_example, ("golden",)),
     ("select_row", _select_band_off_by_one, ts.test_band_width, ()),
     ("select_row", _select_strict, ts.test_topp_reaching_p_exactly_is_inclusive, ()),
+    ("select_row", _select_fixed_variant(float32_product),
+     ts.test_fixed_fraction_count_uses_the_float32_fraction, ()),
+    ("select_row", _select_fixed_variant(nearest),
+     ts.test_fixed_fraction_count_uses_the_float32_fraction, ()),
     ("attention_rows", _attention_rows_with_pads, ta.test_padded_keys_are_excluded, ()),
     ("attention_rows", _attention_rows_v_is_k, ta.test_all_blocks_kept_equals_dense_sdpa,
      ("grid_tile",)),
