@@ -404,3 +404,20 @@ def test_block_mask_noalloc_argument_errors(mod):
     # bitmaps and counts beyond 16 MiB: 200 heads of 1182 blocks
     assert f(FAKE, FAKE2, 1, 200, 1182, 64, 0.1, tp, None, 1, FAKE, FAKE2, 200 * 1182 * 1182,
              None) == E_WS
+
+
+def test_attn_workspace_holds_step_lists_and_staged_v(mod):
+    """The attention workspace has room for two list words per key sub-block of
+    every item (the step walk's steps; the entry walk uses one), four 64-token
+    query sub-blocks per item, plus V^T of every (batch, head) at head_dim 128
+    in bf16 (host-only size query, no GPU)."""
+    for geo, B, H in ((mod.Geometry(21, 45, 80, 4, 4, 4), 1, 40),     # Wan2.1-720p
+                      (mod.Geometry(33, 45, 80, 4, 4, 4), 1, 24),     # HunyuanVideo-720p
+                      (mod.Geometry(21, 45, 80, 3, 8, 16, True), 2, 3),
+                      (mod.Geometry(9, 21, 35, 2, 4, 4), 2, 2)):     # 32-token blocks
+        sub = 64 if geo.Bk % 64 == 0 else 32
+        nbs = geo.N_pad // sub if geo.pad3d else -(-geo.N // sub)   # key sub-blocks
+        items = B * H * -(-nbs // (256 // sub))                      # 256 query rows per item
+        need = items * nbs * 2 * 4 + B * H * nbs * sub * 128 * 2
+        got = mod.svsa_attn_workspace_bytes(B, H, geo)
+        assert got >= need, (geo, got, need)
