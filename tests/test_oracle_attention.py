@@ -116,3 +116,26 @@ def test_kept_flops_counts_valid_tokens_only():
     rp = np.array([0, 1, 2, 3, 4, 5, 7]); ci = np.array([0, 1, 2, 3, 4, 0, 5], np.int32)
     # rows 0..4: 16*16 each; row 5 (tail, 10 valid): 10*16 + 10*10
     assert orc.kept_flops(rp, ci, N, Bk, D) == 4 * D * (5 * 256 + 160 + 100)
+
+
+def test_sparse_row_closed_form_two_kept_blocks_with_a_tail():
+    # Three blocks of two slots, N = 5 (block 2 holds one valid token and a
+    # padding slot).  Query block 1 keeps blocks 0 and 2; keys are equal within
+    # block 0, so with x_j = scale * q . k_j the weight of block 0 is the
+    # logistic sigma(x_0 - x_2 + ln 2) (two keys against one) and the output is
+    # that mix of block 0's mean value and block 2's one value.  Block 1 and the
+    # padding slot carry huge keys and values: any leak shows at once.
+    N, Bk, D, scale = 5, 2, 2, 0.7
+    qp = np.zeros((1, 1, 6, D)); kp = np.zeros_like(qp); vp = np.zeros_like(qp)
+    qp[0, 0, 2] = [1.0, 0.0]; qp[0, 0, 3] = [0.0, 1.0]           # query block 1
+    kp[0, 0, 0:2] = [0.4, -1.2]; vp[0, 0, 0] = [1.0, 0.0]; vp[0, 0, 1] = [3.0, 0.0]
+    kp[0, 0, 2:4] = 100.0; vp[0, 0, 2:4] = 1e3                     # block 1: not kept
+    kp[0, 0, 4] = [-0.3, 0.9]; vp[0, 0, 4] = [0.0, 5.0]           # block 2, valid
+    kp[0, 0, 5] = 50.0; vp[0, 0, 5] = 1e3                          # block 2, padding
+    for cols in ([0, 2], [2, 0]):
+        out = orc.attention_rows(qp, kp, vp, 0, 0, 1, cols, N, Bk, scale)
+        for r, q in enumerate(([1.0, 0.0], [0.0, 1.0])):
+            x0 = scale * float(np.dot(q, [0.4, -1.2]))
+            x2 = scale * float(np.dot(q, [-0.3, 0.9]))
+            w0 = 1.0 / (1.0 + np.exp(-(x0 - x2 + np.log(2.0))))
+            np.testing.assert_allclose(out[r], [2.0 * w0, 5.0 * (1.0 - w0)], rtol=1e-13)

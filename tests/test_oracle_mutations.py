@@ -104,6 +104,10 @@ def _attention_rows_v_is_k(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None)
     return _orig_rows(qp, kp, kp, b, h, i, cols, N, Bk, scale, counts)
 
 
+
+def _attention_rows_no_scale(qp, kp, vp, b, h, i, cols, N, Bk, scale, counts=None):
+    return _orig_rows(qp, kp, vp, b, h, i, cols, N, Bk, 1.0, counts)
+
 _orig_rows = orc.attention_rows
 
 
@@ -297,6 +301,10 @@ MUTATIONS = [
     ("select_row", _select_fixed_variant(nearest),
      ts.test_fixed_fraction_count_uses_the_float32_fraction, ()),
     ("attention_rows", _attention_rows_with_pads, ta.test_padded_keys_are_excluded, ()),
+    ("attention_rows", _attention_rows_with_pads,
+     ta.test_sparse_row_closed_form_two_kept_blocks_with_a_tail, ()),
+    ("attention_rows", _attention_rows_no_scale,
+     ta.test_sparse_row_closed_form_two_kept_blocks_with_a_tail, ()),
     ("attention_rows", _attention_rows_v_is_k, ta.test_all_blocks_kept_equals_dense_sdpa,
      ("grid_tile",)),
     ("_band_cond", _band_wider, tst.test_stripe_svg_special_case_is_a_plain_window, ()),
